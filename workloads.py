@@ -1,0 +1,232 @@
+"""Seeded synthetic inputs for the batched speculative-verify causal conv1d update.
+
+This module is shared by the CPU oracle's tests, the GPU parity tests and the
+benchmark. It holds shapes, seeds and random draws only: none of the method's
+arithmetic lives here (no convolution, activation, normalisation or window
+logic), so the oracle and the HIP path stay independent of each other.
+
+Workloads (sizes and value distributions follow the pages' workloads):
+
+* ``tiny_fp32_dense``      - n_seq 1, d_inner 512 (q|k 256 in two heads of 128), T 2,
+                             fp32 everywhere, dense windows, bias on.
+* ``gdn_k17_dense``        - n_seq 8, d_inner 8192 (q|k 4096), T 17 draft tokens
+                             (the K=17 verify of the Atlas fused batched verify doc),
+                             bf16, dense windows, no bias.
+* ``dedup_bs128_t8``       - n_seq 128, d_inner 10240 (q|k 4096), T 8, bf16, dedup rows,
+                             bias on (the GB300 workload of sglang PR 46184, "Motivation"
+                             and "Benchmarking and Profiling").
+* ``kda_t1_f32state``      - n_seq 256, d_inner 12288 (q|k|v = 3 x 32 heads x 128), T 1,
+                             bf16 activations with an fp32 conv_state (Atlas KDA block,
+                             ``KdaSeqState``), dense windows, no bias.
+* ``stress_dedup_t16``     - n_seq 512, d_inner 10240, T 16, bf16, dedup rows, bias on,
+                             per-row num_accept_tokens ~ U{0..T-1}, ~10% padded rows,
+                             state_len = T + 2.  Pass ``b`` trims d_inner to 10200.
+
+Distributions: state ~ N(0,1), x ~ N(0,1), weight ~ U(-0.5,0.5), bias ~ U(-0.5,0.5),
+drawn as float32 from ``numpy.random.Generator(PCG64(seed))`` in exactly that order,
+then rounded to the storage dtype (round-to-nearest-even for bf16).  bf16 arrays are
+carried as ``numpy.uint16`` bit patterns, fp32 arrays as ``numpy.float32``.
+"""
+
+from __future__ import annotations
+
+import dataclasses
+from typing import Optional
+
+import numpy as np
+
+BASE_SEED = 20261202
+L2_EPS = 1e-6
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    name: str
+    n_seq: int
+    d_inner: int
+    qk_channels: int
+    head_dim: int
+    d_conv: int
+    T: int
+    x_dtype: str          # "f32" | "bf16" : x, weight, bias, out
+    state_dtype: str      # "f32" | "bf16" : conv_state and rollback windows
+    layout: str           # "dense" | "dedup"
+    bias: bool
+    state_len: int        # columns per state channel (>= d_conv - 1)
+    seed: int
+    accept_offsets: bool = False   # num_accept_tokens ~ U{0..T-1}
+    pad_frac: float = 0.0          # Bernoulli probability that a row is padded (slot -1)
+    permute_slots: bool = False    # non-padded row i -> slot perm[i]
+    x_tok_stride: Optional[int] = None   # elements; None = d_inner (contiguous)
+    l2_eps: float = L2_EPS
+    dist: str = "normal"          # "normal": the distributions above; "dyadic": see below
+    extra_slots: int = 0          # pool slots no row references (must stay untouched)
+
+    @property
+    def win_cols(self) -> int:
+        return self.d_conv - 1
+
+    @property
+    def row_cols(self) -> int:
+        return self.T + self.d_conv - 2
+
+    @property
+    def n_slots(self) -> int:
+        return self.n_seq + self.extra_slots
+
+
+WORKLOADS = {
+    0: Workload("tiny_fp32_dense", 1, 512, 256, 128, 4, 2, "f32", "f32", "dense",
+                True, 3, BASE_SEED + 0),
+    1: Workload("gdn_k17_dense", 8, 8192, 4096, 128, 4, 17, "bf16", "bf16", "dense",
+                False, 3, BASE_SEED + 1),
+    2: Workload("dedup_bs128_t8", 128, 10240, 4096, 128, 4, 8, "bf16", "bf16", "dedup",
+                True, 3, BASE_SEED + 2),
+    3: Workload("kda_t1_f32state", 256, 12288, 8192, 128, 4, 1, "bf16", "f32", "dense",
+                False, 3, BASE_SEED + 3),
+    4: Workload("stress_dedup_t16", 512, 10240, 4096, 128, 4, 16, "bf16", "bf16", "dedup",
+                True, 18, BASE_SEED + 4, accept_offsets=True, pad_frac=0.1,
+                permute_slots=True),
+    "4b": Workload("stress_dedup_t16_d10200", 512, 10200, 4096, 128, 4, 16, "bf16", "bf16",
+                   "dedup", True, 18, BASE_SEED + 104, accept_offsets=True, pad_frac=0.1,
+                   permute_slots=True),
+    "4s": Workload("stress_dedup_t16_d10200_xstride10240", 512, 10200, 4096, 128, 4, 16,
+                   "bf16", "bf16", "dedup", True, 18, BASE_SEED + 104, accept_offsets=True,
+                   pad_frac=0.1, permute_slots=True, x_tok_stride=10240),
+}
+
+
+def f32_to_bf16_bits(a: np.ndarray) -> np.ndarray:
+    """Round float32 values to bf16 (nearest, ties to even); return uint16 bit patterns.
+
+    NaNs become the quiet NaN 0x7FC0 with their sign kept.  Input preparation only.
+    """
+    a = np.ascontiguousarray(a, dtype=np.float32)
+    u = a.view(np.uint32).astype(np.uint64)
+    lsb = (u >> 16) & 1
+    r = ((u + 0x7FFF + lsb) >> 16).astype(np.uint16)
+    nan = np.isnan(a)
+    if nan.any():
+        r[nan] = ((u[nan] >> 16) & 0x8000).astype(np.uint16) | 0x7FC0
+    return r
+
+
+def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    """Widen bf16 bit patterns to float32 (exact)."""
+    return (np.asarray(b, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+def to_storage(a: np.ndarray, dtype: str) -> np.ndarray:
+    if dtype == "f32":
+        return np.ascontiguousarray(a, dtype=np.float32)
+    if dtype == "bf16":
+        return f32_to_bf16_bits(a)
+    raise ValueError(dtype)
+
+
+def storage_np_dtype(dtype: str):
+    return np.float32 if dtype == "f32" else np.uint16
+
+
+@dataclasses.dataclass
+class Inputs:
+    """One seeded problem.  Arrays are host numpy arrays in storage dtype."""
+    wl: Workload
+    x: np.ndarray            # [n_seq, T, x_tok_stride] (first d_inner columns used)
+    weight: np.ndarray       # [d_inner, d_conv]
+    bias: Optional[np.ndarray]     # [d_inner] or None
+    conv_state: np.ndarray   # [n_slots, d_inner, state_len]
+    slot_idx: Optional[np.ndarray]   # int32 [n_seq] or None (identity)
+    num_accept_tokens: Optional[np.ndarray]  # int32 [n_seq] or None
+
+
+def make_inputs(wl: Workload, seed: Optional[int] = None) -> Inputs:
+    """Draw one problem in the fixed order state, x, weight, bias, offsets, pads, slots."""
+    rng = np.random.Generator(np.random.PCG64(wl.seed if seed is None else seed))
+    n, T, d, D = wl.n_seq, wl.T, wl.d_inner, wl.d_conv
+    xs = wl.x_tok_stride or d
+    if wl.dist == "normal":
+        state = rng.standard_normal((wl.n_slots, d, wl.state_len), dtype=np.float32)
+        x = rng.standard_normal((n, T, d), dtype=np.float32)
+        weight = rng.uniform(-0.5, 0.5, size=(d, D)).astype(np.float32)
+        bias = rng.uniform(-0.5, 0.5, size=(d,)).astype(np.float32) if wl.bias else None
+    elif wl.dist == "dyadic":
+        # activations in {k/8 : |k| <= 16}, weights and bias in {j/16 : |j| <= 8}: every
+        # product and every 4-term sum is exactly representable in fp32.
+        state = (rng.integers(-16, 17, size=(wl.n_slots, d, wl.state_len)) / 8).astype(np.float32)
+        x = (rng.integers(-16, 17, size=(n, T, d)) / 8).astype(np.float32)
+        weight = (rng.integers(-8, 9, size=(d, D)) / 16).astype(np.float32)
+        bias = (rng.integers(-8, 9, size=(d,)) / 16).astype(np.float32) if wl.bias else None
+    else:
+        raise ValueError(wl.dist)
+    nat = None
+    if wl.accept_offsets:
+        nat = rng.integers(0, T, size=n, dtype=np.int64).astype(np.int32)
+    slot = None
+    if wl.pad_frac > 0 or wl.permute_slots:
+        pad = rng.random(n) < wl.pad_frac if wl.pad_frac > 0 else np.zeros(n, dtype=bool)
+        perm = rng.permutation(wl.n_slots).astype(np.int32) if wl.permute_slots \
+            else np.arange(n, dtype=np.int32)
+        slot = np.where(pad, np.int32(-1), perm[:n]).astype(np.int32)
+    x_st = to_storage(x, wl.x_dtype)
+    if xs != d:
+        pad_val = 0x7FBF if wl.x_dtype == "bf16" else np.float32(np.nan)
+        xfull = np.full((n, T, xs), pad_val, dtype=storage_np_dtype(wl.x_dtype))
+        xfull[:, :, :d] = x_st
+        x_st = xfull
+    return Inputs(
+        wl=wl,
+        x=x_st,
+        weight=to_storage(weight, wl.x_dtype),
+        bias=None if bias is None else to_storage(bias, wl.x_dtype),
+        conv_state=to_storage(state, wl.state_dtype),
+        slot_idx=slot,
+        num_accept_tokens=nat,
+    )
+
+
+def custom(name="custom", *, n_seq=2, d_inner=256, qk_channels=128, head_dim=64, d_conv=4,
+           T=3, x_dtype="bf16", state_dtype="bf16", layout="dense", bias=True,
+           state_len=None, seed=BASE_SEED + 1000, **kw) -> Workload:
+    """A small problem of any shape, drawn by the same seeded generator."""
+    if state_len is None:
+        state_len = d_conv - 1 + ((T - 1) if kw.get("accept_offsets") else 0)
+    return Workload(name, n_seq, d_inner, qk_channels, head_dim, d_conv, T, x_dtype,
+                    state_dtype, layout, bias, state_len, seed, **kw)
+
+
+def poison_like_windows(wl: Workload) -> np.ndarray:
+    """A poison-filled rollback-window buffer (dense or dedup layout) for wl.
+
+    Poison is a NaN bit pattern that no input draw produces, so any element the call
+    fails to write (or writes when it must not) is visible bit-for-bit.
+    """
+    if wl.layout == "dense":
+        shape = (wl.n_slots, wl.T, wl.d_inner, wl.win_cols)
+    else:
+        shape = (wl.n_slots, wl.d_inner, wl.row_cols)
+    return poison(shape, wl.state_dtype)
+
+
+def poison(shape, dtype: str) -> np.ndarray:
+    if dtype == "bf16":
+        return np.full(shape, 0x7FBF, dtype=np.uint16)
+    return np.full(shape, 0x7FBFDEAD, dtype=np.uint32).view(np.float32)
+
+
+def algorithmic_bytes(wl: Workload, inputs: Optional[Inputs] = None) -> int:
+    """Bytes one launch must move, counting active (non-padded) rows only.
+
+    x + out + conv_state window read (d_conv-1 columns) + committed window write
+    (d_conv-1 columns) + rollback windows (dense: T*(d_conv-1), dedup: T+d_conv-2 per
+    channel) + weight + bias (once).
+    """
+    xb = 4 if wl.x_dtype == "f32" else 2
+    sb = 4 if wl.state_dtype == "f32" else 2
+    active = wl.n_seq
+    if inputs is not None and inputs.slot_idx is not None:
+        active = int((inputs.slot_idx >= 0).sum())
+    win = wl.T * wl.win_cols if wl.layout == "dense" else wl.row_cols
+    per_chan = 2 * wl.T * xb + 2 * wl.win_cols * sb + win * sb
+    once = wl.d_inner * wl.d_conv * xb + (wl.d_inner * xb if wl.bias else 0)
+    return active * wl.d_inner * per_chan + once
