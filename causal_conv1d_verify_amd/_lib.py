@@ -1,0 +1,84 @@
+"""ctypes view of libconvverify.so (the C ABI declared in include/conv_verify.h)."""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libconvverify.so")
+
+CV_F32 = 0
+CV_BF16 = 1
+CV_OK = 0
+CV_EINVAL = -22
+CV_ENOTSUP = -95
+CV_EHIP_BASE = -1000
+
+EXPORTS = (
+    "conv_verify_update_dense",
+    "conv_verify_update_dedup",
+    "conv_verify_describe",
+    "conv_verify_strerror",
+    "conv_verify_last_error",
+    "conv_verify_abi_version",
+)
+
+
+class CvShape(ctypes.Structure):
+    _fields_ = [
+        ("n_seq", ctypes.c_int32), ("T", ctypes.c_int32),
+        ("d_inner", ctypes.c_int32), ("d_conv", ctypes.c_int32),
+        ("qk_channels", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+        ("l2_eps", ctypes.c_float),
+        ("x_dtype", ctypes.c_int32), ("state_dtype", ctypes.c_int32),
+        ("n_slots", ctypes.c_int32), ("state_len", ctypes.c_int32),
+        ("x_seq_stride", ctypes.c_int64), ("x_tok_stride", ctypes.c_int64),
+        ("out_seq_stride", ctypes.c_int64), ("out_tok_stride", ctypes.c_int64),
+        ("state_slot_stride", ctypes.c_int64),
+        ("win_slot_stride", ctypes.c_int64),
+    ]
+
+
+class CvLaunchInfo(ctypes.Structure):
+    _fields_ = [
+        ("workgroups", ctypes.c_int64), ("threads", ctypes.c_int32),
+        ("channel_blocks", ctypes.c_int32), ("channels_per_wave", ctypes.c_int32),
+        ("channels_per_lane", ctypes.c_int32), ("token_bucket", ctypes.c_int32),
+        ("lds_bytes", ctypes.c_int32), ("head_lanes", ctypes.c_int32),
+    ]
+
+
+_lib = None
+
+
+def load() -> ctypes.CDLL:
+    """Load the HIP library.  Raises if it has not been built: there is no fallback."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is missing: build it with `python -m causal_conv1d_verify_amd.build` "
+            "(or __graft_entry__.build()); the verify conv has no non-HIP implementation")
+    lib = ctypes.CDLL(LIB_PATH)
+    upd = [ctypes.POINTER(CvShape)] + [ctypes.c_void_p] * 9
+    for name in ("conv_verify_update_dense", "conv_verify_update_dedup"):
+        fn = getattr(lib, name)
+        fn.restype = ctypes.c_int
+        fn.argtypes = upd
+    lib.conv_verify_describe.restype = ctypes.c_int
+    lib.conv_verify_describe.argtypes = [ctypes.c_int, ctypes.POINTER(CvShape),
+                                         ctypes.POINTER(CvLaunchInfo)]
+    lib.conv_verify_strerror.restype = ctypes.c_char_p
+    lib.conv_verify_strerror.argtypes = [ctypes.c_int]
+    lib.conv_verify_last_error.restype = ctypes.c_char_p
+    lib.conv_verify_last_error.argtypes = []
+    lib.conv_verify_abi_version.restype = ctypes.c_int
+    lib.conv_verify_abi_version.argtypes = []
+    _lib = lib
+    return lib
+
+
+def error_message(lib, code: int) -> str:
+    detail = lib.conv_verify_last_error().decode()
+    return f"{lib.conv_verify_strerror(code).decode()} ({code}): {detail}"

@@ -1,0 +1,71 @@
+"""Builds libconvverify.so (HIP kernels for gfx950 + the C ABI) in-tree with hipcc.
+
+Usage: python -m causal_conv1d_verify_amd.build   (or __graft_entry__.build())
+"""
+
+from __future__ import annotations
+
+import os
+import subprocess
+import sys
+import time
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+BUILD = os.path.join(ROOT, "_build")
+LIB = os.path.join(PKG, "libconvverify.so")
+
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+ARCH = "gfx950"
+
+# Packed fp32 instructions are kept out of every kernel: hipcc would otherwise form
+# v_pk_{add,mul,fma}_f32 from ordinary float code.
+DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wextra", "-Wno-unused-parameter",
+          f"-I{INCLUDE}", f"-I{CSRC}"]
+
+SOURCES = [
+    ("cv_kernels.hip", [f"--offload-arch={ARCH}", *DEVICE_FLAGS]),
+    ("cv_api.cpp", []),
+]
+
+
+def _run(cmd):
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"build step failed ({res.returncode}):\n{' '.join(cmd)}\n"
+                           f"{res.stdout}\n{res.stderr}")
+    return res
+
+
+def build(verbose: bool = True) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    objs = []
+    procs = []
+    t0 = time.time()
+    for src, extra in SOURCES:
+        obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
+        cmd = [HIPCC, *COMMON, *extra, "-c", os.path.join(CSRC, src), "-o", obj]
+        procs.append((cmd, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.PIPE,
+                                            text=True)))
+        objs.append(obj)
+    for cmd, p in procs:
+        out, err = p.communicate()
+        if p.returncode != 0:
+            raise RuntimeError(f"build step failed ({p.returncode}):\n{' '.join(cmd)}\n{out}\n{err}")
+        noise = [ln for ln in err.splitlines()
+                 if ln.strip() and "packed-fp32-ops' is not a recognized feature" not in ln]
+        if verbose and noise:
+            print("\n".join(noise), file=sys.stderr)
+    tmp = LIB + ".tmp"
+    _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp])
+    os.replace(tmp, LIB)
+    if verbose:
+        print(f"built {LIB} in {time.time() - t0:.1f}s", file=sys.stderr)
+    return LIB
+
+
+if __name__ == "__main__":
+    build()

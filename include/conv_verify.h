@@ -1,0 +1,174 @@
+/*
+ * conv_verify.h - C ABI of the batched speculative-verify causal conv1d update,
+ * hand-written HIP kernels for AMD Instinct MI355X (gfx950).
+ *
+ * One call = one kernel launch that, for every row i < n_seq of a batch of
+ * speculative-decode chains and every draft position t < T, computes
+ *
+ *   pre[i,t,c] = bias[c] + sum_{w < D} weight[c,w] * v[t+w]       (depthwise, causal)
+ *   y          = SiLU(pre) = pre / (1 + exp(-pre))
+ *   y          = y / sqrt(sum_{c' in head(c)} y[c']^2 + l2_eps)   for c < qk_channels
+ *   out[i,t,c] = y rounded once (nearest even) to the x dtype
+ *
+ * over the sequence v = [conv_state[s, c, a .. a+D-2], x[i,0,c], ..., x[i,T-1,c]]
+ * with s = slot_idx[i] and a = num_accept_tokens[i], writes every per-token
+ * rollback window (the window after consuming x_t is v[t+1 .. t+D-1]) and leaves
+ * conv_state[s, c, 0 .. D-2] holding the committed window v[T .. T+D-2].
+ *
+ * Sources (page title, section):
+ *  - Atlas docs, fn spark_model::layers::ops::gdn_verify_fused_conv_kn_batched:
+ *    all K draft positions in one launch, every per-token rollback snapshot written
+ *    inline to a strided intermediates array, conv_state left holding the committed
+ *    window (also snapshot K-1), per-token and per-sequence strides, one launch over
+ *    n_seq sequences whose windows are independent.
+ *  - sglang PR 46184 (dedup conv window tile store), "Motivation" and
+ *    "Modifications": the deduplicated per-slot row [dim, T+K-2] viewed as an
+ *    overlapping [T, dim, K-1] window with step stride == window stride, written
+ *    once instead of per token; padded rows exit before any store; a
+ *    num_accept_tokens state offset.  "Scope": dense [T, dim, K-1] windows.
+ *  - Atlas glm5next_kda/mod.rs, Glm5NextKdaConfig: conv -> SiLU -> L2 on q|k only,
+ *    FLA convention 1/sqrt(sum + eps), V never normalised, qk_channels = 2*heads*hd.
+ *
+ * Conventions shared by both entry points
+ * ---------------------------------------
+ *  - Every data pointer is a DEVICE pointer (HBM of the GPU current on the calling
+ *    thread); only `shape` is a host pointer.  The caller owns every buffer.  The
+ *    library allocates nothing, keeps no pointer after returning, performs no
+ *    host<->device copy and never synchronizes: the call enqueues exactly one kernel
+ *    on `hip_stream` (a hipStream_t; NULL = the null stream) and returns.
+ *  - Thread-safe and stateless (apart from a thread-local error detail string).
+ *  - All validation happens on the host before any HIP call; a call that returns an
+ *    error has launched nothing and written nothing.  Faults inside the kernel can
+ *    only surface at the caller's next synchronization of the stream.
+ *  - Element layouts (strides in ELEMENTS, innermost dimension contiguous):
+ *      x           [n_seq, T, d_inner]     x[i,t,c]   = x   + i*x_seq_stride   + t*x_tok_stride   + c
+ *      out         [n_seq, T, d_inner]     out[i,t,c] = out + i*out_seq_stride + t*out_tok_stride + c
+ *      weight      [d_inner, d_conv]       contiguous; weight[c, d_conv-1] multiplies x_t
+ *      bias        [d_inner]               contiguous, or NULL (no bias)
+ *      conv_state  [n_slots, d_inner, state_len]
+ *                  state[s,c,k] = conv_state + s*state_slot_stride + c*state_len + k
+ *      slot_idx    [n_seq] int32 or NULL (row i uses slot i).  -1 marks a padded row.
+ *      num_accept_tokens [n_seq] int32 or NULL (all 0): start column a of row i's window.
+ *  - A padded row (slot -1) writes nothing at all: not out, not conv_state, not the
+ *    windows.  Slots no row references are never touched.
+ *  - Device-side preconditions (not checked on the host, which never reads device
+ *    memory): the slots of non-padded rows are distinct; 0 <= a <= state_len-(d_conv-1).
+ *    A row whose slot is >= n_slots or < -1, or whose a is out of that range, is
+ *    skipped like a padded row (nothing written), so bad indices never address
+ *    memory outside the buffers.  Two rows sharing a slot race.
+ *  - Buffers must not overlap each other (x and weight/bias may).
+ *  - Alignment (else CV_ENOTSUP): every pointer 16-byte aligned; d_inner, the x/out
+ *    strides and head_dim multiples of 16/sizeof(x element) (8 for bf16, 4 for fp32);
+ *    state_slot_stride and win_slot_stride multiples of 16 bytes.
+ *  - Numerics: the conv accumulates in fp32 as acc = bias (or +0); for w = 0..D-1:
+ *    acc = fma(weight[c,w], v[t+w], acc), each step one correctly rounded fused
+ *    multiply-add.  SiLU and L2 run in fp32.  Windows and conv_state are moved as bit
+ *    patterns (bf16 -> fp32 widening is exact), so -0.0, subnormals and NaN payloads
+ *    survive.
+ */
+#ifndef CONV_VERIFY_H
+#define CONV_VERIFY_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define CONV_VERIFY_ABI_VERSION 1
+
+/* Element types. */
+typedef enum cv_dtype { CV_F32 = 0, CV_BF16 = 1 } cv_dtype_t;
+
+/* Return codes. */
+#define CV_OK 0
+#define CV_EINVAL (-22)      /* malformed arguments: NULL pointer, bad size or stride */
+#define CV_ENOTSUP (-95)     /* well-formed but outside what the kernels implement */
+#define CV_EHIP_BASE (-1000) /* launch failure: returns CV_EHIP_BASE - (int)hipError_t */
+
+/* Problem description (host memory, read during the call only). */
+typedef struct cv_shape {
+    int32_t n_seq;        /* rows in the batch, >= 0 (0: nothing to do, returns CV_OK)      */
+    int32_t T;            /* draft positions per row, 1..32                                 */
+    int32_t d_inner;      /* channels, >= 0 (0: nothing to do)                              */
+    int32_t d_conv;       /* conv width D, 2..4                                             */
+    int32_t qk_channels;  /* leading channels normalised per head, 0..d_inner; 0 = no L2    */
+    int32_t head_dim;     /* channels per L2 head: qk_channels % head_dim == 0 and
+                             head_dim / (16/sizeof(x element)) a power of two <= 64         */
+    float l2_eps;         /* >= 0 and finite                                                */
+    int32_t x_dtype;      /* cv_dtype_t of x, weight, bias and out                          */
+    int32_t state_dtype;  /* cv_dtype_t of conv_state and the windows.  Supported pairs
+                             (x, state): (F32, F32), (BF16, BF16), (BF16, F32)              */
+    int32_t n_slots;      /* slots in the conv_state pool and in the window buffer, >= 0;
+                             >= n_seq when slot_idx is NULL                                 */
+    int32_t state_len;    /* columns per state channel, >= d_conv-1                         */
+    int64_t x_seq_stride, x_tok_stride;      /* elements, >= 0                              */
+    int64_t out_seq_stride, out_tok_stride;  /* elements; rows/tokens of out must not overlap */
+    int64_t state_slot_stride;               /* elements, >= d_inner*state_len if n_slots>1 */
+    int64_t win_slot_stride;                 /* elements of the window buffer per slot,
+                                                >= its per-slot size if n_slots > 1         */
+} cv_shape_t;
+
+/*
+ * Dense rollback windows (sglang PR 46184, "Scope": UnifiedMambaPool, KDA/Kimi-Linear;
+ * Atlas gdn_verify_fused_conv_kn_batched's conv_state_inter).
+ *
+ *   snapshots [n_slots, T, d_inner, d_conv-1]:
+ *     snapshots[s,t,c,j] = snapshots + s*win_slot_stride + (t*d_inner + c)*(d_conv-1) + j
+ *                        = v[t+1+j]   (the window after consuming x_t; t = T-1 is the
+ *                                      committed window)
+ *
+ * Returns CV_OK after enqueueing the launch, or an error code (nothing launched).
+ */
+int conv_verify_update_dense(const cv_shape_t *shape, const void *x, const void *weight,
+                             const void *bias, void *conv_state, const int32_t *slot_idx,
+                             const int32_t *num_accept_tokens, void *out, void *snapshots,
+                             void *hip_stream);
+
+/*
+ * Deduplicated rollback windows (sglang PR 46184, "Motivation", "Modifications":
+ * MambaPool's one row per slot, written once).
+ *
+ *   window_rows [n_slots, d_inner, T+d_conv-2]:
+ *     rows[s,c,k] = window_rows + s*win_slot_stride + c*(T+d_conv-2) + k  = v[k+1]
+ *   so the window after consuming x_t is columns t .. t+d_conv-2 of the row: the
+ *   overlapping [T, d_inner, d_conv-1] view with step stride == window stride.
+ *
+ * Returns CV_OK after enqueueing the launch, or an error code (nothing launched).
+ */
+int conv_verify_update_dedup(const cv_shape_t *shape, const void *x, const void *weight,
+                             const void *bias, void *conv_state, const int32_t *slot_idx,
+                             const int32_t *num_accept_tokens, void *out, void *window_rows,
+                             void *hip_stream);
+
+/* Launch geometry the library would use for a shape (validation of the shape only;
+ * pointers are not examined).  Lets a caller or a test check, on the host, what the
+ * kernel and its grid will assume. */
+typedef struct cv_launch_info {
+    int64_t workgroups;        /* 1-D grid: n_seq * channel_blocks                        */
+    int32_t threads;           /* per workgroup: one 64-lane wavefront                     */
+    int32_t channel_blocks;    /* ceil(d_inner / channels_per_wave)                        */
+    int32_t channels_per_wave; /* 64 lanes * channels per lane                             */
+    int32_t channels_per_lane; /* 16 bytes of x per lane per token                         */
+    int32_t token_bucket;      /* compile-time token capacity of the chosen kernel (>= T)  */
+    int32_t lds_bytes;         /* dynamic LDS per workgroup                                */
+    int32_t head_lanes;        /* lanes per L2 head (0 when qk_channels == 0)              */
+} cv_launch_info_t;
+
+/* dedup: 0 = dense snapshots, 1 = deduplicated rows.  Returns CV_OK or an error code. */
+int conv_verify_describe(int dedup, const cv_shape_t *shape, cv_launch_info_t *info);
+
+/* Static description of an error code (never NULL). */
+const char *conv_verify_strerror(int code);
+
+/* Detail of the last error returned on the calling thread (empty string if none). */
+const char *conv_verify_last_error(void);
+
+/* CONV_VERIFY_ABI_VERSION of the loaded library. */
+int conv_verify_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CONV_VERIFY_H */

@@ -1,0 +1,234 @@
+"""Host-side tests of the C ABI: exports, validation, launch geometry.  No GPU needed.
+
+Nothing here launches a kernel.  Shape validation goes through conv_verify_describe
+(no pointers at all); the pointer checks of the update entry points run in a child
+process that sees no GPU, so even a validation bug could not turn a fake pointer into
+a launch.
+"""
+
+import ctypes
+import json
+import os
+import re
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "conv_verify.h")
+
+lib_mod = pytest.importorskip("causal_conv1d_verify_amd._lib")
+
+
+def _lib():
+    if not os.path.exists(lib_mod.LIB_PATH):
+        pytest.skip("libconvverify.so not built (run __graft_entry__.build())")
+    return lib_mod.load()
+
+
+def _header_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(conv_verify_\w+)\s*\(", text,
+                                 re.M)))
+
+
+def test_header_and_binding_agree():
+    assert _header_functions() == sorted(lib_mod.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    _lib()
+    res = subprocess.run(["nm", "-D", "--defined-only", lib_mod.LIB_PATH], capture_output=True,
+                         text=True, check=True)
+    exported = set(re.findall(r"\bT (\w+)$", res.stdout, re.M))
+    for name in _header_functions():
+        assert name in exported, f"{name} declared in conv_verify.h but not exported"
+    assert not any(n.startswith("orc_") for n in exported), "oracle code linked into the library"
+
+
+def test_abi_version_matches_header():
+    lib = _lib()
+    want = int(re.search(r"#define CONV_VERIFY_ABI_VERSION (\d+)", open(HEADER).read()).group(1))
+    assert lib.conv_verify_abi_version() == want
+
+
+def test_shape_struct_layout():
+    # offsets of the int64 strides must match the C struct (4-byte fields then 8-aligned)
+    assert lib_mod.CvShape.x_seq_stride.offset == 48
+    assert ctypes.sizeof(lib_mod.CvShape) == 96
+    assert ctypes.sizeof(lib_mod.CvLaunchInfo) == 40
+
+
+def shape(**kw):
+    d = dict(n_seq=4, T=8, d_inner=1024, d_conv=4, qk_channels=512, head_dim=128, l2_eps=1e-6,
+             x_dtype=lib_mod.CV_BF16, state_dtype=lib_mod.CV_BF16, n_slots=4, state_len=3,
+             x_seq_stride=8 * 1024, x_tok_stride=1024, out_seq_stride=8 * 1024,
+             out_tok_stride=1024, state_slot_stride=1024 * 3, win_slot_stride=8 * 1024 * 3)
+    d.update(kw)
+    return lib_mod.CvShape(**d)
+
+
+def describe(dedup, s):
+    lib = _lib()
+    info = lib_mod.CvLaunchInfo()
+    rc = lib.conv_verify_describe(dedup, ctypes.byref(s), ctypes.byref(info))
+    return rc, info, lib.conv_verify_last_error().decode()
+
+
+EINVAL, ENOTSUP = lib_mod.CV_EINVAL, lib_mod.CV_ENOTSUP
+BAD_SHAPES = [
+    ("n_seq<0", dict(n_seq=-1), EINVAL),
+    ("T=0", dict(T=0), EINVAL),
+    ("T=33", dict(T=33), ENOTSUP),
+    ("d_inner<0", dict(d_inner=-8), EINVAL),
+    ("d_conv=0", dict(d_conv=0), EINVAL),
+    ("d_conv=1", dict(d_conv=1), ENOTSUP),
+    ("d_conv=5", dict(d_conv=5), ENOTSUP),
+    ("dtype=7", dict(x_dtype=7), EINVAL),
+    ("f32x_bf16state", dict(x_dtype=lib_mod.CV_F32), ENOTSUP),
+    ("d_inner%8", dict(d_inner=1020, qk_channels=0), ENOTSUP),
+    ("qk>d", dict(qk_channels=2048), EINVAL),
+    ("qk<0", dict(qk_channels=-128), EINVAL),
+    ("qk%head", dict(qk_channels=520, head_dim=128), EINVAL),
+    ("head<=0", dict(head_dim=0), EINVAL),
+    ("head%8", dict(qk_channels=12 * 20, head_dim=12), ENOTSUP),
+    ("head_lanes_not_pow2", dict(qk_channels=96 * 5, head_dim=96), ENOTSUP),
+    ("head_lanes>64", dict(qk_channels=1024, head_dim=1024), ENOTSUP),
+    ("eps<0", dict(l2_eps=-1.0), EINVAL),
+    ("eps_nan", dict(l2_eps=float("nan")), EINVAL),
+    ("eps_inf", dict(l2_eps=float("inf")), EINVAL),
+    ("n_slots<0", dict(n_slots=-1), EINVAL),
+    ("state_len<D-1", dict(state_len=2), EINVAL),
+    ("neg_stride", dict(x_tok_stride=-1024), EINVAL),
+    ("out_tok_overlap", dict(out_tok_stride=512), EINVAL),
+    ("out_seq_overlap", dict(out_seq_stride=4 * 1024), EINVAL),
+    ("state_slot_overlap", dict(state_slot_stride=1024), EINVAL),
+    ("x_stride%8", dict(x_tok_stride=1028, x_seq_stride=8 * 1028), ENOTSUP),
+    ("state_slot_unaligned", dict(state_slot_stride=3 * 1024 + 4), ENOTSUP),
+]
+
+
+@pytest.mark.parametrize("name,kw,code", BAD_SHAPES, ids=[b[0] for b in BAD_SHAPES])
+def test_describe_rejects(name, kw, code):
+    rc, _, detail = describe(0, shape(**kw))
+    assert rc == code, (rc, detail)
+    assert detail, "error detail missing"
+
+
+def test_window_stride_checked_per_layout():
+    # dense per slot = T*d*(D-1) = 24576; dedup per slot = d*(T+D-2) = 10240
+    assert describe(0, shape(win_slot_stride=10240))[0] == EINVAL
+    assert describe(1, shape(win_slot_stride=10240))[0] == 0
+
+
+def test_dedup_lds_limit():
+    # bf16 x with fp32 state, T=32: 34 rows of 512 fp32 + pad = 70176 bytes > 64 KiB
+    rc, _, detail = describe(1, shape(T=32, state_dtype=lib_mod.CV_F32, x_seq_stride=32 * 1024,
+                                      out_seq_stride=32 * 1024, win_slot_stride=1024 * 34))
+    assert rc == ENOTSUP and "LDS" in detail
+
+
+@pytest.mark.parametrize("key", [0, 1, 2, 3, 4, "4b", "4s"])
+def test_launch_geometry_of_workloads(key):
+    import workloads
+
+    wl = workloads.WORKLOADS[key]
+    xb = 4 if wl.x_dtype == "f32" else 2
+    sb = 4 if wl.state_dtype == "f32" else 2
+    xs = wl.x_tok_stride or wl.d_inner
+    win = wl.row_cols * wl.d_inner if wl.layout == "dedup" else wl.T * wl.d_inner * wl.win_cols
+    s = shape(n_seq=wl.n_seq, T=wl.T, d_inner=wl.d_inner, d_conv=wl.d_conv,
+              qk_channels=wl.qk_channels, head_dim=wl.head_dim,
+              x_dtype=lib_mod.CV_F32 if xb == 4 else lib_mod.CV_BF16,
+              state_dtype=lib_mod.CV_F32 if sb == 4 else lib_mod.CV_BF16, n_slots=wl.n_slots,
+              state_len=wl.state_len, x_seq_stride=wl.T * xs, x_tok_stride=xs,
+              out_seq_stride=wl.T * xs, out_tok_stride=xs,
+              state_slot_stride=wl.d_inner * wl.state_len, win_slot_stride=win)
+    rc, info, detail = describe(int(wl.layout == "dedup"), s)
+    assert rc == 0, detail
+    cpl = 16 // xb
+    assert info.channels_per_lane == cpl and info.threads == 64
+    assert info.channels_per_wave == 64 * cpl
+    assert info.channel_blocks == -(-wl.d_inner // (64 * cpl))
+    # the grid covers every (row, channel block) exactly once
+    assert info.workgroups == wl.n_seq * info.channel_blocks
+    assert info.channel_blocks * info.channels_per_wave >= wl.d_inner
+    assert (info.channel_blocks - 1) * info.channels_per_wave < wl.d_inner
+    assert info.token_bucket >= wl.T and info.token_bucket < 2 * wl.T + 1
+    assert info.head_lanes * cpl == wl.head_dim
+    if wl.layout == "dedup":
+        assert info.lds_bytes == wl.row_cols * (64 * cpl * sb + 16) <= 65536
+    else:
+        assert info.lds_bytes == 0
+
+
+_CHILD = r"""
+import ctypes, json, sys
+sys.path.insert(0, sys.argv[1])
+from causal_conv1d_verify_amd import _lib as L
+lib = L.load()
+def shape(**kw):
+    d = dict(n_seq=4, T=8, d_inner=1024, d_conv=4, qk_channels=512, head_dim=128, l2_eps=1e-6,
+             x_dtype=L.CV_BF16, state_dtype=L.CV_BF16, n_slots=4, state_len=3,
+             x_seq_stride=8192, x_tok_stride=1024, out_seq_stride=8192, out_tok_stride=1024,
+             state_slot_stride=3072, win_slot_stride=24576)
+    d.update(kw)
+    return L.CvShape(**d)
+A = 0x10000   # a 16-byte aligned stand-in address; never dereferenced on the host
+res = {}
+def call(name, dedup, s, ptrs):
+    fn = lib.conv_verify_update_dedup if dedup else lib.conv_verify_update_dense
+    rc = fn(ctypes.byref(s), *ptrs, None)
+    res[name] = [rc, lib.conv_verify_last_error().decode()]
+good = [A, A, None, A, None, None, A, A]
+res["null_shape"] = [lib.conv_verify_update_dense(None, *good, None), ""]
+call("null_x", 0, shape(), [None] + good[1:])
+call("null_weight", 0, shape(), [A, None] + good[2:])
+call("null_state", 1, shape(win_slot_stride=10240), [A, A, None, None, None, None, A, A])
+call("null_out", 0, shape(), [A, A, None, A, None, None, None, A])
+call("null_win", 1, shape(win_slot_stride=10240), [A, A, None, A, None, None, A, None])
+call("misaligned_x", 0, shape(), [A + 2] + good[1:])
+call("misaligned_bias", 0, shape(), [A, A, A + 8, A, None, None, A, A])
+call("misaligned_win", 0, shape(), good[:7] + [A + 4])
+call("identity_slots_short", 0, shape(n_slots=3), good)
+call("empty_batch_no_pointers", 0, shape(n_seq=0), [None] * 8)
+call("empty_channels_no_pointers", 1, shape(d_inner=0, qk_channels=0, win_slot_stride=0,
+                                            state_slot_stride=0), [None] * 8)
+print(json.dumps(res))
+"""
+
+
+def test_update_entry_points_validate_before_launch():
+    _lib()
+    env = dict(os.environ, HIP_VISIBLE_DEVICES="-1", ROCR_VISIBLE_DEVICES="-1",
+               CUDA_VISIBLE_DEVICES="-1")
+    out = subprocess.run([sys.executable, "-c", _CHILD, ROOT], capture_output=True, text=True,
+                         env=env, timeout=120)
+    assert out.returncode == 0, out.stderr
+    res = json.loads(out.stdout.strip().splitlines()[-1])
+    expect = {
+        "null_shape": EINVAL, "null_x": EINVAL, "null_weight": EINVAL, "null_state": EINVAL,
+        "null_out": EINVAL, "null_win": EINVAL, "misaligned_x": ENOTSUP,
+        "misaligned_bias": ENOTSUP, "misaligned_win": ENOTSUP,
+        "identity_slots_short": EINVAL, "empty_batch_no_pointers": 0,
+        "empty_channels_no_pointers": 0,
+    }
+    for k, code in expect.items():
+        assert res[k][0] == code, (k, res[k])
+
+
+def test_strerror_covers_codes():
+    lib = _lib()
+    for code in (0, EINVAL, ENOTSUP, lib_mod.CV_EHIP_BASE - 1, 12345):
+        assert lib.conv_verify_strerror(code)
+
+
+def test_product_never_touches_the_oracle():
+    pkg = os.path.join(ROOT, "causal_conv1d_verify_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".cpp", ".h")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert not re.search(r"^\s*(import|from)\s+oracle\b", text, re.M), f
+                assert "conv_verify_oracle" not in text and "liboracle" not in text, f
