@@ -90,6 +90,9 @@ def main(argv=None):
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-check", action="store_true", help="skip the full-size parity check")
     ap.add_argument("--sets", type=int, default=0, help="buffer sets (0: auto, >= 2x MALL)")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="run only a plain 256 MiB -> 256 MiB elementwise copy (10 dispatches), "
+                         "the reference for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE")
     args = ap.parse_args(argv)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -102,6 +105,17 @@ def main(argv=None):
 
     import causal_conv1d_verify_amd as cv
     import gpu_harness as gh
+
+    if args.calibrate_copy:
+        n = 64 * 2 ** 20   # fp32 elements: 256 MiB read + 256 MiB written per dispatch
+        src = torch.randn(n, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(10):
+            torch.mul(src, 1.0, out=dst)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibration": "elementwise copy", "read_bytes": 4 * n,
+                          "write_bytes": 4 * n, "dispatches": 10}), flush=True)
+        return 0
 
     key = int(args.workload) if args.workload.isdigit() else args.workload
     wl = workloads.WORKLOADS[key]

@@ -99,8 +99,6 @@ int plan_shape(int dedup, const cv_shape_t *s, cvimpl::Plan *plan) {
         return fail(CV_ENOTSUP, "x/out strides must be multiples of %d elements", cpl);
     if ((s->state_slot_stride * sb) % 16 || (s->win_slot_stride * sb) % 16)
         return fail(CV_ENOTSUP, "state/window slot strides must be multiples of 16 bytes");
-    if (C * s->state_len > INT32_MAX || (int64_t)s->T * C * W1 > INT64_MAX / 4)
-        return fail(CV_ENOTSUP, "d_inner*state_len exceeds 2^31");
 
     const int chw = kWave * cpl;
     const int64_t blocks = (C + chw - 1) / chw;
@@ -109,10 +107,28 @@ int plan_shape(int dedup, const cv_shape_t *s, cvimpl::Plan *plan) {
         return fail(CV_ENOTSUP, "grid of %lld workgroups exceeds the launch limit", (long long)wg);
     int tb = 1;
     while (tb < s->T) tb *= 2;
+    // LDS: the dedup tile (T+D-2 rows of one wavefront's channels) and, when state rows
+    // are wider than the window, the staged [channels, state_len] region; they are used
+    // one after the other and share the allocation.
     int64_t lds = 0;
     if (dedup) lds = (int64_t)(s->T + s->d_conv - 2) * cvimpl::tile_pitch(cpl, sb);
+    if (s->state_len > W1) {
+        const int64_t region = (int64_t)kWave * cpl * s->state_len * sb;
+        if (region > lds) lds = region;
+    }
     if (lds > kMaxLds)
-        return fail(CV_ENOTSUP, "dedup tile needs %lld bytes of LDS (> %d)", (long long)lds, kMaxLds);
+        return fail(CV_ENOTSUP, "kernel needs %lld bytes of LDS (> %d)", (long long)lds, kMaxLds);
+    // Buffer resources span one row's bytes with a 32-bit size; lanes past d_inner use
+    // the offset 2^31, so every span must stay below it.
+    const int64_t lim = ((int64_t)1 << 31) - 16;
+    const int64_t x_span = ((int64_t)(s->T - 1) * s->x_tok_stride + C) * xb;
+    const int64_t o_span = ((int64_t)(s->T - 1) * s->out_tok_stride + C) * xb;
+    const int64_t w_span = dedup ? C * (s->T + s->d_conv - 2) * sb : (int64_t)s->T * C * W1 * sb;
+    const int64_t st_span = C * s->state_len * sb;
+    if (x_span > lim || o_span > lim || w_span > lim || st_span > lim)
+        return fail(CV_ENOTSUP, "a row spans more than 2 GiB (x %lld, out %lld, windows %lld, "
+                                "state %lld bytes)", (long long)x_span, (long long)o_span,
+                    (long long)w_span, (long long)st_span);
 
     plan->dedup = dedup;
     plan->x_bytes = xb;

@@ -82,7 +82,7 @@ __device__ __forceinline__ float silu(float p) {
 
 template <int CTRL>
 __device__ __forceinline__ float dpp(float v) {
-    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, false));
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, true));
 }
 
 // Sum over the 2^hl_log2 lanes of an aligned lane group (all lanes active).  Each
@@ -99,6 +99,47 @@ __device__ __forceinline__ float group_sum(float v, int hl_log2) {
     return v;
 }
 
+// ---- raw buffer access ------------------------------------------------------------------
+//
+// Every global access goes through a buffer resource spanning exactly the bytes the
+// wavefront may touch.  The per-token offset lives in an SGPR (soffset), the per-lane
+// offset in a VGPR, so no 64-bit address arithmetic is repeated per token.  Lanes
+// past the end of d_inner use the lane offset 0x80000000, which the hardware range
+// check turns into a load of zeros / a dropped store.
+
+using rsrc_t = __amdgpu_buffer_rsrc_t;
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+constexpr uint32_t kOffLane = 0x80000000u;
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
+                                             0x00020000);
+}
+
+__device__ __forceinline__ void load16(rsrc_t r, uint32_t voff, uint32_t soff, uint32_t *d) {
+    const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0);
+    d[0] = v.x; d[1] = v.y; d[2] = v.z; d[3] = v.w;
+}
+
+__device__ __forceinline__ void store16(rsrc_t r, uint32_t voff, uint32_t soff, const uint32_t *s) {
+    const u32x4 v = {s[0], s[1], s[2], s[3]};
+    __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)voff, (int)soff, 0);
+}
+
+template <int EB>
+__device__ __forceinline__ uint32_t lds_get(const char *p) {
+    if constexpr (EB == 4) return *(const uint32_t *)p;
+    else return *(const uint16_t *)p;
+}
+
+template <int EB>
+__device__ __forceinline__ void lds_put(char *p, uint32_t v) {
+    if constexpr (EB == 4) *(uint32_t *)p = v;
+    else *(uint16_t *)p = (uint16_t)v;
+}
+
 // ---- the kernel -------------------------------------------------------------------------
 
 template <int XB, int SB, int D, int TB, bool DEDUP>
@@ -107,10 +148,12 @@ __global__ __launch_bounds__(kWave) void cv_verify_kernel(KernelArgs p) {
     constexpr int CHW = kWave * CPL;      // channels per wavefront
     constexpr int W1 = D - 1;             // window columns
     constexpr int SW = CPL * SB / 4;      // 32-bit words per state-typed column
-    constexpr int CHUNK_W = CPL * W1 * SB / 4;   // words of a lane's window run
-    static_assert(CHUNK_W % 4 == 0, "window runs are whole 16-byte units");
+    constexpr int RUNW = CPL * W1 * SB / 4;   // words of a lane's [ch][j] window run
+    constexpr int P = tile_pitch(CPL, SB);    // bytes per LDS tile row
+    static_assert(RUNW % 4 == 0 && SW % 4 == 0, "runs and columns are whole 16-byte units");
 
-    extern __shared__ uint4 lds_tile[];
+    extern __shared__ uint4 lds_raw[];
+    char *lds = (char *)lds_raw;
 
     const int lane = threadIdx.x;
     const int row = (int)(blockIdx.x / (unsigned)p.channel_blocks);
@@ -123,35 +166,36 @@ __global__ __launch_bounds__(kWave) void cv_verify_kernel(KernelArgs p) {
     if (slot < 0 || slot >= p.n_slots || a < 0 || a > p.state_len - W1) return;
 
     const int T = p.T;
-    const int c0 = cb + lane * CPL;
-    const bool on = c0 < p.d_inner;
+    const int SL = p.state_len;
+    const int nch = min(CHW, p.d_inner - cb);       // channels of this wavefront
+    const bool on = lane * CPL < nch;
+    const uint32_t lane16 = on ? (uint32_t)lane * 16u : kOffLane;
+    const uint32_t lane_run = on ? (uint32_t)lane * (RUNW * 4) : kOffLane;
+    const bool contiguous_state = SL == W1;
 
-    // ---- issue every global load up front --------------------------------------------
-    uint32_t X[TB][4];   // x_t for the lane's CPL channels (16 bytes each)
-    {
-        const char *xr = (const char *)p.x + ((int64_t)row * p.x_seq + c0) * XB;
+    // ---- loads: x (registers), window, weights, bias ----------------------------------
+    const rsrc_t x_r = make_rsrc((const char *)p.x + ((int64_t)row * p.x_seq + cb) * XB,
+                                 (uint32_t)(((int64_t)(T - 1) * p.x_tok + nch) * XB));
+    uint32_t X[TB][4];
 #pragma unroll
-        for (int t = 0; t < TB; ++t) {
-            uint4 v = make_uint4(0, 0, 0, 0);
-            if (t < T && on) v = *(const uint4 *)(xr + (int64_t)t * p.x_tok * XB);
-            X[t][0] = v.x; X[t][1] = v.y; X[t][2] = v.z; X[t][3] = v.w;
+    for (int t = 0; t < TB; ++t) {
+        if (t < T) {
+            load16(x_r, lane16, (uint32_t)(t * p.x_tok * XB), X[t]);
+        } else {
+            X[t][0] = X[t][1] = X[t][2] = X[t][3] = 0u;
         }
     }
 
-    char *srow = (char *)p.state + (int64_t)slot * p.state_slot * SB;
-    const bool contiguous_state = p.state_len == W1;
-    uint32_t S[W1 > 0 ? W1 : 1][SW];   // initial window columns v[0..W1-1]
+    const rsrc_t st_r = make_rsrc((const char *)p.state + ((int64_t)slot * p.state_slot +
+                                                           (int64_t)cb * SL) * SB,
+                                  (uint32_t)(nch * SL * SB));
+    uint32_t S[W1][SW];   // initial window columns v[0..W1-1], state-typed bits
     if (contiguous_state) {
-        uint32_t run[CHUNK_W];
+        uint32_t run[RUNW];
 #pragma unroll
-        for (int q = 0; q < CHUNK_W / 4; ++q) {
-            uint4 v = make_uint4(0, 0, 0, 0);
-            if (on) v = *(const uint4 *)(srow + (int64_t)c0 * W1 * SB + 16 * q);
-            run[4 * q] = v.x; run[4 * q + 1] = v.y; run[4 * q + 2] = v.z; run[4 * q + 3] = v.w;
-        }
-        // run holds [ch][j]; regroup into columns [j][ch]
+        for (int q = 0; q < RUNW / 4; ++q) load16(st_r, lane_run + 16 * q, 0, run + 4 * q);
 #pragma unroll
-        for (int j = 0; j < W1; ++j) {
+        for (int j = 0; j < W1; ++j)
 #pragma unroll
             for (int w = 0; w < SW; ++w) {
                 if constexpr (SB == 4) {
@@ -161,41 +205,51 @@ __global__ __launch_bounds__(kWave) void cv_verify_kernel(KernelArgs p) {
                               (elem_bits<2>(run, (2 * w + 1) * W1 + j) << 16);
                 }
             }
-        }
     } else {
-        const char *rec = srow + ((int64_t)c0 * p.state_len + a) * SB;
+        // Rows wider than the window (an accept offset): every sector of the row
+        // holds window bytes, so the wavefront's whole [nch, state_len] region is
+        // moved once, coalesced, through LDS - in directly, out after the commit.
+        const int rchunks = nch * SL * SB / 16;
+        for (int j = 0; j * kWave < rchunks; ++j) {
+            const int q = j * kWave + lane;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                st_r, (lds_void_t *)(lds + j * (kWave * 16)), 16,
+                q < rchunks ? q * 16 : (int)kOffLane, 0, 0, 0);
+        }
+        __syncthreads();
+        const char *rec = lds + (lane * CPL * SL + a) * SB;
 #pragma unroll
-        for (int j = 0; j < W1; ++j) {
+        for (int j = 0; j < W1; ++j)
 #pragma unroll
             for (int w = 0; w < SW; ++w) {
                 if constexpr (SB == 4) {
-                    S[j][w] = on ? *(const uint32_t *)(rec + ((int64_t)w * p.state_len + j) * 4) : 0u;
+                    S[j][w] = lds_get<4>(rec + (w * SL + j) * 4);
                 } else {
-                    uint32_t lo = on ? *(const uint16_t *)(rec + ((int64_t)(2 * w) * p.state_len + j) * 2) : 0u;
-                    uint32_t hi = on ? *(const uint16_t *)(rec + ((int64_t)(2 * w + 1) * p.state_len + j) * 2) : 0u;
-                    S[j][w] = lo | (hi << 16);
+                    S[j][w] = lds_get<2>(rec + ((2 * w) * SL + j) * 2) |
+                              (lds_get<2>(rec + ((2 * w + 1) * SL + j) * 2) << 16);
                 }
             }
-        }
     }
 
     float wv[CPL][D];
     float bv[CPL];
     {
-        uint32_t wr[CPL * D * XB / 4];
+        const rsrc_t w_r = make_rsrc((const char *)p.weight + (int64_t)cb * D * XB,
+                                     (uint32_t)(nch * D * XB));
+        uint32_t wr[4 * D];   // CPL*D*XB bytes = 16*D
+        const uint32_t lw = on ? (uint32_t)lane * 16u * D : kOffLane;
 #pragma unroll
-        for (int q = 0; q < D; ++q) {   // CPL*D*XB bytes = 16*D
-            uint4 v = make_uint4(0, 0, 0, 0);
-            if (on) v = *(const uint4 *)((const char *)p.weight + (int64_t)c0 * D * XB + 16 * q);
-            wr[4 * q] = v.x; wr[4 * q + 1] = v.y; wr[4 * q + 2] = v.z; wr[4 * q + 3] = v.w;
-        }
+        for (int q = 0; q < D; ++q) load16(w_r, lw + 16 * q, 0, wr + 4 * q);
 #pragma unroll
         for (int ch = 0; ch < CPL; ++ch)
 #pragma unroll
             for (int w = 0; w < D; ++w) wv[ch][w] = elem_val<XB>(wr, ch * D + w);
-        uint4 bb = make_uint4(0, 0, 0, 0);
-        if (p.bias && on) bb = *(const uint4 *)((const char *)p.bias + (int64_t)c0 * XB);
-        const uint32_t br[4] = {bb.x, bb.y, bb.z, bb.w};
+        uint32_t br[4] = {0u, 0u, 0u, 0u};
+        if (p.bias) {
+            const rsrc_t b_r = make_rsrc((const char *)p.bias + (int64_t)cb * XB,
+                                         (uint32_t)(nch * XB));
+            load16(b_r, lane16, 0, br);
+        }
 #pragma unroll
         for (int ch = 0; ch < CPL; ++ch) bv[ch] = elem_val<XB>(br, ch);
     }
@@ -209,10 +263,10 @@ __global__ __launch_bounds__(kWave) void cv_verify_kernel(KernelArgs p) {
         return k < W1 ? elem_bits<SB>(S[k < W1 ? k : 0], ch)
                       : x_to_state_bits<XB, SB>(elem_bits<XB>(X[k < W1 ? 0 : k - W1], ch));
     };
-    // The lane's CPL x (D-1) run of window v[k0 .. k0+W1-1] ([ch][j] order), packed.
+    // The lane's CPL x (D-1) run of the window v[k0 .. k0+W1-1] ([ch][j] order), packed.
     auto window_run = [&](int k0, uint32_t *run) {
 #pragma unroll
-        for (int w = 0; w < CHUNK_W; ++w) {
+        for (int w = 0; w < RUNW; ++w) {
             if constexpr (SB == 4) {
                 run[w] = sbits(k0 + w % W1, w / W1);
             } else {
@@ -223,6 +277,13 @@ __global__ __launch_bounds__(kWave) void cv_verify_kernel(KernelArgs p) {
     };
     // Column v[k] in the state type (SW words).
     auto column = [&](int k, uint32_t *col) {
+        if constexpr (XB == SB) {
+            if (k >= W1) {
+#pragma unroll
+                for (int w = 0; w < SW; ++w) col[w] = X[k < W1 ? 0 : k - W1][w];
+                return;
+            }
+        }
 #pragma unroll
         for (int w = 0; w < SW; ++w) {
             if constexpr (SB == 4) {
@@ -233,8 +294,31 @@ __global__ __launch_bounds__(kWave) void cv_verify_kernel(KernelArgs p) {
         }
     };
 
-    const int pitch = tile_pitch(CPL, SB);
-    char *tile = (char *)lds_tile;
+    if (!contiguous_state) {
+        // committed window v[T .. T+W1-1] into columns 0..W1-1 of the staged rows, then
+        // the whole region goes back out, coalesced.  Each lane rewrites only its own
+        // channels' records, after having read them above.
+        char *rec = lds + lane * CPL * SL * SB;
+#pragma unroll
+        for (int t = 0; t < TB; ++t) {
+            if (t == T - 1) {
+#pragma unroll
+                for (int ch = 0; ch < CPL; ++ch)
+#pragma unroll
+                    for (int j = 0; j < W1; ++j)
+                        lds_put<SB>(rec + (ch * SL + j) * SB, sbits(t + 1 + j, ch));
+            }
+        }
+        __syncthreads();
+        const int rchunks = nch * SL * SB / 16;
+        for (int q = lane; q < rchunks; q += kWave) {
+            const uint4 v = *(const uint4 *)(lds + q * 16);
+            const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+            store16(st_r, (uint32_t)q * 16u, 0, w4);
+        }
+        __syncthreads();   // the region's LDS is reused by the dedup tile below
+    }
+
     if constexpr (DEDUP) {
         // tile row r holds v[r+1]; rows 0..W1-2 come from the initial window
 #pragma unroll
@@ -243,15 +327,19 @@ __global__ __launch_bounds__(kWave) void cv_verify_kernel(KernelArgs p) {
             column(k, col);
 #pragma unroll
             for (int q = 0; q < SW / 4; ++q)
-                *(uint4 *)(tile + (k - 1) * pitch + lane * (CPL * SB) + 16 * q) =
+                *(uint4 *)(lds + (k - 1) * P + lane * (CPL * SB) + 16 * q) =
                     make_uint4(col[4 * q], col[4 * q + 1], col[4 * q + 2], col[4 * q + 3]);
         }
     }
 
     const bool wave_l2 = cb < p.qk;    // uniform: this wavefront holds q|k channels
-    const bool lane_l2 = c0 < p.qk;
-    char *orow = (char *)p.out + ((int64_t)row * p.out_seq + c0) * XB;
-    char *wbase = (char *)p.win + (int64_t)slot * p.win_slot * SB;
+    const bool lane_l2 = lane * CPL + cb < p.qk;
+    const rsrc_t o_r = make_rsrc((char *)p.out + ((int64_t)row * p.out_seq + cb) * XB,
+                                 (uint32_t)(((int64_t)(T - 1) * p.out_tok + nch) * XB));
+    // dense snapshots (unused by the dedup instantiation)
+    const rsrc_t win_r =
+        make_rsrc((char *)p.win + ((int64_t)slot * p.win_slot + (int64_t)cb * W1) * SB,
+                  (uint32_t)(((int64_t)(T - 1) * p.d_inner * W1 + (int64_t)nch * W1) * SB));
 
 #pragma unroll
     for (int t = 0; t < TB; ++t) {
@@ -275,105 +363,106 @@ __global__ __launch_bounds__(kWave) void cv_verify_kernel(KernelArgs p) {
                     for (int ch = 0; ch < CPL; ++ch) y[ch] *= sc;
                 }
             }
-            if (on) {
-                uint32_t o[4];
-                if constexpr (XB == 4) {
+            uint32_t o[4];
+            if constexpr (XB == 4) {
 #pragma unroll
-                    for (int ch = 0; ch < 4; ++ch) o[ch] = __float_as_uint(y[ch]);
-                } else {
-                    typedef float f2 __attribute__((ext_vector_type(2)));
-                    typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+                for (int ch = 0; ch < 4; ++ch) o[ch] = __float_as_uint(y[ch]);
+            } else {
+                typedef float f2 __attribute__((ext_vector_type(2)));
+                typedef __bf16 b2 __attribute__((ext_vector_type(2)));
 #pragma unroll
-                    for (int w = 0; w < 4; ++w) {
-                        f2 pr = {y[2 * w], y[2 * w + 1]};
-                        o[w] = __builtin_bit_cast(uint32_t, __builtin_convertvector(pr, b2));
-                    }
+                for (int w = 0; w < 4; ++w) {
+                    f2 pr = {y[2 * w], y[2 * w + 1]};
+                    o[w] = __builtin_bit_cast(uint32_t, __builtin_convertvector(pr, b2));
                 }
-                *(uint4 *)(orow + (int64_t)t * p.out_tok * XB) = make_uint4(o[0], o[1], o[2], o[3]);
             }
+            store16(o_r, lane16, (uint32_t)(t * p.out_tok * XB), o);
 
             if constexpr (!DEDUP) {
                 // dense snapshot t = v[t+1 .. t+W1]: the lane's run is contiguous
-                if (on) {
-                    uint32_t run[CHUNK_W];
-                    window_run(t + 1, run);
-                    char *dst = wbase + ((int64_t)t * p.d_inner + c0) * W1 * SB;
+                uint32_t run[RUNW];
+                window_run(t + 1, run);
+                const uint32_t soff = (uint32_t)(t * p.d_inner * W1 * SB);
 #pragma unroll
-                    for (int q = 0; q < CHUNK_W / 4; ++q)
-                        *(uint4 *)(dst + 16 * q) =
-                            make_uint4(run[4 * q], run[4 * q + 1], run[4 * q + 2], run[4 * q + 3]);
-                }
+                for (int q = 0; q < RUNW / 4; ++q) store16(win_r, lane_run + 16 * q, soff, run + 4 * q);
             } else {
                 // x_t is v[t+W1], tile row t+W1-1
                 uint32_t col[SW];
                 column(t + W1, col);
 #pragma unroll
                 for (int q = 0; q < SW / 4; ++q)
-                    *(uint4 *)(tile + (t + W1 - 1) * pitch + lane * (CPL * SB) + 16 * q) =
+                    *(uint4 *)(lds + (t + W1 - 1) * P + lane * (CPL * SB) + 16 * q) =
                         make_uint4(col[4 * q], col[4 * q + 1], col[4 * q + 2], col[4 * q + 3]);
             }
 
-            if (t == T - 1 && on) {
+            if (t == T - 1 && contiguous_state) {
                 // committed window v[T .. T+W1-1] -> conv_state columns 0..W1-1
-                if (contiguous_state) {
-                    uint32_t run[CHUNK_W];
-                    window_run(t + 1, run);
-                    char *dst = srow + (int64_t)c0 * W1 * SB;
+                uint32_t run[RUNW];
+                window_run(t + 1, run);
 #pragma unroll
-                    for (int q = 0; q < CHUNK_W / 4; ++q)
-                        *(uint4 *)(dst + 16 * q) =
-                            make_uint4(run[4 * q], run[4 * q + 1], run[4 * q + 2], run[4 * q + 3]);
-                } else {
-                    char *rec = srow + (int64_t)c0 * p.state_len * SB;
-#pragma unroll
-                    for (int ch = 0; ch < CPL; ++ch)
-#pragma unroll
-                        for (int j = 0; j < W1; ++j) {
-                            const uint32_t b = sbits(t + 1 + j, ch);
-                            if constexpr (SB == 4)
-                                *(uint32_t *)(rec + ((int64_t)ch * p.state_len + j) * 4) = b;
-                            else
-                                *(uint16_t *)(rec + ((int64_t)ch * p.state_len + j) * 2) = (uint16_t)b;
-                        }
-                }
+                for (int q = 0; q < RUNW / 4; ++q) store16(st_r, lane_run + 16 * q, 0, run + 4 * q);
             }
         }
     }
 
     if constexpr (DEDUP) {
-        // Stream the tile out in the row layout [c][k], k < L = T+W1-1, 16 bytes per lane.
+        // Stream the tile out in the row layout [c][k], k < L = T+W1-1: chunk q of the
+        // wavefront's contiguous row block holds elements e = q*EPC .. q*EPC+EPC-1,
+        // element e = (channel e / L, column e % L) = tile row e % L, channel e / L.
         __syncthreads();
         constexpr int EPC = 16 / SB;   // elements per 16-byte chunk
         const int L = T + W1 - 1;
-        const int nch = min(CHW, p.d_inner - cb);
         const int nchunks = nch * L / EPC;   // exact: nch is a multiple of CPL
-        char *dst = wbase + (int64_t)cb * L * SB;
-        int e0 = lane * EPC;
-        int c = e0 / L;
-        int k = e0 - c * L;
-        const int step_c = (kWave * EPC) / L;
-        const int step_k = (kWave * EPC) - step_c * L;
-        for (int q = lane; q < nchunks; q += kWave) {
-            uint32_t w[4];
-            int cc = c, kk = k;
+        const rsrc_t win_r2 = make_rsrc(
+            (char *)p.win + ((int64_t)slot * p.win_slot + (int64_t)cb * L) * SB,
+            (uint32_t)(nch * L * SB));
+        const int e0 = lane * EPC;
+        int cc = e0 / L;
+        int kk = e0 - cc * L;
+        const int dq = (kWave * EPC) / L;
+        const int dr = kWave * EPC - dq * L;
+        if (L >= EPC) {
+            // a chunk spans at most two channels: columns kk.. of channel cc, then
+            // columns 0.. of channel cc+1; each element is one LDS read at a fixed
+            // row step from one of two bases
+            for (int q = lane; q < nchunks; q += kWave) {
+                const int split = L - kk;
+                const uint32_t b1 = (uint32_t)(kk * P + cc * SB);
+                const uint32_t b2 = b1 + (uint32_t)SB - (uint32_t)(L * P);
+                uint32_t w[4];
 #pragma unroll
-            for (int m = 0; m < EPC; ++m) {
-                uint32_t b;
-                if constexpr (SB == 4)
-                    b = *(const uint32_t *)(tile + kk * pitch + cc * 4);
-                else
-                    b = *(const uint16_t *)(tile + kk * pitch + cc * 2);
-                if constexpr (SB == 4) {
-                    w[m] = b;
-                } else {
-                    if (m & 1) w[m >> 1] |= b << 16; else w[m >> 1] = b;
+                for (int m = 0; m < EPC; ++m) {
+                    const uint32_t b = lds_get<SB>(lds + ((m < split ? b1 : b2) + m * P));
+                    if constexpr (SB == 4) {
+                        w[m] = b;
+                    } else {
+                        if (m & 1) w[m >> 1] |= b << 16; else w[m >> 1] = b;
+                    }
                 }
-                if (++kk == L) { kk = 0; ++cc; }
+                store16(win_r2, (uint32_t)q * 16u, 0, w);
+                cc += dq;
+                kk += dr;
+                if (kk >= L) { kk -= L; ++cc; }
             }
-            *(uint4 *)(dst + (int64_t)q * 16) = make_uint4(w[0], w[1], w[2], w[3]);
-            c += step_c;
-            k += step_k;
-            if (k >= L) { k -= L; ++c; }
+        } else {
+            for (int q = lane; q < nchunks; q += kWave) {
+                uint32_t w[4];
+                int c2 = cc, k2 = kk;
+#pragma unroll
+                for (int m = 0; m < EPC; ++m) {
+                    const uint32_t b = lds_get<SB>(lds + k2 * P + c2 * SB);
+                    if constexpr (SB == 4) {
+                        w[m] = b;
+                    } else {
+                        if (m & 1) w[m >> 1] |= b << 16; else w[m >> 1] = b;
+                    }
+                    if (++k2 == L) { k2 = 0; ++c2; }
+                }
+                store16(win_r2, (uint32_t)q * 16u, 0, w);
+                cc += dq;
+                kk += dr;
+                while (kk >= L) { kk -= L; ++cc; }
+            }
         }
     }
 }
