@@ -22,14 +22,21 @@ ARCH = "gfx950"
 
 # Packed fp32 instructions are kept out of every kernel: hipcc would otherwise form
 # v_pk_{add,mul,fma}_f32 from ordinary float code.
-DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+                # the token loop is unrolled over its compile-time bucket (up to 32) so
+                # every register index is static; allow that size
+                "-mllvm", "-pragma-unroll-threshold=1000000"]
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wextra", "-Wno-unused-parameter",
           f"-I{INCLUDE}", f"-I{CSRC}"]
 
+# The kernel source is compiled once per (x bytes, state bytes, layout); the six
+# objects build in parallel.
 SOURCES = [
-    ("cv_kernels.hip", [f"--offload-arch={ARCH}", *DEVICE_FLAGS]),
-    ("cv_api.cpp", []),
-]
+    (f"cv_kernels.hip", f"cv_kernels_{xb}_{sb}_{dd}",
+     [f"--offload-arch={ARCH}", *DEVICE_FLAGS, f"-DCV_XB={xb}", f"-DCV_SB={sb}",
+      f"-DCV_DEDUP={dd}"])
+    for xb, sb in ((4, 4), (2, 2), (2, 4)) for dd in (0, 1)
+] + [("cv_api.cpp", "cv_api", [])]
 
 
 def _run(cmd):
@@ -45,8 +52,8 @@ def build(verbose: bool = True) -> str:
     objs = []
     procs = []
     t0 = time.time()
-    for src, extra in SOURCES:
-        obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
+    for src, stem, extra in SOURCES:
+        obj = os.path.join(BUILD, stem + ".o")
         cmd = [HIPCC, *COMMON, *extra, "-c", os.path.join(CSRC, src), "-o", obj]
         procs.append((cmd, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.PIPE,
                                             text=True)))

@@ -105,17 +105,16 @@ int plan_shape(int dedup, const cv_shape_t *s, cvimpl::Plan *plan) {
     const int64_t wg = blocks * (int64_t)s->n_seq;
     if (wg * kWave > (int64_t)UINT32_MAX)
         return fail(CV_ENOTSUP, "grid of %lld workgroups exceeds the launch limit", (long long)wg);
-    int tb = 1;
-    while (tb < s->T) tb *= 2;
-    // LDS: the dedup tile (T+D-2 rows of one wavefront's channels) and, when state rows
-    // are wider than the window, the staged [channels, state_len] region; they are used
-    // one after the other and share the allocation.
-    int64_t lds = 0;
-    if (dedup) lds = (int64_t)(s->T + s->d_conv - 2) * cvimpl::tile_pitch(cpl, sb);
-    if (s->state_len > W1) {
-        const int64_t region = (int64_t)kWave * cpl * s->state_len * sb;
-        if (region > lds) lds = region;
-    }
+    int tb = 1;                                  // token buckets: 1 2 4 8 16 24 32
+    while (tb < s->T && tb < 16) tb *= 2;
+    if (tb < s->T) tb = s->T <= 24 ? 24 : 32;
+    // LDS: the wavefront's conv_state region [channels, state_len] passes through first;
+    // afterwards the same allocation holds the dedup tile (T+D-2 rows of the
+    // wavefront's channels) or one or two dense snapshot slabs [channels, D-1].
+    const int64_t region = (int64_t)kWave * cpl * s->state_len * sb;
+    const int64_t later = dedup ? (int64_t)(s->T + s->d_conv - 2) * cvimpl::tile_pitch(cpl, sb)
+                                : (int64_t)kWave * cpl * W1 * sb * (s->T > 1 ? 2 : 1);
+    const int64_t lds = region > later ? region : later;
     if (lds > kMaxLds)
         return fail(CV_ENOTSUP, "kernel needs %lld bytes of LDS (> %d)", (long long)lds, kMaxLds);
     // Buffer resources span one row's bytes with a 32-bit size; lanes past d_inner use
@@ -142,6 +141,25 @@ int plan_shape(int dedup, const cv_shape_t *s, cvimpl::Plan *plan) {
     plan->head_lanes = head_lanes;
     (void)hl_log2;
     return CV_OK;
+}
+
+const void *pick_kernel(const cvimpl::Plan &plan) {
+    using namespace cvimpl;
+    const int xb = plan.x_bytes, sb = plan.state_bytes, d = plan.d_conv, tb = plan.token_bucket;
+    if (xb == 4 && sb == 4) return plan.dedup ? pick_kernel_4_4_1(d, tb) : pick_kernel_4_4_0(d, tb);
+    if (xb == 2 && sb == 2) return plan.dedup ? pick_kernel_2_2_1(d, tb) : pick_kernel_2_2_0(d, tb);
+    if (xb == 2 && sb == 4) return plan.dedup ? pick_kernel_2_4_1(d, tb) : pick_kernel_2_4_0(d, tb);
+    return nullptr;
+}
+
+// Enqueues the kernel; returns a hipError_t value (0 = success).
+int launch(const cvimpl::Plan &plan, const cvimpl::KernelArgs &args, void *stream) {
+    const void *fn = pick_kernel(plan);
+    if (!fn) return (int)hipErrorInvalidDeviceFunction;
+    cvimpl::KernelArgs a = args;
+    void *kargs[] = {&a};
+    return (int)hipLaunchKernel(fn, dim3((unsigned)plan.workgroups), dim3(cvimpl::kWave), kargs,
+                                (size_t)plan.lds_bytes, (hipStream_t)stream);
 }
 
 int update(int dedup, const cv_shape_t *s, const void *x, const void *weight, const void *bias,
@@ -188,7 +206,7 @@ int update(int dedup, const cv_shape_t *s, const void *x, const void *weight, co
     while (plan.head_lanes && (1 << hl_log2) < plan.head_lanes) ++hl_log2;
     a.head_lanes_log2 = hl_log2;
     a.eps = s->l2_eps;
-    int e = cvimpl::launch(plan, a, stream);
+    int e = launch(plan, a, stream);
     if (e != 0)
         return fail(CV_EHIP_BASE - e, "kernel launch failed: %s",
                     hipGetErrorString(static_cast<hipError_t>(e)));

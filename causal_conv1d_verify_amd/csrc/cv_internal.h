@@ -32,7 +32,7 @@ struct Plan {
     int dedup;                 // 0 dense, 1 dedup
     int x_bytes, state_bytes;  // element sizes: (4,4), (2,2) or (2,4)
     int d_conv;                // 2..4
-    int token_bucket;          // 1,2,4,8,16,32 >= T
+    int token_bucket;          // 1,2,4,8,16,24,32 >= T
     int channels_per_lane;     // 16 / x_bytes
     int channel_blocks;
     int64_t workgroups;
@@ -46,7 +46,13 @@ constexpr int tile_pitch(int channels_per_lane, int state_bytes) {
     return kWave * channels_per_lane * state_bytes + 16;
 }
 
-// Enqueues the kernel; returns a hipError_t value (0 = success).
-int launch(const Plan &plan, const KernelArgs &args, void *stream);
+// Kernel pickers, one per compiled (x bytes, state bytes, dedup) object: the kernel
+// for (d_conv, token bucket), or nullptr.
+const void *pick_kernel_4_4_0(int d_conv, int token_bucket);
+const void *pick_kernel_4_4_1(int d_conv, int token_bucket);
+const void *pick_kernel_2_2_0(int d_conv, int token_bucket);
+const void *pick_kernel_2_2_1(int d_conv, int token_bucket);
+const void *pick_kernel_2_4_0(int d_conv, int token_bucket);
+const void *pick_kernel_2_4_1(int d_conv, int token_bucket);
 
 }  // namespace cvimpl

@@ -112,6 +112,9 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void_t;
 
 constexpr uint32_t kOffLane = 0x80000000u;
+// Cache policy of every global access: nt (streaming).  Each byte is read or written
+// once per launch, so nothing is worth keeping in L2 or the Infinity Cache.
+constexpr int kNT = 2;
 
 __device__ __forceinline__ rsrc_t make_rsrc(const void *base, uint32_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
@@ -119,13 +122,13 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void *base, uint32_t bytes) {
 }
 
 __device__ __forceinline__ void load16(rsrc_t r, uint32_t voff, uint32_t soff, uint32_t *d) {
-    const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0);
+    const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, kNT);
     d[0] = v.x; d[1] = v.y; d[2] = v.z; d[3] = v.w;
 }
 
 __device__ __forceinline__ void store16(rsrc_t r, uint32_t voff, uint32_t soff, const uint32_t *s) {
     const u32x4 v = {s[0], s[1], s[2], s[3]};
-    __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)voff, (int)soff, 0);
+    __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)voff, (int)soff, kNT);
 }
 
 template <int EB>
@@ -138,6 +141,15 @@ template <int EB>
 __device__ __forceinline__ void lds_put(char *p, uint32_t v) {
     if constexpr (EB == 4) *(uint32_t *)p = v;
     else *(uint16_t *)p = (uint16_t)v;
+}
+
+// Orders LDS accesses across the workgroup (one wavefront) without waiting for the
+// wavefront's global stores: __syncthreads() is a release fence for all memory, which
+// would make every LDS hand-off wait for the writes issued before it to reach memory.
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
 // ---- the kernel -------------------------------------------------------------------------
@@ -170,7 +182,6 @@ __global__ __launch_bounds__(kWave) void cv_verify_kernel(KernelArgs p) {
     const int nch = min(CHW, p.d_inner - cb);       // channels of this wavefront
     const bool on = lane * CPL < nch;
     const uint32_t lane16 = on ? (uint32_t)lane * 16u : kOffLane;
-    const uint32_t lane_run = on ? (uint32_t)lane * (RUNW * 4) : kOffLane;
     const bool contiguous_state = SL == W1;
 
     // ---- loads: x (registers), window, weights, bias ----------------------------------
@@ -186,14 +197,47 @@ __global__ __launch_bounds__(kWave) void cv_verify_kernel(KernelArgs p) {
         }
     }
 
+    // weights and bias: loaded with everything else, before the first barrier, so no
+    // load is outstanding once the stores start (vmcnt counts loads and stores together)
+    uint32_t wr[4 * D];   // CPL*D*XB bytes = 16*D
+    uint32_t br[4] = {0u, 0u, 0u, 0u};
+    {
+        const rsrc_t w_r = make_rsrc((const char *)p.weight + (int64_t)cb * D * XB,
+                                     (uint32_t)(nch * D * XB));
+        const uint32_t lw = on ? (uint32_t)lane * 16u * D : kOffLane;
+#pragma unroll
+        for (int q = 0; q < D; ++q) load16(w_r, lw + 16 * q, 0, wr + 4 * q);
+        if (p.bias) {
+            const rsrc_t b_r = make_rsrc((const char *)p.bias + (int64_t)cb * XB,
+                                         (uint32_t)(nch * XB));
+            load16(b_r, lane16, 0, br);
+        }
+    }
+
+    // conv_state: the wavefront's [nch, state_len] region is contiguous.  It comes in
+    // whole through LDS (direct loads, coalesced), each lane picks its channels'
+    // window out of it, writes its committed window back into it, and the region
+    // leaves whole (coalesced) - so every state byte is read once and written once
+    // in full 16-byte lane-contiguous units, whatever state_len and the offset are.
     const rsrc_t st_r = make_rsrc((const char *)p.state + ((int64_t)slot * p.state_slot +
                                                            (int64_t)cb * SL) * SB,
                                   (uint32_t)(nch * SL * SB));
+    const int rchunks = nch * SL * SB / 16;   // exact: nch * SB is a multiple of 16
+    for (int j = 0; j * kWave < rchunks; ++j) {
+        const int q = j * kWave + lane;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(st_r, (lds_void_t *)(lds + j * (kWave * 16)), 16,
+                                                 q < rchunks ? q * 16 : (int)kOffLane, 0, 0, kNT);
+    }
+    __syncthreads();   // waits for the direct loads (and x): nothing has been stored yet
     uint32_t S[W1][SW];   // initial window columns v[0..W1-1], state-typed bits
     if (contiguous_state) {
+        // the lane's [CPL][W1] run: RUNW/4 aligned 16-byte LDS reads
         uint32_t run[RUNW];
 #pragma unroll
-        for (int q = 0; q < RUNW / 4; ++q) load16(st_r, lane_run + 16 * q, 0, run + 4 * q);
+        for (int q = 0; q < RUNW / 4; ++q) {
+            const uint4 v = *(const uint4 *)(lds + lane * (RUNW * 4) + 16 * q);
+            run[4 * q] = v.x; run[4 * q + 1] = v.y; run[4 * q + 2] = v.z; run[4 * q + 3] = v.w;
+        }
 #pragma unroll
         for (int j = 0; j < W1; ++j)
 #pragma unroll
@@ -206,17 +250,6 @@ __global__ __launch_bounds__(kWave) void cv_verify_kernel(KernelArgs p) {
                 }
             }
     } else {
-        // Rows wider than the window (an accept offset): every sector of the row
-        // holds window bytes, so the wavefront's whole [nch, state_len] region is
-        // moved once, coalesced, through LDS - in directly, out after the commit.
-        const int rchunks = nch * SL * SB / 16;
-        for (int j = 0; j * kWave < rchunks; ++j) {
-            const int q = j * kWave + lane;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                st_r, (lds_void_t *)(lds + j * (kWave * 16)), 16,
-                q < rchunks ? q * 16 : (int)kOffLane, 0, 0, 0);
-        }
-        __syncthreads();
         const char *rec = lds + (lane * CPL * SL + a) * SB;
 #pragma unroll
         for (int j = 0; j < W1; ++j)
@@ -233,25 +266,11 @@ __global__ __launch_bounds__(kWave) void cv_verify_kernel(KernelArgs p) {
 
     float wv[CPL][D];
     float bv[CPL];
-    {
-        const rsrc_t w_r = make_rsrc((const char *)p.weight + (int64_t)cb * D * XB,
-                                     (uint32_t)(nch * D * XB));
-        uint32_t wr[4 * D];   // CPL*D*XB bytes = 16*D
-        const uint32_t lw = on ? (uint32_t)lane * 16u * D : kOffLane;
 #pragma unroll
-        for (int q = 0; q < D; ++q) load16(w_r, lw + 16 * q, 0, wr + 4 * q);
+    for (int ch = 0; ch < CPL; ++ch) {
 #pragma unroll
-        for (int ch = 0; ch < CPL; ++ch)
-#pragma unroll
-            for (int w = 0; w < D; ++w) wv[ch][w] = elem_val<XB>(wr, ch * D + w);
-        uint32_t br[4] = {0u, 0u, 0u, 0u};
-        if (p.bias) {
-            const rsrc_t b_r = make_rsrc((const char *)p.bias + (int64_t)cb * XB,
-                                         (uint32_t)(nch * XB));
-            load16(b_r, lane16, 0, br);
-        }
-#pragma unroll
-        for (int ch = 0; ch < CPL; ++ch) bv[ch] = elem_val<XB>(br, ch);
+        for (int w = 0; w < D; ++w) wv[ch][w] = elem_val<XB>(wr, ch * D + w);
+        bv[ch] = elem_val<XB>(br, ch);
     }
 
     // v[k] accessors: k < W1 -> initial window, else x_{k-W1}.  k is compile-time.
@@ -277,70 +296,194 @@ __global__ __launch_bounds__(kWave) void cv_verify_kernel(KernelArgs p) {
     };
     // Column v[k] in the state type (SW words).
     auto column = [&](int k, uint32_t *col) {
-        if constexpr (XB == SB) {
-            if (k >= W1) {
+        if (k < W1) {
 #pragma unroll
-                for (int w = 0; w < SW; ++w) col[w] = X[k < W1 ? 0 : k - W1][w];
-                return;
-            }
-        }
+            for (int w = 0; w < SW; ++w) col[w] = S[k < W1 ? k : 0][w];
+        } else if constexpr (XB == SB) {
 #pragma unroll
-        for (int w = 0; w < SW; ++w) {
-            if constexpr (SB == 4) {
-                col[w] = sbits(k, w);
-            } else {
-                col[w] = sbits(k, 2 * w) | (sbits(k, 2 * w + 1) << 16);
-            }
+            for (int w = 0; w < SW; ++w) col[w] = X[k < W1 ? 0 : k - W1][w];
+        } else {
+#pragma unroll
+            for (int w = 0; w < SW; ++w)   // bf16 -> fp32 widening, channel w
+                col[w] = x_to_state_bits<XB, SB>(elem_bits<XB>(X[k < W1 ? 0 : k - W1], w));
         }
     };
 
-    if (!contiguous_state) {
+    {
         // committed window v[T .. T+W1-1] into columns 0..W1-1 of the staged rows, then
-        // the whole region goes back out, coalesced.  Each lane rewrites only its own
-        // channels' records, after having read them above.
-        char *rec = lds + lane * CPL * SL * SB;
+        // the whole region goes back out.  Each lane rewrites only its own channels'
+        // records, after having read them above.
 #pragma unroll
         for (int t = 0; t < TB; ++t) {
             if (t == T - 1) {
+                if (contiguous_state) {
+                    uint32_t run[RUNW];
+                    window_run(t + 1, run);
 #pragma unroll
-                for (int ch = 0; ch < CPL; ++ch)
+                    for (int q = 0; q < RUNW / 4; ++q)
+                        *(uint4 *)(lds + lane * (RUNW * 4) + 16 * q) =
+                            make_uint4(run[4 * q], run[4 * q + 1], run[4 * q + 2], run[4 * q + 3]);
+                } else {
+                    char *rec = lds + lane * CPL * SL * SB;
 #pragma unroll
-                    for (int j = 0; j < W1; ++j)
-                        lds_put<SB>(rec + (ch * SL + j) * SB, sbits(t + 1 + j, ch));
+                    for (int ch = 0; ch < CPL; ++ch)
+#pragma unroll
+                        for (int j = 0; j < W1; ++j)
+                            lds_put<SB>(rec + (ch * SL + j) * SB, sbits(t + 1 + j, ch));
+                }
             }
         }
-        __syncthreads();
-        const int rchunks = nch * SL * SB / 16;
+        lds_barrier();
         for (int q = lane; q < rchunks; q += kWave) {
             const uint4 v = *(const uint4 *)(lds + q * 16);
             const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
             store16(st_r, (uint32_t)q * 16u, 0, w4);
         }
-        __syncthreads();   // the region's LDS is reused by the dedup tile below
+        lds_barrier();   // the region's LDS is reused below
     }
 
+    // ---- rollback windows: pure copies of the inputs, written before any arithmetic so
+    // the stores drain while the wavefront computes --------------------------------------
     if constexpr (DEDUP) {
-        // tile row r holds v[r+1]; rows 0..W1-2 come from the initial window
+        const int L = T + W1 - 1;             // row length: v[1 .. T+W1-1]
+        const rsrc_t row_r = make_rsrc(
+            (char *)p.win + ((int64_t)slot * p.win_slot + (int64_t)cb * L) * SB,
+            (uint32_t)(nch * L * SB));
+        if (T == TB) {
+            // Row length known at compile time: each lane assembles its channels' rows
+            // ([CPL][LC], contiguous in the row layout) in registers, 16 bytes at a time,
+            // into LDS at the same offsets, and the wavefront streams the block out in
+            // lane-contiguous 16-byte units.
+            constexpr int LC = TB + W1 - 1;
+            constexpr int CW = CPL * LC * SB / 4;   // 32-bit words of a lane's rows
+            char *mine = lds + lane * (CPL * LC * SB);
 #pragma unroll
-        for (int k = 1; k < W1; ++k) {
-            uint32_t col[SW];
-            column(k, col);
+            for (int q = 0; q < CW / 4; ++q) {
+                uint32_t w4[4];
 #pragma unroll
-            for (int q = 0; q < SW / 4; ++q)
-                *(uint4 *)(lds + (k - 1) * P + lane * (CPL * SB) + 16 * q) =
-                    make_uint4(col[4 * q], col[4 * q + 1], col[4 * q + 2], col[4 * q + 3]);
+                for (int i = 0; i < 4; ++i) {
+                    const int wd = 4 * q + i;
+                    if constexpr (SB == 4) {
+                        w4[i] = sbits(wd % LC + 1, wd / LC);
+                    } else {
+                        const int e0 = 2 * wd, e1 = 2 * wd + 1;
+                        w4[i] = sbits(e0 % LC + 1, e0 / LC) | (sbits(e1 % LC + 1, e1 / LC) << 16);
+                    }
+                }
+                *(uint4 *)(mine + 16 * q) = make_uint4(w4[0], w4[1], w4[2], w4[3]);
+            }
+            lds_barrier();
+            const int nchunks = nch * LC * SB / 16;
+            for (int q = lane; q < nchunks; q += kWave) {
+                const uint4 v = *(const uint4 *)(lds + q * 16);
+                const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+                store16(row_r, (uint32_t)q * 16u, 0, w4);
+            }
+        } else {
+        // Tile row r holds v[r+1] for the wavefront's channels (16-byte LDS writes);
+        // rows 0..W1-2 come from the initial window, the rest are x_0..x_{T-1}.
+#pragma unroll
+        for (int k = 1; k < W1 + TB; ++k) {
+            if (k < W1 + T) {
+                uint32_t col[SW];
+                column(k, col);
+#pragma unroll
+                for (int q = 0; q < SW / 4; ++q)
+                    *(uint4 *)(lds + (k - 1) * P + lane * (CPL * SB) + 16 * q) =
+                        make_uint4(col[4 * q], col[4 * q + 1], col[4 * q + 2], col[4 * q + 3]);
+            }
+        }
+        lds_barrier();
+        // Stream the tile out in the row layout [c][k], k < L: chunk q of the
+        // wavefront's contiguous row block holds elements e = q*EPC .. q*EPC+EPC-1,
+        // element e = (channel e / L, column e % L) = tile row e % L, channel e / L.
+        constexpr int EPC = 16 / SB;   // elements per 16-byte chunk
+        const int nchunks = nch * L / EPC;   // exact: nch is a multiple of CPL
+        const int e0 = lane * EPC;
+        int cc = e0 / L;
+        int kk = e0 - cc * L;
+        const int dq = (kWave * EPC) / L;
+        const int dr = kWave * EPC - dq * L;
+        if (L >= EPC) {
+            // a chunk spans at most two channels: columns kk.. of channel cc, then
+            // columns 0.. of channel cc+1; each element is one LDS read at a fixed
+            // row step from one of two bases
+            for (int q = lane; q < nchunks; q += kWave) {
+                const int split = L - kk;
+                const uint32_t b1 = (uint32_t)(kk * P + cc * SB);
+                const uint32_t b2 = b1 + (uint32_t)SB - (uint32_t)(L * P);
+                uint32_t w[4];
+#pragma unroll
+                for (int m = 0; m < EPC; ++m) {
+                    const uint32_t b = lds_get<SB>(lds + ((m < split ? b1 : b2) + m * P));
+                    if constexpr (SB == 4) {
+                        w[m] = b;
+                    } else {
+                        if (m & 1) w[m >> 1] |= b << 16; else w[m >> 1] = b;
+                    }
+                }
+                store16(row_r, (uint32_t)q * 16u, 0, w);
+                cc += dq;
+                kk += dr;
+                if (kk >= L) { kk -= L; ++cc; }
+            }
+        } else {
+            for (int q = lane; q < nchunks; q += kWave) {
+                uint32_t w[4];
+                int c2 = cc, k2 = kk;
+#pragma unroll
+                for (int m = 0; m < EPC; ++m) {
+                    const uint32_t b = lds_get<SB>(lds + k2 * P + c2 * SB);
+                    if constexpr (SB == 4) {
+                        w[m] = b;
+                    } else {
+                        if (m & 1) w[m >> 1] |= b << 16; else w[m >> 1] = b;
+                    }
+                    if (++k2 == L) { k2 = 0; ++c2; }
+                }
+                store16(row_r, (uint32_t)q * 16u, 0, w);
+                cc += dq;
+                kk += dr;
+                while (kk >= L) { kk -= L; ++cc; }
+            }
+        }
+        }
+    } else {
+        // Dense snapshot t = v[t+1 .. t+W1]: the wavefront's [nch, W1] slab is contiguous.
+        // Lanes drop their [CPL][W1] runs into an LDS slab and the slab leaves in
+        // lane-contiguous 16-byte units.  Two slabs alternate, so one barrier per
+        // token orders both reuse hazards.
+        constexpr int SLAB = CHW * W1 * SB;
+        const int slab_chunks = nch * W1 * SB / 16;
+        const rsrc_t snap_r = make_rsrc(
+            (char *)p.win + ((int64_t)slot * p.win_slot + (int64_t)cb * W1) * SB,
+            (uint32_t)(((int64_t)(T - 1) * p.d_inner * W1 + (int64_t)nch * W1) * SB));
+#pragma unroll
+        for (int t = 0; t < TB; ++t) {
+            if (t < T) {
+                char *slab = lds + (t & 1) * SLAB;
+                uint32_t run[RUNW];
+                window_run(t + 1, run);
+#pragma unroll
+                for (int q = 0; q < RUNW / 4; ++q)
+                    *(uint4 *)(slab + lane * (RUNW * 4) + 16 * q) =
+                        make_uint4(run[4 * q], run[4 * q + 1], run[4 * q + 2], run[4 * q + 3]);
+                lds_barrier();
+                const uint32_t soff = (uint32_t)(t * p.d_inner * W1 * SB);
+                for (int q = lane; q < slab_chunks; q += kWave) {
+                    const uint4 v = *(const uint4 *)(slab + q * 16);
+                    const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+                    store16(snap_r, (uint32_t)q * 16u, soff, w4);
+                }
+            }
         }
     }
 
+    // ---- conv + SiLU + per-head L2 -> out --------------------------------------------------
     const bool wave_l2 = cb < p.qk;    // uniform: this wavefront holds q|k channels
     const bool lane_l2 = lane * CPL + cb < p.qk;
     const rsrc_t o_r = make_rsrc((char *)p.out + ((int64_t)row * p.out_seq + cb) * XB,
                                  (uint32_t)(((int64_t)(T - 1) * p.out_tok + nch) * XB));
-    // dense snapshots (unused by the dedup instantiation)
-    const rsrc_t win_r =
-        make_rsrc((char *)p.win + ((int64_t)slot * p.win_slot + (int64_t)cb * W1) * SB,
-                  (uint32_t)(((int64_t)(T - 1) * p.d_inner * W1 + (int64_t)nch * W1) * SB));
-
 #pragma unroll
     for (int t = 0; t < TB; ++t) {
         if (t < T) {   // uniform guard; the loop itself is fully unrolled
@@ -377,144 +520,46 @@ __global__ __launch_bounds__(kWave) void cv_verify_kernel(KernelArgs p) {
                 }
             }
             store16(o_r, lane16, (uint32_t)(t * p.out_tok * XB), o);
-
-            if constexpr (!DEDUP) {
-                // dense snapshot t = v[t+1 .. t+W1]: the lane's run is contiguous
-                uint32_t run[RUNW];
-                window_run(t + 1, run);
-                const uint32_t soff = (uint32_t)(t * p.d_inner * W1 * SB);
-#pragma unroll
-                for (int q = 0; q < RUNW / 4; ++q) store16(win_r, lane_run + 16 * q, soff, run + 4 * q);
-            } else {
-                // x_t is v[t+W1], tile row t+W1-1
-                uint32_t col[SW];
-                column(t + W1, col);
-#pragma unroll
-                for (int q = 0; q < SW / 4; ++q)
-                    *(uint4 *)(lds + (t + W1 - 1) * P + lane * (CPL * SB) + 16 * q) =
-                        make_uint4(col[4 * q], col[4 * q + 1], col[4 * q + 2], col[4 * q + 3]);
-            }
-
-            if (t == T - 1 && contiguous_state) {
-                // committed window v[T .. T+W1-1] -> conv_state columns 0..W1-1
-                uint32_t run[RUNW];
-                window_run(t + 1, run);
-#pragma unroll
-                for (int q = 0; q < RUNW / 4; ++q) store16(st_r, lane_run + 16 * q, 0, run + 4 * q);
-            }
-        }
-    }
-
-    if constexpr (DEDUP) {
-        // Stream the tile out in the row layout [c][k], k < L = T+W1-1: chunk q of the
-        // wavefront's contiguous row block holds elements e = q*EPC .. q*EPC+EPC-1,
-        // element e = (channel e / L, column e % L) = tile row e % L, channel e / L.
-        __syncthreads();
-        constexpr int EPC = 16 / SB;   // elements per 16-byte chunk
-        const int L = T + W1 - 1;
-        const int nchunks = nch * L / EPC;   // exact: nch is a multiple of CPL
-        const rsrc_t win_r2 = make_rsrc(
-            (char *)p.win + ((int64_t)slot * p.win_slot + (int64_t)cb * L) * SB,
-            (uint32_t)(nch * L * SB));
-        const int e0 = lane * EPC;
-        int cc = e0 / L;
-        int kk = e0 - cc * L;
-        const int dq = (kWave * EPC) / L;
-        const int dr = kWave * EPC - dq * L;
-        if (L >= EPC) {
-            // a chunk spans at most two channels: columns kk.. of channel cc, then
-            // columns 0.. of channel cc+1; each element is one LDS read at a fixed
-            // row step from one of two bases
-            for (int q = lane; q < nchunks; q += kWave) {
-                const int split = L - kk;
-                const uint32_t b1 = (uint32_t)(kk * P + cc * SB);
-                const uint32_t b2 = b1 + (uint32_t)SB - (uint32_t)(L * P);
-                uint32_t w[4];
-#pragma unroll
-                for (int m = 0; m < EPC; ++m) {
-                    const uint32_t b = lds_get<SB>(lds + ((m < split ? b1 : b2) + m * P));
-                    if constexpr (SB == 4) {
-                        w[m] = b;
-                    } else {
-                        if (m & 1) w[m >> 1] |= b << 16; else w[m >> 1] = b;
-                    }
-                }
-                store16(win_r2, (uint32_t)q * 16u, 0, w);
-                cc += dq;
-                kk += dr;
-                if (kk >= L) { kk -= L; ++cc; }
-            }
-        } else {
-            for (int q = lane; q < nchunks; q += kWave) {
-                uint32_t w[4];
-                int c2 = cc, k2 = kk;
-#pragma unroll
-                for (int m = 0; m < EPC; ++m) {
-                    const uint32_t b = lds_get<SB>(lds + k2 * P + c2 * SB);
-                    if constexpr (SB == 4) {
-                        w[m] = b;
-                    } else {
-                        if (m & 1) w[m >> 1] |= b << 16; else w[m >> 1] = b;
-                    }
-                    if (++k2 == L) { k2 = 0; ++c2; }
-                }
-                store16(win_r2, (uint32_t)q * 16u, 0, w);
-                cc += dq;
-                kk += dr;
-                while (kk >= L) { kk -= L; ++cc; }
-            }
         }
     }
 }
 
-// ---- dispatch table -------------------------------------------------------------------
-
-using KernelFn = void (*)(KernelArgs);
+// ---- instantiation ----------------------------------------------------------------------
+//
+// This file is compiled once per (x dtype, state dtype, layout) with CV_XB, CV_SB and
+// CV_DEDUP defined, so the instantiations build in parallel; each object exports one
+// picker over (d_conv, token bucket).
 
 template <int XB, int SB, int D, bool DEDUP>
-KernelFn pick_bucket(int tb) {
+const void *pick_bucket(int tb) {
     switch (tb) {
-        case 1: return cv_verify_kernel<XB, SB, D, 1, DEDUP>;
-        case 2: return cv_verify_kernel<XB, SB, D, 2, DEDUP>;
-        case 4: return cv_verify_kernel<XB, SB, D, 4, DEDUP>;
-        case 8: return cv_verify_kernel<XB, SB, D, 8, DEDUP>;
-        case 16: return cv_verify_kernel<XB, SB, D, 16, DEDUP>;
-        case 32: return cv_verify_kernel<XB, SB, D, 32, DEDUP>;
+        case 1: return (const void *)cv_verify_kernel<XB, SB, D, 1, DEDUP>;
+        case 2: return (const void *)cv_verify_kernel<XB, SB, D, 2, DEDUP>;
+        case 4: return (const void *)cv_verify_kernel<XB, SB, D, 4, DEDUP>;
+        case 8: return (const void *)cv_verify_kernel<XB, SB, D, 8, DEDUP>;
+        case 16: return (const void *)cv_verify_kernel<XB, SB, D, 16, DEDUP>;
+        case 24: return (const void *)cv_verify_kernel<XB, SB, D, 24, DEDUP>;
+        case 32: return (const void *)cv_verify_kernel<XB, SB, D, 32, DEDUP>;
         default: return nullptr;
     }
-}
-
-template <int XB, int SB, bool DEDUP>
-KernelFn pick_d(int d, int tb) {
-    switch (d) {
-        case 2: return pick_bucket<XB, SB, 2, DEDUP>(tb);
-        case 3: return pick_bucket<XB, SB, 3, DEDUP>(tb);
-        case 4: return pick_bucket<XB, SB, 4, DEDUP>(tb);
-        default: return nullptr;
-    }
-}
-
-template <bool DEDUP>
-KernelFn pick_types(int xb, int sb, int d, int tb) {
-    if (xb == 4 && sb == 4) return pick_d<4, 4, DEDUP>(d, tb);
-    if (xb == 2 && sb == 2) return pick_d<2, 2, DEDUP>(d, tb);
-    if (xb == 2 && sb == 4) return pick_d<2, 4, DEDUP>(d, tb);
-    return nullptr;
 }
 
 }  // namespace
 
-int launch(const Plan &plan, const KernelArgs &args, void *stream) {
-    KernelFn fn = plan.dedup ? pick_types<true>(plan.x_bytes, plan.state_bytes, plan.d_conv,
-                                                plan.token_bucket)
-                             : pick_types<false>(plan.x_bytes, plan.state_bytes, plan.d_conv,
-                                                 plan.token_bucket);
-    if (!fn) return (int)hipErrorInvalidDeviceFunction;
-    KernelArgs a = args;
-    void *kargs[] = {&a};
-    hipError_t e = hipLaunchKernel((const void *)fn, dim3((unsigned)plan.workgroups), dim3(kWave),
-                                   kargs, (size_t)plan.lds_bytes, (hipStream_t)stream);
-    return (int)e;
+#if !defined(CV_XB) || !defined(CV_SB) || !defined(CV_DEDUP)
+#error "compile with -DCV_XB=<2|4> -DCV_SB=<2|4> -DCV_DEDUP=<0|1>"
+#endif
+
+#define CV_PICK_NAME(xb, sb, dd) pick_kernel_##xb##_##sb##_##dd
+#define CV_PICK(xb, sb, dd) CV_PICK_NAME(xb, sb, dd)
+
+const void *CV_PICK(CV_XB, CV_SB, CV_DEDUP)(int d_conv, int token_bucket) {
+    switch (d_conv) {
+        case 2: return pick_bucket<CV_XB, CV_SB, 2, CV_DEDUP != 0>(token_bucket);
+        case 3: return pick_bucket<CV_XB, CV_SB, 3, CV_DEDUP != 0>(token_bucket);
+        case 4: return pick_bucket<CV_XB, CV_SB, 4, CV_DEDUP != 0>(token_bucket);
+        default: return nullptr;
+    }
 }
 
 }  // namespace cvimpl

@@ -157,11 +157,12 @@ def test_launch_geometry_of_workloads(key):
     assert (info.channel_blocks - 1) * info.channels_per_wave < wl.d_inner
     assert info.token_bucket >= wl.T and info.token_bucket < 2 * wl.T + 1
     assert info.head_lanes * cpl == wl.head_dim
+    region = 64 * cpl * wl.state_len * sb
     if wl.layout == "dedup":
-        assert info.lds_bytes == max(wl.row_cols * (64 * cpl * sb + 16),
-                                     64 * cpl * wl.state_len * sb if wl.state_len > 3 else 0)
+        later = wl.row_cols * (64 * cpl * sb + 16)
     else:
-        assert info.lds_bytes == 0
+        later = 64 * cpl * wl.win_cols * sb * (2 if wl.T > 1 else 1)
+    assert info.lds_bytes == max(region, later) <= 65536
 
 
 _CHILD = r"""
