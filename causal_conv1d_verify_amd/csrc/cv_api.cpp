@@ -51,9 +51,12 @@ int plan_shape(int dedup, const cv_shape_t *s, cvimpl::Plan *plan) {
     if (!xb || !sb) return fail(CV_EINVAL, "unknown dtype (x %d, state %d)", s->x_dtype, s->state_dtype);
     if (!((xb == 4 && sb == 4) || (xb == 2 && sb == 2) || (xb == 2 && sb == 4)))
         return fail(CV_ENOTSUP, "dtype pair (x f32, state bf16) is not supported");
-    const int cpl = 16 / xb;
-    if (s->d_inner % cpl)
-        return fail(CV_ENOTSUP, "d_inner (%d) must be a multiple of %d", s->d_inner, cpl);
+    // channels and x/out strides come in 16-byte units of the x dtype, so every
+    // wavefront's share of every buffer is a whole number of 16-byte chunks
+    const int align = 16 / xb;
+    const int cpl = cvimpl::kChannelsPerLane;
+    if (s->d_inner % align)
+        return fail(CV_ENOTSUP, "d_inner (%d) must be a multiple of %d", s->d_inner, align);
     if (s->qk_channels < 0 || s->qk_channels > s->d_inner)
         return fail(CV_EINVAL, "qk_channels (%d) outside 0..d_inner", s->qk_channels);
     int hl_log2 = 0, head_lanes = 0;
@@ -94,9 +97,9 @@ int plan_shape(int dedup, const cv_shape_t *s, cvimpl::Plan *plan) {
     if (s->n_slots > 1 && s->win_slot_stride < win_per_slot)
         return fail(CV_EINVAL, "win_slot_stride (%lld) < %lld elements per slot",
                     (long long)s->win_slot_stride, (long long)win_per_slot);
-    if (s->x_seq_stride % cpl || s->x_tok_stride % cpl || s->out_seq_stride % cpl ||
-        s->out_tok_stride % cpl)
-        return fail(CV_ENOTSUP, "x/out strides must be multiples of %d elements", cpl);
+    if (s->x_seq_stride % align || s->x_tok_stride % align || s->out_seq_stride % align ||
+        s->out_tok_stride % align)
+        return fail(CV_ENOTSUP, "x/out strides must be multiples of %d elements", align);
     if ((s->state_slot_stride * sb) % 16 || (s->win_slot_stride * sb) % 16)
         return fail(CV_ENOTSUP, "state/window slot strides must be multiples of 16 bytes");
 
@@ -112,7 +115,7 @@ int plan_shape(int dedup, const cv_shape_t *s, cvimpl::Plan *plan) {
     // afterwards the same allocation holds the dedup tile (T+D-2 rows of the
     // wavefront's channels) or one or two dense snapshot slabs [channels, D-1].
     const int64_t region = (int64_t)kWave * cpl * s->state_len * sb;
-    const int64_t later = dedup ? (int64_t)(s->T + s->d_conv - 2) * cvimpl::tile_pitch(cpl, sb)
+    const int64_t later = dedup ? (int64_t)(s->T + s->d_conv - 2) * cvimpl::tile_pitch(sb)
                                 : (int64_t)kWave * cpl * W1 * sb * (s->T > 1 ? 2 : 1);
     const int64_t lds = region > later ? region : later;
     if (lds > kMaxLds)

@@ -7,6 +7,7 @@
 namespace cvimpl {
 
 constexpr int kWave = 64;        // lanes per wavefront on CDNA; one wavefront per workgroup
+constexpr int kChannelsPerLane = 4;   // 256 channels per wavefront
 constexpr int kMaxT = 32;        // largest token bucket compiled
 constexpr int kMaxLds = 65536;   // dynamic LDS a workgroup may request
 
@@ -33,7 +34,7 @@ struct Plan {
     int x_bytes, state_bytes;  // element sizes: (4,4), (2,2) or (2,4)
     int d_conv;                // 2..4
     int token_bucket;          // 1,2,4,8,16,24,32 >= T
-    int channels_per_lane;     // 16 / x_bytes
+    int channels_per_lane;     // kChannelsPerLane
     int channel_blocks;
     int64_t workgroups;
     int lds_bytes;
@@ -42,8 +43,8 @@ struct Plan {
 
 // Bytes between consecutive rows of the dedup LDS tile: one wavefront's channels of
 // one sequence position, plus 16 bytes so successive rows start on different banks.
-constexpr int tile_pitch(int channels_per_lane, int state_bytes) {
-    return kWave * channels_per_lane * state_bytes + 16;
+constexpr int tile_pitch(int state_bytes) {
+    return kWave * kChannelsPerLane * state_bytes + 16;
 }
 
 // Kernel pickers, one per compiled (x bytes, state bytes, dedup) object: the kernel

@@ -7,31 +7,28 @@
 // What the pages fix (Atlas docs, fn gdn_verify_fused_conv_kn_batched; sglang PR
 // 46184, "Motivation" / "Modifications"; Atlas glm5next_kda/mod.rs,
 // Glm5NextKdaConfig) is restated in include/conv_verify.h.  This file is the MI355X
-// design of it:
+// design of it.  The op moves ~3 bytes per flop, so the design is about HBM:
 //
-//  * One 64-lane wavefront per workgroup.  Lane l owns CPL = 16 / sizeof(x element)
-//    consecutive channels (8 for bf16, 4 for fp32), so every per-token load of x and
-//    every store of out is one 16-byte access per lane and one contiguous 1 KiB span
-//    per wavefront.  The grid is 1-D: n_seq * ceil(d_inner / (64 * CPL)) workgroups.
-//  * The whole window sequence v[0 .. T+D-2] of the lane's channels lives in
-//    registers: all T loads of x are issued before the first use, and the token loop
-//    is unrolled over a compile-time bucket TB >= T so every register index is static.
+//  * One 64-lane wavefront per workgroup, 4 channels per lane, 256 channels per
+//    wavefront; the 1-D grid is n_seq * ceil(d_inner / 256) workgroups.  (256-channel
+//    blocks stream measurably faster on MI355X than 512-channel ones for this traffic
+//    mix: twice the wavefronts keep more requests in flight.)
+//  * Every global access is a lane-contiguous 8- or 16-byte buffer access with the
+//    nt (streaming) policy: x and out per token, and every run of conv_state, the
+//    dense snapshots and the dedup rows, which are staged through LDS so that they
+//    too leave in lane-contiguous units.  Per-token offsets live in SGPRs.
+//  * All loads (x for every token, conv_state, weights, bias) are issued before the
+//    first barrier; after it the wavefront only stores, so no wait on a load is ever
+//    stuck behind stores (vmcnt counts both).  Later LDS hand-offs use barriers that
+//    order LDS only.
+//  * The rollback windows and the committed state are pure copies of the inputs; they
+//    are written first, and the arithmetic runs while they drain.
 //  * The conv is one fused multiply-add per tap in tap order (bias first), the same
 //    order as the per-token path it replaces, so the pre-activation is bit-identical
 //    to a correctly rounded fp32 evaluation of that order.
-//  * L2: with head_dim = H and CPL channels per lane a head spans H / CPL lanes
-//    (16 at H = 128, bf16), a power of two; the sum of squares is a butterfly over
-//    those lanes with DPP (quad_perm, row_half_mirror, row_mirror inside a 16-lane
-//    row; ds_swizzle / bpermute beyond).  Every lane of a head ends with the same sum.
-//  * Dense snapshots: the lane's CPL x (D-1) window elements of token t are
-//    contiguous in memory, so they leave as 16-byte stores assembled in registers.
-//  * Dedup rows: the row [d_inner, T+D-2] of a slot is contiguous per wavefront;
-//    each sequence position is written once into an LDS tile (16-byte conflict-free
-//    writes), then the wavefront streams the tile out in row order with 16-byte,
-//    fully coalesced stores.  Nothing is written per token and nothing twice.
-//  * conv_state: when its rows are exactly D-1 wide the lane's window is one
-//    contiguous run (16-byte loads/stores); with wider rows (an accept offset) the
-//    D-1 elements per channel are moved one by one.
+//  * L2: a head of H channels spans H/4 lanes; its sum of squares is a butterfly with
+//    DPP inside 16-lane rows (quad_perm, row_half_mirror, row_mirror) and ds_swizzle /
+//    bpermute beyond; every lane of a head ends with the same sum.
 //  * Windows and conv_state move as bit patterns; only the conv reads them as floats.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -41,7 +38,7 @@
 namespace cvimpl {
 namespace {
 
-// ---- bit-pattern helpers (compile-time channel indices) ------------------------------
+// ---- bit-pattern helpers (compile-time element indices) -----------------------------
 
 // Element `e` of a packed word array of EB-byte elements, as raw bits.
 template <int EB>
@@ -75,7 +72,7 @@ __device__ __forceinline__ uint32_t x_to_state_bits(uint32_t xbits) {
 }
 
 __device__ __forceinline__ float silu(float p) {
-    // p * sigmoid(p); v_exp_f32 and v_rcp_f32.  For p << 0 the exponential
+    // p * sigmoid(p) with v_exp_f32 and v_rcp_f32.  For p << 0 the exponential
     // saturates to +inf and the result is -0.
     return p * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(p * -1.4426950408889634f));
 }
@@ -109,6 +106,7 @@ __device__ __forceinline__ float group_sum(float v, int hl_log2) {
 
 using rsrc_t = __amdgpu_buffer_rsrc_t;
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) void lds_void_t;
 
 constexpr uint32_t kOffLane = 0x80000000u;
@@ -121,14 +119,62 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void *base, uint32_t bytes) {
                                              0x00020000);
 }
 
-__device__ __forceinline__ void load16(rsrc_t r, uint32_t voff, uint32_t soff, uint32_t *d) {
-    const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, kNT);
-    d[0] = v.x; d[1] = v.y; d[2] = v.z; d[3] = v.w;
+// NB-byte (8 or 16) global load / store of words d[0 .. NB/4).
+template <int NB>
+__device__ __forceinline__ void gload(rsrc_t r, uint32_t voff, uint32_t soff, uint32_t *d) {
+    if constexpr (NB == 16) {
+        const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, kNT);
+        d[0] = v.x; d[1] = v.y; d[2] = v.z; d[3] = v.w;
+    } else {
+        static_assert(NB == 8, "8- or 16-byte accesses");
+        const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(r, (int)voff, (int)soff, kNT);
+        d[0] = v.x; d[1] = v.y;
+    }
 }
 
-__device__ __forceinline__ void store16(rsrc_t r, uint32_t voff, uint32_t soff, const uint32_t *s) {
-    const u32x4 v = {s[0], s[1], s[2], s[3]};
-    __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)voff, (int)soff, kNT);
+template <int NB>
+__device__ __forceinline__ void gstore(rsrc_t r, uint32_t voff, uint32_t soff, const uint32_t *s) {
+    if constexpr (NB == 16) {
+        const u32x4 v = {s[0], s[1], s[2], s[3]};
+        __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)voff, (int)soff, kNT);
+    } else {
+        static_assert(NB == 8, "8- or 16-byte accesses");
+        const u32x2 v = {s[0], s[1]};
+        __builtin_amdgcn_raw_buffer_store_b64(v, r, (int)voff, (int)soff, kNT);
+    }
+}
+
+// A run of NB bytes (a multiple of 8) between registers and LDS, in the widest units
+// that divide it.
+template <int NB>
+__device__ __forceinline__ void lds_write_run(char *p, const uint32_t *s) {
+    static_assert(NB % 8 == 0, "runs are whole 8-byte units");
+    if constexpr (NB % 16 == 0) {
+#pragma unroll
+        for (int q = 0; q < NB / 16; ++q)
+            *(uint4 *)(p + 16 * q) = make_uint4(s[4 * q], s[4 * q + 1], s[4 * q + 2], s[4 * q + 3]);
+    } else {
+#pragma unroll
+        for (int q = 0; q < NB / 8; ++q) *(uint2 *)(p + 8 * q) = make_uint2(s[2 * q], s[2 * q + 1]);
+    }
+}
+
+template <int NB>
+__device__ __forceinline__ void lds_read_run(const char *p, uint32_t *d) {
+    static_assert(NB % 8 == 0, "runs are whole 8-byte units");
+    if constexpr (NB % 16 == 0) {
+#pragma unroll
+        for (int q = 0; q < NB / 16; ++q) {
+            const uint4 v = *(const uint4 *)(p + 16 * q);
+            d[4 * q] = v.x; d[4 * q + 1] = v.y; d[4 * q + 2] = v.z; d[4 * q + 3] = v.w;
+        }
+    } else {
+#pragma unroll
+        for (int q = 0; q < NB / 8; ++q) {
+            const uint2 v = *(const uint2 *)(p + 8 * q);
+            d[2 * q] = v.x; d[2 * q + 1] = v.y;
+        }
+    }
 }
 
 template <int EB>
@@ -141,6 +187,16 @@ template <int EB>
 __device__ __forceinline__ void lds_put(char *p, uint32_t v) {
     if constexpr (EB == 4) *(uint32_t *)p = v;
     else *(uint16_t *)p = (uint16_t)v;
+}
+
+// Streams `chunks` 16-byte chunks from LDS (offset 0) to a buffer, lane-contiguous.
+__device__ __forceinline__ void lds_to_global(const char *lds, int chunks, rsrc_t r, uint32_t soff,
+                                              int lane) {
+    for (int q = lane; q < chunks; q += kWave) {
+        const uint4 v = *(const uint4 *)(lds + q * 16);
+        const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+        gstore<16>(r, (uint32_t)q * 16u, soff, w4);
+    }
 }
 
 // Orders LDS accesses across the workgroup (one wavefront) without waiting for the
@@ -156,13 +212,16 @@ __device__ __forceinline__ void lds_barrier() {
 
 template <int XB, int SB, int D, int TB, bool DEDUP>
 __global__ __launch_bounds__(kWave) void cv_verify_kernel(KernelArgs p) {
-    constexpr int CPL = 16 / XB;          // channels per lane
-    constexpr int CHW = kWave * CPL;      // channels per wavefront
-    constexpr int W1 = D - 1;             // window columns
-    constexpr int SW = CPL * SB / 4;      // 32-bit words per state-typed column
-    constexpr int RUNW = CPL * W1 * SB / 4;   // words of a lane's [ch][j] window run
-    constexpr int P = tile_pitch(CPL, SB);    // bytes per LDS tile row
-    static_assert(RUNW % 4 == 0 && SW % 4 == 0, "runs and columns are whole 16-byte units");
+    constexpr int CPL = kChannelsPerLane;     // channels per lane
+    constexpr int CHW = kWave * CPL;          // channels per wavefront
+    constexpr int W1 = D - 1;                 // window columns
+    constexpr int VB = CPL * XB;              // bytes of x / out per lane per token (8 or 16)
+    constexpr int XW = VB / 4;
+    constexpr int SCB = CPL * SB;             // bytes of a state-typed column per lane
+    constexpr int SW = SCB / 4;
+    constexpr int RUNB = CPL * W1 * SB;       // bytes of a lane's [CPL][W1] window run
+    constexpr int RUNW = RUNB / 4;
+    constexpr int P = tile_pitch(SB);         // bytes per LDS tile row
 
     extern __shared__ uint4 lds_raw[];
     char *lds = (char *)lds_raw;
@@ -179,65 +238,85 @@ __global__ __launch_bounds__(kWave) void cv_verify_kernel(KernelArgs p) {
 
     const int T = p.T;
     const int SL = p.state_len;
-    const int nch = min(CHW, p.d_inner - cb);       // channels of this wavefront
+    const int nch = min(CHW, p.d_inner - cb);   // channels of this wavefront
     const bool on = lane * CPL < nch;
-    const uint32_t lane16 = on ? (uint32_t)lane * 16u : kOffLane;
+    const uint32_t laneV = on ? (uint32_t)(lane * VB) : kOffLane;
     const bool contiguous_state = SL == W1;
 
-    // ---- loads: x (registers), window, weights, bias ----------------------------------
+    // ---- every load, issued up front -------------------------------------------------------
     const rsrc_t x_r = make_rsrc((const char *)p.x + ((int64_t)row * p.x_seq + cb) * XB,
                                  (uint32_t)(((int64_t)(T - 1) * p.x_tok + nch) * XB));
-    uint32_t X[TB][4];
+    uint32_t X[TB][XW];   // x_t for the lane's channels
 #pragma unroll
     for (int t = 0; t < TB; ++t) {
         if (t < T) {
-            load16(x_r, lane16, (uint32_t)(t * p.x_tok * XB), X[t]);
+            gload<VB>(x_r, laneV, (uint32_t)(t * p.x_tok * XB), X[t]);
         } else {
-            X[t][0] = X[t][1] = X[t][2] = X[t][3] = 0u;
+#pragma unroll
+            for (int w = 0; w < XW; ++w) X[t][w] = 0u;
         }
     }
 
-    // weights and bias: loaded with everything else, before the first barrier, so no
-    // load is outstanding once the stores start (vmcnt counts loads and stores together)
-    uint32_t wr[4 * D];   // CPL*D*XB bytes = 16*D
-    uint32_t br[4] = {0u, 0u, 0u, 0u};
+    uint32_t wr[XW * D];          // weights [CPL][D]
+    uint32_t br[XW];              // bias [CPL]
     {
         const rsrc_t w_r = make_rsrc((const char *)p.weight + (int64_t)cb * D * XB,
                                      (uint32_t)(nch * D * XB));
-        const uint32_t lw = on ? (uint32_t)lane * 16u * D : kOffLane;
+        const uint32_t lw = on ? (uint32_t)(lane * VB * D) : kOffLane;
 #pragma unroll
-        for (int q = 0; q < D; ++q) load16(w_r, lw + 16 * q, 0, wr + 4 * q);
+        for (int q = 0; q < D; ++q) gload<VB>(w_r, lw + VB * q, 0, wr + XW * q);
+#pragma unroll
+        for (int w = 0; w < XW; ++w) br[w] = 0u;
         if (p.bias) {
             const rsrc_t b_r = make_rsrc((const char *)p.bias + (int64_t)cb * XB,
                                          (uint32_t)(nch * XB));
-            load16(b_r, lane16, 0, br);
+            gload<VB>(b_r, laneV, 0, br);
         }
     }
 
     // conv_state: the wavefront's [nch, state_len] region is contiguous.  It comes in
-    // whole through LDS (direct loads, coalesced), each lane picks its channels'
-    // window out of it, writes its committed window back into it, and the region
-    // leaves whole (coalesced) - so every state byte is read once and written once
-    // in full 16-byte lane-contiguous units, whatever state_len and the offset are.
+    // whole (coalesced 16-byte loads, issued with the other loads) and is staged in
+    // LDS; each lane picks its channels' window out of it, writes its committed window
+    // back into it, and the region leaves whole - so every state byte is read once and
+    // written once in lane-contiguous 16-byte units, whatever state_len and the offset
+    // are.  (Direct global->LDS loads measured slower here than loads through VGPRs.)
     const rsrc_t st_r = make_rsrc((const char *)p.state + ((int64_t)slot * p.state_slot +
                                                            (int64_t)cb * SL) * SB,
                                   (uint32_t)(nch * SL * SB));
     const int rchunks = nch * SL * SB / 16;   // exact: nch * SB is a multiple of 16
-    for (int j = 0; j * kWave < rchunks; ++j) {
+    // chunks per lane, all in flight at once up to RJ; longer regions go in rounds
+    constexpr int RJ = (W1 * SB + 3) / 4 > 12 ? (W1 * SB + 3) / 4 : 12;
+    uint32_t sreg[RJ][4];
+#pragma unroll
+    for (int j = 0; j < RJ; ++j) {
         const int q = j * kWave + lane;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(st_r, (lds_void_t *)(lds + j * (kWave * 16)), 16,
-                                                 q < rchunks ? q * 16 : (int)kOffLane, 0, 0, kNT);
+        if (j * kWave < rchunks) gload<16>(st_r, q < rchunks ? (uint32_t)q * 16u : kOffLane, 0, sreg[j]);
     }
-    __syncthreads();   // waits for the direct loads (and x): nothing has been stored yet
+#pragma unroll
+    for (int j = 0; j < RJ; ++j) {
+        const int q = j * kWave + lane;
+        if (j * kWave < rchunks && q < rchunks)
+            *(uint4 *)(lds + q * 16) = make_uint4(sreg[j][0], sreg[j][1], sreg[j][2], sreg[j][3]);
+    }
+    for (int j0 = RJ; j0 * kWave < rchunks; j0 += RJ) {   // state_len beyond the in-flight set
+#pragma unroll
+        for (int j = 0; j < RJ; ++j) {
+            const int q = (j0 + j) * kWave + lane;
+            if ((j0 + j) * kWave < rchunks) gload<16>(st_r, q < rchunks ? (uint32_t)q * 16u : kOffLane, 0, sreg[j]);
+        }
+#pragma unroll
+        for (int j = 0; j < RJ; ++j) {
+            const int q = (j0 + j) * kWave + lane;
+            if ((j0 + j) * kWave < rchunks && q < rchunks)
+                *(uint4 *)(lds + q * 16) = make_uint4(sreg[j][0], sreg[j][1], sreg[j][2], sreg[j][3]);
+        }
+    }
+    lds_barrier();
+
     uint32_t S[W1][SW];   // initial window columns v[0..W1-1], state-typed bits
     if (contiguous_state) {
-        // the lane's [CPL][W1] run: RUNW/4 aligned 16-byte LDS reads
-        uint32_t run[RUNW];
-#pragma unroll
-        for (int q = 0; q < RUNW / 4; ++q) {
-            const uint4 v = *(const uint4 *)(lds + lane * (RUNW * 4) + 16 * q);
-            run[4 * q] = v.x; run[4 * q + 1] = v.y; run[4 * q + 2] = v.z; run[4 * q + 3] = v.w;
-        }
+        uint32_t run[RUNW];   // the lane's [CPL][W1] run
+        lds_read_run<RUNB>(lds + lane * RUNB, run);
 #pragma unroll
         for (int j = 0; j < W1; ++j)
 #pragma unroll
@@ -282,7 +361,7 @@ __global__ __launch_bounds__(kWave) void cv_verify_kernel(KernelArgs p) {
         return k < W1 ? elem_bits<SB>(S[k < W1 ? k : 0], ch)
                       : x_to_state_bits<XB, SB>(elem_bits<XB>(X[k < W1 ? 0 : k - W1], ch));
     };
-    // The lane's CPL x (D-1) run of the window v[k0 .. k0+W1-1] ([ch][j] order), packed.
+    // The lane's [CPL][W1] run of the window v[k0 .. k0+W1-1], packed.
     auto window_run = [&](int k0, uint32_t *run) {
 #pragma unroll
         for (int w = 0; w < RUNW; ++w) {
@@ -294,7 +373,7 @@ __global__ __launch_bounds__(kWave) void cv_verify_kernel(KernelArgs p) {
             }
         }
     };
-    // Column v[k] in the state type (SW words).
+    // Column v[k] (the lane's CPL channels) in the state type.
     auto column = [&](int k, uint32_t *col) {
         if (k < W1) {
 #pragma unroll
@@ -309,41 +388,32 @@ __global__ __launch_bounds__(kWave) void cv_verify_kernel(KernelArgs p) {
         }
     };
 
-    {
-        // committed window v[T .. T+W1-1] into columns 0..W1-1 of the staged rows, then
-        // the whole region goes back out.  Each lane rewrites only its own channels'
-        // records, after having read them above.
+    // ---- committed window -> conv_state -----------------------------------------------------
+    // v[T .. T+W1-1] into columns 0..W1-1 of the staged rows (each lane rewrites only
+    // its own channels' records, after having read them above), then the region leaves.
 #pragma unroll
-        for (int t = 0; t < TB; ++t) {
-            if (t == T - 1) {
-                if (contiguous_state) {
-                    uint32_t run[RUNW];
-                    window_run(t + 1, run);
+    for (int t = 0; t < TB; ++t) {
+        if (t == T - 1) {
+            if (contiguous_state) {
+                uint32_t run[RUNW];
+                window_run(t + 1, run);
+                lds_write_run<RUNB>(lds + lane * RUNB, run);
+            } else {
+                char *rec = lds + lane * CPL * SL * SB;
 #pragma unroll
-                    for (int q = 0; q < RUNW / 4; ++q)
-                        *(uint4 *)(lds + lane * (RUNW * 4) + 16 * q) =
-                            make_uint4(run[4 * q], run[4 * q + 1], run[4 * q + 2], run[4 * q + 3]);
-                } else {
-                    char *rec = lds + lane * CPL * SL * SB;
+                for (int ch = 0; ch < CPL; ++ch)
 #pragma unroll
-                    for (int ch = 0; ch < CPL; ++ch)
-#pragma unroll
-                        for (int j = 0; j < W1; ++j)
-                            lds_put<SB>(rec + (ch * SL + j) * SB, sbits(t + 1 + j, ch));
-                }
+                    for (int j = 0; j < W1; ++j)
+                        lds_put<SB>(rec + (ch * SL + j) * SB, sbits(t + 1 + j, ch));
             }
         }
-        lds_barrier();
-        for (int q = lane; q < rchunks; q += kWave) {
-            const uint4 v = *(const uint4 *)(lds + q * 16);
-            const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
-            store16(st_r, (uint32_t)q * 16u, 0, w4);
-        }
-        lds_barrier();   // the region's LDS is reused below
     }
+    lds_barrier();
+    lds_to_global(lds, rchunks, st_r, 0, lane);
+    lds_barrier();   // the region's LDS is reused below
 
-    // ---- rollback windows: pure copies of the inputs, written before any arithmetic so
-    // the stores drain while the wavefront computes --------------------------------------
+    // ---- rollback windows: pure copies of the inputs, written before the arithmetic so
+    // the stores drain while the wavefront computes ------------------------------------------
     if constexpr (DEDUP) {
         const int L = T + W1 - 1;             // row length: v[1 .. T+W1-1]
         const rsrc_t row_r = make_rsrc(
@@ -351,18 +421,19 @@ __global__ __launch_bounds__(kWave) void cv_verify_kernel(KernelArgs p) {
             (uint32_t)(nch * L * SB));
         if (T == TB) {
             // Row length known at compile time: each lane assembles its channels' rows
-            // ([CPL][LC], contiguous in the row layout) in registers, 16 bytes at a time,
-            // into LDS at the same offsets, and the wavefront streams the block out in
-            // lane-contiguous 16-byte units.
+            // ([CPL][LC], contiguous in the row layout) in registers into LDS at the
+            // same offsets, and the wavefront streams the block out lane-contiguously.
             constexpr int LC = TB + W1 - 1;
-            constexpr int CW = CPL * LC * SB / 4;   // 32-bit words of a lane's rows
-            char *mine = lds + lane * (CPL * LC * SB);
+            constexpr int LANEB = CPL * LC * SB;   // bytes of a lane's rows
+            constexpr int CW = LANEB / 4;
+            constexpr int PIECE = (LANEB % 16 == 0) ? 16 : 8;
+            char *mine = lds + lane * LANEB;
 #pragma unroll
-            for (int q = 0; q < CW / 4; ++q) {
-                uint32_t w4[4];
+            for (int q = 0; q < CW / (PIECE / 4); ++q) {
+                uint32_t w4[PIECE / 4];
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int wd = 4 * q + i;
+                for (int i = 0; i < PIECE / 4; ++i) {
+                    const int wd = (PIECE / 4) * q + i;
                     if constexpr (SB == 4) {
                         w4[i] = sbits(wd % LC + 1, wd / LC);
                     } else {
@@ -370,83 +441,75 @@ __global__ __launch_bounds__(kWave) void cv_verify_kernel(KernelArgs p) {
                         w4[i] = sbits(e0 % LC + 1, e0 / LC) | (sbits(e1 % LC + 1, e1 / LC) << 16);
                     }
                 }
-                *(uint4 *)(mine + 16 * q) = make_uint4(w4[0], w4[1], w4[2], w4[3]);
+                lds_write_run<PIECE>(mine + PIECE * q, w4);
             }
             lds_barrier();
-            const int nchunks = nch * LC * SB / 16;
-            for (int q = lane; q < nchunks; q += kWave) {
-                const uint4 v = *(const uint4 *)(lds + q * 16);
-                const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
-                store16(row_r, (uint32_t)q * 16u, 0, w4);
-            }
+            lds_to_global(lds, nch * LC * SB / 16, row_r, 0, lane);
         } else {
-        // Tile row r holds v[r+1] for the wavefront's channels (16-byte LDS writes);
-        // rows 0..W1-2 come from the initial window, the rest are x_0..x_{T-1}.
+            // Tile row r holds v[r+1] for the wavefront's channels; rows 0..W1-2 come
+            // from the initial window, the rest are x_0..x_{T-1}.
 #pragma unroll
-        for (int k = 1; k < W1 + TB; ++k) {
-            if (k < W1 + T) {
-                uint32_t col[SW];
-                column(k, col);
-#pragma unroll
-                for (int q = 0; q < SW / 4; ++q)
-                    *(uint4 *)(lds + (k - 1) * P + lane * (CPL * SB) + 16 * q) =
-                        make_uint4(col[4 * q], col[4 * q + 1], col[4 * q + 2], col[4 * q + 3]);
-            }
-        }
-        lds_barrier();
-        // Stream the tile out in the row layout [c][k], k < L: chunk q of the
-        // wavefront's contiguous row block holds elements e = q*EPC .. q*EPC+EPC-1,
-        // element e = (channel e / L, column e % L) = tile row e % L, channel e / L.
-        constexpr int EPC = 16 / SB;   // elements per 16-byte chunk
-        const int nchunks = nch * L / EPC;   // exact: nch is a multiple of CPL
-        const int e0 = lane * EPC;
-        int cc = e0 / L;
-        int kk = e0 - cc * L;
-        const int dq = (kWave * EPC) / L;
-        const int dr = kWave * EPC - dq * L;
-        if (L >= EPC) {
-            // a chunk spans at most two channels: columns kk.. of channel cc, then
-            // columns 0.. of channel cc+1; each element is one LDS read at a fixed
-            // row step from one of two bases
-            for (int q = lane; q < nchunks; q += kWave) {
-                const int split = L - kk;
-                const uint32_t b1 = (uint32_t)(kk * P + cc * SB);
-                const uint32_t b2 = b1 + (uint32_t)SB - (uint32_t)(L * P);
-                uint32_t w[4];
-#pragma unroll
-                for (int m = 0; m < EPC; ++m) {
-                    const uint32_t b = lds_get<SB>(lds + ((m < split ? b1 : b2) + m * P));
-                    if constexpr (SB == 4) {
-                        w[m] = b;
-                    } else {
-                        if (m & 1) w[m >> 1] |= b << 16; else w[m >> 1] = b;
-                    }
+            for (int k = 1; k < W1 + TB; ++k) {
+                if (k < W1 + T) {
+                    uint32_t col[SW];
+                    column(k, col);
+                    lds_write_run<SCB>(lds + (k - 1) * P + lane * SCB, col);
                 }
-                store16(row_r, (uint32_t)q * 16u, 0, w);
-                cc += dq;
-                kk += dr;
-                if (kk >= L) { kk -= L; ++cc; }
             }
-        } else {
-            for (int q = lane; q < nchunks; q += kWave) {
-                uint32_t w[4];
-                int c2 = cc, k2 = kk;
+            lds_barrier();
+            // Stream the tile out in the row layout [c][k], k < L: chunk q of the
+            // wavefront's contiguous row block holds elements e = q*EPC .. q*EPC+EPC-1,
+            // element e = (channel e / L, column e % L) = tile row e % L, channel e / L.
+            constexpr int EPC = 16 / SB;   // elements per 16-byte chunk
+            const int nchunks = nch * L / EPC;   // exact: nch * SB is a multiple of 16
+            const int e0 = lane * EPC;
+            int cc = e0 / L;
+            int kk = e0 - cc * L;
+            const int dq = (kWave * EPC) / L;
+            const int dr = kWave * EPC - dq * L;
+            if (L >= EPC) {
+                // a chunk spans at most two channels: columns kk.. of channel cc, then
+                // columns 0.. of channel cc+1; each element is one LDS read at a fixed
+                // row step from one of two bases
+                for (int q = lane; q < nchunks; q += kWave) {
+                    const int split = L - kk;
+                    const uint32_t b1 = (uint32_t)(kk * P + cc * SB);
+                    const uint32_t b2 = b1 + (uint32_t)SB - (uint32_t)(L * P);
+                    uint32_t w[4];
 #pragma unroll
-                for (int m = 0; m < EPC; ++m) {
-                    const uint32_t b = lds_get<SB>(lds + k2 * P + c2 * SB);
-                    if constexpr (SB == 4) {
-                        w[m] = b;
-                    } else {
-                        if (m & 1) w[m >> 1] |= b << 16; else w[m >> 1] = b;
+                    for (int m = 0; m < EPC; ++m) {
+                        const uint32_t b = lds_get<SB>(lds + ((m < split ? b1 : b2) + m * P));
+                        if constexpr (SB == 4) {
+                            w[m] = b;
+                        } else {
+                            if (m & 1) w[m >> 1] |= b << 16; else w[m >> 1] = b;
+                        }
                     }
-                    if (++k2 == L) { k2 = 0; ++c2; }
+                    gstore<16>(row_r, (uint32_t)q * 16u, 0, w);
+                    cc += dq;
+                    kk += dr;
+                    if (kk >= L) { kk -= L; ++cc; }
                 }
-                store16(row_r, (uint32_t)q * 16u, 0, w);
-                cc += dq;
-                kk += dr;
-                while (kk >= L) { kk -= L; ++cc; }
+            } else {
+                for (int q = lane; q < nchunks; q += kWave) {
+                    uint32_t w[4];
+                    int c2 = cc, k2 = kk;
+#pragma unroll
+                    for (int m = 0; m < EPC; ++m) {
+                        const uint32_t b = lds_get<SB>(lds + k2 * P + c2 * SB);
+                        if constexpr (SB == 4) {
+                            w[m] = b;
+                        } else {
+                            if (m & 1) w[m >> 1] |= b << 16; else w[m >> 1] = b;
+                        }
+                        if (++k2 == L) { k2 = 0; ++c2; }
+                    }
+                    gstore<16>(row_r, (uint32_t)q * 16u, 0, w);
+                    cc += dq;
+                    kk += dr;
+                    while (kk >= L) { kk -= L; ++cc; }
+                }
             }
-        }
         }
     } else {
         // Dense snapshot t = v[t+1 .. t+W1]: the wavefront's [nch, W1] slab is contiguous.
@@ -464,17 +527,9 @@ __global__ __launch_bounds__(kWave) void cv_verify_kernel(KernelArgs p) {
                 char *slab = lds + (t & 1) * SLAB;
                 uint32_t run[RUNW];
                 window_run(t + 1, run);
-#pragma unroll
-                for (int q = 0; q < RUNW / 4; ++q)
-                    *(uint4 *)(slab + lane * (RUNW * 4) + 16 * q) =
-                        make_uint4(run[4 * q], run[4 * q + 1], run[4 * q + 2], run[4 * q + 3]);
+                lds_write_run<RUNB>(slab + lane * RUNB, run);
                 lds_barrier();
-                const uint32_t soff = (uint32_t)(t * p.d_inner * W1 * SB);
-                for (int q = lane; q < slab_chunks; q += kWave) {
-                    const uint4 v = *(const uint4 *)(slab + q * 16);
-                    const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
-                    store16(snap_r, (uint32_t)q * 16u, soff, w4);
-                }
+                lds_to_global(slab, slab_chunks, snap_r, (uint32_t)(t * p.d_inner * W1 * SB), lane);
             }
         }
     }
@@ -506,20 +561,20 @@ __global__ __launch_bounds__(kWave) void cv_verify_kernel(KernelArgs p) {
                     for (int ch = 0; ch < CPL; ++ch) y[ch] *= sc;
                 }
             }
-            uint32_t o[4];
+            uint32_t o[XW];
             if constexpr (XB == 4) {
 #pragma unroll
-                for (int ch = 0; ch < 4; ++ch) o[ch] = __float_as_uint(y[ch]);
+                for (int ch = 0; ch < CPL; ++ch) o[ch] = __float_as_uint(y[ch]);
             } else {
                 typedef float f2 __attribute__((ext_vector_type(2)));
                 typedef __bf16 b2 __attribute__((ext_vector_type(2)));
 #pragma unroll
-                for (int w = 0; w < 4; ++w) {
+                for (int w = 0; w < XW; ++w) {
                     f2 pr = {y[2 * w], y[2 * w + 1]};
                     o[w] = __builtin_bit_cast(uint32_t, __builtin_convertvector(pr, b2));
                 }
             }
-            store16(o_r, lane16, (uint32_t)(t * p.out_tok * XB), o);
+            gstore<VB>(o_r, laneV, (uint32_t)(t * p.out_tok * XB), o);
         }
     }
 }

@@ -58,8 +58,9 @@
  *    memory outside the buffers.  Two rows sharing a slot race.
  *  - Buffers must not overlap each other (x and weight/bias may).
  *  - Alignment (else CV_ENOTSUP): every pointer 16-byte aligned; d_inner, the x/out
- *    strides and head_dim multiples of 16/sizeof(x element) (8 for bf16, 4 for fp32);
- *    state_slot_stride and win_slot_stride multiples of 16 bytes.
+ *    strides multiples of 16/sizeof(x element) (8 for bf16, 4 for fp32);
+ *    state_slot_stride and win_slot_stride multiples of 16 bytes; head_dim one of
+ *    4, 8, 16, 32, 64, 128, 256 (a head is reduced inside one 256-channel wavefront).
  *  - Numerics: the conv accumulates in fp32 as acc = bias (or +0); for w = 0..D-1:
  *    acc = fma(weight[c,w], v[t+w], acc), each step one correctly rounded fused
  *    multiply-add.  SiLU and L2 run in fp32.  Windows and conv_state are moved as bit
@@ -94,7 +95,7 @@ typedef struct cv_shape {
     int32_t d_conv;       /* conv width D, 2..4                                             */
     int32_t qk_channels;  /* leading channels normalised per head, 0..d_inner; 0 = no L2    */
     int32_t head_dim;     /* channels per L2 head: qk_channels % head_dim == 0 and
-                             head_dim / (16/sizeof(x element)) a power of two <= 64         */
+                             head_dim / 4 a power of two <= 64 (4 channels per lane)        */
     float l2_eps;         /* >= 0 and finite                                                */
     int32_t x_dtype;      /* cv_dtype_t of x, weight, bias and out                          */
     int32_t state_dtype;  /* cv_dtype_t of conv_state and the windows.  Supported pairs

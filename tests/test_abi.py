@@ -92,9 +92,10 @@ BAD_SHAPES = [
     ("qk<0", dict(qk_channels=-128), EINVAL),
     ("qk%head", dict(qk_channels=520, head_dim=128), EINVAL),
     ("head<=0", dict(head_dim=0), EINVAL),
-    ("head%8", dict(qk_channels=12 * 20, head_dim=12), ENOTSUP),
+    ("head%4", dict(qk_channels=6 * 20, head_dim=6), ENOTSUP),
+    ("head_lanes_3", dict(qk_channels=12 * 20, head_dim=12), ENOTSUP),
     ("head_lanes_not_pow2", dict(qk_channels=96 * 5, head_dim=96), ENOTSUP),
-    ("head_lanes>64", dict(qk_channels=1024, head_dim=1024), ENOTSUP),
+    ("head_lanes>64", dict(qk_channels=1024, head_dim=512), ENOTSUP),
     ("eps<0", dict(l2_eps=-1.0), EINVAL),
     ("eps_nan", dict(l2_eps=float("nan")), EINVAL),
     ("eps_inf", dict(l2_eps=float("inf")), EINVAL),
@@ -122,11 +123,14 @@ def test_window_stride_checked_per_layout():
     assert describe(1, shape(win_slot_stride=10240))[0] == 0
 
 
-def test_dedup_lds_limit():
-    # bf16 x with fp32 state, T=32: 34 rows of 512 fp32 + pad = 70176 bytes > 64 KiB
-    rc, _, detail = describe(1, shape(T=32, state_dtype=lib_mod.CV_F32, x_seq_stride=32 * 1024,
-                                      out_seq_stride=32 * 1024, win_slot_stride=1024 * 34))
+def test_lds_limit():
+    # a 256-channel wavefront stages its [256, state_len] state rows in LDS: fp32 rows
+    # of 65 columns need 66560 bytes > 64 KiB
+    rc, _, detail = describe(1, shape(state_dtype=lib_mod.CV_F32, state_len=65,
+                                      state_slot_stride=1024 * 65, win_slot_stride=1024 * 10))
     assert rc == ENOTSUP and "LDS" in detail
+    assert describe(1, shape(state_dtype=lib_mod.CV_F32, state_len=64,
+                             state_slot_stride=1024 * 64, win_slot_stride=1024 * 10))[0] == 0
 
 
 @pytest.mark.parametrize("key", [0, 1, 2, 3, 4, "4b", "4s"])
@@ -147,7 +151,7 @@ def test_launch_geometry_of_workloads(key):
               state_slot_stride=wl.d_inner * wl.state_len, win_slot_stride=win)
     rc, info, detail = describe(int(wl.layout == "dedup"), s)
     assert rc == 0, detail
-    cpl = 16 // xb
+    cpl = 4
     assert info.channels_per_lane == cpl and info.threads == 64
     assert info.channels_per_wave == 64 * cpl
     assert info.channel_blocks == -(-wl.d_inner // (64 * cpl))

@@ -59,7 +59,7 @@ def _sweep():
                                qk_channels=256, head_dim=128 if xd == "bf16" else 64, T=T,
                                x_dtype=xd, state_dtype=sd, layout=layout,
                                accept_offsets=(T > 1), permute_slots=True, pad_frac=0.3))
-    for hd in (8, 16, 32, 64, 256, 512):
+    for hd in (4, 8, 16, 32, 64, 256):
         cases.append(c(f"head{hd}", n_seq=2, d_inner=1536, qk_channels=1024, head_dim=hd, T=4,
                        layout="dedup"))
     for hd in (4, 8, 16, 32, 256):
