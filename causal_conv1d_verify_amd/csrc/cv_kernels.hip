@@ -82,18 +82,34 @@ __device__ __forceinline__ float dpp(float v) {
     return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, true));
 }
 
-// Sum over the 2^hl_log2 lanes of an aligned lane group (all lanes active).  Each
-// step adds the two halves of a group symmetrically, so all lanes of a group hold
-// the bit-identical sum.
-__device__ __forceinline__ float group_sum(float v, int hl_log2) {
-    if (hl_log2 >= 1) v += dpp<0xB1>(v);    // quad_perm [1,0,3,2]: lane ^ 1
-    if (hl_log2 >= 2) v += dpp<0x4E>(v);    // quad_perm [2,3,0,1]: lane ^ 2
-    if (hl_log2 >= 3) v += dpp<0x141>(v);   // row_half_mirror: other quad of the 8
-    if (hl_log2 >= 4) v += dpp<0x140>(v);   // row_mirror: other half of the 16-lane row
-    if (hl_log2 >= 5)                       // lane ^ 16 inside 32 (ds_swizzle xor mode)
-        v += __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x401F));
-    if (hl_log2 >= 6) v += __shfl_xor(v, 32);
-    return v;
+// Sums over the 2^hl_log2 lanes of an aligned lane group (all lanes active), for each
+// of G independent values at once: every stage is applied to all G values before the
+// next, so their cross-lane latencies overlap.  Each step adds the two halves of a
+// group symmetrically, so all lanes of a group hold the bit-identical sum.
+template <int G>
+__device__ __forceinline__ void group_sums(float (&v)[G], int hl_log2) {
+    if (hl_log2 >= 1)   // quad_perm [1,0,3,2]: lane ^ 1
+#pragma unroll
+        for (int g = 0; g < G; ++g) v[g] += dpp<0xB1>(v[g]);
+    if (hl_log2 >= 2)   // quad_perm [2,3,0,1]: lane ^ 2
+#pragma unroll
+        for (int g = 0; g < G; ++g) v[g] += dpp<0x4E>(v[g]);
+    if (hl_log2 >= 3)   // row_half_mirror: the other quad of the 8
+#pragma unroll
+        for (int g = 0; g < G; ++g) v[g] += dpp<0x141>(v[g]);
+    if (hl_log2 >= 4)   // row_mirror: the other half of the 16-lane row
+#pragma unroll
+        for (int g = 0; g < G; ++g) v[g] += dpp<0x140>(v[g]);
+    if (hl_log2 >= 5)   // lane ^ 16 inside 32 (ds_swizzle xor mode)
+#pragma unroll
+        for (int g = 0; g < G; ++g)
+            v[g] += __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v[g]), 0x401F));
+    if (hl_log2 >= 6) {  // lane ^ 32
+        const int src = (int)((threadIdx.x ^ 32u) << 2);
+#pragma unroll
+        for (int g = 0; g < G; ++g)
+            v[g] += __int_as_float(__builtin_amdgcn_ds_bpermute(src, __float_as_int(v[g])));
+    }
 }
 
 // ---- raw buffer access ------------------------------------------------------------------
@@ -199,6 +215,13 @@ __device__ __forceinline__ void lds_to_global(const char *lds, int chunks, rsrc_
     }
 }
 
+// A wavefront-uniform int read through the constant address space, so it is a scalar
+// load: it waits on its own counter, not behind the vector loads already in flight.
+// Only for data no kernel writes while this one runs (slot indices, offsets).
+__device__ __forceinline__ int scalar_read(const int32_t *p, int i) {
+    return *((const __attribute__((address_space(4))) int32_t *)p + i);
+}
+
 // Orders LDS accesses across the workgroup (one wavefront) without waiting for the
 // wavefront's global stores: __syncthreads() is a release fence for all memory, which
 // would make every LDS hand-off wait for the writes issued before it to reach memory.
@@ -230,11 +253,10 @@ __global__ __launch_bounds__(kWave) void cv_verify_kernel(KernelArgs p) {
     const int row = (int)(blockIdx.x / (unsigned)p.channel_blocks);
     const int cb = (int)(blockIdx.x - (unsigned)row * (unsigned)p.channel_blocks) * CHW;
 
-    const int slot = p.slot_idx ? p.slot_idx[row] : row;
-    const int a = p.nat ? p.nat[row] : 0;
-    // Padded rows (slot -1) leave before any store; rows with an index that would
-    // address outside the buffers are skipped the same way.
-    if (slot < 0 || slot >= p.n_slots || a < 0 || a > p.state_len - W1) return;
+    // The row's slot and offset are read now (scalar loads) and tested once the loads
+    // that do not depend on them are on their way.
+    const int slot = p.slot_idx ? scalar_read(p.slot_idx, row) : row;
+    const int a = p.nat ? scalar_read(p.nat, row) : 0;
 
     const int T = p.T;
     const int SL = p.state_len;
@@ -244,6 +266,10 @@ __global__ __launch_bounds__(kWave) void cv_verify_kernel(KernelArgs p) {
     const bool contiguous_state = SL == W1;
 
     // ---- every load, issued up front -------------------------------------------------------
+    // Raised wave priority while this wavefront issues its loads: when several
+    // wavefronts of a SIMD are ready, the ones still issuing loads go first, so reads
+    // enter the memory pipeline ahead of other wavefronts' stores.
+    __builtin_amdgcn_s_setprio(3);
     const rsrc_t x_r = make_rsrc((const char *)p.x + ((int64_t)row * p.x_seq + cb) * XB,
                                  (uint32_t)(((int64_t)(T - 1) * p.x_tok + nch) * XB));
     uint32_t X[TB][XW];   // x_t for the lane's channels
@@ -272,6 +298,14 @@ __global__ __launch_bounds__(kWave) void cv_verify_kernel(KernelArgs p) {
                                          (uint32_t)(nch * XB));
             gload<VB>(b_r, laneV, 0, br);
         }
+    }
+
+    // Padded rows (slot -1) leave before any store; rows with an index that would
+    // address outside the buffers are skipped the same way.  The loads above stay in
+    // bounds for every row; wait for them before leaving.
+    if (slot < 0 || slot >= p.n_slots || a < 0 || a > p.state_len - W1) {
+        __builtin_amdgcn_s_waitcnt(0);
+        return;
     }
 
     // conv_state: the wavefront's [nch, state_len] region is contiguous.  It comes in
@@ -311,6 +345,7 @@ __global__ __launch_bounds__(kWave) void cv_verify_kernel(KernelArgs p) {
                 *(uint4 *)(lds + q * 16) = make_uint4(sreg[j][0], sreg[j][1], sreg[j][2], sreg[j][3]);
         }
     }
+    __builtin_amdgcn_s_setprio(0);
     lds_barrier();
 
     uint32_t S[W1][SW];   // initial window columns v[0..W1-1], state-typed bits
@@ -388,6 +423,70 @@ __global__ __launch_bounds__(kWave) void cv_verify_kernel(KernelArgs p) {
         }
     };
 
+    // ---- conv + SiLU + per-head L2 -> out --------------------------------------------------
+    // The arithmetic runs as soon as the inputs are in, before the copies below: while
+    // the memory pipeline is still full of other wavefronts' traffic, a wavefront that
+    // stores first would stall at its stores with its arithmetic still ahead of it.
+    const bool wave_l2 = cb < p.qk;    // uniform: this wavefront holds q|k channels
+    const bool lane_l2 = lane * CPL + cb < p.qk;
+    const rsrc_t o_r = make_rsrc((char *)p.out + ((int64_t)row * p.out_seq + cb) * XB,
+                                 (uint32_t)(((int64_t)(T - 1) * p.out_tok + nch) * XB));
+    // Tokens go in chunks of up to 8 with no branch inside a chunk: x past T reads as
+    // zeros and those tokens are computed but never stored.  The chunk's exponentials,
+    // reciprocals and cross-lane sums are then independent and overlap.
+    constexpr int G = TB < 8 ? TB : 8;
+#pragma unroll
+    for (int t0 = 0; t0 < TB; t0 += G) {
+        if (t0 < T) {   // uniform guard; the loops are fully unrolled
+            float y[G][CPL];
+#pragma unroll
+            for (int g = 0; g < G; ++g)
+#pragma unroll
+                for (int ch = 0; ch < CPL; ++ch) {
+                    float acc = bv[ch];
+#pragma unroll
+                    for (int w = 0; w < D; ++w)
+                        acc = __builtin_fmaf(wv[ch][w], val(t0 + g + w, ch), acc);
+                    y[g][ch] = silu(acc);
+                }
+            if (wave_l2) {
+                float ss[G];
+#pragma unroll
+                for (int g = 0; g < G; ++g) {
+                    ss[g] = 0.0f;
+#pragma unroll
+                    for (int ch = 0; ch < CPL; ++ch) ss[g] = __builtin_fmaf(y[g][ch], y[g][ch], ss[g]);
+                }
+                group_sums<G>(ss, p.head_lanes_log2);
+#pragma unroll
+                for (int g = 0; g < G; ++g) {
+                    const float sc = lane_l2 ? __builtin_amdgcn_rsqf(ss[g] + p.eps) : 1.0f;
+#pragma unroll
+                    for (int ch = 0; ch < CPL; ++ch) y[g][ch] *= sc;
+                }
+            }
+#pragma unroll
+            for (int g = 0; g < G; ++g) {
+                const int t = t0 + g;
+                if (t < T) {
+                    uint32_t o[XW];
+                    if constexpr (XB == 4) {
+#pragma unroll
+                        for (int ch = 0; ch < CPL; ++ch) o[ch] = __float_as_uint(y[g][ch]);
+                    } else {
+                        typedef float f2 __attribute__((ext_vector_type(2)));
+                        typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+#pragma unroll
+                        for (int w = 0; w < XW; ++w) {
+                            f2 pr = {y[g][2 * w], y[g][2 * w + 1]};
+                            o[w] = __builtin_bit_cast(uint32_t, __builtin_convertvector(pr, b2));
+                        }
+                    }
+                    gstore<VB>(o_r, laneV, (uint32_t)(t * p.out_tok * XB), o);
+                }
+            }
+        }
+    }
     // ---- committed window -> conv_state -----------------------------------------------------
     // v[T .. T+W1-1] into columns 0..W1-1 of the staged rows (each lane rewrites only
     // its own channels' records, after having read them above), then the region leaves.
@@ -412,8 +511,7 @@ __global__ __launch_bounds__(kWave) void cv_verify_kernel(KernelArgs p) {
     lds_to_global(lds, rchunks, st_r, 0, lane);
     lds_barrier();   // the region's LDS is reused below
 
-    // ---- rollback windows: pure copies of the inputs, written before the arithmetic so
-    // the stores drain while the wavefront computes ------------------------------------------
+    // ---- rollback windows: pure copies of the inputs ---------------------------------------
     if constexpr (DEDUP) {
         const int L = T + W1 - 1;             // row length: v[1 .. T+W1-1]
         const rsrc_t row_r = make_rsrc(
@@ -534,49 +632,6 @@ __global__ __launch_bounds__(kWave) void cv_verify_kernel(KernelArgs p) {
         }
     }
 
-    // ---- conv + SiLU + per-head L2 -> out --------------------------------------------------
-    const bool wave_l2 = cb < p.qk;    // uniform: this wavefront holds q|k channels
-    const bool lane_l2 = lane * CPL + cb < p.qk;
-    const rsrc_t o_r = make_rsrc((char *)p.out + ((int64_t)row * p.out_seq + cb) * XB,
-                                 (uint32_t)(((int64_t)(T - 1) * p.out_tok + nch) * XB));
-#pragma unroll
-    for (int t = 0; t < TB; ++t) {
-        if (t < T) {   // uniform guard; the loop itself is fully unrolled
-            float y[CPL];
-#pragma unroll
-            for (int ch = 0; ch < CPL; ++ch) {
-                float acc = bv[ch];
-#pragma unroll
-                for (int w = 0; w < D; ++w) acc = __builtin_fmaf(wv[ch][w], val(t + w, ch), acc);
-                y[ch] = silu(acc);
-            }
-            if (wave_l2) {
-                float ss = 0.0f;
-#pragma unroll
-                for (int ch = 0; ch < CPL; ++ch) ss = __builtin_fmaf(y[ch], y[ch], ss);
-                ss = group_sum(ss, p.head_lanes_log2);
-                const float sc = __builtin_amdgcn_rsqf(ss + p.eps);
-                if (lane_l2) {
-#pragma unroll
-                    for (int ch = 0; ch < CPL; ++ch) y[ch] *= sc;
-                }
-            }
-            uint32_t o[XW];
-            if constexpr (XB == 4) {
-#pragma unroll
-                for (int ch = 0; ch < CPL; ++ch) o[ch] = __float_as_uint(y[ch]);
-            } else {
-                typedef float f2 __attribute__((ext_vector_type(2)));
-                typedef __bf16 b2 __attribute__((ext_vector_type(2)));
-#pragma unroll
-                for (int w = 0; w < XW; ++w) {
-                    f2 pr = {y[2 * w], y[2 * w + 1]};
-                    o[w] = __builtin_bit_cast(uint32_t, __builtin_convertvector(pr, b2));
-                }
-            }
-            gstore<VB>(o_r, laneV, (uint32_t)(t * p.out_tok * XB), o);
-        }
-    }
 }
 
 // ---- instantiation ----------------------------------------------------------------------
