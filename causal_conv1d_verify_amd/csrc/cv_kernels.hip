@@ -431,10 +431,12 @@ __global__ __launch_bounds__(kWave) void cv_verify_kernel(KernelArgs p) {
     const bool lane_l2 = lane * CPL + cb < p.qk;
     const rsrc_t o_r = make_rsrc((char *)p.out + ((int64_t)row * p.out_seq + cb) * XB,
                                  (uint32_t)(((int64_t)(T - 1) * p.out_tok + nch) * XB));
-    // Tokens go in chunks of up to 8 with no branch inside a chunk: x past T reads as
-    // zeros and those tokens are computed but never stored.  The chunk's exponentials,
-    // reciprocals and cross-lane sums are then independent and overlap.
-    constexpr int G = TB < 8 ? TB : 8;
+    // Tokens go in chunks with no branch inside a chunk: x past T reads as zeros and
+    // those tokens are computed but never stored.  The chunk's exponentials,
+    // reciprocals and cross-lane sums are then independent and overlap.  Buckets up
+    // to 8 are one chunk; larger ones use chunks of 4, which bounds the registers and
+    // the work spent past T.
+    constexpr int G = TB <= 8 ? TB : 4;
 #pragma unroll
     for (int t0 = 0; t0 < TB; t0 += G) {
         if (t0 < T) {   // uniform guard; the loops are fully unrolled
