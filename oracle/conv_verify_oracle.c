@@ -165,19 +165,70 @@ static float state_bits_val(const orc_problem *p, uint32_t bits) {
 }
 
 /*
- * Runs the whole batch.  conv_state is updated in place; out and windows are
- * written for active rows only.  pre_dbg (fp32) and y_dbg (fp64, after L2, before
- * rounding), if not NULL, receive [n_seq, T, d_inner] contiguous copies of the
- * intermediate values for the self-tests.
- *
- * Returns ORC_BAD if the problem is malformed or a row's slot or offset is out of
- * range (nothing is written then), ORC_NOMEM on allocation failure.
+ * Window layouts of the rollback buffer (T = p->n_tok, the buffer's token count):
+ *   ORC_DENSE  win[s, t, c, j]                       [T, dim, K-1] per slot
+ *   ORC_ROWS   win[s, c, t + j], row length T+K-2    one [dim, T+K-2] row per slot
+ *   ORC_ROWS_T win[s, t + j, c]                      the same row stored time-major,
+ *                                                    [T+K-2, dim] per slot
+ * ORC_ROWS is MambaPool's deduplicated row; ORC_ROWS_T is its axis-0 layout seen
+ * transposed: in both the view's step stride equals its window stride.  [sglang PR
+ * 46184, "Modifications" (the step stride == window stride condition, "for any layout
+ * with those strides") and its test coverage list ("MambaPool's axis-0 window layout
+ * seen transposed").]
  */
-int orc_conv_verify(const orc_problem *p, const void *x, const void *weight,
-                    const void *bias, void *conv_state, const int32_t *slot_idx,
-                    const int32_t *num_accept_tokens, void *out, void *windows,
-                    float *pre_dbg, double *y_dbg) {
+enum { ORC_DENSE = 0, ORC_ROWS = 1, ORC_ROWS_T = 2 };
+
+static int64_t win_index(const orc_problem *p, int layout, int s, int t, int c, int j) {
+    const int64_t C = p->d_inner, W1 = p->d_conv - 1, L = p->n_tok + p->d_conv - 2;
+    const int64_t base = (int64_t)s * p->win_slot_stride;
+    if (layout == ORC_DENSE)
+        return base + ((int64_t)t * C + c) * W1 + j;
+    if (layout == ORC_ROWS)
+        return base + (int64_t)c * L + t + j;
+    return base + (int64_t)(t + j) * C + c;
+}
+
+/*
+ * The general per-token loop.  Beyond the plain batched verify it takes:
+ *
+ *   cu_seqlens [n_seq+1] or NULL: packed rows.  Row i holds T_i = cu[i+1]-cu[i] <= T
+ *     tokens, token t at x/out index (cu[i] + t) * tok_stride (the seq strides are
+ *     unused).  A row with T_i = 0 writes nothing.  [sglang PR 46184, "Related
+ *     upstream work": packed variable-length rows, ragged tokens.]
+ *   parent [n_seq, parent_stride] or NULL: tree verify.  Token t's window continues
+ *     the window of token parent[i,t] (-1: the row's starting window) instead of
+ *     token t-1's; the chain is parent[i,t] = t-1.  Tree windows are dense only and
+ *     the call commits nothing to conv_state: the accepted path is known only after
+ *     verification, and the restore below writes it.  [sglang PR 46184, "Scope" (tree
+ *     verify keeps dense windows) and "Modifications" (the tile path is not used with
+ *     a tree mask).]
+ *   has_init [n_seq] or NULL: 0 starts row i from a zero window instead of its state
+ *     (a prompt with no earlier state).
+ *   do_l2 = 0 skips the per-head L2; windows = NULL writes no rollback windows; commit
+ *     = 0 leaves conv_state alone.
+ *
+ * The arithmetic of each token is the plain verify's: conv + bias in fp32 FMAs in
+ * tap order, SiLU and L2 in fp64, one rounding to the output dtype.
+ */
+typedef struct {
+    int32_t layout;
+    const int32_t *cu_seqlens;
+    const int32_t *parent;
+    int64_t parent_stride;
+    const int32_t *has_init;
+    int32_t do_l2;
+    int32_t commit;
+} orc_ext;
+
+int orc_verify_general(const orc_problem *p, const orc_ext *e, const void *x,
+                       const void *weight, const void *bias, void *conv_state,
+                       const int32_t *slot_idx, const int32_t *num_accept_tokens,
+                       void *out, void *windows, float *pre_dbg, double *y_dbg) {
     if (check_problem(p) != ORC_OK)
+        return ORC_BAD;
+    if (e->layout < ORC_DENSE || e->layout > ORC_ROWS_T)
+        return ORC_BAD;
+    if (e->parent && (e->layout != ORC_DENSE || e->commit))
         return ORC_BAD;
     const int D = p->d_conv, W1 = p->d_conv - 1, T = p->n_tok, C = p->d_inner;
 
@@ -188,12 +239,24 @@ int orc_conv_verify(const orc_problem *p, const void *x, const void *weight,
             continue;
         if (s >= p->n_slots || a < 0 || a > p->state_len - W1)
             return ORC_BAD;
+        int Ti = e->cu_seqlens ? e->cu_seqlens[i + 1] - e->cu_seqlens[i] : T;
+        if (Ti < 0 || Ti > T)
+            return ORC_BAD;
+        for (int t = 0; e->parent && t < Ti; ++t) {
+            int pt = e->parent[(int64_t)i * e->parent_stride + t];
+            if (pt < -1 || pt >= t)
+                return ORC_BAD;
+        }
     }
 
-    uint32_t *win = malloc(sizeof(uint32_t) * (size_t)(C > 0 ? C : 1) * (size_t)W1);
+    /* hist[t] = the window after token t; root = the row's starting window */
+    const size_t cw = (size_t)(C > 0 ? C : 1) * (size_t)W1;
+    uint32_t *root = malloc(sizeof(uint32_t) * cw);
+    uint32_t *hist = malloc(sizeof(uint32_t) * cw * (size_t)T);
     double *y = malloc(sizeof(double) * (size_t)(C > 0 ? C : 1));
-    if (!win || !y) {
-        free(win);
+    if (!root || !hist || !y) {
+        free(root);
+        free(hist);
         free(y);
         return ORC_NOMEM;
     }
@@ -203,21 +266,31 @@ int orc_conv_verify(const orc_problem *p, const void *x, const void *weight,
         if (s < 0)
             continue;               /* padded row: no write anywhere */
         int a = num_accept_tokens ? num_accept_tokens[i] : 0;
+        int Ti = e->cu_seqlens ? e->cu_seqlens[i + 1] - e->cu_seqlens[i] : T;
+        if (Ti == 0)
+            continue;
         const int64_t st_base = (int64_t)s * p->state_slot_stride;
+        const int init = e->has_init ? e->has_init[i] != 0 : 1;
 
         for (int c = 0; c < C; ++c)
             for (int j = 0; j < W1; ++j)
-                win[(int64_t)c * W1 + j] =
-                    state_get(p, conv_state, st_base + (int64_t)c * p->state_len + a + j);
+                root[(int64_t)c * W1 + j] =
+                    init ? state_get(p, conv_state, st_base + (int64_t)c * p->state_len + a + j)
+                         : 0u;
 
-        for (int t = 0; t < T; ++t) {
-            const int64_t x_base = (int64_t)i * p->x_seq_stride + (int64_t)t * p->x_tok_stride;
+        for (int t = 0; t < Ti; ++t) {
+            int pt = e->parent ? e->parent[(int64_t)i * e->parent_stride + t] : t - 1;
+            const uint32_t *pw = pt < 0 ? root : hist + (size_t)pt * cw;
+            uint32_t *nw = hist + (size_t)t * cw;
+            const int64_t tok = e->cu_seqlens ? (int64_t)e->cu_seqlens[i] + t : t;
+            const int64_t x_base = (e->cu_seqlens ? 0 : (int64_t)i * p->x_seq_stride) +
+                                   tok * p->x_tok_stride;
 
             /* conv + bias, then SiLU, channel by channel */
             for (int c = 0; c < C; ++c) {
                 float acc = bias ? x_val(p, bias, c) : 0.0f;
                 for (int w = 0; w < D; ++w) {
-                    float v = (w < W1) ? state_bits_val(p, win[(int64_t)c * W1 + w])
+                    float v = (w < W1) ? state_bits_val(p, pw[(int64_t)c * W1 + w])
                                        : x_val(p, x, x_base + c);
                     acc = fmaf(x_val(p, weight, (int64_t)c * D + w), v, acc);
                 }
@@ -228,7 +301,7 @@ int orc_conv_verify(const orc_problem *p, const void *x, const void *weight,
             }
 
             /* per-head L2 over the q|k channels only */
-            if (p->qk_channels > 0) {
+            if (p->qk_channels > 0 && e->do_l2) {
                 for (int h0 = 0; h0 < p->qk_channels; h0 += p->head_dim) {
                     double ss = 0.0;
                     for (int c = h0; c < h0 + p->head_dim; ++c)
@@ -239,7 +312,8 @@ int orc_conv_verify(const orc_problem *p, const void *x, const void *weight,
                 }
             }
 
-            const int64_t o_base = (int64_t)i * p->out_seq_stride + (int64_t)t * p->out_tok_stride;
+            const int64_t o_base = (e->cu_seqlens ? 0 : (int64_t)i * p->out_seq_stride) +
+                                   tok * p->out_tok_stride;
             for (int c = 0; c < C; ++c) {
                 if (y_dbg)
                     y_dbg[((int64_t)i * T + t) * C + c] = y[c];
@@ -249,31 +323,114 @@ int orc_conv_verify(const orc_problem *p, const void *x, const void *weight,
                     ((float *)out)[o_base + c] = orc_round_f32(y[c]);
             }
 
-            /* shift the window and copy it into the rollback buffer */
+            /* the new window: the parent's shifted by one, x_t appended; then its copy
+             * into the rollback buffer */
             for (int c = 0; c < C; ++c) {
-                uint32_t *wc = win + (int64_t)c * W1;
+                const uint32_t *pc = pw + (int64_t)c * W1;
+                uint32_t *wc = nw + (int64_t)c * W1;
                 for (int j = 0; j + 1 < W1; ++j)
-                    wc[j] = wc[j + 1];
+                    wc[j] = pc[j + 1];
                 wc[W1 - 1] = x_as_state_bits(p, x, x_base + c);
-                for (int j = 0; j < W1; ++j) {
-                    int64_t idx;
-                    if (p->dedup)
-                        idx = (int64_t)s * p->win_slot_stride +
-                              (int64_t)c * (T + D - 2) + t + j;
-                    else
-                        idx = (int64_t)s * p->win_slot_stride +
-                              ((int64_t)t * C + c) * W1 + j;
-                    state_put(p, windows, idx, wc[j]);
-                }
+                for (int j = 0; windows && j < W1; ++j)
+                    state_put(p, windows, win_index(p, e->layout, s, t, c, j), wc[j]);
             }
         }
 
-        for (int c = 0; c < C; ++c)
+        const uint32_t *last = hist + (size_t)(Ti - 1) * cw;
+        for (int c = 0; e->commit && c < C; ++c)
             for (int j = 0; j < W1; ++j)
                 state_put(p, conv_state, st_base + (int64_t)c * p->state_len + j,
-                          win[(int64_t)c * W1 + j]);
+                          last[(int64_t)c * W1 + j]);
     }
-    free(win);
+    free(root);
+    free(hist);
     free(y);
+    return ORC_OK;
+}
+
+/*
+ * The plain batched verify: every row T tokens, chain windows in the dense or the
+ * deduplicated-row layout, L2 on, the committed window written to conv_state.
+ *
+ * conv_state is updated in place; out and windows are written for active rows only.
+ * pre_dbg (fp32) and y_dbg (fp64, after L2, before rounding), if not NULL, receive
+ * [n_seq, T, d_inner] contiguous copies of the intermediate values for the
+ * self-tests.  Returns ORC_BAD if the problem is malformed or a row's slot or offset
+ * is out of range (nothing is written then), ORC_NOMEM on allocation failure.
+ */
+int orc_conv_verify(const orc_problem *p, const void *x, const void *weight,
+                    const void *bias, void *conv_state, const int32_t *slot_idx,
+                    const int32_t *num_accept_tokens, void *out, void *windows,
+                    float *pre_dbg, double *y_dbg) {
+    orc_ext e = {p->dedup ? ORC_ROWS : ORC_DENSE, NULL, NULL, 0, NULL, 1, 1};
+    return orc_verify_general(p, &e, x, weight, bias, conv_state, slot_idx,
+                              num_accept_tokens, out, windows, pre_dbg, y_dbg);
+}
+
+/*
+ * Accepted-prefix restore: conv_state[s, c, 0..K-2] = window k of slot s, k =
+ * win_index[i] (chain verify: the number of accepted tokens minus one; tree verify:
+ * the position of the last accepted token).  k = -1 restores nothing for that row,
+ * as does slot -1.  [sglang PR 46184, "Motivation": the window lets the accepted
+ * prefix's conv state be restored after verify; Atlas glm5next_kda/mod.rs, decode_k:
+ * the snapshot after row t is what a partial accept rewinds to.]
+ */
+int orc_restore(const orc_problem *p, int layout, void *conv_state, const void *windows,
+                const int32_t *slot_idx, const int32_t *win_k) {
+    if (check_problem(p) != ORC_OK || layout < ORC_DENSE || layout > ORC_ROWS_T)
+        return ORC_BAD;
+    const int W1 = p->d_conv - 1;
+    for (int i = 0; i < p->n_seq; ++i) {
+        int s = slot_idx ? slot_idx[i] : i;
+        int k = win_k[i];
+        if (s < 0 || k < 0)
+            continue;
+        if (s >= p->n_slots || k >= p->n_tok)
+            return ORC_BAD;
+    }
+    for (int i = 0; i < p->n_seq; ++i) {
+        int s = slot_idx ? slot_idx[i] : i;
+        int k = win_k[i];
+        if (s < 0 || k < 0)
+            continue;
+        const int64_t st_base = (int64_t)s * p->state_slot_stride;
+        for (int c = 0; c < p->d_inner; ++c)
+            for (int j = 0; j < W1; ++j)
+                state_put(p, conv_state, st_base + (int64_t)c * p->state_len + j,
+                          state_get(p, windows, win_index(p, layout, s, k, c, j)));
+    }
+    return ORC_OK;
+}
+
+/*
+ * Separate per-head L2 over the q|k channels, in place, on rows of x (the prefill
+ * conv's output): y <- y / sqrt(sum_head y^2 + eps) in fp64, rounded once to x's
+ * dtype.  V channels are untouched.  [Atlas glm5next_kda/mod.rs, module doc: "Decode
+ * conv fuses L2; prefill does not and needs a separate l2_norm_bf16 over q|k", and
+ * the prefill body: "Prefill conv is conv + SiLU ONLY — L2 is a separate launch
+ * over q|k".]
+ */
+int orc_l2norm(const orc_problem *p, int64_t n_rows, int64_t row_stride, void *x) {
+    if (p->qk_channels < 0 || p->qk_channels > p->d_inner ||
+        (p->qk_channels > 0 && (p->head_dim <= 0 || p->qk_channels % p->head_dim)))
+        return ORC_BAD;
+    for (int64_t r = 0; r < n_rows; ++r) {
+        const int64_t base = r * row_stride;
+        for (int h0 = 0; h0 < p->qk_channels; h0 += p->head_dim) {
+            double ss = 0.0;
+            for (int c = h0; c < h0 + p->head_dim; ++c) {
+                double v = (double)x_val(p, x, base + c);
+                ss += v * v;
+            }
+            double scale = 1.0 / sqrt(ss + (double)p->l2_eps);
+            for (int c = h0; c < h0 + p->head_dim; ++c) {
+                double v = (double)x_val(p, x, base + c) * scale;
+                if (p->x_bf16)
+                    ((uint16_t *)x)[base + c] = orc_round_bf16(v);
+                else
+                    ((float *)x)[base + c] = orc_round_f32(v);
+            }
+        }
+    }
     return ORC_OK;
 }

@@ -140,3 +140,89 @@ def brute(x, weight, bias, conv_state, *, d_inner, qk_channels, head_dim, l2_eps
         out = y.astype(np.float32)
     return {"pre": pre, "y": y, "out": out, "windows": win, "conv_state": state_after,
             "active": active}
+
+
+def brute_general(x, weight, bias, conv_state, *, T, d_inner, qk_channels, head_dim, l2_eps,
+                  x_dtype, state_dtype, layout="dense", slot_idx=None,
+                  num_accept_tokens=None, cu_seqlens=None, parent=None, has_init=None,
+                  do_l2=True, commit=True):
+    """The general verify by paths instead of a rolling window.
+
+    For token t of row i the input sequence is the row's starting window (the state
+    columns a..a+D-2, or zeros for a row without an initial state) followed by x along
+    the token's ancestor path ..., parent(parent(t)), parent(t), t (for a chain, every
+    token before t).  The conv of token t is the dot product of the last D values of
+    that sequence with the taps; its window is the last D-1 values.  Rows may be packed
+    (``cu_seqlens``).  Windows are returned in the layout's shape with the sentinel
+    0xFFFFFFFF where nothing is written; the state is the committed copy (chain only).
+    """
+    D = weight.shape[1]
+    W1 = D - 1
+    C = d_inner
+    n_slots, _, state_len = conv_state.shape
+    n_seq = len(cu_seqlens) - 1 if cu_seqlens is not None else x.shape[0]
+    xv_all = values(x[..., :C], x_dtype)
+    xb_all = x_bits_as_state(x[..., :C], x_dtype, state_dtype)
+    wv = values(weight, x_dtype)
+    bv = values(bias, x_dtype) if bias is not None else np.zeros(C)
+    sv = values(conv_state, state_dtype)
+    sb = bits(conv_state, state_dtype)
+    pre = np.full((n_seq, T, C), np.nan)
+    y = np.full((n_seq, T, C), np.nan)
+    state_after = sb.copy()
+    L = T + D - 2
+    shape = {"dense": (n_slots, T, C, W1), "dedup": (n_slots, C, L),
+             "dedup_t": (n_slots, L, C)}[layout]
+    win = np.full(shape, 0xFFFFFFFF, np.uint64)
+    active = []
+    for i in range(n_seq):
+        s = i if slot_idx is None else int(slot_idx[i])
+        if s < 0:
+            continue
+        if cu_seqlens is not None:
+            t0, Ti = int(cu_seqlens[i]), int(cu_seqlens[i + 1] - cu_seqlens[i])
+            xv, xb = xv_all[t0:t0 + Ti], xb_all[t0:t0 + Ti]
+        else:
+            Ti = T
+            xv, xb = xv_all[i], xb_all[i]
+        if Ti == 0:
+            continue
+        a = 0 if num_accept_tokens is None else int(num_accept_tokens[i])
+        init = True if has_init is None else bool(has_init[i])
+        active.append((i, s))
+        rv = sv[s, :, a:a + W1] if init else np.zeros((C, W1))
+        rb = sb[s, :, a:a + W1] if init else np.zeros((C, W1), np.uint32)
+        for t in range(Ti):
+            path = [t]
+            while True:
+                q = path[-1]
+                pq = (q - 1) if parent is None else int(parent[i, q])
+                if pq < 0:
+                    break
+                path.append(pq)
+            path = path[::-1]
+            seqv = np.concatenate([rv, xv[path].T], axis=1)       # [C, W1 + len(path)]
+            seqb = np.concatenate([rb, xb[path].T], axis=1)
+            p = (seqv[:, -D:] * wv).sum(axis=1) + bv
+            yy = silu(p)
+            if qk_channels and do_l2:
+                h = yy[:qk_channels].reshape(qk_channels // head_dim, head_dim)
+                ss = (h * h).sum(axis=1, keepdims=True)
+                yy[:qk_channels] = (h / np.sqrt(ss + np.float64(np.float32(l2_eps)))).reshape(-1)
+            pre[i, t] = p
+            y[i, t] = yy
+            wnd = seqb[:, -W1:]
+            if layout == "dense":
+                win[s, t] = wnd
+            elif layout == "dedup":
+                win[s, :, t:t + W1] = wnd
+            else:
+                win[s, t:t + W1, :] = wnd.T
+            if commit and t == Ti - 1:
+                state_after[s, :, :W1] = wnd
+    if x_dtype == "bf16":
+        out = round_bf16_exact(np.where(np.isnan(y), 0.0, y))
+    else:
+        out = y.astype(np.float32)
+    return {"pre": pre, "y": y, "out": out, "windows": win, "conv_state": state_after,
+            "active": active}

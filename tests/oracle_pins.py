@@ -11,6 +11,7 @@ a planted mistake and requires that at least one fails.
 
 from __future__ import annotations
 
+import dataclasses
 import os
 
 import numpy as np
@@ -376,6 +377,225 @@ def pin_fma_chain_exact(lib):
                     assert float(r["pre"][i, t, c]) == float(acc), "fma chain"
 
 
+# ---- the general loop: packed rows, trees, all window layouts, restore, prefill ----------
+
+def _general_oracle(inp, lib, *, layout=None, do_l2=True, commit=None):
+    wl = inp.wl
+    state = inp.conv_state.copy()
+    out = workloads.poison(inp.x.shape, wl.x_dtype)
+    windows = None if wl.prefill else workloads.poison(
+        workloads.window_shape(dataclasses.replace(wl, layout=layout or wl.layout)),
+        wl.state_dtype)
+    commit = (not wl.tree) if commit is None else commit
+    pre, y = oracle.verify_general(
+        inp.x, inp.weight, inp.bias, state, out, windows, T=wl.T, d_inner=wl.d_inner,
+        qk_channels=wl.qk_channels, head_dim=wl.head_dim, l2_eps=wl.l2_eps,
+        x_dtype=wl.x_dtype, state_dtype=wl.state_dtype, layout=layout or wl.layout,
+        slot_idx=inp.slot_idx, num_accept_tokens=inp.num_accept_tokens,
+        cu_seqlens=inp.cu_seqlens, parent=inp.parent, has_init=inp.has_init,
+        do_l2=do_l2, commit=commit, debug=True, lib=lib)
+    return {"out": out, "windows": windows, "conv_state": state, "pre": pre, "y": y}
+
+
+def _brute_general(inp, *, layout=None, do_l2=True, commit=None):
+    wl = inp.wl
+    return brute.brute_general(
+        inp.x, inp.weight, inp.bias, inp.conv_state, T=wl.T, d_inner=wl.d_inner,
+        qk_channels=wl.qk_channels, head_dim=wl.head_dim, l2_eps=wl.l2_eps,
+        x_dtype=wl.x_dtype, state_dtype=wl.state_dtype, layout=layout or wl.layout,
+        slot_idx=inp.slot_idx, num_accept_tokens=inp.num_accept_tokens,
+        cu_seqlens=inp.cu_seqlens, parent=inp.parent, has_init=inp.has_init,
+        do_l2=do_l2, commit=(not wl.tree) if commit is None else commit)
+
+
+def _token_rows(inp, active):
+    """(row, token, index into out's leading dims) of every token the call computes."""
+    lens = inp.lengths
+    for i, _ in active:
+        for t in range(int(lens[i])):
+            yield i, t, ((int(inp.cu_seqlens[i]) + t,) if inp.cu_seqlens is not None else (i, t))
+
+
+def _check_general(inp, lib, *, layout=None, exact=True, do_l2=True):
+    wl = inp.wl
+    r = _general_oracle(inp, lib, layout=layout, do_l2=do_l2)
+    b = _brute_general(inp, layout=layout, do_l2=do_l2)
+    if r["windows"] is not None:
+        wb = _windows_bits(r["windows"], wl.state_dtype)
+        untouched = b["windows"] == 0xFFFFFFFF
+        poison_bits = _windows_bits(workloads.poison(r["windows"].shape, wl.state_dtype),
+                                    wl.state_dtype)
+        assert np.array_equal(wb[~untouched], b["windows"][~untouched]), "rollback windows differ"
+        assert np.array_equal(wb[untouched], poison_bits[untouched]), "untouched windows written"
+    assert np.array_equal(brute.bits(r["conv_state"], wl.state_dtype),
+                          b["conv_state"]), "conv_state differs"
+    written = np.zeros(inp.x.shape[:-1], bool)
+    for i, t, idx in _token_rows(inp, b["active"]):
+        written[idx] = True
+        po, pb = np.float64(r["pre"][i, t]), b["pre"][i, t]
+        ob = brute.bits(r["out"][idx][:wl.d_inner], wl.x_dtype).astype(np.int64)
+        bb = brute.bits(b["out"][i, t], wl.x_dtype).astype(np.int64)
+        if exact:
+            assert np.array_equal(po, pb), f"conv pre-activation differs (row {i}, token {t})"
+            assert np.array_equal(ob, bb), f"outputs differ (row {i}, token {t})"
+        else:
+            assert np.allclose(r["y"][i, t], b["y"][i, t], rtol=1e-5, atol=1e-6)
+    pz = brute.bits(workloads.poison(inp.x.shape, wl.x_dtype), wl.x_dtype)
+    assert np.array_equal(brute.bits(r["out"], wl.x_dtype)[~written], pz[~written]), \
+        "out written for a token the call does not compute"
+
+
+def pin_window_layouts(lib):
+    """Chain verify in all three window layouts (time-major rows included) against the
+    path brute force, exactly, with offsets, permuted slots, padded rows, spare slots."""
+    for layout in ("dense", "dedup", "dedup_t"):
+        for D, T in ((4, 5), (3, 2), (2, 4)):
+            wl = workloads.custom(f"lay_{layout}_{D}_{T}", n_seq=5, d_inner=24, qk_channels=16,
+                                  head_dim=8, d_conv=D, T=T, layout=layout, dist="dyadic",
+                                  accept_offsets=True, permute_slots=True, pad_frac=0.3,
+                                  extra_slots=2, seed=workloads.BASE_SEED + 2100 + D * 10 + T)
+            _check_general(workloads.make_inputs(wl), lib)
+
+
+def pin_packed_rows(lib):
+    """Packed variable-length rows (zero-length rows included) against the brute force
+    run row by row on each row's own tokens, in every layout."""
+    for k, layout in enumerate(("dense", "dedup", "dedup_t")):
+        for xd, sd in (("bf16", "bf16"), ("bf16", "f32"), ("f32", "f32")):
+            wl = workloads.custom(f"var_{layout}_{xd}_{sd}", n_seq=6, d_inner=16,
+                                  qk_channels=8, head_dim=4, T=6, layout=layout, x_dtype=xd,
+                                  state_dtype=sd, dist="dyadic", varlen=True,
+                                  accept_offsets=True, permute_slots=True, pad_frac=0.2,
+                                  seed=workloads.BASE_SEED + 2200 + k * 7 + len(xd + sd))
+            _check_general(workloads.make_inputs(wl), lib)
+
+
+def pin_tree_paths(lib):
+    """Tree verify: each token's conv over its root window and the x of its ancestor
+    path, windows dense, nothing committed - against the path brute force, exactly;
+    also with packed rows and a zero-start row."""
+    for k, (D, T, var) in enumerate(((4, 7, False), (3, 5, False), (4, 6, True))):
+        wl = workloads.custom(f"tree_{D}_{T}_{var}", n_seq=5, d_inner=16, qk_channels=8,
+                              head_dim=8, d_conv=D, T=T, dist="dyadic", tree=True,
+                              varlen=var, accept_offsets=True, permute_slots=True,
+                              pad_frac=0.2, init_frac=0.7,
+                              seed=workloads.BASE_SEED + 2300 + k)
+        _check_general(workloads.make_inputs(wl), lib)
+
+
+def pin_tree_with_chain_parents(lib):
+    """A tree whose parents form a chain (parent = t-1) gives the chain's outputs and
+    windows; it leaves conv_state alone where the chain commits."""
+    wl = workloads.custom("chain_tree", n_seq=4, d_inner=32, qk_channels=16, head_dim=8, T=6,
+                          accept_offsets=True, permute_slots=True, pad_frac=0.25)
+    inp = workloads.make_inputs(wl)
+    chain = _general_oracle(inp, lib)
+    inp.parent = np.tile(np.arange(-1, wl.T - 1, dtype=np.int32), (wl.n_seq, 1))
+    tree = _general_oracle(inp, lib, commit=False)
+    assert np.array_equal(brute.bits(chain["out"], wl.x_dtype), brute.bits(tree["out"], wl.x_dtype))
+    assert np.array_equal(brute.bits(chain["windows"], wl.state_dtype),
+                          brute.bits(tree["windows"], wl.state_dtype))
+    assert np.array_equal(brute.bits(tree["conv_state"], wl.state_dtype),
+                          brute.bits(inp.conv_state, wl.state_dtype)), "tree verify committed"
+
+
+def pin_restore(lib):
+    """Accepted-prefix restore: window k of the slot (chain or tree, every layout) lands in
+    state columns 0..D-2 - compared with the brute force's window k, i.e. the committed
+    state of a verify of the first k+1 tokens; later columns, slot -1 and k = -1 rows
+    untouched."""
+    cases = [("dense", False), ("dedup", False), ("dedup_t", False), ("dense", True)]
+    for n, (layout, tree) in enumerate(cases):
+        wl = workloads.custom(f"restore_{layout}_{tree}", n_seq=6, d_inner=16, qk_channels=8,
+                              head_dim=8, T=5, layout=layout, tree=tree, restore=True,
+                              accept_offsets=True, permute_slots=True, pad_frac=0.2,
+                              extra_slots=1, seed=workloads.BASE_SEED + 2400 + n)
+        inp = workloads.make_inputs(wl)
+        r = _general_oracle(inp, lib)
+        b = _brute_general(inp)
+        state = r["conv_state"].copy()
+        oracle.restore(state, r["windows"], inp.restore_k, T=wl.T, d_conv=wl.d_conv,
+                       state_dtype=wl.state_dtype, layout=layout, slot_idx=inp.slot_idx,
+                       lib=lib)
+        want = brute.bits(r["conv_state"], wl.state_dtype).copy()
+        W1 = wl.win_cols
+        for i, s in b["active"]:
+            k = int(inp.restore_k[i])
+            if k < 0:
+                continue
+            if layout == "dense":
+                w = b["windows"][s, k]
+            elif layout == "dedup":
+                w = b["windows"][s, :, k:k + W1]
+            else:
+                w = b["windows"][s, k:k + W1, :].T
+            want[s, :, :W1] = w
+        assert np.array_equal(brute.bits(state, wl.state_dtype), want), f"restore ({layout})"
+
+
+def pin_prefill_torch(lib):
+    """Prefill conv (conv + SiLU, no L2, no windows) over packed prompts against torch's
+    depthwise conv1d: rows without an initial state are the textbook causal conv
+    (zero left padding), rows with one prepend their state window; the last window
+    is committed."""
+    import torch
+    import torch.nn.functional as F
+
+    wl = workloads.custom("prefill", n_seq=5, d_inner=16, qk_channels=8, head_dim=8, T=40,
+                          dist="dyadic", varlen=True, prefill=True, init_frac=0.5,
+                          permute_slots=True, seed=workloads.BASE_SEED + 2500)
+    inp = workloads.make_inputs(wl)
+    state = inp.conv_state.copy()
+    out = workloads.poison(inp.x.shape, wl.x_dtype)
+    oracle.prefill(inp.x, inp.weight, inp.bias, state, out, inp.cu_seqlens, d_inner=wl.d_inner,
+                   x_dtype=wl.x_dtype, state_dtype=wl.state_dtype, slot_idx=inp.slot_idx,
+                   has_init=inp.has_init, lib=lib)
+    W1, D, C = wl.win_cols, wl.d_conv, wl.d_inner
+    w = torch.from_numpy(brute.values(inp.weight, wl.x_dtype)).reshape(C, 1, D)
+    bvec = torch.from_numpy(brute.values(inp.bias, wl.x_dtype))
+    for i in range(wl.n_seq):
+        s = int(inp.slot_idx[i])
+        t0, Ti = int(inp.cu_seqlens[i]), int(inp.cu_seqlens[i + 1] - inp.cu_seqlens[i])
+        xr = torch.from_numpy(brute.values(inp.x[t0:t0 + Ti, :C], wl.x_dtype)).T   # [C, Ti]
+        if inp.has_init[i]:
+            left = torch.from_numpy(brute.values(inp.conv_state[s, :, :W1], wl.state_dtype))
+        else:
+            left = torch.zeros(C, W1, dtype=torch.float64)
+        seq = torch.cat([left, xr], dim=1)
+        pre = F.conv1d(seq[None], w, bvec, groups=C)[0]                       # [C, Ti]
+        y = F.silu(pre).T.numpy()
+        got = brute.bits(out[t0:t0 + Ti, :C], wl.x_dtype)
+        assert np.array_equal(got, brute.round_bf16_exact(y).astype(np.uint32)), f"prefill row {i}"
+        if Ti > 0:
+            tail = np.concatenate([brute.bits(inp.conv_state[s, :, :W1], wl.state_dtype)
+                                   if inp.has_init[i] else np.zeros((C, W1), np.uint32),
+                                   brute.x_bits_as_state(inp.x[t0:t0 + Ti, :C], wl.x_dtype,
+                                                         wl.state_dtype).T], axis=1)[:, -W1:]
+            assert np.array_equal(brute.bits(state[s, :, :W1], wl.state_dtype), tail), \
+                f"prefill row {i} committed window"
+        assert np.array_equal(state[s, :, W1:], inp.conv_state[s, :, W1:])
+
+
+def pin_separate_l2(lib):
+    """The separate L2 pass: every q|k head ends with sum y^2 = S/(S+eps) (S the head's
+    sum of squares before), V channels keep their bits, for fp32 and bf16 rows and a
+    large eps that makes the eps term visible."""
+    rng = np.random.default_rng(workloads.BASE_SEED + 2600)
+    for xd, eps, tol in (("f32", 1e-6, 1e-6), ("f32", 10.0, 1e-6), ("bf16", 10.0, 2e-2)):
+        C, qk, hd, rows = 48, 32, 8, 5
+        x0 = workloads.to_storage(rng.standard_normal((rows, C + 8)).astype(np.float32), xd)
+        x = x0.copy()
+        oracle.l2norm(x, d_inner=C, qk_channels=qk, head_dim=hd, l2_eps=eps, x_dtype=xd, lib=lib)
+        v0 = brute.values(x0, xd)
+        v1 = brute.values(x, xd)
+        for h in range(qk // hd):
+            sl = slice(h * hd, (h + 1) * hd)
+            S = (v0[:, sl] ** 2).sum(axis=1)
+            got = (v1[:, sl] ** 2).sum(axis=1)
+            assert np.allclose(got, S / (S + eps), rtol=tol, atol=0), f"L2 head {h} ({xd}, eps {eps})"
+        assert np.array_equal(brute.bits(x[:, qk:], xd), brute.bits(x0[:, qk:], xd)), "V written"
+
+
 def load_golden(path):
     """Parse a ``key: v1 v2 ...`` fixture (lines starting with # are comments)."""
     g = {}
@@ -392,4 +612,6 @@ def load_golden(path):
 PINS = [pin_brute_dyadic, pin_brute_normal, pin_fma_chain_exact, pin_torch_conv1d,
         pin_one_hot_taps,
         pin_l2_closed_form, pin_window_invariants, pin_batched_equals_rows,
-        pin_offset_equivalence, pin_golden_window_indexing, pin_rounding, pin_bit_copies]
+        pin_offset_equivalence, pin_golden_window_indexing, pin_rounding, pin_bit_copies,
+        pin_window_layouts, pin_packed_rows, pin_tree_paths, pin_tree_with_chain_parents,
+        pin_restore, pin_prefill_torch, pin_separate_l2]

@@ -22,6 +22,15 @@ Workloads (sizes and value distributions follow the pages' workloads):
                              per-row num_accept_tokens ~ U{0..T-1}, ~10% padded rows,
                              state_len = T + 2.  Pass ``b`` trims d_inner to 10200.
 
+Beyond the fixed-T chain verify, a workload may ask for packed rows (``varlen``: row
+i holds T_i ~ U{0..T} tokens, packed back to back, ``cu_seqlens`` their offsets), a
+tree (``tree``: parent[i, 0] = -1, parent[i, t] ~ U{-1..t-1}), accepted-prefix
+restore indices (``restore``: k_i ~ U{-1..T_i-1}), rows that start from zeros
+(``init_frac``: Bernoulli probability that a row has an initial state), or a
+prefill (``prefill``: long packed prompts, conv + SiLU with no rollback windows and
+the per-head L2 as a separate pass).  These extra draws come after all the draws
+above, so they never change the data of a workload that does not use them.
+
 Distributions: state ~ N(0,1), x ~ N(0,1), weight ~ U(-0.5,0.5), bias ~ U(-0.5,0.5),
 drawn as float32 from ``numpy.random.Generator(PCG64(seed))`` in exactly that order,
 then rounded to the storage dtype (round-to-nearest-even for bf16).  bf16 arrays are
@@ -50,7 +59,7 @@ class Workload:
     T: int
     x_dtype: str          # "f32" | "bf16" : x, weight, bias, out
     state_dtype: str      # "f32" | "bf16" : conv_state and rollback windows
-    layout: str           # "dense" | "dedup"
+    layout: str           # "dense" | "dedup" (rows [d, T+D-2]) | "dedup_t" (rows [T+D-2, d])
     bias: bool
     state_len: int        # columns per state channel (>= d_conv - 1)
     seed: int
@@ -61,6 +70,12 @@ class Workload:
     l2_eps: float = L2_EPS
     dist: str = "normal"          # "normal": the distributions above; "dyadic": see below
     extra_slots: int = 0          # pool slots no row references (must stay untouched)
+    varlen: bool = False          # packed rows of T_i ~ U{0..T} tokens
+    min_len: int = 0              # lower bound of T_i when varlen
+    tree: bool = False            # per-token parents (dense windows, no commit)
+    restore: bool = False         # draw accepted-prefix restore indices
+    init_frac: float = 1.0        # probability that a row starts from its state
+    prefill: bool = False         # conv + SiLU only, no windows; L2 as a separate pass
 
     @property
     def win_cols(self) -> int:
@@ -138,6 +153,17 @@ class Inputs:
     conv_state: np.ndarray   # [n_slots, d_inner, state_len]
     slot_idx: Optional[np.ndarray]   # int32 [n_seq] or None (identity)
     num_accept_tokens: Optional[np.ndarray]  # int32 [n_seq] or None
+    cu_seqlens: Optional[np.ndarray] = None  # int32 [n_seq+1] (varlen): x is [total, xs]
+    parent: Optional[np.ndarray] = None      # int32 [n_seq, T] (tree)
+    restore_k: Optional[np.ndarray] = None   # int32 [n_seq] (restore)
+    has_init: Optional[np.ndarray] = None    # int32 [n_seq] (init_frac < 1)
+
+    @property
+    def lengths(self) -> np.ndarray:
+        """Tokens per row."""
+        if self.cu_seqlens is not None:
+            return np.diff(self.cu_seqlens).astype(np.int64)
+        return np.full(self.wl.n_seq, self.wl.T, np.int64)
 
 
 def make_inputs(wl: Workload, seed: Optional[int] = None) -> Inputs:
@@ -168,11 +194,29 @@ def make_inputs(wl: Workload, seed: Optional[int] = None) -> Inputs:
         perm = rng.permutation(wl.n_slots).astype(np.int32) if wl.permute_slots \
             else np.arange(n, dtype=np.int32)
         slot = np.where(pad, np.int32(-1), perm[:n]).astype(np.int32)
+    cu = parent = rk = has_init = None
+    lengths = np.full(n, T, np.int64)
+    if wl.varlen:
+        lengths = rng.integers(wl.min_len, T + 1, size=n)
+        cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    if wl.tree:
+        parent = np.full((n, T), -1, np.int32)
+        for t in range(1, T):
+            parent[:, t] = rng.integers(-1, t, size=n)
+    if wl.restore:
+        rk = np.array([rng.integers(-1, max(int(L), 0)) if L > 0 else -1 for L in lengths],
+                      dtype=np.int32)
+    if wl.init_frac < 1.0:
+        has_init = (rng.random(n) < wl.init_frac).astype(np.int32)
     x_st = to_storage(x, wl.x_dtype)
+    if cu is not None:
+        # packed rows: row i's first T_i draws, back to back
+        x_st = np.concatenate([x_st[i, :lengths[i]] for i in range(n)] +
+                              [np.zeros((0, d), x_st.dtype)], axis=0)
     if xs != d:
         pad_val = 0x7FBF if wl.x_dtype == "bf16" else np.float32(np.nan)
-        xfull = np.full((n, T, xs), pad_val, dtype=storage_np_dtype(wl.x_dtype))
-        xfull[:, :, :d] = x_st
+        xfull = np.full(x_st.shape[:-1] + (xs,), pad_val, dtype=storage_np_dtype(wl.x_dtype))
+        xfull[..., :d] = x_st
         x_st = xfull
     return Inputs(
         wl=wl,
@@ -182,6 +226,10 @@ def make_inputs(wl: Workload, seed: Optional[int] = None) -> Inputs:
         conv_state=to_storage(state, wl.state_dtype),
         slot_idx=slot,
         num_accept_tokens=nat,
+        cu_seqlens=cu,
+        parent=parent,
+        restore_k=rk,
+        has_init=has_init,
     )
 
 
@@ -201,11 +249,18 @@ def poison_like_windows(wl: Workload) -> np.ndarray:
     Poison is a NaN bit pattern that no input draw produces, so any element the call
     fails to write (or writes when it must not) is visible bit-for-bit.
     """
+    return poison(window_shape(wl), wl.state_dtype)
+
+
+def window_shape(wl: Workload):
+    """Shape of the rollback-window buffer of wl's layout."""
     if wl.layout == "dense":
-        shape = (wl.n_slots, wl.T, wl.d_inner, wl.win_cols)
-    else:
-        shape = (wl.n_slots, wl.d_inner, wl.row_cols)
-    return poison(shape, wl.state_dtype)
+        return (wl.n_slots, wl.T, wl.d_inner, wl.win_cols)
+    if wl.layout == "dedup":
+        return (wl.n_slots, wl.d_inner, wl.row_cols)
+    if wl.layout == "dedup_t":
+        return (wl.n_slots, wl.row_cols, wl.d_inner)
+    raise ValueError(wl.layout)
 
 
 def poison(shape, dtype: str) -> np.ndarray:
@@ -223,10 +278,31 @@ def algorithmic_bytes(wl: Workload, inputs: Optional[Inputs] = None) -> int:
     """
     xb = 4 if wl.x_dtype == "f32" else 2
     sb = 4 if wl.state_dtype == "f32" else 2
-    active = wl.n_seq
-    if inputs is not None and inputs.slot_idx is not None:
-        active = int((inputs.slot_idx >= 0).sum())
-    win = wl.T * wl.win_cols if wl.layout == "dense" else wl.row_cols
-    per_chan = 2 * wl.T * xb + 2 * wl.win_cols * sb + win * sb
     once = wl.d_inner * wl.d_conv * xb + (wl.d_inner * xb if wl.bias else 0)
-    return active * wl.d_inner * per_chan + once
+    if inputs is None:
+        rows = [(wl.T, True)] * wl.n_seq
+    else:
+        lens = inputs.lengths
+        act = np.ones(wl.n_seq, bool) if inputs.slot_idx is None else inputs.slot_idx >= 0
+        init = np.ones(wl.n_seq, bool) if inputs.has_init is None else inputs.has_init != 0
+        rows = [(int(lens[i]), bool(init[i])) for i in range(wl.n_seq) if act[i] and lens[i] > 0]
+    total = 0
+    for Ti, init in rows:
+        if wl.prefill:
+            # x and out, the starting window (when the row has one), the committed window
+            per_chan = 2 * Ti * xb + (wl.win_cols * sb if init else 0) + wl.win_cols * sb
+        else:
+            win = Ti * wl.win_cols if wl.layout == "dense" else Ti + wl.d_conv - 2
+            commit = 0 if wl.tree else wl.win_cols * sb
+            per_chan = 2 * Ti * xb + wl.win_cols * sb + commit + win * sb
+        total += wl.d_inner * per_chan
+    return total + once
+
+
+def restore_bytes(wl: Workload, inputs: Inputs) -> int:
+    """Bytes an accepted-prefix restore must move: one window read and one state write of
+    d_conv-1 columns per channel, for rows with a slot and an index >= 0."""
+    sb = 4 if wl.state_dtype == "f32" else 2
+    act = np.ones(wl.n_seq, bool) if inputs.slot_idx is None else inputs.slot_idx >= 0
+    n = int((act & (inputs.restore_k >= 0)).sum())
+    return n * wl.d_inner * 2 * wl.win_cols * sb
