@@ -13,10 +13,19 @@ CV_OK = 0
 CV_EINVAL = -22
 CV_ENOTSUP = -95
 CV_EHIP_BASE = -1000
+CV_WIN_DENSE = 0
+CV_WIN_ROWS = 1
+CV_WIN_ROWS_T = 2
+CV_VARIANT_TREE = 3
 
 EXPORTS = (
     "conv_verify_update_dense",
     "conv_verify_update_dedup",
+    "conv_verify_update",
+    "conv_verify_update_tree",
+    "conv_verify_restore",
+    "conv_prefill",
+    "conv_qk_l2norm",
     "conv_verify_describe",
     "conv_verify_strerror",
     "conv_verify_last_error",
@@ -66,6 +75,17 @@ def load() -> ctypes.CDLL:
         fn = getattr(lib, name)
         fn.restype = ctypes.c_int
         fn.argtypes = upd
+    P, V, I32 = ctypes.POINTER(CvShape), ctypes.c_void_p, ctypes.c_int32
+    lib.conv_verify_update.restype = ctypes.c_int
+    lib.conv_verify_update.argtypes = [P, I32] + [V] * 10
+    lib.conv_verify_update_tree.restype = ctypes.c_int
+    lib.conv_verify_update_tree.argtypes = [P] + [V] * 11
+    lib.conv_verify_restore.restype = ctypes.c_int
+    lib.conv_verify_restore.argtypes = [P, I32] + [V] * 5
+    lib.conv_prefill.restype = ctypes.c_int
+    lib.conv_prefill.argtypes = [P] + [V] * 9
+    lib.conv_qk_l2norm.restype = ctypes.c_int
+    lib.conv_qk_l2norm.argtypes = [P, ctypes.c_int64, ctypes.c_int64, V, V]
     lib.conv_verify_describe.restype = ctypes.c_int
     lib.conv_verify_describe.argtypes = [ctypes.c_int, ctypes.POINTER(CvShape),
                                          ctypes.POINTER(CvLaunchInfo)]

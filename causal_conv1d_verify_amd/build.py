@@ -26,17 +26,20 @@ DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
                 # the token loop is unrolled over its compile-time bucket (up to 32) so
                 # every register index is static; allow that size
                 "-mllvm", "-pragma-unroll-threshold=1000000"]
-COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wextra", "-Wno-unused-parameter",
+COMMON = ["-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden", "-Wall", "-Wextra", "-Wno-unused-parameter",
           f"-I{INCLUDE}", f"-I{CSRC}"]
 
-# The kernel source is compiled once per (x bytes, state bytes, layout); the six
-# objects build in parallel.
+# The verify kernel source is compiled once per (x bytes, state bytes, variant:
+# 0 dense, 1 rows, 2 time-major rows, 3 tree); those objects, the restore / prefill /
+# L2 kernels and the C ABI build in parallel.
 SOURCES = [
-    (f"cv_kernels.hip", f"cv_kernels_{xb}_{sb}_{dd}",
+    ("cv_kernels.hip", f"cv_kernels_{xb}_{sb}_{v}",
      [f"--offload-arch={ARCH}", *DEVICE_FLAGS, f"-DCV_XB={xb}", f"-DCV_SB={sb}",
-      f"-DCV_DEDUP={dd}"])
-    for xb, sb in ((4, 4), (2, 2), (2, 4)) for dd in (0, 1)
-] + [("cv_api.cpp", "cv_api", [])]
+      f"-DCV_VARIANT={v}"])
+    for xb, sb in ((4, 4), (2, 2), (2, 4)) for v in (0, 1, 2, 3)
+] + [("cv_aux_kernels.hip", "cv_aux_kernels", [f"--offload-arch={ARCH}", *DEVICE_FLAGS]),
+     ("cv_api.cpp", "cv_api", [])]
+MAX_JOBS = max(1, min(len(SOURCES), int(os.environ.get("MAX_JOBS", os.cpu_count() or 4))))
 
 
 def _run(cmd):
@@ -50,22 +53,32 @@ def _run(cmd):
 def build(verbose: bool = True) -> str:
     os.makedirs(BUILD, exist_ok=True)
     objs = []
-    procs = []
     t0 = time.time()
+    pending = []
     for src, stem, extra in SOURCES:
         obj = os.path.join(BUILD, stem + ".o")
-        cmd = [HIPCC, *COMMON, *extra, "-c", os.path.join(CSRC, src), "-o", obj]
-        procs.append((cmd, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.PIPE,
-                                            text=True)))
+        pending.append([HIPCC, *COMMON, *extra, "-c", os.path.join(CSRC, src), "-o", obj])
         objs.append(obj)
-    for cmd, p in procs:
+    running = []
+
+    def reap(cmd, p):
         out, err = p.communicate()
         if p.returncode != 0:
+            for _, q in running:
+                q.kill()
             raise RuntimeError(f"build step failed ({p.returncode}):\n{' '.join(cmd)}\n{out}\n{err}")
         noise = [ln for ln in err.splitlines()
                  if ln.strip() and "packed-fp32-ops' is not a recognized feature" not in ln]
         if verbose and noise:
             print("\n".join(noise), file=sys.stderr)
+
+    while pending or running:
+        while pending and len(running) < MAX_JOBS:
+            cmd = pending.pop(0)
+            running.append((cmd, subprocess.Popen(cmd, stdout=subprocess.PIPE,
+                                                  stderr=subprocess.PIPE, text=True)))
+        cmd, p = running.pop(0)
+        reap(cmd, p)
     tmp = LIB + ".tmp"
     _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp])
     os.replace(tmp, LIB)

@@ -33,17 +33,15 @@ int dtype_bytes(int32_t dt) {
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-// Shape-only validation and launch planning.
-int plan_shape(int dedup, const cv_shape_t *s, cvimpl::Plan *plan) {
-    using cvimpl::kMaxLds;
-    using cvimpl::kMaxT;
-    using cvimpl::kWave;
+constexpr int64_t kSpanLimit = ((int64_t)1 << 31) - 16;   // buffer-resource offsets stay below 2^31
+constexpr int kChw = cvimpl::kWave * cvimpl::kChannelsPerLane;
+
+// Checks shared by every entry point: dtypes, d_conv, channels, state geometry.
+int check_common(const cv_shape_t *s, int *xb_out, int *sb_out) {
     if (!s) return fail(CV_EINVAL, "shape is NULL");
-    if (dedup != 0 && dedup != 1) return fail(CV_EINVAL, "dedup must be 0 or 1");
     if (s->n_seq < 0) return fail(CV_EINVAL, "n_seq (%d) < 0", s->n_seq);
     if (s->d_inner < 0) return fail(CV_EINVAL, "d_inner (%d) < 0", s->d_inner);
     if (s->T < 1) return fail(CV_EINVAL, "T (%d) < 1", s->T);
-    if (s->T > kMaxT) return fail(CV_ENOTSUP, "T (%d) > %d", s->T, kMaxT);
     if (s->d_conv < 1) return fail(CV_EINVAL, "d_conv (%d) < 1", s->d_conv);
     if (s->d_conv < 2 || s->d_conv > 4)
         return fail(CV_ENOTSUP, "d_conv (%d) outside 2..4", s->d_conv);
@@ -51,60 +49,94 @@ int plan_shape(int dedup, const cv_shape_t *s, cvimpl::Plan *plan) {
     if (!xb || !sb) return fail(CV_EINVAL, "unknown dtype (x %d, state %d)", s->x_dtype, s->state_dtype);
     if (!((xb == 4 && sb == 4) || (xb == 2 && sb == 2) || (xb == 2 && sb == 4)))
         return fail(CV_ENOTSUP, "dtype pair (x f32, state bf16) is not supported");
-    // channels and x/out strides come in 16-byte units of the x dtype, so every
-    // wavefront's share of every buffer is a whole number of 16-byte chunks
+    // channels come in 16-byte units of the x dtype, so every wavefront's share of
+    // every buffer is a whole number of 16-byte chunks
     const int align = 16 / xb;
-    const int cpl = cvimpl::kChannelsPerLane;
     if (s->d_inner % align)
         return fail(CV_ENOTSUP, "d_inner (%d) must be a multiple of %d", s->d_inner, align);
-    if (s->qk_channels < 0 || s->qk_channels > s->d_inner)
-        return fail(CV_EINVAL, "qk_channels (%d) outside 0..d_inner", s->qk_channels);
-    int hl_log2 = 0, head_lanes = 0;
-    if (s->qk_channels > 0) {
-        if (s->head_dim <= 0) return fail(CV_EINVAL, "head_dim (%d) <= 0", s->head_dim);
-        if (s->qk_channels % s->head_dim)
-            return fail(CV_EINVAL, "qk_channels (%d) %% head_dim (%d) != 0", s->qk_channels,
-                        s->head_dim);
-        if (s->head_dim % cpl)
-            return fail(CV_ENOTSUP, "head_dim (%d) must be a multiple of %d", s->head_dim, cpl);
-        head_lanes = s->head_dim / cpl;
-        if (head_lanes > kWave || (head_lanes & (head_lanes - 1)))
-            return fail(CV_ENOTSUP, "head_dim / %d (%d) must be a power of two <= %d", cpl,
-                        head_lanes, kWave);
-        while ((1 << hl_log2) < head_lanes) ++hl_log2;
-    }
-    if (!std::isfinite(s->l2_eps) || s->l2_eps < 0.0f)
-        return fail(CV_EINVAL, "l2_eps must be finite and >= 0");
     if (s->n_slots < 0) return fail(CV_EINVAL, "n_slots (%d) < 0", s->n_slots);
     const int W1 = s->d_conv - 1;
     if (s->state_len < W1)
         return fail(CV_EINVAL, "state_len (%d) < d_conv-1 (%d)", s->state_len, W1);
-    if (s->x_seq_stride < 0 || s->x_tok_stride < 0 || s->out_seq_stride < 0 ||
-        s->out_tok_stride < 0 || s->state_slot_stride < 0 || s->win_slot_stride < 0)
-        return fail(CV_EINVAL, "negative stride");
+    if (s->state_slot_stride < 0 || s->win_slot_stride < 0)
+        return fail(CV_EINVAL, "negative slot stride");
     const int64_t C = s->d_inner;
-    if (s->T > 1 && s->out_tok_stride < C)
-        return fail(CV_EINVAL, "out_tok_stride (%lld) < d_inner: tokens of out overlap",
-                    (long long)s->out_tok_stride);
-    if (s->n_seq > 1 && s->out_seq_stride < (s->T - 1) * s->out_tok_stride + C)
-        return fail(CV_EINVAL, "out_seq_stride (%lld) too small: rows of out overlap",
-                    (long long)s->out_seq_stride);
     if (s->n_slots > 1 && s->state_slot_stride < C * s->state_len)
         return fail(CV_EINVAL, "state_slot_stride (%lld) < d_inner*state_len",
                     (long long)s->state_slot_stride);
-    const int64_t win_per_slot =
-        dedup ? C * (s->T + s->d_conv - 2) : (int64_t)s->T * C * W1;
-    if (s->n_slots > 1 && s->win_slot_stride < win_per_slot)
+    if ((s->state_slot_stride * sb) % 16 || (s->win_slot_stride * sb) % 16)
+        return fail(CV_ENOTSUP, "state/window slot strides must be multiples of 16 bytes");
+    if (C * s->state_len * sb > kSpanLimit)
+        return fail(CV_ENOTSUP, "a slot's state spans more than 2 GiB");
+    *xb_out = xb;
+    *sb_out = sb;
+    return CV_OK;
+}
+
+int head_lanes_of(const cv_shape_t *s, int *head_lanes, int *hl_log2) {
+    using cvimpl::kWave;
+    const int cpl = cvimpl::kChannelsPerLane;
+    *head_lanes = 0;
+    *hl_log2 = 0;
+    if (s->qk_channels < 0 || s->qk_channels > s->d_inner)
+        return fail(CV_EINVAL, "qk_channels (%d) outside 0..d_inner", s->qk_channels);
+    if (s->qk_channels == 0) return CV_OK;
+    if (s->head_dim <= 0) return fail(CV_EINVAL, "head_dim (%d) <= 0", s->head_dim);
+    if (s->qk_channels % s->head_dim)
+        return fail(CV_EINVAL, "qk_channels (%d) %% head_dim (%d) != 0", s->qk_channels, s->head_dim);
+    if (s->head_dim % cpl)
+        return fail(CV_ENOTSUP, "head_dim (%d) must be a multiple of %d", s->head_dim, cpl);
+    const int hl = s->head_dim / cpl;
+    if (hl > kWave || (hl & (hl - 1)))
+        return fail(CV_ENOTSUP, "head_dim / %d (%d) must be a power of two <= %d", cpl, hl, kWave);
+    *head_lanes = hl;
+    while ((1 << *hl_log2) < hl) ++*hl_log2;
+    if (!std::isfinite(s->l2_eps) || s->l2_eps < 0.0f)
+        return fail(CV_EINVAL, "l2_eps must be finite and >= 0");
+    return CV_OK;
+}
+
+int64_t win_per_slot(int layout, const cv_shape_t *s) {
+    const int64_t C = s->d_inner, W1 = s->d_conv - 1, L = s->T + W1 - 1;
+    return layout == cvimpl::kDense ? (int64_t)s->T * C * W1 : C * L;
+}
+
+// Shape-only validation and launch planning of a verify call.
+int plan_verify(int layout, bool tree, bool packed, const cv_shape_t *s, cvimpl::Plan *plan) {
+    using cvimpl::kMaxLds;
+    using cvimpl::kMaxT;
+    using cvimpl::kWave;
+    int xb = 0, sb = 0;
+    int rc = check_common(s, &xb, &sb);
+    if (rc) return rc;
+    if (layout < cvimpl::kDense || layout > cvimpl::kRowsT)
+        return fail(CV_EINVAL, "unknown window layout %d", layout);
+    if (tree && layout != cvimpl::kDense)
+        return fail(CV_EINVAL, "tree verify writes dense windows");
+    if (s->T > kMaxT) return fail(CV_ENOTSUP, "T (%d) > %d", s->T, kMaxT);
+    int head_lanes = 0, hl_log2 = 0;
+    rc = head_lanes_of(s, &head_lanes, &hl_log2);
+    if (rc) return rc;
+    if (s->x_seq_stride < 0 || s->x_tok_stride < 0 || s->out_seq_stride < 0 || s->out_tok_stride < 0)
+        return fail(CV_EINVAL, "negative x/out stride");
+    const int align = 16 / xb;
+    const int W1 = s->d_conv - 1;
+    const int64_t C = s->d_inner;
+    if ((s->T > 1 || packed) && s->out_tok_stride < C)
+        return fail(CV_EINVAL, "out_tok_stride (%lld) < d_inner: tokens of out overlap",
+                    (long long)s->out_tok_stride);
+    if (!packed && s->n_seq > 1 && s->out_seq_stride < (s->T - 1) * s->out_tok_stride + C)
+        return fail(CV_EINVAL, "out_seq_stride (%lld) too small: rows of out overlap",
+                    (long long)s->out_seq_stride);
+    const int64_t wps = win_per_slot(layout, s);
+    if (s->n_slots > 1 && s->win_slot_stride < wps)
         return fail(CV_EINVAL, "win_slot_stride (%lld) < %lld elements per slot",
-                    (long long)s->win_slot_stride, (long long)win_per_slot);
+                    (long long)s->win_slot_stride, (long long)wps);
     if (s->x_seq_stride % align || s->x_tok_stride % align || s->out_seq_stride % align ||
         s->out_tok_stride % align)
         return fail(CV_ENOTSUP, "x/out strides must be multiples of %d elements", align);
-    if ((s->state_slot_stride * sb) % 16 || (s->win_slot_stride * sb) % 16)
-        return fail(CV_ENOTSUP, "state/window slot strides must be multiples of 16 bytes");
 
-    const int chw = kWave * cpl;
-    const int64_t blocks = (C + chw - 1) / chw;
+    const int64_t blocks = (C + kChw - 1) / kChw;
     const int64_t wg = blocks * (int64_t)s->n_seq;
     if (wg * kWave > (int64_t)UINT32_MAX)
         return fail(CV_ENOTSUP, "grid of %lld workgroups exceeds the launch limit", (long long)wg);
@@ -112,70 +144,87 @@ int plan_shape(int dedup, const cv_shape_t *s, cvimpl::Plan *plan) {
     while (tb < s->T && tb < 16) tb *= 2;
     if (tb < s->T) tb = s->T <= 24 ? 24 : 32;
     // LDS: the wavefront's conv_state region [channels, state_len] passes through first;
-    // afterwards the same allocation holds the dedup tile (T+D-2 rows of the
-    // wavefront's channels) or one or two dense snapshot slabs [channels, D-1].
-    const int64_t region = (int64_t)kWave * cpl * s->state_len * sb;
-    const int64_t later = dedup ? (int64_t)(s->T + s->d_conv - 2) * cvimpl::tile_pitch(sb)
-                                : (int64_t)kWave * cpl * W1 * sb * (s->T > 1 ? 2 : 1);
+    // afterwards the same allocation holds the rows tile (T+D-2 rows of the
+    // wavefront's channels) or one or two dense snapshot slabs [channels, D-1] - after
+    // the tree's v tile (D-1+bucket rows) in tree verify.
+    const int pitch = cvimpl::tile_pitch(sb);
+    const int64_t region = (int64_t)kChw * s->state_len * sb;
+    const int64_t slabs = (int64_t)kChw * W1 * sb * (s->T > 1 ? 2 : 1);
+    int64_t later = 0;
+    if (layout == cvimpl::kRows) later = (int64_t)(s->T + s->d_conv - 2) * pitch;
+    if (layout == cvimpl::kDense) later = (tree ? (int64_t)(W1 + tb) * pitch : 0) + slabs;
     const int64_t lds = region > later ? region : later;
     if (lds > kMaxLds)
         return fail(CV_ENOTSUP, "kernel needs %lld bytes of LDS (> %d)", (long long)lds, kMaxLds);
     // Buffer resources span one row's bytes with a 32-bit size; lanes past d_inner use
     // the offset 2^31, so every span must stay below it.
-    const int64_t lim = ((int64_t)1 << 31) - 16;
     const int64_t x_span = ((int64_t)(s->T - 1) * s->x_tok_stride + C) * xb;
     const int64_t o_span = ((int64_t)(s->T - 1) * s->out_tok_stride + C) * xb;
-    const int64_t w_span = dedup ? C * (s->T + s->d_conv - 2) * sb : (int64_t)s->T * C * W1 * sb;
-    const int64_t st_span = C * s->state_len * sb;
-    if (x_span > lim || o_span > lim || w_span > lim || st_span > lim)
-        return fail(CV_ENOTSUP, "a row spans more than 2 GiB (x %lld, out %lld, windows %lld, "
-                                "state %lld bytes)", (long long)x_span, (long long)o_span,
-                    (long long)w_span, (long long)st_span);
+    const int64_t w_span = wps * sb;
+    if (x_span > kSpanLimit || o_span > kSpanLimit || w_span > kSpanLimit)
+        return fail(CV_ENOTSUP, "a row spans more than 2 GiB (x %lld, out %lld, windows %lld bytes)",
+                    (long long)x_span, (long long)o_span, (long long)w_span);
 
-    plan->dedup = dedup;
+    plan->layout = layout;
+    plan->tree = tree ? 1 : 0;
     plan->x_bytes = xb;
     plan->state_bytes = sb;
     plan->d_conv = s->d_conv;
     plan->token_bucket = tb;
-    plan->channels_per_lane = cpl;
+    plan->channels_per_lane = cvimpl::kChannelsPerLane;
     plan->channel_blocks = (int)blocks;
     plan->workgroups = wg;
     plan->lds_bytes = (int)lds;
     plan->head_lanes = head_lanes;
-    (void)hl_log2;
     return CV_OK;
 }
 
-const void *pick_kernel(const cvimpl::Plan &plan) {
+const void *pick_verify(const cvimpl::Plan &plan) {
     using namespace cvimpl;
-    const int xb = plan.x_bytes, sb = plan.state_bytes, d = plan.d_conv, tb = plan.token_bucket;
-    if (xb == 4 && sb == 4) return plan.dedup ? pick_kernel_4_4_1(d, tb) : pick_kernel_4_4_0(d, tb);
-    if (xb == 2 && sb == 2) return plan.dedup ? pick_kernel_2_2_1(d, tb) : pick_kernel_2_2_0(d, tb);
-    if (xb == 2 && sb == 4) return plan.dedup ? pick_kernel_2_4_1(d, tb) : pick_kernel_2_4_0(d, tb);
+    const int d = plan.d_conv, tb = plan.token_bucket;
+    const int v = plan.tree ? 3 : plan.layout;
+#define CV_PICK_FOR(xb, sb)                                  \
+    switch (v) {                                             \
+        case 0: return pick_kernel_##xb##_##sb##_0(d, tb);   \
+        case 1: return pick_kernel_##xb##_##sb##_1(d, tb);   \
+        case 2: return pick_kernel_##xb##_##sb##_2(d, tb);   \
+        case 3: return pick_kernel_##xb##_##sb##_3(d, tb);   \
+        default: return nullptr;                             \
+    }
+    if (plan.x_bytes == 4 && plan.state_bytes == 4) { CV_PICK_FOR(4, 4) }
+    if (plan.x_bytes == 2 && plan.state_bytes == 2) { CV_PICK_FOR(2, 2) }
+    if (plan.x_bytes == 2 && plan.state_bytes == 4) { CV_PICK_FOR(2, 4) }
+#undef CV_PICK_FOR
     return nullptr;
 }
 
-// Enqueues the kernel; returns a hipError_t value (0 = success).
-int launch(const cvimpl::Plan &plan, const cvimpl::KernelArgs &args, void *stream) {
-    const void *fn = pick_kernel(plan);
-    if (!fn) return (int)hipErrorInvalidDeviceFunction;
-    cvimpl::KernelArgs a = args;
+// Enqueues one 1-D launch of 64-lane workgroups; returns CV_OK or the launch error.
+template <typename Args>
+int launch(const void *fn, int64_t workgroups, int lds_bytes, const Args &args, void *stream) {
+    if (!fn)
+        return fail(CV_EHIP_BASE - (int)hipErrorInvalidDeviceFunction,
+                    "no kernel compiled for this case");
+    Args a = args;
     void *kargs[] = {&a};
-    return (int)hipLaunchKernel(fn, dim3((unsigned)plan.workgroups), dim3(cvimpl::kWave), kargs,
-                                (size_t)plan.lds_bytes, (hipStream_t)stream);
+    const hipError_t e = hipLaunchKernel(fn, dim3((unsigned)workgroups), dim3(cvimpl::kWave), kargs,
+                                         (size_t)lds_bytes, (hipStream_t)stream);
+    if (e != hipSuccess)
+        return fail(CV_EHIP_BASE - (int)e, "kernel launch failed: %s", hipGetErrorString(e));
+    return CV_OK;
 }
 
-int update(int dedup, const cv_shape_t *s, const void *x, const void *weight, const void *bias,
-           void *conv_state, const int32_t *slot_idx, const int32_t *nat, void *out, void *win,
-           void *stream) {
+int verify(int layout, bool tree, const cv_shape_t *s, const void *x, const void *weight,
+           const void *bias, void *conv_state, const int32_t *slot_idx, const int32_t *nat,
+           const int32_t *cu, const int32_t *parent, void *out, void *win, void *stream) {
     g_detail[0] = 0;
     cvimpl::Plan plan;
-    int rc = plan_shape(dedup, s, &plan);
+    int rc = plan_verify(layout, tree, cu != nullptr, s, &plan);
     if (rc) return rc;
     if (s->n_seq == 0 || s->d_inner == 0) return CV_OK;   // nothing to do, nothing launched
     if (!x || !weight || !conv_state || !out || !win)
         return fail(CV_EINVAL, "NULL data pointer (x %p, weight %p, conv_state %p, out %p, "
                                "windows %p)", x, weight, conv_state, out, win);
+    if (tree && !parent) return fail(CV_EINVAL, "parent is NULL");
     if (!aligned16(x) || !aligned16(weight) || (bias && !aligned16(bias)) ||
         !aligned16(conv_state) || !aligned16(out) || !aligned16(win))
         return fail(CV_ENOTSUP, "data pointers must be 16-byte aligned");
@@ -192,6 +241,8 @@ int update(int dedup, const cv_shape_t *s, const void *x, const void *weight, co
     a.nat = nat;
     a.out = out;
     a.win = win;
+    a.cu = cu;
+    a.parent = parent;
     a.x_seq = s->x_seq_stride;
     a.x_tok = s->x_tok_stride;
     a.out_seq = s->out_seq_stride;
@@ -209,11 +260,7 @@ int update(int dedup, const cv_shape_t *s, const void *x, const void *weight, co
     while (plan.head_lanes && (1 << hl_log2) < plan.head_lanes) ++hl_log2;
     a.head_lanes_log2 = hl_log2;
     a.eps = s->l2_eps;
-    int e = launch(plan, a, stream);
-    if (e != 0)
-        return fail(CV_EHIP_BASE - e, "kernel launch failed: %s",
-                    hipGetErrorString(static_cast<hipError_t>(e)));
-    return CV_OK;
+    return launch(pick_verify(plan), plan.workgroups, plan.lds_bytes, a, stream);
 }
 
 }  // namespace
@@ -224,23 +271,172 @@ int conv_verify_update_dense(const cv_shape_t *shape, const void *x, const void 
                              const void *bias, void *conv_state, const int32_t *slot_idx,
                              const int32_t *num_accept_tokens, void *out, void *snapshots,
                              void *hip_stream) {
-    return update(0, shape, x, weight, bias, conv_state, slot_idx, num_accept_tokens, out,
-                  snapshots, hip_stream);
+    return verify(cvimpl::kDense, false, shape, x, weight, bias, conv_state, slot_idx,
+                  num_accept_tokens, nullptr, nullptr, out, snapshots, hip_stream);
 }
 
 int conv_verify_update_dedup(const cv_shape_t *shape, const void *x, const void *weight,
                              const void *bias, void *conv_state, const int32_t *slot_idx,
                              const int32_t *num_accept_tokens, void *out, void *window_rows,
                              void *hip_stream) {
-    return update(1, shape, x, weight, bias, conv_state, slot_idx, num_accept_tokens, out,
-                  window_rows, hip_stream);
+    return verify(cvimpl::kRows, false, shape, x, weight, bias, conv_state, slot_idx,
+                  num_accept_tokens, nullptr, nullptr, out, window_rows, hip_stream);
 }
 
-int conv_verify_describe(int dedup, const cv_shape_t *shape, cv_launch_info_t *info) {
+int conv_verify_update(const cv_shape_t *shape, int32_t layout, const void *x,
+                       const void *weight, const void *bias, void *conv_state,
+                       const int32_t *slot_idx, const int32_t *num_accept_tokens,
+                       const int32_t *cu_seqlens, void *out, void *windows, void *hip_stream) {
+    return verify(layout, false, shape, x, weight, bias, conv_state, slot_idx,
+                  num_accept_tokens, cu_seqlens, nullptr, out, windows, hip_stream);
+}
+
+int conv_verify_update_tree(const cv_shape_t *shape, const void *x, const void *weight,
+                            const void *bias, const void *conv_state,
+                            const int32_t *slot_idx, const int32_t *num_accept_tokens,
+                            const int32_t *cu_seqlens, const int32_t *parent, void *out,
+                            void *windows, void *hip_stream) {
+    // conv_state is only read in tree verify (that kernel variant stores nothing to it)
+    return verify(cvimpl::kDense, true, shape, x, weight, bias, const_cast<void *>(conv_state),
+                  slot_idx, num_accept_tokens, cu_seqlens, parent, out, windows, hip_stream);
+}
+
+int conv_verify_restore(const cv_shape_t *s, int32_t layout, void *conv_state,
+                        const void *windows, const int32_t *slot_idx,
+                        const int32_t *window_index, void *hip_stream) {
+    g_detail[0] = 0;
+    int xb = 0, sb = 0;
+    int rc = check_common(s, &xb, &sb);
+    if (rc) return rc;
+    if (layout < cvimpl::kDense || layout > cvimpl::kRowsT)
+        return fail(CV_EINVAL, "unknown window layout %d", layout);
+    if (s->T > cvimpl::kMaxT) return fail(CV_ENOTSUP, "T (%d) > %d", s->T, cvimpl::kMaxT);
+    const int64_t wps = win_per_slot(layout, s);
+    if (s->n_slots > 1 && s->win_slot_stride < wps)
+        return fail(CV_EINVAL, "win_slot_stride (%lld) < %lld elements per slot",
+                    (long long)s->win_slot_stride, (long long)wps);
+    if (wps * sb > kSpanLimit) return fail(CV_ENOTSUP, "a slot's windows span more than 2 GiB");
+    if (s->n_seq == 0 || s->d_inner == 0) return CV_OK;
+    if (!conv_state || !windows || !window_index)
+        return fail(CV_EINVAL, "NULL pointer (conv_state %p, windows %p, window_index %p)",
+                    conv_state, windows, (const void *)window_index);
+    if (!aligned16(conv_state) || !aligned16(windows))
+        return fail(CV_ENOTSUP, "data pointers must be 16-byte aligned");
+    if (!slot_idx && s->n_slots < s->n_seq)
+        return fail(CV_EINVAL, "n_slots (%d) < n_seq (%d) with identity slots", s->n_slots, s->n_seq);
+    const int64_t blocks = (s->d_inner + kChw - 1) / kChw;
+    const int64_t wg = blocks * (int64_t)s->n_seq;
+    if (wg * cvimpl::kWave > (int64_t)UINT32_MAX)
+        return fail(CV_ENOTSUP, "grid of %lld workgroups exceeds the launch limit", (long long)wg);
+    const int lds = layout == cvimpl::kRows ? kChw * (s->T + s->d_conv - 2) * sb : 0;
+    cvimpl::RestoreArgs a;
+    a.state = conv_state;
+    a.win = windows;
+    a.slot_idx = slot_idx;
+    a.widx = window_index;
+    a.state_slot = s->state_slot_stride;
+    a.win_slot = s->win_slot_stride;
+    a.n_seq = s->n_seq;
+    a.T = s->T;
+    a.d_inner = s->d_inner;
+    a.n_slots = s->n_slots;
+    a.state_len = s->state_len;
+    a.channel_blocks = (int)blocks;
+    return launch(cvimpl::pick_restore(sb, s->d_conv, layout), wg, lds, a, hip_stream);
+}
+
+int conv_prefill(const cv_shape_t *s, const void *x, const void *weight, const void *bias,
+                 void *conv_state, const int32_t *slot_idx, const int32_t *cu_seqlens,
+                 const int32_t *has_initial_state, void *out, void *hip_stream) {
+    g_detail[0] = 0;
+    int xb = 0, sb = 0;
+    int rc = check_common(s, &xb, &sb);
+    if (rc) return rc;
+    const int align = 16 / xb;
+    const int64_t C = s->d_inner;
+    if (s->x_tok_stride < C || s->out_tok_stride < C)
+        return fail(CV_EINVAL, "x/out token strides must be >= d_inner");
+    if (s->x_tok_stride % align || s->out_tok_stride % align)
+        return fail(CV_ENOTSUP, "x/out token strides must be multiples of %d elements", align);
+    const int64_t x_span = ((int64_t)(s->T - 1) * s->x_tok_stride + C) * xb;
+    const int64_t o_span = ((int64_t)(s->T - 1) * s->out_tok_stride + C) * xb;
+    if (x_span > kSpanLimit || o_span > kSpanLimit)
+        return fail(CV_ENOTSUP, "a prompt spans more than 2 GiB");
+    if (s->n_seq == 0 || s->d_inner == 0) return CV_OK;
+    if (!x || !weight || !conv_state || !out || !cu_seqlens)
+        return fail(CV_EINVAL, "NULL pointer (x %p, weight %p, conv_state %p, out %p, cu_seqlens %p)",
+                    x, weight, conv_state, out, (const void *)cu_seqlens);
+    if (!aligned16(x) || !aligned16(weight) || (bias && !aligned16(bias)) ||
+        !aligned16(conv_state) || !aligned16(out))
+        return fail(CV_ENOTSUP, "data pointers must be 16-byte aligned");
+    if (!slot_idx && s->n_slots < s->n_seq)
+        return fail(CV_EINVAL, "n_slots (%d) < n_seq (%d) with identity slots", s->n_slots, s->n_seq);
+    const int64_t blocks = (C + kChw - 1) / kChw;
+    const int64_t chunks = (s->T + cvimpl::kPrefillChunk - 1) / cvimpl::kPrefillChunk;
+    const int64_t wg = blocks * chunks * (int64_t)s->n_seq;
+    if (wg * cvimpl::kWave > (int64_t)UINT32_MAX)
+        return fail(CV_ENOTSUP, "grid of %lld workgroups exceeds the launch limit", (long long)wg);
+    cvimpl::PrefillArgs a;
+    a.x = x;
+    a.weight = weight;
+    a.bias = bias;
+    a.state = conv_state;
+    a.slot_idx = slot_idx;
+    a.cu = cu_seqlens;
+    a.has_init = has_initial_state;
+    a.out = out;
+    a.x_tok = s->x_tok_stride;
+    a.out_tok = s->out_tok_stride;
+    a.state_slot = s->state_slot_stride;
+    a.n_seq = s->n_seq;
+    a.T = s->T;
+    a.d_inner = s->d_inner;
+    a.n_slots = s->n_slots;
+    a.state_len = s->state_len;
+    a.channel_blocks = (int)blocks;
+    a.chunks = (int)chunks;
+    return launch(cvimpl::pick_prefill(xb, sb, s->d_conv), wg, 0, a, hip_stream);
+}
+
+int conv_qk_l2norm(const cv_shape_t *s, int64_t n_rows, int64_t row_stride, void *x,
+                   void *hip_stream) {
+    g_detail[0] = 0;
+    if (!s) return fail(CV_EINVAL, "shape is NULL");
+    const int xb = dtype_bytes(s->x_dtype);
+    if (!xb) return fail(CV_EINVAL, "unknown x dtype %d", s->x_dtype);
+    if (s->d_inner < 0) return fail(CV_EINVAL, "d_inner (%d) < 0", s->d_inner);
+    int head_lanes = 0, hl_log2 = 0;
+    int rc = head_lanes_of(s, &head_lanes, &hl_log2);
+    if (rc) return rc;
+    if (n_rows < 0) return fail(CV_EINVAL, "n_rows (%lld) < 0", (long long)n_rows);
+    if (row_stride < s->qk_channels) return fail(CV_EINVAL, "row_stride < qk_channels");
+    if (row_stride % (16 / xb)) return fail(CV_ENOTSUP, "row_stride must be a multiple of %d", 16 / xb);
+    if (s->qk_channels % (16 / xb))
+        return fail(CV_ENOTSUP, "qk_channels must be a multiple of %d", 16 / xb);
+    if (n_rows == 0 || s->qk_channels == 0) return CV_OK;
+    if (!x) return fail(CV_EINVAL, "x is NULL");
+    if (!aligned16(x)) return fail(CV_ENOTSUP, "x must be 16-byte aligned");
+    const int64_t blocks = (s->qk_channels + kChw - 1) / kChw;
+    const int64_t wg = blocks * n_rows;
+    if (wg * cvimpl::kWave > (int64_t)UINT32_MAX)
+        return fail(CV_ENOTSUP, "grid of %lld workgroups exceeds the launch limit", (long long)wg);
+    cvimpl::L2Args a;
+    a.x = x;
+    a.row_stride = row_stride;
+    a.qk = s->qk_channels;
+    a.qk_blocks = (int)blocks;
+    a.head_lanes_log2 = hl_log2;
+    a.eps = s->l2_eps;
+    return launch(cvimpl::pick_l2(xb), wg, 0, a, hip_stream);
+}
+
+int conv_verify_describe(int variant, const cv_shape_t *shape, cv_launch_info_t *info) {
     g_detail[0] = 0;
     if (!info) return fail(CV_EINVAL, "info is NULL");
+    if (variant < 0 || variant > CV_VARIANT_TREE) return fail(CV_EINVAL, "unknown variant %d", variant);
     cvimpl::Plan plan;
-    int rc = plan_shape(dedup, shape, &plan);
+    const bool tree = variant == CV_VARIANT_TREE;
+    int rc = plan_verify(tree ? cvimpl::kDense : variant, tree, false, shape, &plan);
     if (rc) return rc;
     info->workgroups = plan.workgroups;
     info->threads = cvimpl::kWave;

@@ -1,0 +1,423 @@
+// HIP kernels (gfx950) around the verify launch: the accepted-prefix restore, the
+// prefill conv over packed prompts, and the separate per-head L2 over q|k.
+//
+//  * Restore (sglang PR 46184, "Motivation": the window lets the accepted prefix's
+//    conv state be restored after verify): one wavefront per (row, 256 channels)
+//    copies window k of the row's slot into conv_state columns 0..D-2.
+//  * Prefill (Atlas glm5next_kda/mod.rs, prefill body: conv + SiLU only): one
+//    wavefront per (row, 16-token chunk, 256 channels); the chunk's D-1 earlier inputs
+//    come from x (or, for the first chunk, from the row's state window or zeros), and
+//    the first chunk's wavefront also commits the row's last window - it is the one
+//    that read the state, so the read and the write of a slot stay in one wavefront.
+//  * L2 (same page, module doc: prefill L2 is a separate pass over q|k): one wavefront
+//    per (token row, 256 q|k channels), the same cross-lane head sums as the verify.
+//
+// Every global access is a lane-contiguous 8/16-byte buffer access with the streaming
+// policy, except element stores where a state row is wider than the window.
+#include "cv_device.h"
+#include "cv_internal.h"
+
+namespace cvimpl {
+namespace {
+
+constexpr int CPL = kChannelsPerLane;
+constexpr int CHW = kWave * kChannelsPerLane;
+
+// One EB-byte element load (2 or 4 bytes), zero-extended.
+template <int EB>
+__device__ __forceinline__ uint32_t gload_elem(rsrc_t r, uint32_t voff) {
+    if constexpr (EB == 4) {
+        return __builtin_amdgcn_raw_buffer_load_b32(r, (int)voff, 0, kNT);
+    } else {
+        return (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, (int)voff, 0, kNT);
+    }
+}
+
+// Element (ch, j) of a lane's packed [CPL][W1] run of SB-byte elements.
+template <int SB, int W1>
+__device__ __forceinline__ uint32_t run_elem(const uint32_t *run, int ch, int j) {
+    return elem_bits<SB>(run, ch * W1 + j);
+}
+
+template <int SB, int W1>
+__device__ __forceinline__ void pack_run(const uint32_t (&e)[CPL][W1], uint32_t *run) {
+    constexpr int RUNW = CPL * W1 * SB / 4;
+#pragma unroll
+    for (int w = 0; w < RUNW; ++w) {
+        if constexpr (SB == 4) {
+            run[w] = e[w / W1][w % W1];
+        } else {
+            const int e0 = 2 * w, e1 = 2 * w + 1;
+            run[w] = e[e0 / W1][e0 % W1] | (e[e1 / W1][e1 % W1] << 16);
+        }
+    }
+}
+
+// conv_state[s, c, 0..W1-1] of the lane's channels <- e: one lane-contiguous run when
+// a state row is exactly the window, element stores otherwise (columns >= W1 stay).
+template <int SB, int W1>
+__device__ __forceinline__ void store_window(rsrc_t st_r, int SL, bool on, int lane,
+                                             const uint32_t (&e)[CPL][W1]) {
+    constexpr int RUNB = CPL * W1 * SB;
+    if (SL == W1) {
+        uint32_t run[RUNB / 4];
+        pack_run<SB, W1>(e, run);
+        const uint32_t lo = on ? (uint32_t)(lane * RUNB) : kOffLane;
+#pragma unroll
+        for (int q = 0; q < RUNB / 8; ++q) gstore<8>(st_r, lo + 8 * q, 0, run + 2 * q);
+    } else {
+#pragma unroll
+        for (int ch = 0; ch < CPL; ++ch)
+#pragma unroll
+            for (int j = 0; j < W1; ++j)
+                gstore_elem<SB>(st_r, on ? (uint32_t)(((lane * CPL + ch) * SL + j) * SB) : kOffLane,
+                                e[ch][j]);
+    }
+}
+
+// ---- accepted-prefix restore ------------------------------------------------------------
+
+template <int SB, int D, int LAYOUT>
+__global__ __launch_bounds__(kWave) void cv_restore_kernel(RestoreArgs p) {
+    constexpr int W1 = D - 1;
+    constexpr int SCB = CPL * SB;
+    constexpr int SW = SCB / 4;
+    constexpr int RUNB = CPL * W1 * SB;
+    extern __shared__ uint4 lds_raw[];
+    char *lds = (char *)lds_raw;
+
+    const int lane = threadIdx.x;
+    const int row = (int)(blockIdx.x / (unsigned)p.channel_blocks);
+    const int cb = (int)(blockIdx.x - (unsigned)row * (unsigned)p.channel_blocks) * CHW;
+    const int slot = p.slot_idx ? scalar_read(p.slot_idx, row) : row;
+    const int k = scalar_read(p.widx, row);
+    if (slot < 0 || slot >= p.n_slots || k < 0 || k >= p.T) return;
+    const int nch = min(CHW, p.d_inner - cb);
+    const bool on = lane * CPL < nch;
+
+    uint32_t e[CPL][W1];   // the window's elements of the lane's channels, as bits
+    if constexpr (LAYOUT == kDense) {
+        // window k of the slot: the wavefront's [nch, W1] slab is contiguous
+        const rsrc_t w_r = make_rsrc(
+            (const char *)p.win + ((int64_t)slot * p.win_slot + ((int64_t)k * p.d_inner + cb) * W1) * SB,
+            (uint32_t)(nch * W1 * SB));
+        uint32_t run[RUNB / 4];
+        const uint32_t lo = on ? (uint32_t)(lane * RUNB) : kOffLane;
+#pragma unroll
+        for (int q = 0; q < RUNB / 8; ++q) gload<8>(w_r, lo + 8 * q, 0, run + 2 * q);
+#pragma unroll
+        for (int ch = 0; ch < CPL; ++ch)
+#pragma unroll
+            for (int j = 0; j < W1; ++j) e[ch][j] = run_elem<SB, W1>(run, ch, j);
+    } else if constexpr (LAYOUT == kRows) {
+        // columns k..k+W1-1 of each channel's row: every 32-byte sector of the
+        // wavefront's row block holds some of them, so the block comes in whole
+        // (coalesced) through LDS and each lane picks its elements out
+        const int LS = p.T + W1 - 1;
+        const rsrc_t row_r = make_rsrc(
+            (const char *)p.win + ((int64_t)slot * p.win_slot + (int64_t)cb * LS) * SB,
+            (uint32_t)(nch * LS * SB));
+        const int chunks = nch * LS * SB / 16;
+        for (int q = lane; q < chunks; q += kWave) {
+            uint32_t w4[4];
+            gload<16>(row_r, (uint32_t)q * 16u, 0, w4);
+            *(uint4 *)(lds + q * 16) = make_uint4(w4[0], w4[1], w4[2], w4[3]);
+        }
+        lds_barrier();
+#pragma unroll
+        for (int ch = 0; ch < CPL; ++ch)
+#pragma unroll
+            for (int j = 0; j < W1; ++j)
+                e[ch][j] = on ? lds_get<SB>(lds + ((lane * CPL + ch) * LS + k + j) * SB) : 0u;
+    } else {
+        // time-major rows: column k+j holds the d channels contiguously
+        const int LS = p.T + W1 - 1;
+        const rsrc_t rt_r = make_rsrc(
+            (const char *)p.win + ((int64_t)slot * p.win_slot + cb) * SB,
+            (uint32_t)(((int64_t)(LS - 1) * p.d_inner + nch) * SB));
+        const uint32_t laneS = on ? (uint32_t)(lane * SCB) : kOffLane;
+#pragma unroll
+        for (int j = 0; j < W1; ++j) {
+            uint32_t col[SW];
+            gload<SCB>(rt_r, laneS, (uint32_t)((k + j) * p.d_inner * SB), col);
+#pragma unroll
+            for (int ch = 0; ch < CPL; ++ch) e[ch][j] = elem_bits<SB>(col, ch);
+        }
+    }
+
+    const rsrc_t st_r = make_rsrc(
+        (char *)p.state + ((int64_t)slot * p.state_slot + (int64_t)cb * p.state_len) * SB,
+        (uint32_t)(nch * p.state_len * SB));
+    store_window<SB, W1>(st_r, p.state_len, on, lane, e);
+}
+
+// ---- prefill conv -----------------------------------------------------------------------
+
+template <int XB, int SB, int D, int TC>
+__global__ __launch_bounds__(kWave) void cv_prefill_kernel(PrefillArgs p) {
+    constexpr int W1 = D - 1;
+    constexpr int VB = CPL * XB;
+    constexpr int XW = VB / 4;
+    constexpr int RUNB = CPL * W1 * SB;
+    constexpr int G = 4;   // tokens per branch-free arithmetic chunk
+
+    const int lane = threadIdx.x;
+    const unsigned b = blockIdx.x;
+    const unsigned r2 = b / (unsigned)p.channel_blocks;
+    const int cb = (int)(b - r2 * (unsigned)p.channel_blocks) * CHW;
+    const int row = (int)(r2 / (unsigned)p.chunks);
+    const int chunk = (int)(r2 - (unsigned)row * (unsigned)p.chunks);
+
+    const int c0 = scalar_read(p.cu, row);
+    const int Ti = scalar_read(p.cu, row + 1) - c0;
+    const int slot = p.slot_idx ? scalar_read(p.slot_idx, row) : row;
+    const bool init = p.has_init ? scalar_read(p.has_init, row) != 0 : true;
+    const int t0 = chunk * TC;
+    if (Ti < 1 || Ti > p.T || t0 >= Ti || slot < 0 || slot >= p.n_slots) return;
+    const int nt = min(TC, Ti - t0);
+    const int nch = min(CHW, p.d_inner - cb);
+    const bool on = lane * CPL < nch;
+    const uint32_t laneV = on ? (uint32_t)(lane * VB) : kOffLane;
+    const int SL = p.state_len;
+
+    __builtin_amdgcn_s_setprio(3);
+    const rsrc_t x_r = make_rsrc((const char *)p.x + ((int64_t)c0 * p.x_tok + cb) * XB,
+                                 (uint32_t)(((int64_t)(Ti - 1) * p.x_tok + nch) * XB));
+    uint32_t X[TC][XW];   // x_{t0+t}
+#pragma unroll
+    for (int t = 0; t < TC; ++t) {
+        if (t < nt) {
+            gload<VB>(x_r, laneV, (uint32_t)((t0 + t) * p.x_tok * XB), X[t]);
+        } else {
+#pragma unroll
+            for (int w = 0; w < XW; ++w) X[t][w] = 0u;
+        }
+    }
+    uint32_t wr[XW * D];
+    uint32_t br[XW];
+    {
+        const rsrc_t w_r = make_rsrc((const char *)p.weight + (int64_t)cb * D * XB,
+                                     (uint32_t)(nch * D * XB));
+        const uint32_t lw = on ? (uint32_t)(lane * VB * D) : kOffLane;
+#pragma unroll
+        for (int q = 0; q < D; ++q) gload<VB>(w_r, lw + VB * q, 0, wr + XW * q);
+#pragma unroll
+        for (int w = 0; w < XW; ++w) br[w] = 0u;
+        if (p.bias) {
+            const rsrc_t b_r = make_rsrc((const char *)p.bias + (int64_t)cb * XB, (uint32_t)(nch * XB));
+            gload<VB>(b_r, laneV, 0, br);
+        }
+    }
+    // The W1 inputs before token t0: x for later chunks; for the first chunk the
+    // state window (columns 0..W1-1) or zeros.
+    float hv[W1][CPL];
+    uint32_t hs[W1][CPL];   // first chunk: the state window's bits (zero without one)
+    const rsrc_t st_r = make_rsrc(
+        (char *)p.state + ((int64_t)slot * p.state_slot + (int64_t)cb * SL) * SB,
+        (uint32_t)(nch * SL * SB));
+    if (t0 > 0) {
+#pragma unroll
+        for (int j = 0; j < W1; ++j) {
+            uint32_t h[XW];
+            gload<VB>(x_r, laneV, (uint32_t)((t0 - W1 + j) * p.x_tok * XB), h);
+#pragma unroll
+            for (int ch = 0; ch < CPL; ++ch) {
+                hv[j][ch] = elem_val<XB>(h, ch);
+                hs[j][ch] = 0u;
+            }
+        }
+    } else {
+#pragma unroll
+        for (int ch = 0; ch < CPL; ++ch)
+#pragma unroll
+            for (int j = 0; j < W1; ++j)
+                hs[j][ch] = init ? gload_elem<SB>(st_r, on ? (uint32_t)(((lane * CPL + ch) * SL + j) * SB)
+                                                           : kOffLane)
+                                 : 0u;
+#pragma unroll
+        for (int ch = 0; ch < CPL; ++ch)
+#pragma unroll
+            for (int j = 0; j < W1; ++j) {
+                const uint32_t bits = hs[j][ch];
+                hv[j][ch] = SB == 4 ? __uint_as_float(bits) : __uint_as_float(bits << 16);
+            }
+    }
+    // The first chunk also commits the row's last window: the last W1 of
+    // [start window | x_0 .. x_{Ti-1}].
+    uint32_t cx[W1][XW];
+    if (chunk == 0) {
+#pragma unroll
+        for (int j = 0; j < W1; ++j) {
+            if (Ti - W1 + j >= 0) {
+                gload<VB>(x_r, laneV, (uint32_t)((Ti - W1 + j) * p.x_tok * XB), cx[j]);
+            } else {
+#pragma unroll
+                for (int w = 0; w < XW; ++w) cx[j][w] = 0u;
+            }
+        }
+    }
+    __builtin_amdgcn_s_setprio(0);
+
+    float wv[CPL][D];
+    float bv[CPL];
+#pragma unroll
+    for (int ch = 0; ch < CPL; ++ch) {
+#pragma unroll
+        for (int w = 0; w < D; ++w) wv[ch][w] = elem_val<XB>(wr, ch * D + w);
+        bv[ch] = elem_val<XB>(br, ch);
+    }
+    // v[k]: k < W1 the inputs before t0, else x_{t0+k-W1}; k compile-time
+    auto val = [&](int k, int ch) -> float {
+        return k < W1 ? hv[k < W1 ? k : 0][ch] : elem_val<XB>(X[k < W1 ? 0 : k - W1], ch);
+    };
+
+    const rsrc_t o_r = make_rsrc((char *)p.out + ((int64_t)c0 * p.out_tok + cb) * XB,
+                                 (uint32_t)(((int64_t)(Ti - 1) * p.out_tok + nch) * XB));
+#pragma unroll
+    for (int g0 = 0; g0 < TC; g0 += G) {
+        if (g0 < nt) {
+            float y[G][CPL];
+#pragma unroll
+            for (int g = 0; g < G; ++g)
+#pragma unroll
+                for (int ch = 0; ch < CPL; ++ch) {
+                    float acc = bv[ch];
+#pragma unroll
+                    for (int w = 0; w < D; ++w)
+                        acc = __builtin_fmaf(wv[ch][w], val(g0 + g + w, ch), acc);
+                    y[g][ch] = silu(acc);
+                }
+#pragma unroll
+            for (int g = 0; g < G; ++g) {
+                if (g0 + g < nt) {
+                    uint32_t o[XW];
+                    if constexpr (XB == 4) {
+#pragma unroll
+                        for (int ch = 0; ch < CPL; ++ch) o[ch] = __float_as_uint(y[g][ch]);
+                    } else {
+                        typedef float f2 __attribute__((ext_vector_type(2)));
+                        typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+#pragma unroll
+                        for (int w = 0; w < XW; ++w) {
+                            f2 pr = {y[g][2 * w], y[g][2 * w + 1]};
+                            o[w] = __builtin_bit_cast(uint32_t, __builtin_convertvector(pr, b2));
+                        }
+                    }
+                    gstore<VB>(o_r, laneV, (uint32_t)((t0 + g0 + g) * p.out_tok * XB), o);
+                }
+            }
+        }
+    }
+
+    if (chunk == 0) {
+        // u = [start window | x_0 ..]: the committed window is u[Ti .. Ti+W1-1]; an
+        // element with u-index m < W1 is start window column m (rows shorter than W1).
+        uint32_t e[CPL][W1];
+#pragma unroll
+        for (int j = 0; j < W1; ++j) {
+            const int m = Ti + j;
+#pragma unroll
+            for (int ch = 0; ch < CPL; ++ch) {
+                uint32_t v = x_to_state_bits<XB, SB>(elem_bits<XB>(cx[j], ch));
+#pragma unroll
+                for (int q = 0; q < W1; ++q)
+                    if (m == q) v = hs[q][ch];
+                e[ch][j] = v;
+            }
+        }
+        store_window<SB, W1>(st_r, SL, on, lane, e);
+    }
+    (void)RUNB;
+}
+
+// ---- separate per-head L2 over q|k -------------------------------------------------------
+
+template <int XB>
+__global__ __launch_bounds__(kWave) void cv_l2_kernel(L2Args p) {
+    constexpr int VB = CPL * XB;
+    constexpr int XW = VB / 4;
+    const int lane = threadIdx.x;
+    const int64_t r = (int64_t)(blockIdx.x / (unsigned)p.qk_blocks);
+    const int cb = (int)(blockIdx.x - (unsigned)r * (unsigned)p.qk_blocks) * CHW;
+    const int nch = min(CHW, p.qk - cb);
+    const bool on = lane * CPL < nch;
+    const uint32_t laneV = on ? (uint32_t)(lane * VB) : kOffLane;
+    const rsrc_t x_r = make_rsrc((char *)p.x + (r * p.row_stride + cb) * XB, (uint32_t)(nch * XB));
+    uint32_t w[XW];
+    gload<VB>(x_r, laneV, 0, w);
+    float y[CPL];
+    float ss[1] = {0.0f};
+#pragma unroll
+    for (int ch = 0; ch < CPL; ++ch) {
+        y[ch] = elem_val<XB>(w, ch);
+        ss[0] = __builtin_fmaf(y[ch], y[ch], ss[0]);
+    }
+    // a head never straddles q|k's end (qk is a multiple of head_dim), so lanes past
+    // it form whole groups of their own
+    group_sums<1>(ss, p.head_lanes_log2);
+    const float sc = __builtin_amdgcn_rsqf(ss[0] + p.eps);
+    uint32_t o[XW];
+    if constexpr (XB == 4) {
+#pragma unroll
+        for (int ch = 0; ch < CPL; ++ch) o[ch] = __float_as_uint(y[ch] * sc);
+    } else {
+        typedef float f2 __attribute__((ext_vector_type(2)));
+        typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+#pragma unroll
+        for (int q = 0; q < XW; ++q) {
+            f2 pr = {y[2 * q] * sc, y[2 * q + 1] * sc};
+            o[q] = __builtin_bit_cast(uint32_t, __builtin_convertvector(pr, b2));
+        }
+    }
+    gstore<VB>(x_r, laneV, 0, o);
+}
+
+template <int SB, int LAYOUT>
+const void *restore_for(int d_conv) {
+    switch (d_conv) {
+        case 2: return (const void *)cv_restore_kernel<SB, 2, LAYOUT>;
+        case 3: return (const void *)cv_restore_kernel<SB, 3, LAYOUT>;
+        case 4: return (const void *)cv_restore_kernel<SB, 4, LAYOUT>;
+        default: return nullptr;
+    }
+}
+
+template <int XB, int SB>
+const void *prefill_for(int d_conv) {
+    switch (d_conv) {
+        case 2: return (const void *)cv_prefill_kernel<XB, SB, 2, kPrefillChunk>;
+        case 3: return (const void *)cv_prefill_kernel<XB, SB, 3, kPrefillChunk>;
+        case 4: return (const void *)cv_prefill_kernel<XB, SB, 4, kPrefillChunk>;
+        default: return nullptr;
+    }
+}
+
+}  // namespace
+
+const void *pick_restore(int state_bytes, int d_conv, int layout) {
+    if (state_bytes == 4) {
+        if (layout == kDense) return restore_for<4, kDense>(d_conv);
+        if (layout == kRows) return restore_for<4, kRows>(d_conv);
+        if (layout == kRowsT) return restore_for<4, kRowsT>(d_conv);
+    } else if (state_bytes == 2) {
+        if (layout == kDense) return restore_for<2, kDense>(d_conv);
+        if (layout == kRows) return restore_for<2, kRows>(d_conv);
+        if (layout == kRowsT) return restore_for<2, kRowsT>(d_conv);
+    }
+    return nullptr;
+}
+
+const void *pick_prefill(int x_bytes, int state_bytes, int d_conv) {
+    if (x_bytes == 4 && state_bytes == 4) return prefill_for<4, 4>(d_conv);
+    if (x_bytes == 2 && state_bytes == 2) return prefill_for<2, 2>(d_conv);
+    if (x_bytes == 2 && state_bytes == 4) return prefill_for<2, 4>(d_conv);
+    return nullptr;
+}
+
+const void *pick_l2(int x_bytes) {
+    if (x_bytes == 4) return (const void *)cv_l2_kernel<4>;
+    if (x_bytes == 2) return (const void *)cv_l2_kernel<2>;
+    return nullptr;
+}
+
+}  // namespace cvimpl

@@ -1,0 +1,219 @@
+// Device-side helpers shared by the HIP kernels of the library (verify, restore,
+// prefill, L2): bit-pattern access to packed elements, SiLU, cross-lane sums, raw
+// buffer loads/stores with the streaming policy, LDS runs and barriers.  Internal;
+// included by the .hip sources only.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "cv_internal.h"
+
+namespace cvimpl {
+namespace {
+
+// ---- bit-pattern helpers (compile-time element indices) -----------------------------
+
+// Element `e` of a packed word array of EB-byte elements, as raw bits.
+template <int EB>
+__device__ __forceinline__ uint32_t elem_bits(const uint32_t *w, int e) {
+    if constexpr (EB == 4) {
+        return w[e];
+    } else {
+        return (e & 1) ? (w[e >> 1] >> 16) : (w[e >> 1] & 0xFFFFu);
+    }
+}
+
+// Element `e` as a float (bf16 widening is exact).
+template <int EB>
+__device__ __forceinline__ float elem_val(const uint32_t *w, int e) {
+    if constexpr (EB == 4) {
+        return __uint_as_float(w[e]);
+    } else {
+        return __uint_as_float((e & 1) ? (w[e >> 1] & 0xFFFF0000u) : (w[e >> 1] << 16));
+    }
+}
+
+// x-element bits re-expressed in the state element type (bf16 -> fp32 is exact).
+template <int XB, int SB>
+__device__ __forceinline__ uint32_t x_to_state_bits(uint32_t xbits) {
+    if constexpr (XB == SB) {
+        return xbits;
+    } else {
+        static_assert(XB == 2 && SB == 4, "only bf16 -> fp32 widening");
+        return xbits << 16;
+    }
+}
+
+__device__ __forceinline__ float silu(float p) {
+    // p * sigmoid(p) with v_exp_f32 and v_rcp_f32.  For p << 0 the exponential
+    // saturates to +inf and the result is -0.
+    return p * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(p * -1.4426950408889634f));
+}
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, true));
+}
+
+// Sums over the 2^hl_log2 lanes of an aligned lane group (all lanes active), for each
+// of G independent values at once: every stage is applied to all G values before the
+// next, so their cross-lane latencies overlap.  Each step adds the two halves of a
+// group symmetrically, so all lanes of a group hold the bit-identical sum.
+template <int G>
+__device__ __forceinline__ void group_sums(float (&v)[G], int hl_log2) {
+    if (hl_log2 >= 1)   // quad_perm [1,0,3,2]: lane ^ 1
+#pragma unroll
+        for (int g = 0; g < G; ++g) v[g] += dpp<0xB1>(v[g]);
+    if (hl_log2 >= 2)   // quad_perm [2,3,0,1]: lane ^ 2
+#pragma unroll
+        for (int g = 0; g < G; ++g) v[g] += dpp<0x4E>(v[g]);
+    if (hl_log2 >= 3)   // row_half_mirror: the other quad of the 8
+#pragma unroll
+        for (int g = 0; g < G; ++g) v[g] += dpp<0x141>(v[g]);
+    if (hl_log2 >= 4)   // row_mirror: the other half of the 16-lane row
+#pragma unroll
+        for (int g = 0; g < G; ++g) v[g] += dpp<0x140>(v[g]);
+    if (hl_log2 >= 5)   // lane ^ 16 inside 32 (ds_swizzle xor mode)
+#pragma unroll
+        for (int g = 0; g < G; ++g)
+            v[g] += __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v[g]), 0x401F));
+    if (hl_log2 >= 6) {  // lane ^ 32
+        const int src = (int)((threadIdx.x ^ 32u) << 2);
+#pragma unroll
+        for (int g = 0; g < G; ++g)
+            v[g] += __int_as_float(__builtin_amdgcn_ds_bpermute(src, __float_as_int(v[g])));
+    }
+}
+
+// ---- raw buffer access ------------------------------------------------------------------
+//
+// Every global access goes through a buffer resource spanning exactly the bytes the
+// wavefront may touch.  The per-token offset lives in an SGPR (soffset), the per-lane
+// offset in a VGPR, so no 64-bit address arithmetic is repeated per token.  Lanes
+// past the end of d_inner use the lane offset 0x80000000, which the hardware range
+// check turns into a load of zeros / a dropped store.
+
+using rsrc_t = __amdgpu_buffer_rsrc_t;
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+constexpr uint32_t kOffLane = 0x80000000u;
+// Cache policy of every global access: nt (streaming).  Each byte is read or written
+// once per launch, so nothing is worth keeping in L2 or the Infinity Cache.
+constexpr int kNT = 2;
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
+                                             0x00020000);
+}
+
+// NB-byte (8 or 16) global load / store of words d[0 .. NB/4).
+template <int NB>
+__device__ __forceinline__ void gload(rsrc_t r, uint32_t voff, uint32_t soff, uint32_t *d) {
+    if constexpr (NB == 16) {
+        const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, kNT);
+        d[0] = v.x; d[1] = v.y; d[2] = v.z; d[3] = v.w;
+    } else {
+        static_assert(NB == 8, "8- or 16-byte accesses");
+        const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(r, (int)voff, (int)soff, kNT);
+        d[0] = v.x; d[1] = v.y;
+    }
+}
+
+template <int NB>
+__device__ __forceinline__ void gstore(rsrc_t r, uint32_t voff, uint32_t soff, const uint32_t *s) {
+    if constexpr (NB == 16) {
+        const u32x4 v = {s[0], s[1], s[2], s[3]};
+        __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)voff, (int)soff, kNT);
+    } else {
+        static_assert(NB == 8, "8- or 16-byte accesses");
+        const u32x2 v = {s[0], s[1]};
+        __builtin_amdgcn_raw_buffer_store_b64(v, r, (int)voff, (int)soff, kNT);
+    }
+}
+
+// One EB-byte (2 or 4) element store, for the ends of rows that do not fill a chunk.
+template <int EB>
+__device__ __forceinline__ void gstore_elem(rsrc_t r, uint32_t voff, uint32_t bits) {
+    if constexpr (EB == 4) {
+        __builtin_amdgcn_raw_buffer_store_b32(bits, r, (int)voff, 0, kNT);
+    } else {
+        __builtin_amdgcn_raw_buffer_store_b16((unsigned short)bits, r, (int)voff, 0, kNT);
+    }
+}
+
+// A run of NB bytes (a multiple of 8) between registers and LDS, in the widest units
+// that divide it.
+template <int NB>
+__device__ __forceinline__ void lds_write_run(char *p, const uint32_t *s) {
+    static_assert(NB % 8 == 0, "runs are whole 8-byte units");
+    if constexpr (NB % 16 == 0) {
+#pragma unroll
+        for (int q = 0; q < NB / 16; ++q)
+            *(uint4 *)(p + 16 * q) = make_uint4(s[4 * q], s[4 * q + 1], s[4 * q + 2], s[4 * q + 3]);
+    } else {
+#pragma unroll
+        for (int q = 0; q < NB / 8; ++q) *(uint2 *)(p + 8 * q) = make_uint2(s[2 * q], s[2 * q + 1]);
+    }
+}
+
+template <int NB>
+__device__ __forceinline__ void lds_read_run(const char *p, uint32_t *d) {
+    static_assert(NB % 8 == 0, "runs are whole 8-byte units");
+    if constexpr (NB % 16 == 0) {
+#pragma unroll
+        for (int q = 0; q < NB / 16; ++q) {
+            const uint4 v = *(const uint4 *)(p + 16 * q);
+            d[4 * q] = v.x; d[4 * q + 1] = v.y; d[4 * q + 2] = v.z; d[4 * q + 3] = v.w;
+        }
+    } else {
+#pragma unroll
+        for (int q = 0; q < NB / 8; ++q) {
+            const uint2 v = *(const uint2 *)(p + 8 * q);
+            d[2 * q] = v.x; d[2 * q + 1] = v.y;
+        }
+    }
+}
+
+template <int EB>
+__device__ __forceinline__ uint32_t lds_get(const char *p) {
+    if constexpr (EB == 4) return *(const uint32_t *)p;
+    else return *(const uint16_t *)p;
+}
+
+template <int EB>
+__device__ __forceinline__ void lds_put(char *p, uint32_t v) {
+    if constexpr (EB == 4) *(uint32_t *)p = v;
+    else *(uint16_t *)p = (uint16_t)v;
+}
+
+// Streams `chunks` 16-byte chunks from LDS (offset 0) to a buffer, lane-contiguous.
+__device__ __forceinline__ void lds_to_global(const char *lds, int chunks, rsrc_t r, uint32_t soff,
+                                              int lane) {
+    for (int q = lane; q < chunks; q += kWave) {
+        const uint4 v = *(const uint4 *)(lds + q * 16);
+        const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+        gstore<16>(r, (uint32_t)q * 16u, soff, w4);
+    }
+}
+
+// A wavefront-uniform int read through the constant address space, so it is a scalar
+// load: it waits on its own counter, not behind the vector loads already in flight.
+// Only for data no kernel writes while this one runs (slot indices, offsets).
+__device__ __forceinline__ int scalar_read(const int32_t *p, int i) {
+    return *((const __attribute__((address_space(4))) int32_t *)p + i);
+}
+
+// Orders LDS accesses across the workgroup (one wavefront) without waiting for the
+// wavefront's global stores: __syncthreads() is a release fence for all memory, which
+// would make every LDS hand-off wait for the writes issued before it to reach memory.
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+}  // namespace
+}  // namespace cvimpl

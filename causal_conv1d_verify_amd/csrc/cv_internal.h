@@ -11,6 +11,9 @@ constexpr int kChannelsPerLane = 4;   // 256 channels per wavefront
 constexpr int kMaxT = 32;        // largest token bucket compiled
 constexpr int kMaxLds = 65536;   // dynamic LDS a workgroup may request
 
+// Rollback-window layouts.
+enum WinLayout { kDense = 0, kRows = 1, kRowsT = 2 };
+
 // Kernel arguments, by value.  Strides are in elements.
 struct KernelArgs {
     const void *x;
@@ -21,6 +24,8 @@ struct KernelArgs {
     const int32_t *nat;        // nullable (num_accept_tokens)
     void *out;
     void *win;                 // dense snapshots or dedup rows
+    const int32_t *cu;         // nullable: packed rows, [n_seq+1] token offsets
+    const int32_t *parent;     // tree: [n_seq, T] parent positions (-1: the row's start)
     int64_t x_seq, x_tok, out_seq, out_tok, state_slot, win_slot;
     int32_t n_seq, T, d_inner, qk, n_slots, state_len;
     int32_t channel_blocks;    // workgroups per row
@@ -30,7 +35,8 @@ struct KernelArgs {
 
 // What the host decided to launch.
 struct Plan {
-    int dedup;                 // 0 dense, 1 dedup
+    int layout;                // WinLayout
+    int tree;                  // per-token parents (dense windows)
     int x_bytes, state_bytes;  // element sizes: (4,4), (2,2) or (2,4)
     int d_conv;                // 2..4
     int token_bucket;          // 1,2,4,8,16,24,32 >= T
@@ -41,19 +47,63 @@ struct Plan {
     int head_lanes;
 };
 
+// Accepted-prefix restore: window widx[i] of row i's slot -> conv_state columns 0..D-2.
+struct RestoreArgs {
+    void *state;
+    const void *win;
+    const int32_t *slot_idx;   // nullable
+    const int32_t *widx;       // [n_seq] window index per row (-1: nothing)
+    int64_t state_slot, win_slot;
+    int32_t n_seq, T, d_inner, n_slots, state_len;
+    int32_t channel_blocks;
+};
+
+// Prefill conv over packed prompts (conv + SiLU, no L2, no windows).
+constexpr int kPrefillChunk = 16;   // tokens per wavefront
+struct PrefillArgs {
+    const void *x;
+    const void *weight;
+    const void *bias;          // nullable
+    void *state;
+    const int32_t *slot_idx;   // nullable
+    const int32_t *cu;         // [n_seq+1]
+    const int32_t *has_init;   // nullable
+    void *out;
+    int64_t x_tok, out_tok, state_slot;
+    int32_t n_seq, T, d_inner, n_slots, state_len;
+    int32_t channel_blocks;
+    int32_t chunks;            // token chunks per row: ceil(T / kPrefillChunk)
+};
+
+// Separate per-head L2 over the q|k channels of token rows, in place.
+struct L2Args {
+    void *x;
+    int64_t row_stride;
+    int32_t qk, qk_blocks, head_lanes_log2;
+    float eps;
+};
+
 // Bytes between consecutive rows of the dedup LDS tile: one wavefront's channels of
 // one sequence position, plus 16 bytes so successive rows start on different banks.
 constexpr int tile_pitch(int state_bytes) {
     return kWave * kChannelsPerLane * state_bytes + 16;
 }
 
-// Kernel pickers, one per compiled (x bytes, state bytes, dedup) object: the kernel
-// for (d_conv, token bucket), or nullptr.
-const void *pick_kernel_4_4_0(int d_conv, int token_bucket);
-const void *pick_kernel_4_4_1(int d_conv, int token_bucket);
-const void *pick_kernel_2_2_0(int d_conv, int token_bucket);
-const void *pick_kernel_2_2_1(int d_conv, int token_bucket);
-const void *pick_kernel_2_4_0(int d_conv, int token_bucket);
-const void *pick_kernel_2_4_1(int d_conv, int token_bucket);
+// Kernel pickers, one per compiled (x bytes, state bytes, variant) object - variant 0
+// dense, 1 rows, 2 time-major rows, 3 tree: the kernel for (d_conv, token bucket), or
+// nullptr.
+#define CV_DECLARE_PICKERS(xb, sb)                                   \
+    const void *pick_kernel_##xb##_##sb##_0(int d_conv, int token_bucket); \
+    const void *pick_kernel_##xb##_##sb##_1(int d_conv, int token_bucket); \
+    const void *pick_kernel_##xb##_##sb##_2(int d_conv, int token_bucket); \
+    const void *pick_kernel_##xb##_##sb##_3(int d_conv, int token_bucket);
+CV_DECLARE_PICKERS(4, 4)
+CV_DECLARE_PICKERS(2, 2)
+CV_DECLARE_PICKERS(2, 4)
+#undef CV_DECLARE_PICKERS
+
+const void *pick_restore(int state_bytes, int d_conv, int layout);
+const void *pick_prefill(int x_bytes, int state_bytes, int d_conv);
+const void *pick_l2(int x_bytes);
 
 }  // namespace cvimpl

@@ -18,11 +18,11 @@
 //    dense snapshots and the dedup rows, which are staged through LDS so that they
 //    too leave in lane-contiguous units.  Per-token offsets live in SGPRs.
 //  * All loads (x for every token, conv_state, weights, bias) are issued before the
-//    first barrier; after it the wavefront only stores, so no wait on a load is ever
-//    stuck behind stores (vmcnt counts both).  Later LDS hand-offs use barriers that
-//    order LDS only.
-//  * The rollback windows and the committed state are pure copies of the inputs; they
-//    are written first, and the arithmetic runs while they drain.
+//    first barrier, with raised wave priority; after it the wavefront only stores, so
+//    no wait on a load is ever stuck behind stores (vmcnt counts both).  Later LDS
+//    hand-offs use barriers that order LDS only.
+//  * The arithmetic runs as soon as the inputs are in, in branch-free token chunks;
+//    the rollback windows and the committed state (pure copies of the inputs) follow.
 //  * The conv is one fused multiply-add per tap in tap order (bias first), the same
 //    order as the per-token path it replaces, so the pre-activation is bit-identical
 //    to a correctly rounded fp32 evaluation of that order.
@@ -33,208 +33,19 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "cv_device.h"
 #include "cv_internal.h"
 
 namespace cvimpl {
 namespace {
 
-// ---- bit-pattern helpers (compile-time element indices) -----------------------------
-
-// Element `e` of a packed word array of EB-byte elements, as raw bits.
-template <int EB>
-__device__ __forceinline__ uint32_t elem_bits(const uint32_t *w, int e) {
-    if constexpr (EB == 4) {
-        return w[e];
-    } else {
-        return (e & 1) ? (w[e >> 1] >> 16) : (w[e >> 1] & 0xFFFFu);
-    }
-}
-
-// Element `e` as a float (bf16 widening is exact).
-template <int EB>
-__device__ __forceinline__ float elem_val(const uint32_t *w, int e) {
-    if constexpr (EB == 4) {
-        return __uint_as_float(w[e]);
-    } else {
-        return __uint_as_float((e & 1) ? (w[e >> 1] & 0xFFFF0000u) : (w[e >> 1] << 16));
-    }
-}
-
-// x-element bits re-expressed in the state element type (bf16 -> fp32 is exact).
-template <int XB, int SB>
-__device__ __forceinline__ uint32_t x_to_state_bits(uint32_t xbits) {
-    if constexpr (XB == SB) {
-        return xbits;
-    } else {
-        static_assert(XB == 2 && SB == 4, "only bf16 -> fp32 widening");
-        return xbits << 16;
-    }
-}
-
-__device__ __forceinline__ float silu(float p) {
-    // p * sigmoid(p) with v_exp_f32 and v_rcp_f32.  For p << 0 the exponential
-    // saturates to +inf and the result is -0.
-    return p * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(p * -1.4426950408889634f));
-}
-
-template <int CTRL>
-__device__ __forceinline__ float dpp(float v) {
-    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, true));
-}
-
-// Sums over the 2^hl_log2 lanes of an aligned lane group (all lanes active), for each
-// of G independent values at once: every stage is applied to all G values before the
-// next, so their cross-lane latencies overlap.  Each step adds the two halves of a
-// group symmetrically, so all lanes of a group hold the bit-identical sum.
-template <int G>
-__device__ __forceinline__ void group_sums(float (&v)[G], int hl_log2) {
-    if (hl_log2 >= 1)   // quad_perm [1,0,3,2]: lane ^ 1
-#pragma unroll
-        for (int g = 0; g < G; ++g) v[g] += dpp<0xB1>(v[g]);
-    if (hl_log2 >= 2)   // quad_perm [2,3,0,1]: lane ^ 2
-#pragma unroll
-        for (int g = 0; g < G; ++g) v[g] += dpp<0x4E>(v[g]);
-    if (hl_log2 >= 3)   // row_half_mirror: the other quad of the 8
-#pragma unroll
-        for (int g = 0; g < G; ++g) v[g] += dpp<0x141>(v[g]);
-    if (hl_log2 >= 4)   // row_mirror: the other half of the 16-lane row
-#pragma unroll
-        for (int g = 0; g < G; ++g) v[g] += dpp<0x140>(v[g]);
-    if (hl_log2 >= 5)   // lane ^ 16 inside 32 (ds_swizzle xor mode)
-#pragma unroll
-        for (int g = 0; g < G; ++g)
-            v[g] += __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v[g]), 0x401F));
-    if (hl_log2 >= 6) {  // lane ^ 32
-        const int src = (int)((threadIdx.x ^ 32u) << 2);
-#pragma unroll
-        for (int g = 0; g < G; ++g)
-            v[g] += __int_as_float(__builtin_amdgcn_ds_bpermute(src, __float_as_int(v[g])));
-    }
-}
-
-// ---- raw buffer access ------------------------------------------------------------------
-//
-// Every global access goes through a buffer resource spanning exactly the bytes the
-// wavefront may touch.  The per-token offset lives in an SGPR (soffset), the per-lane
-// offset in a VGPR, so no 64-bit address arithmetic is repeated per token.  Lanes
-// past the end of d_inner use the lane offset 0x80000000, which the hardware range
-// check turns into a load of zeros / a dropped store.
-
-using rsrc_t = __amdgpu_buffer_rsrc_t;
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
-typedef __attribute__((address_space(3))) void lds_void_t;
-
-constexpr uint32_t kOffLane = 0x80000000u;
-// Cache policy of every global access: nt (streaming).  Each byte is read or written
-// once per launch, so nothing is worth keeping in L2 or the Infinity Cache.
-constexpr int kNT = 2;
-
-__device__ __forceinline__ rsrc_t make_rsrc(const void *base, uint32_t bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
-                                             0x00020000);
-}
-
-// NB-byte (8 or 16) global load / store of words d[0 .. NB/4).
-template <int NB>
-__device__ __forceinline__ void gload(rsrc_t r, uint32_t voff, uint32_t soff, uint32_t *d) {
-    if constexpr (NB == 16) {
-        const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, kNT);
-        d[0] = v.x; d[1] = v.y; d[2] = v.z; d[3] = v.w;
-    } else {
-        static_assert(NB == 8, "8- or 16-byte accesses");
-        const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(r, (int)voff, (int)soff, kNT);
-        d[0] = v.x; d[1] = v.y;
-    }
-}
-
-template <int NB>
-__device__ __forceinline__ void gstore(rsrc_t r, uint32_t voff, uint32_t soff, const uint32_t *s) {
-    if constexpr (NB == 16) {
-        const u32x4 v = {s[0], s[1], s[2], s[3]};
-        __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)voff, (int)soff, kNT);
-    } else {
-        static_assert(NB == 8, "8- or 16-byte accesses");
-        const u32x2 v = {s[0], s[1]};
-        __builtin_amdgcn_raw_buffer_store_b64(v, r, (int)voff, (int)soff, kNT);
-    }
-}
-
-// A run of NB bytes (a multiple of 8) between registers and LDS, in the widest units
-// that divide it.
-template <int NB>
-__device__ __forceinline__ void lds_write_run(char *p, const uint32_t *s) {
-    static_assert(NB % 8 == 0, "runs are whole 8-byte units");
-    if constexpr (NB % 16 == 0) {
-#pragma unroll
-        for (int q = 0; q < NB / 16; ++q)
-            *(uint4 *)(p + 16 * q) = make_uint4(s[4 * q], s[4 * q + 1], s[4 * q + 2], s[4 * q + 3]);
-    } else {
-#pragma unroll
-        for (int q = 0; q < NB / 8; ++q) *(uint2 *)(p + 8 * q) = make_uint2(s[2 * q], s[2 * q + 1]);
-    }
-}
-
-template <int NB>
-__device__ __forceinline__ void lds_read_run(const char *p, uint32_t *d) {
-    static_assert(NB % 8 == 0, "runs are whole 8-byte units");
-    if constexpr (NB % 16 == 0) {
-#pragma unroll
-        for (int q = 0; q < NB / 16; ++q) {
-            const uint4 v = *(const uint4 *)(p + 16 * q);
-            d[4 * q] = v.x; d[4 * q + 1] = v.y; d[4 * q + 2] = v.z; d[4 * q + 3] = v.w;
-        }
-    } else {
-#pragma unroll
-        for (int q = 0; q < NB / 8; ++q) {
-            const uint2 v = *(const uint2 *)(p + 8 * q);
-            d[2 * q] = v.x; d[2 * q + 1] = v.y;
-        }
-    }
-}
-
-template <int EB>
-__device__ __forceinline__ uint32_t lds_get(const char *p) {
-    if constexpr (EB == 4) return *(const uint32_t *)p;
-    else return *(const uint16_t *)p;
-}
-
-template <int EB>
-__device__ __forceinline__ void lds_put(char *p, uint32_t v) {
-    if constexpr (EB == 4) *(uint32_t *)p = v;
-    else *(uint16_t *)p = (uint16_t)v;
-}
-
-// Streams `chunks` 16-byte chunks from LDS (offset 0) to a buffer, lane-contiguous.
-__device__ __forceinline__ void lds_to_global(const char *lds, int chunks, rsrc_t r, uint32_t soff,
-                                              int lane) {
-    for (int q = lane; q < chunks; q += kWave) {
-        const uint4 v = *(const uint4 *)(lds + q * 16);
-        const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
-        gstore<16>(r, (uint32_t)q * 16u, soff, w4);
-    }
-}
-
-// A wavefront-uniform int read through the constant address space, so it is a scalar
-// load: it waits on its own counter, not behind the vector loads already in flight.
-// Only for data no kernel writes while this one runs (slot indices, offsets).
-__device__ __forceinline__ int scalar_read(const int32_t *p, int i) {
-    return *((const __attribute__((address_space(4))) int32_t *)p + i);
-}
-
-// Orders LDS accesses across the workgroup (one wavefront) without waiting for the
-// wavefront's global stores: __syncthreads() is a release fence for all memory, which
-// would make every LDS hand-off wait for the writes issued before it to reach memory.
-__device__ __forceinline__ void lds_barrier() {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-    __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-}
-
 // ---- the kernel -------------------------------------------------------------------------
 
-template <int XB, int SB, int D, int TB, bool DEDUP>
+// LAYOUT: kDense, kRows or kRowsT (rollback windows); TREE: per-token parents (dense
+// windows, nothing committed).  Packed rows (p.cu) are a runtime option of every variant.
+template <int XB, int SB, int D, int TB, int LAYOUT, bool TREE>
 __global__ __launch_bounds__(kWave) void cv_verify_kernel(KernelArgs p) {
+    static_assert(!TREE || LAYOUT == kDense, "tree windows are dense");
     constexpr int CPL = kChannelsPerLane;     // channels per lane
     constexpr int CHW = kWave * CPL;          // channels per wavefront
     constexpr int W1 = D - 1;                 // window columns
@@ -258,7 +69,17 @@ __global__ __launch_bounds__(kWave) void cv_verify_kernel(KernelArgs p) {
     const int slot = p.slot_idx ? scalar_read(p.slot_idx, row) : row;
     const int a = p.nat ? scalar_read(p.nat, row) : 0;
 
-    const int T = p.T;
+    // Tokens of this row and where they start.  Packed rows take both from cu_seqlens;
+    // an empty row (or one outside 1..T) has nothing to compute and writes nothing.
+    int T = p.T;
+    int64_t xrow = (int64_t)row * p.x_seq, orow = (int64_t)row * p.out_seq;
+    if (p.cu) {
+        const int c0 = scalar_read(p.cu, row);
+        T = scalar_read(p.cu, row + 1) - c0;
+        xrow = (int64_t)c0 * p.x_tok;
+        orow = (int64_t)c0 * p.out_tok;
+        if (T < 1 || T > p.T) return;
+    }
     const int SL = p.state_len;
     const int nch = min(CHW, p.d_inner - cb);   // channels of this wavefront
     const bool on = lane * CPL < nch;
@@ -270,7 +91,7 @@ __global__ __launch_bounds__(kWave) void cv_verify_kernel(KernelArgs p) {
     // wavefronts of a SIMD are ready, the ones still issuing loads go first, so reads
     // enter the memory pipeline ahead of other wavefronts' stores.
     __builtin_amdgcn_s_setprio(3);
-    const rsrc_t x_r = make_rsrc((const char *)p.x + ((int64_t)row * p.x_seq + cb) * XB,
+    const rsrc_t x_r = make_rsrc((const char *)p.x + (xrow + cb) * XB,
                                  (uint32_t)(((int64_t)(T - 1) * p.x_tok + nch) * XB));
     uint32_t X[TB][XW];   // x_t for the lane's channels
 #pragma unroll
@@ -344,6 +165,10 @@ __global__ __launch_bounds__(kWave) void cv_verify_kernel(KernelArgs p) {
             if ((j0 + j) * kWave < rchunks && q < rchunks)
                 *(uint4 *)(lds + q * 16) = make_uint4(sreg[j][0], sreg[j][1], sreg[j][2], sreg[j][3]);
         }
+    }
+    int par = -1;   // tree: lane t < T holds parent[row, t]
+    if constexpr (TREE) {
+        if (lane < T) par = p.parent[(int64_t)row * p.T + lane];
     }
     __builtin_amdgcn_s_setprio(0);
     lds_barrier();
@@ -423,13 +248,48 @@ __global__ __launch_bounds__(kWave) void cv_verify_kernel(KernelArgs p) {
         }
     };
 
+    // ---- tree: the v tile and each token's ancestor columns ---------------------------------
+    // Tile row k of LDS holds v[k] (k < W1: the starting window, else x_{k-W1}) for the
+    // wavefront's channels, in the state type.  vidx[m] of lane t is the v index of
+    // the value m steps back along token t's path: m = 0 is x_t itself; a step past the
+    // root lands in the starting window.  Token t's taps are then v[vidx[W1]], ...,
+    // v[vidx[1]], x_t and its window is v[vidx[W1-1]], ..., v[vidx[0]].
+    constexpr int TILE = TREE ? (W1 + TB) * P : 0;   // LDS bytes of the tile
+    int vidx[D];
+    if constexpr (TREE) {
+        if (__builtin_amdgcn_ballot_w64(lane < T && (par < -1 || par >= lane)))
+            return;   // a malformed tree: nothing written for this row
+        lds_barrier();   // every lane has read its window out of the state region
+#pragma unroll
+        for (int k = 0; k < W1 + TB; ++k) {
+            if (k < W1 + T) {
+                uint32_t col[SW];
+                column(k, col);
+                lds_write_run<SCB>(lds + k * P + lane * SCB, col);
+            }
+        }
+        vidx[0] = W1 + lane;
+#pragma unroll
+        for (int m = 1; m <= W1; ++m) {
+            const int up = __builtin_amdgcn_ds_bpermute((par < 0 ? lane : par) << 2, vidx[m - 1]);
+            vidx[m] = par < 0 ? W1 - m : up;
+        }
+        lds_barrier();
+    }
+    // Token t's v index m steps back, uniform across the wavefront (t compile-time).
+    auto tree_idx = [&](int t, int m) -> int {
+        return __builtin_amdgcn_readfirstlane(__builtin_amdgcn_readlane(vidx[m], t));
+    };
+    // The lane's CPL channels of tile row k, in the state type.
+    auto tile_col = [&](int k, uint32_t *col) { lds_read_run<SCB>(lds + k * P + lane * SCB, col); };
+
     // ---- conv + SiLU + per-head L2 -> out --------------------------------------------------
     // The arithmetic runs as soon as the inputs are in, before the copies below: while
     // the memory pipeline is still full of other wavefronts' traffic, a wavefront that
     // stores first would stall at its stores with its arithmetic still ahead of it.
     const bool wave_l2 = cb < p.qk;    // uniform: this wavefront holds q|k channels
     const bool lane_l2 = lane * CPL + cb < p.qk;
-    const rsrc_t o_r = make_rsrc((char *)p.out + ((int64_t)row * p.out_seq + cb) * XB,
+    const rsrc_t o_r = make_rsrc((char *)p.out + (orow + cb) * XB,
                                  (uint32_t)(((int64_t)(T - 1) * p.out_tok + nch) * XB));
     // Tokens go in chunks with no branch inside a chunk: x past T reads as zeros and
     // those tokens are computed but never stored.  The chunk's exponentials,
@@ -441,14 +301,28 @@ __global__ __launch_bounds__(kWave) void cv_verify_kernel(KernelArgs p) {
     for (int t0 = 0; t0 < TB; t0 += G) {
         if (t0 < T) {   // uniform guard; the loops are fully unrolled
             float y[G][CPL];
+            uint32_t tv[TREE ? G : 1][W1][SW];   // tree: the taps before x_t, from the tile
+            if constexpr (TREE) {
+#pragma unroll
+                for (int g = 0; g < G; ++g)
+#pragma unroll
+                    for (int w = 0; w < W1; ++w)
+                        if (t0 + g < T) tile_col(tree_idx(t0 + g, W1 - w), tv[g][w]);
+            }
 #pragma unroll
             for (int g = 0; g < G; ++g)
 #pragma unroll
                 for (int ch = 0; ch < CPL; ++ch) {
                     float acc = bv[ch];
 #pragma unroll
-                    for (int w = 0; w < D; ++w)
-                        acc = __builtin_fmaf(wv[ch][w], val(t0 + g + w, ch), acc);
+                    for (int w = 0; w < D; ++w) {
+                        float v;
+                        if constexpr (TREE)
+                            v = w < W1 ? elem_val<SB>(tv[g][w < W1 ? w : 0], ch) : val(t0 + g + W1, ch);
+                        else
+                            v = val(t0 + g + w, ch);
+                        acc = __builtin_fmaf(wv[ch][w], v, acc);
+                    }
                     y[g][ch] = silu(acc);
                 }
             if (wave_l2) {
@@ -489,37 +363,40 @@ __global__ __launch_bounds__(kWave) void cv_verify_kernel(KernelArgs p) {
             }
         }
     }
-    // ---- committed window -> conv_state -----------------------------------------------------
-    // v[T .. T+W1-1] into columns 0..W1-1 of the staged rows (each lane rewrites only
-    // its own channels' records, after having read them above), then the region leaves.
-#pragma unroll
-    for (int t = 0; t < TB; ++t) {
-        if (t == T - 1) {
-            if (contiguous_state) {
-                uint32_t run[RUNW];
-                window_run(t + 1, run);
-                lds_write_run<RUNB>(lds + lane * RUNB, run);
-            } else {
-                char *rec = lds + lane * CPL * SL * SB;
-#pragma unroll
-                for (int ch = 0; ch < CPL; ++ch)
-#pragma unroll
-                    for (int j = 0; j < W1; ++j)
-                        lds_put<SB>(rec + (ch * SL + j) * SB, sbits(t + 1 + j, ch));
+    if constexpr (!TREE) {
+        // ---- committed window -> conv_state -----------------------------------------------------
+        // v[T .. T+W1-1] into columns 0..W1-1 of the staged rows (each lane rewrites only
+        // its own channels' records, after having read them above), then the region leaves.
+    #pragma unroll
+        for (int t = 0; t < TB; ++t) {
+            if (t == T - 1) {
+                if (contiguous_state) {
+                    uint32_t run[RUNW];
+                    window_run(t + 1, run);
+                    lds_write_run<RUNB>(lds + lane * RUNB, run);
+                } else {
+                    char *rec = lds + lane * CPL * SL * SB;
+    #pragma unroll
+                    for (int ch = 0; ch < CPL; ++ch)
+    #pragma unroll
+                        for (int j = 0; j < W1; ++j)
+                            lds_put<SB>(rec + (ch * SL + j) * SB, sbits(t + 1 + j, ch));
+                }
             }
         }
+        lds_barrier();
+        lds_to_global(lds, rchunks, st_r, 0, lane);
+        lds_barrier();   // the region's LDS is reused below
     }
-    lds_barrier();
-    lds_to_global(lds, rchunks, st_r, 0, lane);
-    lds_barrier();   // the region's LDS is reused below
 
     // ---- rollback windows: pure copies of the inputs ---------------------------------------
-    if constexpr (DEDUP) {
-        const int L = T + W1 - 1;             // row length: v[1 .. T+W1-1]
+    if constexpr (LAYOUT == kRows) {
+        const int L = T + W1 - 1;             // columns this row writes: v[1 .. T+W1-1]
+        const int LS = p.T + W1 - 1;          // columns per channel in the buffer
         const rsrc_t row_r = make_rsrc(
-            (char *)p.win + ((int64_t)slot * p.win_slot + (int64_t)cb * L) * SB,
-            (uint32_t)(nch * L * SB));
-        if (T == TB) {
+            (char *)p.win + ((int64_t)slot * p.win_slot + (int64_t)cb * LS) * SB,
+            (uint32_t)(nch * LS * SB));
+        if (T == TB && L == LS) {
             // Row length known at compile time: each lane assembles its channels' rows
             // ([CPL][LC], contiguous in the row layout) in registers into LDS at the
             // same offsets, and the wavefront streams the block out lane-contiguously.
@@ -557,17 +434,17 @@ __global__ __launch_bounds__(kWave) void cv_verify_kernel(KernelArgs p) {
                 }
             }
             lds_barrier();
-            // Stream the tile out in the row layout [c][k], k < L: chunk q of the
+            // Stream the tile out in the row layout [c][k], k < LS: chunk q of the
             // wavefront's contiguous row block holds elements e = q*EPC .. q*EPC+EPC-1,
-            // element e = (channel e / L, column e % L) = tile row e % L, channel e / L.
+            // element e = (channel e / LS, column e % LS) = tile row e % LS, channel e / LS.
             constexpr int EPC = 16 / SB;   // elements per 16-byte chunk
-            const int nchunks = nch * L / EPC;   // exact: nch * SB is a multiple of 16
+            const int nchunks = nch * LS / EPC;   // exact: nch * SB is a multiple of 16
             const int e0 = lane * EPC;
-            int cc = e0 / L;
-            int kk = e0 - cc * L;
-            const int dq = (kWave * EPC) / L;
-            const int dr = kWave * EPC - dq * L;
-            if (L >= EPC) {
+            int cc = e0 / LS;
+            int kk = e0 - cc * LS;
+            const int dq = (kWave * EPC) / LS;
+            const int dr = kWave * EPC - dq * LS;
+            if (L == LS && L >= EPC) {
                 // a chunk spans at most two channels: columns kk.. of channel cc, then
                 // columns 0.. of channel cc+1; each element is one LDS read at a fixed
                 // row step from one of two bases
@@ -591,24 +468,57 @@ __global__ __launch_bounds__(kWave) void cv_verify_kernel(KernelArgs p) {
                     if (kk >= L) { kk -= L; ++cc; }
                 }
             } else {
+                // Short rows (L < EPC), or a packed row shorter than the buffer's rows:
+                // columns >= L are not this call's to write, so chunks that reach
+                // past L store only their columns below it.
                 for (int q = lane; q < nchunks; q += kWave) {
-                    uint32_t w[4];
+                    uint32_t w[4] = {0u, 0u, 0u, 0u};
+                    uint32_t valid = 0;
                     int c2 = cc, k2 = kk;
 #pragma unroll
                     for (int m = 0; m < EPC; ++m) {
-                        const uint32_t b = lds_get<SB>(lds + k2 * P + c2 * SB);
+                        const bool ok = k2 < L;
+                        const uint32_t b = ok ? lds_get<SB>(lds + k2 * P + c2 * SB) : 0u;
+                        valid |= (ok ? 1u : 0u) << m;
                         if constexpr (SB == 4) {
                             w[m] = b;
                         } else {
                             if (m & 1) w[m >> 1] |= b << 16; else w[m >> 1] = b;
                         }
-                        if (++k2 == L) { k2 = 0; ++c2; }
+                        if (++k2 == LS) { k2 = 0; ++c2; }
                     }
-                    gstore<16>(row_r, (uint32_t)q * 16u, 0, w);
+                    if (valid == (1u << EPC) - 1u) {
+                        gstore<16>(row_r, (uint32_t)q * 16u, 0, w);
+                    } else if (valid) {
+#pragma unroll
+                        for (int m = 0; m < EPC; ++m) {
+                            if ((valid >> m) & 1u) {
+                                const uint32_t bits = SB == 4 ? w[m] : (w[m >> 1] >> ((m & 1) * 16)) & 0xFFFFu;
+                                gstore_elem<SB>(row_r, (uint32_t)(q * 16 + m * SB), bits);
+                            }
+                        }
+                    }
                     cc += dq;
                     kk += dr;
-                    while (kk >= L) { kk -= L; ++cc; }
+                    while (kk >= LS) { kk -= LS; ++cc; }
                 }
+            }
+        }
+    } else if constexpr (LAYOUT == kRowsT) {
+        // Time-major rows: buffer column k (= v[k+1]) holds the d channels contiguously,
+        // so each lane stores its CPL channels of every column straight from registers.
+        const int L = T + W1 - 1;
+        const int LS = p.T + W1 - 1;
+        const uint32_t laneS = on ? (uint32_t)(lane * SCB) : kOffLane;
+        const rsrc_t rt_r = make_rsrc(
+            (char *)p.win + ((int64_t)slot * p.win_slot + cb) * SB,
+            (uint32_t)(((int64_t)(LS - 1) * p.d_inner + nch) * SB));
+#pragma unroll
+        for (int k = 1; k < W1 + TB; ++k) {
+            if (k - 1 < L) {
+                uint32_t col[SW];
+                column(k, col);
+                gstore<SCB>(rt_r, laneS, (uint32_t)((k - 1) * p.d_inner * SB), col);
             }
         }
     } else {
@@ -624,9 +534,26 @@ __global__ __launch_bounds__(kWave) void cv_verify_kernel(KernelArgs p) {
 #pragma unroll
         for (int t = 0; t < TB; ++t) {
             if (t < T) {
-                char *slab = lds + (t & 1) * SLAB;
+                char *slab = lds + TILE + (t & 1) * SLAB;
                 uint32_t run[RUNW];
-                window_run(t + 1, run);
+                if constexpr (TREE) {
+                    uint32_t cols[W1][SW];   // the window's columns, oldest first
+#pragma unroll
+                    for (int j = 0; j < W1; ++j) tile_col(tree_idx(t, W1 - 1 - j), cols[j]);
+#pragma unroll
+                    for (int w = 0; w < RUNW; ++w) {   // [CPL][W1] run, channel-major
+                        if constexpr (SB == 4) {
+                            run[w] = cols[w % W1][w / W1];
+                        } else {
+                            const int e0 = 2 * w, e1 = 2 * w + 1;
+                            const uint32_t lo = (cols[e0 % W1][(e0 / W1) >> 1] >> (((e0 / W1) & 1) * 16)) & 0xFFFFu;
+                            const uint32_t hi = (cols[e1 % W1][(e1 / W1) >> 1] >> (((e1 / W1) & 1) * 16)) & 0xFFFFu;
+                            run[w] = lo | (hi << 16);
+                        }
+                    }
+                } else {
+                    window_run(t + 1, run);
+                }
                 lds_write_run<RUNB>(slab + lane * RUNB, run);
                 lds_barrier();
                 lds_to_global(slab, slab_chunks, snap_r, (uint32_t)(t * p.d_inner * W1 * SB), lane);
@@ -638,38 +565,40 @@ __global__ __launch_bounds__(kWave) void cv_verify_kernel(KernelArgs p) {
 
 // ---- instantiation ----------------------------------------------------------------------
 //
-// This file is compiled once per (x dtype, state dtype, layout) with CV_XB, CV_SB and
-// CV_DEDUP defined, so the instantiations build in parallel; each object exports one
-// picker over (d_conv, token bucket).
-
-template <int XB, int SB, int D, bool DEDUP>
+// This file is compiled once per (x bytes, state bytes, variant) with CV_XB, CV_SB and
+// CV_VARIANT defined (0 dense, 1 rows, 2 time-major rows, 3 tree with dense windows),
+// so the instantiations build in parallel; each object exports one picker over
+// (d_conv, token bucket).
+template <int XB, int SB, int D, int LAYOUT, bool TREE>
 const void *pick_bucket(int tb) {
     switch (tb) {
-        case 1: return (const void *)cv_verify_kernel<XB, SB, D, 1, DEDUP>;
-        case 2: return (const void *)cv_verify_kernel<XB, SB, D, 2, DEDUP>;
-        case 4: return (const void *)cv_verify_kernel<XB, SB, D, 4, DEDUP>;
-        case 8: return (const void *)cv_verify_kernel<XB, SB, D, 8, DEDUP>;
-        case 16: return (const void *)cv_verify_kernel<XB, SB, D, 16, DEDUP>;
-        case 24: return (const void *)cv_verify_kernel<XB, SB, D, 24, DEDUP>;
-        case 32: return (const void *)cv_verify_kernel<XB, SB, D, 32, DEDUP>;
+        case 1: return (const void *)cv_verify_kernel<XB, SB, D, 1, LAYOUT, TREE>;
+        case 2: return (const void *)cv_verify_kernel<XB, SB, D, 2, LAYOUT, TREE>;
+        case 4: return (const void *)cv_verify_kernel<XB, SB, D, 4, LAYOUT, TREE>;
+        case 8: return (const void *)cv_verify_kernel<XB, SB, D, 8, LAYOUT, TREE>;
+        case 16: return (const void *)cv_verify_kernel<XB, SB, D, 16, LAYOUT, TREE>;
+        case 24: return (const void *)cv_verify_kernel<XB, SB, D, 24, LAYOUT, TREE>;
+        case 32: return (const void *)cv_verify_kernel<XB, SB, D, 32, LAYOUT, TREE>;
         default: return nullptr;
     }
 }
 
 }  // namespace
 
-#if !defined(CV_XB) || !defined(CV_SB) || !defined(CV_DEDUP)
-#error "compile with -DCV_XB=<2|4> -DCV_SB=<2|4> -DCV_DEDUP=<0|1>"
+#if !defined(CV_XB) || !defined(CV_SB) || !defined(CV_VARIANT)
+#error "compile with -DCV_XB=<2|4> -DCV_SB=<2|4> -DCV_VARIANT=<0..3>"
 #endif
 
-#define CV_PICK_NAME(xb, sb, dd) pick_kernel_##xb##_##sb##_##dd
-#define CV_PICK(xb, sb, dd) CV_PICK_NAME(xb, sb, dd)
+#define CV_PICK_NAME(xb, sb, v) pick_kernel_##xb##_##sb##_##v
+#define CV_PICK(xb, sb, v) CV_PICK_NAME(xb, sb, v)
 
-const void *CV_PICK(CV_XB, CV_SB, CV_DEDUP)(int d_conv, int token_bucket) {
+const void *CV_PICK(CV_XB, CV_SB, CV_VARIANT)(int d_conv, int token_bucket) {
+    constexpr int layout = CV_VARIANT == 3 ? kDense : CV_VARIANT;
+    constexpr bool tree = CV_VARIANT == 3;
     switch (d_conv) {
-        case 2: return pick_bucket<CV_XB, CV_SB, 2, CV_DEDUP != 0>(token_bucket);
-        case 3: return pick_bucket<CV_XB, CV_SB, 3, CV_DEDUP != 0>(token_bucket);
-        case 4: return pick_bucket<CV_XB, CV_SB, 4, CV_DEDUP != 0>(token_bucket);
+        case 2: return pick_bucket<CV_XB, CV_SB, 2, layout, tree>(token_bucket);
+        case 3: return pick_bucket<CV_XB, CV_SB, 3, layout, tree>(token_bucket);
+        case 4: return pick_bucket<CV_XB, CV_SB, 4, layout, tree>(token_bucket);
         default: return nullptr;
     }
 }

@@ -29,7 +29,20 @@
  *  - Atlas glm5next_kda/mod.rs, Glm5NextKdaConfig: conv -> SiLU -> L2 on q|k only,
  *    FLA convention 1/sqrt(sum + eps), V never normalised, qk_channels = 2*heads*hd.
  *
- * Conventions shared by both entry points
+ * Beyond that chain verify the library covers, with the same kernels family:
+ *  - packed variable-length rows (cu_seqlens), sglang PR 46184, "Related upstream
+ *    work" (packed ragged tokens in the verify kernel, so the tile store covers them);
+ *  - the time-major row layout (MambaPool's axis-0 window layout seen transposed),
+ *    sglang PR 46184, "Modifications" (test coverage);
+ *  - tree verify (per-token parents, dense windows), sglang PR 46184, "Scope";
+ *  - the accepted-prefix restore (window k -> conv_state), sglang PR 46184,
+ *    "Motivation"; Atlas glm5next_kda/mod.rs, decode_k (snapshots a partial accept
+ *    rewinds to);
+ *  - the prefill conv (conv + SiLU, no L2, no windows) and the separate q|k L2 pass,
+ *    Atlas glm5next_kda/mod.rs, module doc and the prefill body ("Prefill conv is
+ *    conv + SiLU ONLY - L2 is a separate launch over q|k").
+ *
+ * Conventions shared by every entry point
  * ---------------------------------------
  *  - Every data pointer is a DEVICE pointer (HBM of the GPU current on the calling
  *    thread); only `shape` is a host pointer.  The caller owns every buffer.  The
@@ -76,7 +89,10 @@
 extern "C" {
 #endif
 
-#define CONV_VERIFY_ABI_VERSION 1
+#define CONV_VERIFY_ABI_VERSION 2
+
+/* Only the entry points below are exported from the shared library. */
+#define CV_API __attribute__((visibility("default")))
 
 /* Element types. */
 typedef enum cv_dtype { CV_F32 = 0, CV_BF16 = 1 } cv_dtype_t;
@@ -87,10 +103,22 @@ typedef enum cv_dtype { CV_F32 = 0, CV_BF16 = 1 } cv_dtype_t;
 #define CV_ENOTSUP (-95)     /* well-formed but outside what the kernels implement */
 #define CV_EHIP_BASE (-1000) /* launch failure: returns CV_EHIP_BASE - (int)hipError_t */
 
+/* Rollback-window layouts (T = shape->T, W1 = d_conv - 1, L = T + W1 - 1):
+ *   CV_WIN_DENSE  [n_slots, T, d_inner, W1]  win[s,t,c,j] = base + s*ws + (t*d_inner + c)*W1 + j
+ *                                             = the window after consuming x_t
+ *   CV_WIN_ROWS   [n_slots, d_inner, L]      row[s,c,k]   = base + s*ws + c*L + k = v[k+1]
+ *   CV_WIN_ROWS_T [n_slots, L, d_inner]      row[s,k,c]   = base + s*ws + k*d_inner + c = v[k+1]
+ * In both row layouts the window after consuming x_t is columns t .. t+W1-1: the view
+ * [T, d_inner, W1] has step stride == window stride (sglang PR 46184, "Modifications").
+ * ws = shape->win_slot_stride. */
+typedef enum cv_layout { CV_WIN_DENSE = 0, CV_WIN_ROWS = 1, CV_WIN_ROWS_T = 2 } cv_layout_t;
+
 /* Problem description (host memory, read during the call only). */
 typedef struct cv_shape {
     int32_t n_seq;        /* rows in the batch, >= 0 (0: nothing to do, returns CV_OK)      */
-    int32_t T;            /* draft positions per row, 1..32                                 */
+    int32_t T;            /* draft positions per row, 1..32 (packed rows: the most a row
+                             may hold, and the T of the window buffer's geometry);
+                             conv_prefill: the longest prompt, >= 1                         */
     int32_t d_inner;      /* channels, >= 0 (0: nothing to do)                              */
     int32_t d_conv;       /* conv width D, 2..4                                             */
     int32_t qk_channels;  /* leading channels normalised per head, 0..d_inner; 0 = no L2    */
@@ -121,7 +149,7 @@ typedef struct cv_shape {
  *
  * Returns CV_OK after enqueueing the launch, or an error code (nothing launched).
  */
-int conv_verify_update_dense(const cv_shape_t *shape, const void *x, const void *weight,
+CV_API int conv_verify_update_dense(const cv_shape_t *shape, const void *x, const void *weight,
                              const void *bias, void *conv_state, const int32_t *slot_idx,
                              const int32_t *num_accept_tokens, void *out, void *snapshots,
                              void *hip_stream);
@@ -137,10 +165,88 @@ int conv_verify_update_dense(const cv_shape_t *shape, const void *x, const void 
  *
  * Returns CV_OK after enqueueing the launch, or an error code (nothing launched).
  */
-int conv_verify_update_dedup(const cv_shape_t *shape, const void *x, const void *weight,
+CV_API int conv_verify_update_dedup(const cv_shape_t *shape, const void *x, const void *weight,
                              const void *bias, void *conv_state, const int32_t *slot_idx,
                              const int32_t *num_accept_tokens, void *out, void *window_rows,
                              void *hip_stream);
+
+/*
+ * The general verify: any window layout, and optionally packed rows.
+ *
+ *   layout      cv_layout_t of `windows`.
+ *   cu_seqlens  NULL, or [n_seq+1] int32 (device): packed rows.  Row i holds
+ *               T_i = cu[i+1] - cu[i] tokens, token t at x[(cu[i]+t)*x_tok_stride + c]
+ *               and out[(cu[i]+t)*out_tok_stride + c]; the seq strides are unused.  A
+ *               row with T_i = 0 writes nothing (its state keeps its starting window
+ *               where it was).  Its windows are those of t < T_i; in the row layouts
+ *               it writes columns 0 .. T_i+W1-2 and leaves the rest of its row alone.
+ *               Device-side precondition: non-decreasing offsets inside x and out; a
+ *               row with T_i outside 0..T is skipped like a padded row.
+ *
+ * Without cu_seqlens, CV_WIN_DENSE is conv_verify_update_dense and CV_WIN_ROWS is
+ * conv_verify_update_dedup.  Returns CV_OK after enqueueing the launch, or an error.
+ */
+CV_API int conv_verify_update(const cv_shape_t *shape, int32_t layout, const void *x,
+                       const void *weight, const void *bias, void *conv_state,
+                       const int32_t *slot_idx, const int32_t *num_accept_tokens,
+                       const int32_t *cu_seqlens, void *out, void *windows, void *hip_stream);
+
+/*
+ * Tree verify (sglang PR 46184, "Scope": tree verify keeps per-token dense windows).
+ *
+ *   parent [n_seq, T] int32 (device), row stride T: parent[i,t] in -1 .. t-1.  Token
+ *          t's conv runs over the window of its parent token (-1: the row's starting
+ *          window, conv_state[s, c, a .. a+D-2]) followed by x_t, and its window is
+ *          that window shifted by x_t; the chain is parent[i,t] = t-1.
+ *   windows: CV_WIN_DENSE layout.  conv_state is only read: the accepted path is
+ *          known after verification, and conv_verify_restore writes its window.
+ *   cu_seqlens as in conv_verify_update (NULL: T tokens per row).  A row with a
+ *          parent outside -1..t-1 is skipped (nothing written).
+ */
+CV_API int conv_verify_update_tree(const cv_shape_t *shape, const void *x, const void *weight,
+                            const void *bias, const void *conv_state,
+                            const int32_t *slot_idx, const int32_t *num_accept_tokens,
+                            const int32_t *cu_seqlens, const int32_t *parent, void *out,
+                            void *windows, void *hip_stream);
+
+/*
+ * Accepted-prefix restore (sglang PR 46184, "Motivation"; Atlas decode_k snapshots):
+ * for each row i with slot s = slot_idx[i] >= 0 and k = window_index[i] >= 0,
+ *   conv_state[s, c, 0 .. d_conv-2] = the window after consuming x_k, read from
+ *   `windows` in `layout` (chain verify: k = accepted tokens - 1; tree verify: the
+ *   position of the last accepted token).  Columns >= d_conv-1 are not written.
+ * Uses shape fields n_seq, T (the window buffer's), d_inner, d_conv, state_dtype,
+ * n_slots, state_len, state_slot_stride, win_slot_stride (x fields are ignored).
+ * window_index [n_seq] int32 (device).  Rows with k >= T or a slot >= n_slots are
+ * skipped.  One launch; returns CV_OK or an error (nothing launched).
+ */
+CV_API int conv_verify_restore(const cv_shape_t *shape, int32_t layout, void *conv_state,
+                        const void *windows, const int32_t *slot_idx,
+                        const int32_t *window_index, void *hip_stream);
+
+/*
+ * Prefill conv over packed prompts (Atlas glm5next_kda/mod.rs, prefill body: conv +
+ * SiLU only; the L2 is a separate pass, conv_qk_l2norm).  Row i's T_i = cu[i+1]-cu[i]
+ * tokens (0 <= T_i <= shape->T) run through the conv starting from its state window
+ * conv_state[s, c, 0 .. D-2] (s = slot_idx[i], or i), or from zeros where
+ * has_initial_state[i] == 0; out gets SiLU(conv + bias) rounded to the x dtype; the
+ * last window is committed to conv_state[s, c, 0 .. D-2].  No rollback windows, no
+ * L2 (qk_channels and head_dim are ignored).  has_initial_state may be NULL (all 1).
+ * shape->T may exceed 32 here.
+ */
+CV_API int conv_prefill(const cv_shape_t *shape, const void *x, const void *weight, const void *bias,
+                 void *conv_state, const int32_t *slot_idx, const int32_t *cu_seqlens,
+                 const int32_t *has_initial_state, void *out, void *hip_stream);
+
+/*
+ * Separate per-head L2 over the q|k channels, in place: for each of n_rows rows of x
+ * (row r at x + r*row_stride, channel stride 1) and each head of head_dim channels in
+ * [0, qk_channels): y <- y / sqrt(sum_head y^2 + l2_eps) in fp32, rounded to the x
+ * dtype.  Channels >= qk_channels are not touched.  Uses shape fields d_inner,
+ * qk_channels, head_dim, l2_eps, x_dtype.
+ */
+CV_API int conv_qk_l2norm(const cv_shape_t *shape, int64_t n_rows, int64_t row_stride, void *x,
+                   void *hip_stream);
 
 /* Launch geometry the library would use for a shape (validation of the shape only;
  * pointers are not examined).  Lets a caller or a test check, on the host, what the
@@ -156,17 +262,19 @@ typedef struct cv_launch_info {
     int32_t head_lanes;        /* lanes per L2 head (0 when qk_channels == 0)              */
 } cv_launch_info_t;
 
-/* dedup: 0 = dense snapshots, 1 = deduplicated rows.  Returns CV_OK or an error code. */
-int conv_verify_describe(int dedup, const cv_shape_t *shape, cv_launch_info_t *info);
+/* variant: a cv_layout_t, or CV_VARIANT_TREE for conv_verify_update_tree.  Returns
+ * CV_OK or an error code. */
+#define CV_VARIANT_TREE 3
+CV_API int conv_verify_describe(int variant, const cv_shape_t *shape, cv_launch_info_t *info);
 
 /* Static description of an error code (never NULL). */
-const char *conv_verify_strerror(int code);
+CV_API const char *conv_verify_strerror(int code);
 
 /* Detail of the last error returned on the calling thread (empty string if none). */
-const char *conv_verify_last_error(void);
+CV_API const char *conv_verify_last_error(void);
 
 /* CONV_VERIFY_ABI_VERSION of the loaded library. */
-int conv_verify_abi_version(void);
+CV_API int conv_verify_abi_version(void);
 
 #ifdef __cplusplus
 }

@@ -29,12 +29,21 @@ def _lib():
 
 def _header_functions():
     text = open(HEADER).read()
-    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(conv_verify_\w+)\s*\(", text,
-                                 re.M)))
+    return sorted(set(re.findall(r"^\s*CV_API\s+(?:const\s+)?\w+\s*\*?\s*(conv_\w+)\s*\(",
+                                 text, re.M)))
 
 
 def test_header_and_binding_agree():
     assert _header_functions() == sorted(lib_mod.EXPORTS)
+    assert len(lib_mod.EXPORTS) == 11
+
+
+def test_library_exports_nothing_else():
+    _lib()
+    res = subprocess.run(["nm", "-D", "--defined-only", lib_mod.LIB_PATH], capture_output=True,
+                         text=True, check=True)
+    exported = set(re.findall(r"\bT (\w+)$", res.stdout, re.M))
+    assert exported == set(lib_mod.EXPORTS), sorted(exported ^ set(lib_mod.EXPORTS))
 
 
 def test_library_exports_every_declared_symbol():
@@ -118,9 +127,29 @@ def test_describe_rejects(name, kw, code):
 
 
 def test_window_stride_checked_per_layout():
-    # dense per slot = T*d*(D-1) = 24576; dedup per slot = d*(T+D-2) = 10240
+    # dense per slot = T*d*(D-1) = 24576; both row layouts per slot = d*(T+D-2) = 10240
     assert describe(0, shape(win_slot_stride=10240))[0] == EINVAL
     assert describe(1, shape(win_slot_stride=10240))[0] == 0
+    assert describe(2, shape(win_slot_stride=10240))[0] == 0
+    assert describe(2, shape(win_slot_stride=10232))[0] == EINVAL
+    assert describe(3, shape(win_slot_stride=10240))[0] == EINVAL   # tree: dense windows
+    assert describe(3, shape())[0] == 0
+
+
+def test_describe_rejects_unknown_variants():
+    for v in (-1, 4, 7):
+        rc, _, detail = describe(v, shape())
+        assert rc == EINVAL and detail
+
+
+def test_tree_lds_holds_the_tile_and_the_slabs():
+    # tree: (D-1 + bucket) tile rows of 256 channels (+16 bytes pitch) and two dense slabs
+    for T, tb in ((8, 8), (17, 24), (32, 32)):
+        rc, info, detail = describe(3, shape(T=T, win_slot_stride=T * 1024 * 3,
+                                             x_seq_stride=T * 1024, out_seq_stride=T * 1024))
+        assert rc == 0, detail
+        assert info.token_bucket == tb
+        assert info.lds_bytes == max(256 * 3 * 2, (3 + tb) * (256 * 2 + 16) + 2 * 256 * 3 * 2)
 
 
 def test_lds_limit():
@@ -201,6 +230,27 @@ call("identity_slots_short", 0, shape(n_slots=3), good)
 call("empty_batch_no_pointers", 0, shape(n_seq=0), [None] * 8)
 call("empty_channels_no_pointers", 1, shape(d_inner=0, qk_channels=0, win_slot_stride=0,
                                             state_slot_stride=0), [None] * 8)
+def rc_of(name, rc):
+    res[name] = [rc, lib.conv_verify_last_error().decode()]
+s = shape()
+rc_of("general_bad_layout", lib.conv_verify_update(ctypes.byref(s), 3, A, A, None, A, None,
+                                                    None, None, A, A, None))
+rc_of("general_rows_t_ok_empty", lib.conv_verify_update(ctypes.byref(shape(n_seq=0)), 2, *([None] * 10)))
+rc_of("tree_null_parent", lib.conv_verify_update_tree(ctypes.byref(s), A, A, None, A, None, None,
+                                                       None, None, A, A, None))
+rc_of("restore_null_index", lib.conv_verify_restore(ctypes.byref(s), 0, A, A, None, None, None))
+rc_of("restore_bad_layout", lib.conv_verify_restore(ctypes.byref(s), 5, A, A, None, A, None))
+rc_of("restore_misaligned", lib.conv_verify_restore(ctypes.byref(s), 0, A + 2, A, None, A, None))
+rc_of("restore_T33", lib.conv_verify_restore(ctypes.byref(shape(T=33)), 0, A, A, None, A, None))
+ps = shape(T=100, x_tok_stride=1024, out_tok_stride=1024)
+rc_of("prefill_null_cu", lib.conv_prefill(ctypes.byref(ps), A, A, None, A, None, None, None, A, None))
+rc_of("prefill_tok_overlap", lib.conv_prefill(ctypes.byref(shape(T=100, x_tok_stride=512)),
+                                              A, A, None, A, None, A, None, A, None))
+rc_of("prefill_empty_ok", lib.conv_prefill(ctypes.byref(shape(n_seq=0, T=100)), *([None] * 9)))
+rc_of("l2_null_x", lib.conv_qk_l2norm(ctypes.byref(s), 4, 1024, None, None))
+rc_of("l2_bad_head", lib.conv_qk_l2norm(ctypes.byref(shape(head_dim=96, qk_channels=960)), 4, 1024, A, None))
+rc_of("l2_short_stride", lib.conv_qk_l2norm(ctypes.byref(s), 4, 256, A, None))
+rc_of("l2_no_rows_ok", lib.conv_qk_l2norm(ctypes.byref(s), 0, 1024, None, None))
 print(json.dumps(res))
 """
 
@@ -219,6 +269,11 @@ def test_update_entry_points_validate_before_launch():
         "misaligned_bias": ENOTSUP, "misaligned_win": ENOTSUP,
         "identity_slots_short": EINVAL, "empty_batch_no_pointers": 0,
         "empty_channels_no_pointers": 0,
+        "general_bad_layout": EINVAL, "general_rows_t_ok_empty": 0, "tree_null_parent": EINVAL,
+        "restore_null_index": EINVAL, "restore_bad_layout": EINVAL,
+        "restore_misaligned": ENOTSUP, "restore_T33": ENOTSUP, "prefill_null_cu": EINVAL,
+        "prefill_tok_overlap": EINVAL, "prefill_empty_ok": 0, "l2_null_x": EINVAL,
+        "l2_bad_head": ENOTSUP, "l2_short_stride": EINVAL, "l2_no_rows_ok": 0,
     }
     for k, code in expect.items():
         assert res[k][0] == code, (k, res[k])

@@ -1,0 +1,238 @@
+"""GPU parity of the general entry points against the oracle's general loop.
+
+Packed rows, the time-major row layout, tree verify, the accepted-prefix restore, the
+prefill conv and the separate L2 - through the C ABI (Python binding), against
+oracle.verify_general / restore / prefill / l2norm on the same seeded inputs.  Bars:
+windows and conv_state bit-exact over the whole buffers, out within 1e-5 + 1e-5|r|
+(fp32) or 1 bf16 ulp, and every element a call must not write keeps its poison.
+"""
+
+import dataclasses
+
+import numpy as np
+import pytest
+
+import gpu_harness as gh
+import oracle
+import workloads
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import causal_conv1d_verify_amd._lib as L
+
+    L.load()
+
+
+def _say(*a):
+    print("[case]", *a, flush=True)
+
+
+def _verify_case(wl, layout=None):
+    inp = workloads.make_inputs(wl)
+    _say(wl.name, layout or wl.layout, wl)
+    p = gh.GeneralProblem(inp, layout)
+    p.verify()
+    return gh.compare_general(p.results(), gh.oracle_general(inp, layout), inp)
+
+
+c = workloads.custom
+LAYOUT_CASES = []
+for layout in ("dense", "dedup", "dedup_t"):
+    for T in (1, 3, 8, 9, 17, 32):
+        LAYOUT_CASES.append(c(f"{layout}_T{T}", n_seq=3, d_inner=1032, qk_channels=512,
+                              head_dim=128, T=T, layout=layout, accept_offsets=T > 1,
+                              permute_slots=True, pad_frac=0.25, extra_slots=2))
+    for xd, sd in (("f32", "f32"), ("bf16", "f32")):
+        LAYOUT_CASES.append(c(f"{layout}_{xd}_{sd}", n_seq=3, d_inner=520, qk_channels=256,
+                              head_dim=64, T=5, layout=layout, x_dtype=xd, state_dtype=sd,
+                              accept_offsets=True, permute_slots=True, pad_frac=0.3))
+    for D in (2, 3):
+        LAYOUT_CASES.append(c(f"{layout}_D{D}", n_seq=4, d_inner=520, qk_channels=256,
+                              head_dim=64, d_conv=D, T=6, layout=layout, accept_offsets=True))
+
+
+@pytest.mark.parametrize("wl", LAYOUT_CASES, ids=[w.name for w in LAYOUT_CASES])
+def test_layouts(wl):
+    _verify_case(wl)
+
+
+PACKED = []
+for layout in ("dense", "dedup", "dedup_t"):
+    for T in (2, 8, 16, 17, 32):
+        PACKED.append(c(f"packed_{layout}_T{T}", n_seq=6, d_inner=1032, qk_channels=512,
+                        head_dim=128, T=T, layout=layout, varlen=True, accept_offsets=True,
+                        permute_slots=True, pad_frac=0.2, extra_slots=1))
+    PACKED.append(c(f"packed_{layout}_f32", n_seq=5, d_inner=520, qk_channels=256, head_dim=64,
+                    T=9, layout=layout, x_dtype="f32", state_dtype="f32", varlen=True))
+    PACKED.append(c(f"packed_{layout}_strided", n_seq=5, d_inner=1000, qk_channels=512,
+                    head_dim=128, T=8, layout=layout, varlen=True, x_tok_stride=1024,
+                    accept_offsets=True))
+
+
+@pytest.mark.parametrize("wl", PACKED, ids=[w.name for w in PACKED])
+def test_packed_rows(wl):
+    _verify_case(wl)
+
+
+TREES = []
+for T in (1, 4, 8, 17, 32):
+    TREES.append(c(f"tree_T{T}", n_seq=4, d_inner=1032, qk_channels=512, head_dim=128, T=T,
+                   tree=True, accept_offsets=T > 1, permute_slots=True, pad_frac=0.25))
+for D in (2, 3):
+    TREES.append(c(f"tree_D{D}", n_seq=4, d_inner=520, qk_channels=256, head_dim=64, d_conv=D,
+                   T=7, tree=True))
+for xd, sd in (("f32", "f32"), ("bf16", "f32")):
+    TREES.append(c(f"tree_{xd}_{sd}", n_seq=3, d_inner=520, qk_channels=256, head_dim=64, T=9,
+                   x_dtype=xd, state_dtype=sd, tree=True, accept_offsets=True))
+TREES.append(c("tree_packed", n_seq=6, d_inner=1032, qk_channels=512, head_dim=128, T=12,
+               tree=True, varlen=True, accept_offsets=True, permute_slots=True, pad_frac=0.2))
+
+
+@pytest.mark.parametrize("wl", TREES, ids=[w.name for w in TREES])
+def test_tree(wl):
+    _verify_case(wl)
+
+
+def test_tree_with_chain_parents_equals_chain():
+    wl = c("chain_tree", n_seq=4, d_inner=1032, qk_channels=512, head_dim=128, T=9,
+           accept_offsets=True, permute_slots=True)
+    inp = workloads.make_inputs(wl)
+    _say("tree with chain parents vs chain")
+    chain = gh.GeneralProblem(inp)
+    chain.verify()
+    rc = chain.results()
+    inp_t = dataclasses.replace(inp, wl=dataclasses.replace(wl, tree=True),
+                                parent=np.tile(np.arange(-1, wl.T - 1, dtype=np.int32),
+                                               (wl.n_seq, 1)))
+    tree = gh.GeneralProblem(inp_t)
+    tree.verify()
+    rt = tree.results()
+    assert np.array_equal(rc["out"], rt["out"])
+    assert np.array_equal(rc["windows"], rt["windows"])
+    assert np.array_equal(rt["conv_state"], inp.conv_state), "tree verify wrote conv_state"
+
+
+RESTORES = []
+for layout in ("dense", "dedup", "dedup_t"):
+    for off in (False, True):
+        RESTORES.append(c(f"restore_{layout}_{'off' if off else 'plain'}", n_seq=6,
+                          d_inner=1032, qk_channels=512, head_dim=128, T=8, layout=layout,
+                          restore=True, accept_offsets=off, permute_slots=True, pad_frac=0.2,
+                          extra_slots=1))
+    RESTORES.append(c(f"restore_{layout}_f32_D3", n_seq=4, d_inner=520, qk_channels=256,
+                      head_dim=64, d_conv=3, T=5, layout=layout, x_dtype="f32",
+                      state_dtype="f32", restore=True))
+RESTORES.append(c("restore_tree", n_seq=6, d_inner=1032, qk_channels=512, head_dim=128, T=10,
+                  tree=True, restore=True, accept_offsets=True, permute_slots=True,
+                  pad_frac=0.2))
+RESTORES.append(c("restore_packed_rows", n_seq=6, d_inner=1032, qk_channels=512,
+                  head_dim=128, T=8, layout="dedup", varlen=True, restore=True))
+
+
+@pytest.mark.parametrize("wl", RESTORES, ids=[w.name for w in RESTORES])
+def test_restore_after_verify(wl):
+    inp = workloads.make_inputs(wl)
+    _say(wl.name, wl)
+    p = gh.GeneralProblem(inp)
+    p.verify()
+    p.restore()
+    gh.compare_general(p.results(), gh.oracle_general(inp, restore=True), inp)
+
+
+PREFILLS = []
+for D in (2, 3, 4):
+    for xd, sd in (("bf16", "bf16"), ("f32", "f32"), ("bf16", "f32")):
+        PREFILLS.append(c(f"prefill_D{D}_{xd}_{sd}", n_seq=5, d_inner=520, qk_channels=0,
+                          d_conv=D, T=100, x_dtype=xd, state_dtype=sd, varlen=True,
+                          prefill=True, init_frac=0.5, permute_slots=True,
+                          seed=workloads.BASE_SEED + 3000 + D))
+PREFILLS.append(c("prefill_short_rows", n_seq=8, d_inner=1032, qk_channels=0, T=3,
+                  varlen=True, prefill=True, init_frac=0.5, bias=False))
+PREFILLS.append(c("prefill_wide_state", n_seq=4, d_inner=1032, qk_channels=0, T=40,
+                  state_len=8, varlen=True, prefill=True, init_frac=0.5, pad_frac=0.25,
+                  extra_slots=1))
+PREFILLS.append(c("prefill_strided", n_seq=3, d_inner=1000, qk_channels=0, T=64,
+                  x_tok_stride=1024, varlen=True, prefill=True))
+
+
+@pytest.mark.parametrize("wl", PREFILLS, ids=[w.name for w in PREFILLS])
+def test_prefill(wl):
+    inp = workloads.make_inputs(wl)
+    _say(wl.name, wl)
+    p = gh.GeneralProblem(inp)
+    p.prefill()
+    gh.compare_general(p.results(), gh.oracle_general(inp), inp)
+
+
+@pytest.mark.parametrize("xd", ["bf16", "f32"])
+@pytest.mark.parametrize("hd", [4, 8, 32, 128, 256])
+def test_separate_l2(xd, hd):
+    import causal_conv1d_verify_amd as cv
+
+    rng = np.random.default_rng(workloads.BASE_SEED + 3100 + hd)
+    rows, d, qk = 7, 1280, 768 if hd != 256 else 512
+    x0 = workloads.to_storage(rng.standard_normal((rows, d + 16)).astype(np.float32), xd)
+    ref = x0.copy()
+    oracle.l2norm(ref, d_inner=d, qk_channels=qk, head_dim=hd, l2_eps=1e-6, x_dtype=xd)
+    _say("l2", xd, hd)
+    xt = gh.to_torch(x0, xd)
+    cv.conv_qk_l2norm(xt[:, :d], qk_channels=qk, head_dim=hd, l2_eps=1e-6)
+    got = gh.to_numpy(xt, xd)
+    assert np.array_equal(gh._bits(got[:, qk:]), gh._bits(x0[:, qk:])), "L2 wrote past q|k"
+    gh.compare_out_elements(got[:, :qk], ref[:, :qk], xd, "l2")
+
+
+def test_prefill_then_l2_matches_oracle():
+    wl = c("prefill_l2", n_seq=4, d_inner=1032, qk_channels=512, head_dim=128, T=50,
+           varlen=True, prefill=True, init_frac=0.5)
+    inp = workloads.make_inputs(wl)
+    _say("prefill + l2")
+    p = gh.GeneralProblem(inp)
+    p.prefill()
+    import causal_conv1d_verify_amd as cv
+
+    cv.conv_qk_l2norm(p.out, qk_channels=wl.qk_channels, head_dim=wl.head_dim,
+                      l2_eps=wl.l2_eps)
+    got = p.results()
+    ref = gh.oracle_general(inp)
+    gh.compare_general({"out": got["out"], "conv_state": got["conv_state"]},
+                       {"out": _l2_of(ref["out"], wl), "conv_state": ref["conv_state"]}, inp)
+
+
+def _l2_of(out, wl):
+    out = out.copy()
+    rows = out.reshape(-1, out.shape[-1])
+    oracle.l2norm(rows, d_inner=wl.d_inner, qk_channels=wl.qk_channels, head_dim=wl.head_dim,
+                  l2_eps=wl.l2_eps, x_dtype=wl.x_dtype)
+    return out
+
+
+@pytest.mark.parametrize("key", ["2t", "2v", "1t"])
+def test_full_size_verify(key):
+    wl = workloads.WORKLOADS[key]
+    _verify_case(wl)
+
+
+def test_full_size_restore():
+    wl = workloads.WORKLOADS["2r"]
+    inp = workloads.make_inputs(wl)
+    _say(wl.name)
+    p = gh.GeneralProblem(inp)
+    p.verify()
+    p.restore()
+    gh.compare_general(p.results(), gh.oracle_general(inp, restore=True), inp)
+
+
+def test_full_size_prefill():
+    wl = workloads.WORKLOADS["p"]
+    inp = workloads.make_inputs(wl)
+    _say(wl.name)
+    p = gh.GeneralProblem(inp)
+    p.prefill()
+    gh.compare_general(p.results(), gh.oracle_general(inp), inp)

@@ -108,6 +108,20 @@ WORKLOADS = {
     "4s": Workload("stress_dedup_t16_d10200_xstride10240", 512, 10200, 4096, 128, 4, 16,
                    "bf16", "bf16", "dedup", True, 18, BASE_SEED + 104, accept_offsets=True,
                    pad_frac=0.1, permute_slots=True, x_tok_stride=10240),
+    # the headline shape in the other row layout, with packed rows, and its restore
+    "2t": Workload("dedup_t_bs128_t8", 128, 10240, 4096, 128, 4, 8, "bf16", "bf16", "dedup_t",
+                   True, 3, BASE_SEED + 12),
+    "2v": Workload("packed_dedup_bs128_t8", 128, 10240, 4096, 128, 4, 8, "bf16", "bf16",
+                   "dedup", True, 3, BASE_SEED + 22, varlen=True, min_len=1),
+    "2r": Workload("restore_dedup_bs128_t8", 128, 10240, 4096, 128, 4, 8, "bf16", "bf16",
+                   "dedup", True, 3, BASE_SEED + 32, restore=True),
+    # tree verify at the K=17 GDN shape (dense windows, nothing committed)
+    "1t": Workload("tree_k17_dense", 8, 8192, 4096, 128, 4, 17, "bf16", "bf16", "dense",
+                   False, 3, BASE_SEED + 11, tree=True),
+    # a batch of packed prompts through the prefill conv, then the separate q|k L2
+    "p": Workload("prefill_8x2048", 8, 10240, 4096, 128, 4, 2048, "bf16", "bf16", "dense",
+                  False, 3, BASE_SEED + 40, varlen=True, min_len=1024, prefill=True,
+                  init_frac=0.5),
 }
 
 
