@@ -5,14 +5,20 @@ rollback window + committed state) over one batch of seeded synthetic inputs.
 Default workload: dedup_bs128_t8 (n_seq 128, d_inner 10240, T 8, bf16, dedup rows,
 bias on) - the GB300 workload of sglang PR 46184's benchmark table.
 
-    python bench.py [--steps K] [--warmup W] [--workload 2|0|1|3|4|4b|4s]
+    python bench.py [--steps K] [--warmup W] [--workload KEY]
+
+KEY: 0 1 2 3 4 4b 4s (the chain verify workloads), 2t (time-major rows), 2v (packed
+rows), 1t (tree verify), 2r (accepted-prefix restore: the step is the restore launch
+after an untimed verify), p (prefill: the step is the prefill conv plus the separate
+q|k L2; the roofline is the prefill conv alone).
 
 Prints ONE JSON line.  `value` is achieved algorithmic HBM bandwidth (GB/s): the
-bytes one launch must move (x, out, the conv_state window read and the committed
-window write, the rollback windows, weight and bias; active rows only) divided by the
-mean launch time measured with HIP events on the launch stream.  The inputs rotate
-over enough buffer sets that the working set is >= 2x the 256 MB Infinity Cache, so
-data is fetched from HBM.  The CPU oracle is timed on a bounded sample beside it.
+bytes one step must move (for the verify: x, out, the conv_state window read and the
+committed window write, the rollback windows, weight and bias; active rows only)
+divided by the mean step time measured with HIP events on the launch stream.  The
+inputs rotate over enough buffer sets that the working set is >= 2x the 256 MB
+Infinity Cache, so data is fetched from HBM.  The CPU oracle is timed on a bounded
+sample beside it.
 """
 
 from __future__ import annotations
@@ -56,29 +62,99 @@ def measured_traffic(workload: str):
     return rec.get("bytes_per_launch")
 
 
-def cpu_baseline(inp, alg_bytes, budget_s=10.0, max_reps=50):
-    """The C oracle, single-threaded, on the full problem repeated for ~budget_s."""
+def step_kind(wl) -> str:
+    """What one timed step launches: the verify, the restore after a verify, or the
+    prefill conv followed by the separate L2."""
+    return "prefill" if wl.prefill else "restore" if wl.restore else "verify"
+
+
+def step_bytes(wl, inp) -> int:
+    kind = step_kind(wl)
+    if kind == "restore":
+        return workloads.restore_bytes(wl, inp)
+    if kind == "prefill":
+        return workloads.algorithmic_bytes(wl, inp) + workloads.l2_bytes(wl, inp)
+    return workloads.algorithmic_bytes(wl, inp)
+
+
+def _oracle_l2(out, wl):
+    """The oracle's separate L2 over every row of a packed out (a copy)."""
     import oracle
 
+    out = out.copy()
+    oracle.l2norm(out.reshape(-1, out.shape[-1]), d_inner=wl.d_inner,
+                  qk_channels=wl.qk_channels, head_dim=wl.head_dim, l2_eps=wl.l2_eps,
+                  x_dtype=wl.x_dtype)
+    return out
+
+
+def _oracle_step(inp):
+    """The oracle's result of one step (the restore includes its verify)."""
+    import gpu_harness as gh
+
     wl = inp.wl
-    state = inp.conv_state.copy()
-    out = workloads.poison(inp.x.shape, wl.x_dtype)
-    win = workloads.poison_like_windows(wl)
+    kind = step_kind(wl)
+    ref = gh.oracle_general(inp, restore=kind == "restore")
+    if kind == "prefill":
+        ref["out"] = _oracle_l2(ref["out"], wl)
+    return ref
+
+
+def cpu_baseline(inp, alg_bytes, budget_s=10.0, max_reps=50):
+    """The C oracle, single-threaded, on the full problem repeated for ~budget_s."""
+    wl = inp.wl
     reps, t0 = 0, time.perf_counter()
     while True:
-        oracle.conv_verify(inp.x, inp.weight, inp.bias, state, out, win, d_inner=wl.d_inner,
-                           qk_channels=wl.qk_channels, head_dim=wl.head_dim,
-                           l2_eps=wl.l2_eps, x_dtype=wl.x_dtype, state_dtype=wl.state_dtype,
-                           layout=wl.layout, slot_idx=inp.slot_idx,
-                           num_accept_tokens=inp.num_accept_tokens)
+        _oracle_step(inp)
         reps += 1
         el = time.perf_counter() - t0
         if el >= budget_s or reps >= max_reps:
             break
+    what = {"verify": "", "restore": " (verify + restore; bytes of the restore)",
+            "prefill": " (prefill conv + separate L2)"}[step_kind(wl)]
     return {"value": round(alg_bytes * reps / el / 1e9, 3), "unit": "GB/s", "cores": 1,
             "kind": "oracle",
-            "sample": f"the whole {wl.name} problem, {reps} calls in {el:.1f} s "
+            "sample": f"the whole {wl.name} problem{what}, {reps} calls in {el:.1f} s "
                       f"({el / reps * 1e3:.0f} ms/call), one thread"}
+
+
+def _launches(cv, wl, p, stream):
+    """Zero-argument launch callables of one step on problem p (timed), and of its
+    dominant kernel alone (for the roofline)."""
+    kw = dict(qk_channels=wl.qk_channels, head_dim=wl.head_dim, l2_eps=wl.l2_eps, stream=stream)
+    kind = step_kind(wl)
+    if kind == "prefill":
+        pre = cv.prepare("prefill", p.x, p.weight, p.bias, p.conv_state, p.out, p.cu,
+                         max_len=wl.T, slot_idx=p.slot_idx, has_initial_state=p.has_init,
+                         stream=stream)
+        l2 = cv.prepare("l2", p.out, **kw)
+        return [pre, l2], pre
+    if kind == "restore":
+        p.verify(stream)   # the windows the restore reads
+        rst = cv.prepare("restore", p.conv_state, p.windows, p.restore_k, layout=p.layout,
+                         d_conv=wl.d_conv, slot_idx=p.slot_idx, stream=stream)
+        return [rst], rst
+    args = [p.x, p.weight, p.bias, p.conv_state, p.out, p.windows] + ([p.parent] if wl.tree else [])
+    ver = cv.prepare("tree" if wl.tree else "update", *args, layout=p.layout,
+                     slot_idx=p.slot_idx, num_accept_tokens=p.nat, cu_seqlens=p.cu, **kw)
+    return [ver], ver
+
+
+def _time(torch, fns_per_set, steps, warmup, stream):
+    sets = len(fns_per_set)
+    for i in range(warmup):
+        for f in fns_per_set[i % sets]:
+            f()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for i in range(steps):
+        for f in fns_per_set[i % sets]:
+            f()
+    end.record(stream)
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / steps
 
 
 def main(argv=None):
@@ -120,40 +196,43 @@ def main(argv=None):
     key = int(args.workload) if args.workload.isdigit() else args.workload
     wl = workloads.WORKLOADS[key]
     inp = workloads.make_inputs(wl)
-    alg = workloads.algorithmic_bytes(wl, inp)
+    kind = step_kind(wl)
+    alg = step_bytes(wl, inp)
+    dom_bytes = workloads.algorithmic_bytes(wl, inp) if kind == "prefill" else alg
     torch.cuda.set_device(0)
 
-    set_bytes = alg + wl.n_slots * wl.d_inner * wl.state_len * (4 if wl.state_dtype == "f32" else 2)
+    sb = 4 if wl.state_dtype == "f32" else 2
+    set_bytes = workloads.algorithmic_bytes(wl, inp) + wl.n_slots * wl.d_inner * wl.state_len * sb
     sets = args.sets or max(1, min(32, math.ceil(2 * MALL_BYTES / set_bytes)))
-    problems = [gh.DeviceProblem(inp) for _ in range(sets)]
+    problems = [gh.GeneralProblem(inp) for _ in range(sets)]
     stream = torch.cuda.current_stream()
 
     check = None
     if not args.no_check:
-        import oracle
+        p0 = gh.GeneralProblem(inp)
+        step, _ = _launches(cv, wl, p0, stream)
+        if kind == "prefill":
+            # each stage against the oracle on the same input: the prefill conv, then
+            # the L2 over the GPU's own prefill output
+            step[0]()
+            got = p0.results()
+            check = gh.compare_general(got, gh.oracle_general(inp), inp)
+            ref_l2 = _oracle_l2(got["out"], wl)
+            step[1]()
+            check["l2"] = gh.compare_general(p0.results(), {"out": ref_l2}, inp)
+        else:
+            for f in step:
+                f()
+            check = gh.compare_general(p0.results(), _oracle_step(inp), inp)
+        del p0
 
-        problems[0].run(stream)
-        check = gh.compare(problems[0].results(), oracle.run_inputs(inp), wl,
-                           gh.active_rows(inp))
-
-    dedup = wl.layout == "dedup"
-    launches = [cv.prepare(dedup, p.x, p.weight, p.bias, p.conv_state, p.out, p.windows,
-                           qk_channels=wl.qk_channels, head_dim=wl.head_dim,
-                           l2_eps=wl.l2_eps, slot_idx=p.slot_idx, num_accept_tokens=p.nat,
-                           stream=stream) for p in problems]
-    for i in range(args.warmup):
-        launches[i % sets]()
-    torch.cuda.synchronize()
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
-    start.record(stream)
-    for i in range(args.steps):
-        launches[i % sets]()
-    end.record(stream)
-    torch.cuda.synchronize()
-    ms = start.elapsed_time(end) / args.steps
+    built = [_launches(cv, wl, p, stream) for p in problems]
+    ms = _time(torch, [b[0] for b in built], args.steps, args.warmup, stream)
+    dom_ms = ms if kind != "prefill" else _time(torch, [[b[1]] for b in built], args.steps,
+                                                args.warmup, stream)
     us = ms * 1e3
     gbs = alg / (ms * 1e-3) / 1e9
+    dom_gbs = dom_bytes / (dom_ms * 1e-3) / 1e9
 
     traffic = measured_traffic(wl.name)
     line = {
@@ -170,19 +249,23 @@ def main(argv=None):
         "dtype": "f32",
         "data": "synthetic",
         "config": {
-            "workload": wl.name, "n_seq": wl.n_seq, "T": wl.T, "d_inner": wl.d_inner,
-            "d_conv": wl.d_conv, "qk_channels": wl.qk_channels, "head_dim": wl.head_dim,
-            "layout": wl.layout, "storage": f"x {wl.x_dtype}, state {wl.state_dtype}",
-            "bias": wl.bias, "us_per_launch": round(us, 3), "algorithmic_bytes": alg,
+            "workload": wl.name, "step": kind, "n_seq": wl.n_seq, "T": wl.T,
+            "d_inner": wl.d_inner, "d_conv": wl.d_conv, "qk_channels": wl.qk_channels,
+            "head_dim": wl.head_dim, "layout": wl.layout, "packed_rows": wl.varlen,
+            "tree": wl.tree, "storage": f"x {wl.x_dtype}, state {wl.state_dtype}",
+            "bias": wl.bias, "us_per_step": round(us, 3), "algorithmic_bytes": alg,
             "buffer_sets": sets, "pct_of_peak": round(100 * gbs / PEAK_GBS, 1),
         },
         "roofline": {
-            "bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_GBS, "unit": "GB/s",
-            "frac": round(gbs / PEAK_GBS, 4), "traffic": traffic,
+            "bound": "hbm", "achieved": round(dom_gbs, 1), "peak": PEAK_GBS, "unit": "GB/s",
+            "frac": round(dom_gbs / PEAK_GBS, 4), "traffic": traffic,
         },
     }
     if check is not None:
         line["config"]["parity"] = check
+    if kind == "prefill":
+        line["roofline"]["kernel"] = (f"prefill conv alone: {dom_bytes} bytes in "
+                                      f"{dom_ms * 1e3:.3f} us")
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(inp, alg)
     print(json.dumps(line), flush=True)

@@ -152,6 +152,12 @@ int plan_verify(int layout, bool tree, bool packed, const cv_shape_t *s, cvimpl:
     const int64_t slabs = (int64_t)kChw * W1 * sb * (s->T > 1 ? 2 : 1);
     int64_t later = 0;
     if (layout == cvimpl::kRows) later = (int64_t)(s->T + s->d_conv - 2) * pitch;
+    // packed rows in the rows layout also stage the slot's stored row block after the
+    // state region
+    if (layout == cvimpl::kRows && packed) {
+        const int64_t image = region + (int64_t)kChw * (s->T + s->d_conv - 2) * sb;
+        if (image > later) later = image;
+    }
     if (layout == cvimpl::kDense) later = (tree ? (int64_t)(W1 + tb) * pitch : 0) + slabs;
     const int64_t lds = region > later ? region : later;
     if (lds > kMaxLds)

@@ -147,6 +147,28 @@ __global__ __launch_bounds__(kWave) void cv_verify_kernel(KernelArgs p) {
         const int q = j * kWave + lane;
         if (j * kWave < rchunks) gload<16>(st_r, q < rchunks ? (uint32_t)q * 16u : kOffLane, 0, sreg[j]);
     }
+    // Packed rows shorter than the buffer's, rows layout: the slot's row block comes
+    // into LDS as stored (direct global->LDS loads issued with the other loads, so no
+    // wait on them sits behind a store).  The wavefront later overwrites its columns
+    // below T+W1-1 there and writes the block back whole: the columns past them keep
+    // their bits, and every store stays a coalesced 16-byte one.
+    const bool row_image = LAYOUT == kRows && p.cu != nullptr && T < p.T;
+    const int img_off = CHW * SL * SB;   // LDS offset of the image, past the state region
+    if constexpr (LAYOUT == kRows) {
+        if (row_image) {
+            const int LS = p.T + W1 - 1;
+            const rsrc_t img_r = make_rsrc(
+                (const char *)p.win + ((int64_t)slot * p.win_slot + (int64_t)cb * LS) * SB,
+                (uint32_t)(nch * LS * SB));
+            const int ichunks = nch * LS * SB / 16;
+            for (int j = 0; j * kWave < ichunks; ++j) {
+                const int q = j * kWave + lane;
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    img_r, (lds_void_t *)(lds + img_off + j * kWave * 16), 16,
+                    q < ichunks ? (uint32_t)q * 16u : kOffLane, 0, 0, kNT);
+            }
+        }
+    }
 #pragma unroll
     for (int j = 0; j < RJ; ++j) {
         const int q = j * kWave + lane;
@@ -396,7 +418,21 @@ __global__ __launch_bounds__(kWave) void cv_verify_kernel(KernelArgs p) {
         const rsrc_t row_r = make_rsrc(
             (char *)p.win + ((int64_t)slot * p.win_slot + (int64_t)cb * LS) * SB,
             (uint32_t)(nch * LS * SB));
-        if (T == TB && L == LS) {
+        if (row_image) {
+            // the stored block is in LDS: each lane writes its channels' columns below L
+            // into it, and the block leaves whole
+            constexpr int LC = TB + W1 - 1;   // >= LS
+            char *img = lds + img_off;
+            if (on) {
+#pragma unroll
+                for (int ch = 0; ch < CPL; ++ch)
+#pragma unroll
+                    for (int k = 0; k < LC; ++k)
+                        if (k < L) lds_put<SB>(img + ((lane * CPL + ch) * LS + k) * SB, sbits(k + 1, ch));
+            }
+            lds_barrier();
+            lds_to_global(img, nch * LS * SB / 16, row_r, 0, lane);
+        } else if (T == TB && L == LS) {
             // Row length known at compile time: each lane assembles its channels' rows
             // ([CPL][LC], contiguous in the row layout) in registers into LDS at the
             // same offsets, and the wavefront streams the block out lane-contiguously.

@@ -320,3 +320,11 @@ def restore_bytes(wl: Workload, inputs: Inputs) -> int:
     act = np.ones(wl.n_seq, bool) if inputs.slot_idx is None else inputs.slot_idx >= 0
     n = int((act & (inputs.restore_k >= 0)).sum())
     return n * wl.d_inner * 2 * wl.win_cols * sb
+
+
+def l2_bytes(wl: Workload, inputs: Inputs) -> int:
+    """Bytes the separate q|k L2 pass moves over all token rows it is given (every row
+    of the packed x): the q|k channels, read and written once."""
+    xb = 4 if wl.x_dtype == "f32" else 2
+    tokens = int(np.prod(inputs.x.shape[:-1]))
+    return 2 * tokens * wl.qk_channels * xb
