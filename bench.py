@@ -42,12 +42,17 @@ import workloads  # noqa: E402
 METRIC = "µs/launch and achieved HBM GB/s (% of peak) for verify conv1d+L2, 1 MI355X"
 PEAK_GBS = 8000.0
 MALL_BYTES = 256 * 2 ** 20
-KERNEL_SRC = os.path.join(ROOT, "causal_conv1d_verify_amd", "csrc", "cv_kernels.hip")
+KERNEL_SRCS = [os.path.join(ROOT, "causal_conv1d_verify_amd", "csrc", f)
+               for f in ("cv_kernels.hip", "cv_aux_kernels.hip", "cv_device.h")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
 def kernel_hash() -> str:
-    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+    """sha256[:16] over the device sources (every kernel the steps launch)."""
+    h = hashlib.sha256()
+    for f in KERNEL_SRCS:
+        h.update(open(f, "rb").read())
+    return h.hexdigest()[:16]
 
 
 def measured_traffic(workload: str):
