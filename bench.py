@@ -8,8 +8,8 @@ bias on) - the GB300 workload of sglang PR 46184's benchmark table.
     python bench.py [--steps K] [--warmup W] [--workload KEY]
 
 KEY: 0 1 2 3 4 4b 4s (the chain verify workloads), 2t (time-major rows), 2v (packed
-rows), 1t (tree verify), 2r (accepted-prefix restore: the step is the restore launch
-after an untimed verify), p (prefill: the step is the prefill conv plus the separate
+rows), 1t (tree verify), 2r / 4r (accepted-prefix restore at the headline / stress shape:
+the step is the restore launch after an untimed verify), p (prefill: the step is the prefill conv plus the separate
 q|k L2; the roofline is the prefill conv alone).
 
 Prints ONE JSON line.  `value` is achieved algorithmic HBM bandwidth (GB/s): the

@@ -334,7 +334,11 @@ int conv_verify_restore(const cv_shape_t *s, int32_t layout, void *conv_state,
     const int64_t wg = blocks * (int64_t)s->n_seq;
     if (wg * cvimpl::kWave > (int64_t)UINT32_MAX)
         return fail(CV_ENOTSUP, "grid of %lld workgroups exceeds the launch limit", (long long)wg);
-    const int lds = layout == cvimpl::kRows ? kChw * (s->T + s->d_conv - 2) * sb : 0;
+    // LDS: the channel-major window block (rows layout), then the state region
+    const int64_t lds = (layout == cvimpl::kRows ? (int64_t)kChw * (s->T + s->d_conv - 2) * sb : 0) +
+                        (int64_t)kChw * s->state_len * sb;
+    if (lds > cvimpl::kMaxLds)
+        return fail(CV_ENOTSUP, "restore needs %lld bytes of LDS (> %d)", (long long)lds, cvimpl::kMaxLds);
     cvimpl::RestoreArgs a;
     a.state = conv_state;
     a.win = windows;
@@ -348,7 +352,7 @@ int conv_verify_restore(const cv_shape_t *s, int32_t layout, void *conv_state,
     a.n_slots = s->n_slots;
     a.state_len = s->state_len;
     a.channel_blocks = (int)blocks;
-    return launch(cvimpl::pick_restore(sb, s->d_conv, layout), wg, lds, a, hip_stream);
+    return launch(cvimpl::pick_restore(sb, s->d_conv, layout), wg, (int)lds, a, hip_stream);
 }
 
 int conv_prefill(const cv_shape_t *s, const void *x, const void *weight, const void *bias,
@@ -377,6 +381,9 @@ int conv_prefill(const cv_shape_t *s, const void *x, const void *weight, const v
         return fail(CV_ENOTSUP, "data pointers must be 16-byte aligned");
     if (!slot_idx && s->n_slots < s->n_seq)
         return fail(CV_EINVAL, "n_slots (%d) < n_seq (%d) with identity slots", s->n_slots, s->n_seq);
+    const int64_t lds = (int64_t)kChw * s->state_len * sb;   // a chunk-0 wavefront's state region
+    if (lds > cvimpl::kMaxLds)
+        return fail(CV_ENOTSUP, "prefill needs %lld bytes of LDS (> %d)", (long long)lds, cvimpl::kMaxLds);
     const int64_t blocks = (C + kChw - 1) / kChw;
     const int64_t chunks = (s->T + cvimpl::kPrefillChunk - 1) / cvimpl::kPrefillChunk;
     const int64_t wg = blocks * chunks * (int64_t)s->n_seq;
@@ -401,7 +408,7 @@ int conv_prefill(const cv_shape_t *s, const void *x, const void *weight, const v
     a.state_len = s->state_len;
     a.channel_blocks = (int)blocks;
     a.chunks = (int)chunks;
-    return launch(cvimpl::pick_prefill(xb, sb, s->d_conv), wg, 0, a, hip_stream);
+    return launch(cvimpl::pick_prefill(xb, sb, s->d_conv), wg, (int)lds, a, hip_stream);
 }
 
 int conv_qk_l2norm(const cv_shape_t *s, int64_t n_rows, int64_t row_stride, void *x,

@@ -13,7 +13,7 @@
 //    per (token row, 256 q|k channels), the same cross-lane head sums as the verify.
 //
 // Every global access is a lane-contiguous 8/16-byte buffer access with the streaming
-// policy, except element stores where a state row is wider than the window.
+// policy; conv_state regions always move whole (see region_load).
 #include "cv_device.h"
 #include "cv_internal.h"
 
@@ -23,56 +23,43 @@ namespace {
 constexpr int CPL = kChannelsPerLane;
 constexpr int CHW = kWave * kChannelsPerLane;
 
-// One EB-byte element load (2 or 4 bytes), zero-extended.
-template <int EB>
-__device__ __forceinline__ uint32_t gload_elem(rsrc_t r, uint32_t voff) {
-    if constexpr (EB == 4) {
-        return __builtin_amdgcn_raw_buffer_load_b32(r, (int)voff, 0, kNT);
-    } else {
-        return (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, (int)voff, 0, kNT);
-    }
-}
-
 // Element (ch, j) of a lane's packed [CPL][W1] run of SB-byte elements.
 template <int SB, int W1>
 __device__ __forceinline__ uint32_t run_elem(const uint32_t *run, int ch, int j) {
     return elem_bits<SB>(run, ch * W1 + j);
 }
 
-template <int SB, int W1>
-__device__ __forceinline__ void pack_run(const uint32_t (&e)[CPL][W1], uint32_t *run) {
-    constexpr int RUNW = CPL * W1 * SB / 4;
+// A wavefront's conv_state region [nch, state_len] (contiguous) moves between HBM and
+// LDS in coalesced 16-byte chunks.  State rows wider than the window are always read
+// and written whole: writing only the window's bytes makes partial-sector writes,
+// which measured about five times slower than moving the whole rows.
+__device__ __forceinline__ void region_load(rsrc_t r, char *dst, int chunks, int lane) {
+    constexpr int RJ = 8;   // chunks per lane in flight per round
+    for (int j0 = 0; j0 * kWave < chunks; j0 += RJ) {
+        uint32_t v[RJ][4];
 #pragma unroll
-    for (int w = 0; w < RUNW; ++w) {
-        if constexpr (SB == 4) {
-            run[w] = e[w / W1][w % W1];
-        } else {
-            const int e0 = 2 * w, e1 = 2 * w + 1;
-            run[w] = e[e0 / W1][e0 % W1] | (e[e1 / W1][e1 % W1] << 16);
+        for (int j = 0; j < RJ; ++j) {
+            const int q = (j0 + j) * kWave + lane;
+            if ((j0 + j) * kWave < chunks) gload<16>(r, q < chunks ? (uint32_t)q * 16u : kOffLane, 0, v[j]);
+        }
+#pragma unroll
+        for (int j = 0; j < RJ; ++j) {
+            const int q = (j0 + j) * kWave + lane;
+            if ((j0 + j) * kWave < chunks && q < chunks)
+                *(uint4 *)(dst + q * 16) = make_uint4(v[j][0], v[j][1], v[j][2], v[j][3]);
         }
     }
 }
 
-// conv_state[s, c, 0..W1-1] of the lane's channels <- e: one lane-contiguous run when
-// a state row is exactly the window, element stores otherwise (columns >= W1 stay).
+// Columns 0..W1-1 of the lane's channels in the LDS copy of the region <- e.
 template <int SB, int W1>
-__device__ __forceinline__ void store_window(rsrc_t st_r, int SL, bool on, int lane,
-                                             const uint32_t (&e)[CPL][W1]) {
-    constexpr int RUNB = CPL * W1 * SB;
-    if (SL == W1) {
-        uint32_t run[RUNB / 4];
-        pack_run<SB, W1>(e, run);
-        const uint32_t lo = on ? (uint32_t)(lane * RUNB) : kOffLane;
+__device__ __forceinline__ void put_window(char *region, int SL, bool on, int lane,
+                                           const uint32_t (&e)[CPL][W1]) {
+    if (!on) return;
 #pragma unroll
-        for (int q = 0; q < RUNB / 8; ++q) gstore<8>(st_r, lo + 8 * q, 0, run + 2 * q);
-    } else {
+    for (int ch = 0; ch < CPL; ++ch)
 #pragma unroll
-        for (int ch = 0; ch < CPL; ++ch)
-#pragma unroll
-            for (int j = 0; j < W1; ++j)
-                gstore_elem<SB>(st_r, on ? (uint32_t)(((lane * CPL + ch) * SL + j) * SB) : kOffLane,
-                                e[ch][j]);
-    }
+        for (int j = 0; j < W1; ++j) lds_put<SB>(region + ((lane * CPL + ch) * SL + j) * SB, e[ch][j]);
 }
 
 // ---- accepted-prefix restore ------------------------------------------------------------
@@ -145,10 +132,19 @@ __global__ __launch_bounds__(kWave) void cv_restore_kernel(RestoreArgs p) {
         }
     }
 
+    // the state region: rows wider than the window come in whole first (the window
+    // columns are then replaced in LDS), and the region leaves whole
+    const int SL = p.state_len;
+    const int rchunks = nch * SL * SB / 16;
+    char *region = lds + (LAYOUT == kRows ? CHW * (p.T + W1 - 1) * SB : 0);
     const rsrc_t st_r = make_rsrc(
-        (char *)p.state + ((int64_t)slot * p.state_slot + (int64_t)cb * p.state_len) * SB,
-        (uint32_t)(nch * p.state_len * SB));
-    store_window<SB, W1>(st_r, p.state_len, on, lane, e);
+        (char *)p.state + ((int64_t)slot * p.state_slot + (int64_t)cb * SL) * SB,
+        (uint32_t)(nch * SL * SB));
+    if (SL > W1) region_load(st_r, region, rchunks, lane);
+    lds_barrier();
+    put_window<SB, W1>(region, SL, on, lane, e);
+    lds_barrier();
+    lds_to_global(region, rchunks, st_r, 0, lane);
 }
 
 // ---- prefill conv -----------------------------------------------------------------------
@@ -158,7 +154,6 @@ __global__ __launch_bounds__(kWave) void cv_prefill_kernel(PrefillArgs p) {
     constexpr int W1 = D - 1;
     constexpr int VB = CPL * XB;
     constexpr int XW = VB / 4;
-    constexpr int RUNB = CPL * W1 * SB;
     constexpr int G = 4;   // tokens per branch-free arithmetic chunk
 
     const int lane = threadIdx.x;
@@ -215,6 +210,9 @@ __global__ __launch_bounds__(kWave) void cv_prefill_kernel(PrefillArgs p) {
     const rsrc_t st_r = make_rsrc(
         (char *)p.state + ((int64_t)slot * p.state_slot + (int64_t)cb * SL) * SB,
         (uint32_t)(nch * SL * SB));
+    const int rchunks = nch * SL * SB / 16;
+    extern __shared__ uint4 lds_raw[];
+    char *lds = (char *)lds_raw;
     if (t0 > 0) {
 #pragma unroll
         for (int j = 0; j < W1; ++j) {
@@ -227,13 +225,15 @@ __global__ __launch_bounds__(kWave) void cv_prefill_kernel(PrefillArgs p) {
             }
         }
     } else {
+        // the first chunk takes the wavefront's state region through LDS (coalesced):
+        // its window is the halo, and the region goes back whole with the commit
+        if (init || SL > W1) region_load(st_r, lds, rchunks, lane);
+        lds_barrier();
 #pragma unroll
         for (int ch = 0; ch < CPL; ++ch)
 #pragma unroll
             for (int j = 0; j < W1; ++j)
-                hs[j][ch] = init ? gload_elem<SB>(st_r, on ? (uint32_t)(((lane * CPL + ch) * SL + j) * SB)
-                                                           : kOffLane)
-                                 : 0u;
+                hs[j][ch] = init && on ? lds_get<SB>(lds + ((lane * CPL + ch) * SL + j) * SB) : 0u;
 #pragma unroll
         for (int ch = 0; ch < CPL; ++ch)
 #pragma unroll
@@ -325,9 +325,10 @@ __global__ __launch_bounds__(kWave) void cv_prefill_kernel(PrefillArgs p) {
                 e[ch][j] = v;
             }
         }
-        store_window<SB, W1>(st_r, SL, on, lane, e);
+        put_window<SB, W1>(lds, SL, on, lane, e);
+        lds_barrier();
+        lds_to_global(lds, rchunks, st_r, 0, lane);
     }
-    (void)RUNB;
 }
 
 // ---- separate per-head L2 over q|k -------------------------------------------------------

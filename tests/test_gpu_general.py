@@ -222,8 +222,9 @@ def test_full_size_verify(key):
     _verify_case(wl)
 
 
-def test_full_size_restore():
-    wl = workloads.WORKLOADS["2r"]
+@pytest.mark.parametrize("key", ["2r", "4r"])
+def test_full_size_restore(key):
+    wl = workloads.WORKLOADS[key]
     inp = workloads.make_inputs(wl)
     _say(wl.name)
     p = gh.GeneralProblem(inp)

@@ -115,6 +115,9 @@ WORKLOADS = {
                    "dedup", True, 3, BASE_SEED + 22, varlen=True, min_len=1),
     "2r": Workload("restore_dedup_bs128_t8", 128, 10240, 4096, 128, 4, 8, "bf16", "bf16",
                    "dedup", True, 3, BASE_SEED + 32, restore=True),
+    "4r": Workload("restore_stress_dedup_t16", 512, 10240, 4096, 128, 4, 16, "bf16", "bf16",
+                   "dedup", True, 18, BASE_SEED + 34, accept_offsets=True, pad_frac=0.1,
+                   permute_slots=True, restore=True),
     # tree verify at the K=17 GDN shape (dense windows, nothing committed)
     "1t": Workload("tree_k17_dense", 8, 8192, 4096, 128, 4, 17, "bf16", "bf16", "dense",
                    False, 3, BASE_SEED + 11, tree=True),
