@@ -7,7 +7,8 @@ bias on) - the GB300 workload of sglang PR 46184's benchmark table.
 
     python bench.py [--steps K] [--warmup W] [--workload KEY]
 
-KEY: 0 1 2 3 4 4b 4s (the chain verify workloads), 2t (time-major rows), 2v (packed
+KEY: 0 1 2 3 4 4b 4s (the chain verify workloads), b1 b64 t16 (the pages' table rows:
+bs 1 and 64 at T 8, bs 128 at T 16), 2t (time-major rows), 2v (packed
 rows), 1t (tree verify), 2r / 4r (accepted-prefix restore at the headline / stress shape:
 the step is the restore launch after an untimed verify), p (prefill: the step is the prefill conv plus the separate
 q|k L2; the roofline is the prefill conv alone).
@@ -123,9 +124,9 @@ def cpu_baseline(inp, alg_bytes, budget_s=10.0, max_reps=50):
                       f"({el / reps * 1e3:.0f} ms/call), one thread"}
 
 
-def _launches(cv, wl, p, stream):
+def _launches(cv, wl, p, stream, setup=True):
     """Zero-argument launch callables of one step on problem p (timed), and of its
-    dominant kernel alone (for the roofline)."""
+    dominant kernel alone (for the roofline).  setup: run the restore's verify first."""
     kw = dict(qk_channels=wl.qk_channels, head_dim=wl.head_dim, l2_eps=wl.l2_eps, stream=stream)
     kind = step_kind(wl)
     if kind == "prefill":
@@ -135,7 +136,8 @@ def _launches(cv, wl, p, stream):
         l2 = cv.prepare("l2", p.out, **kw)
         return [pre, l2], pre
     if kind == "restore":
-        p.verify(stream)   # the windows the restore reads
+        if setup:
+            p.verify(stream)   # the windows the restore reads
         rst = cv.prepare("restore", p.conv_state, p.windows, p.restore_k, layout=p.layout,
                          d_conv=wl.d_conv, slot_idx=p.slot_idx, stream=stream)
         return [rst], rst
@@ -143,6 +145,30 @@ def _launches(cv, wl, p, stream):
     ver = cv.prepare("tree" if wl.tree else "update", *args, layout=p.layout,
                      slot_idx=p.slot_idx, num_accept_tokens=p.nat, cu_seqlens=p.cu, **kw)
     return [ver], ver
+
+
+def _graph_time(torch, cv, wl, problems, steps, stream):
+    """Mean step time (ms) when one step per buffer set is captured in a HIP graph and
+    the graph is replayed; the launches are prepared on the capture stream."""
+    side = torch.cuda.Stream()
+    side.wait_stream(stream)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=side):
+        for p in problems:
+            for f in _launches(cv, wl, p, side, setup=False)[0]:
+                f()
+    reps = max(1, steps // len(problems))
+    for _ in range(3):
+        g.replay()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(reps):
+        g.replay()
+    end.record(stream)
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / (reps * len(problems))
 
 
 def _time(torch, fns_per_set, steps, warmup, stream):
@@ -171,6 +197,9 @@ def main(argv=None):
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-check", action="store_true", help="skip the full-size parity check")
     ap.add_argument("--sets", type=int, default=0, help="buffer sets (0: auto, >= 2x MALL)")
+    ap.add_argument("--graph", action="store_true",
+                    help="also time the steps replayed from a captured HIP graph (one graph "
+                         "holds one step per buffer set), reported as config.graph_us_per_step")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run only a plain 256 MiB -> 256 MiB elementwise copy (10 dispatches), "
                          "the reference for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE")
@@ -238,6 +267,9 @@ def main(argv=None):
     us = ms * 1e3
     gbs = alg / (ms * 1e-3) / 1e9
     dom_gbs = dom_bytes / (dom_ms * 1e-3) / 1e9
+    graph_us = None
+    if args.graph:
+        graph_us = _graph_time(torch, cv, wl, problems, args.steps, stream) * 1e3
 
     traffic = measured_traffic(wl.name)
     line = {
@@ -268,6 +300,8 @@ def main(argv=None):
     }
     if check is not None:
         line["config"]["parity"] = check
+    if graph_us is not None:
+        line["config"]["graph_us_per_step"] = round(graph_us, 3)
     if kind == "prefill":
         line["roofline"]["kernel"] = (f"prefill conv alone: {dom_bytes} bytes in "
                                       f"{dom_ms * 1e3:.3f} us")

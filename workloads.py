@@ -108,6 +108,13 @@ WORKLOADS = {
     "4s": Workload("stress_dedup_t16_d10200_xstride10240", 512, 10200, 4096, 128, 4, 16,
                    "bf16", "bf16", "dedup", True, 18, BASE_SEED + 104, accept_offsets=True,
                    pad_frac=0.1, permute_slots=True, x_tok_stride=10240),
+    # the other rows of the benchmark table of sglang PR 46184 ("Benchmarking and Profiling")
+    "b1": Workload("dedup_bs1_t8", 1, 10240, 4096, 128, 4, 8, "bf16", "bf16", "dedup", True, 3,
+                   BASE_SEED + 52),
+    "b64": Workload("dedup_bs64_t8", 64, 10240, 4096, 128, 4, 8, "bf16", "bf16", "dedup", True,
+                    3, BASE_SEED + 62),
+    "t16": Workload("dedup_bs128_t16", 128, 10240, 4096, 128, 4, 16, "bf16", "bf16", "dedup",
+                    True, 3, BASE_SEED + 72),
     # the headline shape in the other row layout, with packed rows, and its restore
     "2t": Workload("dedup_t_bs128_t8", 128, 10240, 4096, 128, 4, 8, "bf16", "bf16", "dedup_t",
                    True, 3, BASE_SEED + 12),
