@@ -293,3 +293,23 @@ def test_product_never_touches_the_oracle():
                 text = open(os.path.join(dirpath, f)).read()
                 assert not re.search(r"^\s*(import|from)\s+oracle\b", text, re.M), f
                 assert "conv_verify_oracle" not in text and "liboracle" not in text, f
+
+
+def test_abi_from_plain_c(tmp_path):
+    """The header and the library used from C: gcc compiles tests/c/abi_from_c.c against
+    include/conv_verify.h, links libconvverify.so and runs it (no GPU: every call is
+    host-side validation or geometry)."""
+    _lib()
+    exe = tmp_path / "abi_from_c"
+    libdir = os.path.dirname(lib_mod.LIB_PATH)
+    cc = subprocess.run(["gcc", "-std=c11", "-Wall", "-Wextra", "-Werror",
+                         f"-I{os.path.join(ROOT, 'include')}",
+                         os.path.join(ROOT, "tests", "c", "abi_from_c.c"),
+                         f"-L{libdir}", "-lconvverify", f"-Wl,-rpath,{libdir}", "-o", str(exe)],
+                        capture_output=True, text=True)
+    assert cc.returncode == 0, cc.stderr
+    env = dict(os.environ, HIP_VISIBLE_DEVICES="-1", ROCR_VISIBLE_DEVICES="-1",
+               CUDA_VISIBLE_DEVICES="-1")
+    run = subprocess.run([str(exe)], capture_output=True, text=True, env=env, timeout=120)
+    assert run.returncode == 0, run.stdout + run.stderr
+    assert "MISMATCH" not in run.stdout

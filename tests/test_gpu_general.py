@@ -240,3 +240,46 @@ def test_full_size_prefill():
     p = gh.GeneralProblem(inp)
     p.prefill()
     gh.compare_general(p.results(), gh.oracle_general(inp), inp)
+
+
+@pytest.mark.parametrize("layout", ["dense", "dedup", "dedup_t"])
+def test_padded_slot_strides(layout):
+    """State and window buffers whose slots are views into a larger allocation (slot
+    strides with padding after each slot): results equal the oracle's, and the padding
+    keeps its poison through a verify and a restore."""
+    import torch
+
+    import causal_conv1d_verify_amd as cv
+
+    wl = c(f"pad_{layout}", n_seq=5, d_inner=1032, qk_channels=512, head_dim=128, T=6,
+           layout=layout, accept_offsets=True, permute_slots=True, pad_frac=0.2, restore=True,
+           extra_slots=1)
+    inp = workloads.make_inputs(wl)
+    _say("padded slots", layout)
+    ref = gh.oracle_general(inp, restore=True)
+    p = gh.GeneralProblem(inp)
+    # re-home conv_state and the windows into padded slots (16 extra elements per slot)
+    pad = 16
+    st_full = torch.empty((wl.n_slots, wl.d_inner * wl.state_len + pad), device="cuda",
+                          dtype=p.conv_state.dtype)
+    st_full.copy_(gh.to_torch(workloads.poison(tuple(st_full.shape), wl.state_dtype),
+                              wl.state_dtype))
+    st = st_full[:, :wl.d_inner * wl.state_len].view(wl.n_slots, wl.d_inner, wl.state_len)
+    st.copy_(p.conv_state)
+    wshape = tuple(p.windows.shape)
+    per = int(np.prod(wshape[1:]))
+    w_full = gh.to_torch(workloads.poison((wl.n_slots, per + pad), wl.state_dtype), wl.state_dtype)
+    win = w_full[:, :per].view(wshape)
+    cv.conv_verify_update(p.x, p.weight, p.bias, st, p.out, win, layout=layout,
+                          qk_channels=wl.qk_channels, head_dim=wl.head_dim, l2_eps=wl.l2_eps,
+                          slot_idx=p.slot_idx, num_accept_tokens=p.nat)
+    cv.conv_verify_restore(st, win, p.restore_k, layout=layout, d_conv=wl.d_conv,
+                           slot_idx=p.slot_idx)
+    torch.cuda.synchronize()
+    got = {"out": gh.to_numpy(p.out_full, wl.x_dtype),
+           "conv_state": gh.to_numpy(st.contiguous(), wl.state_dtype),
+           "windows": gh.to_numpy(win.contiguous(), wl.state_dtype)}
+    gh.compare_general(got, ref, inp)
+    pz = gh._bits(workloads.poison((wl.n_slots, pad), wl.state_dtype))
+    assert np.array_equal(gh._bits(gh.to_numpy(st_full[:, -pad:].contiguous(), wl.state_dtype)), pz)
+    assert np.array_equal(gh._bits(gh.to_numpy(w_full[:, -pad:].contiguous(), wl.state_dtype)), pz)
