@@ -152,14 +152,17 @@ int plan_verify(int layout, bool tree, bool packed, const cv_shape_t *s, cvimpl:
     const int64_t slabs = (int64_t)kChw * W1 * sb * (s->T > 1 ? 2 : 1);
     int64_t later = 0;
     if (layout == cvimpl::kRows) later = (int64_t)(s->T + s->d_conv - 2) * pitch;
-    // packed rows in the rows layout also stage the slot's stored row block after the
-    // state region
+    // While the loads are in flight the weights [channels, d_conv] sit past the state
+    // region, and (packed rows, rows layout) the stored row block past them; both are
+    // filled by direct global->LDS loads, so their spans are whole load-instruction
+    // widths.
+    const int64_t first = region + cvimpl::lds_dma_span(kChw * s->d_conv * xb);
     if (layout == cvimpl::kRows && packed) {
-        const int64_t image = region + (int64_t)kChw * (s->T + s->d_conv - 2) * sb;
+        const int64_t image = first + cvimpl::lds_dma_span(kChw * (s->T + s->d_conv - 2) * sb);
         if (image > later) later = image;
     }
     if (layout == cvimpl::kDense) later = (tree ? (int64_t)(W1 + tb) * pitch : 0) + slabs;
-    const int64_t lds = region > later ? region : later;
+    const int64_t lds = first > later ? first : later;
     if (lds > kMaxLds)
         return fail(CV_ENOTSUP, "kernel needs %lld bytes of LDS (> %d)", (long long)lds, kMaxLds);
     // Buffer resources span one row's bytes with a 32-bit size; lanes past d_inner use

@@ -59,7 +59,10 @@ struct RestoreArgs {
 };
 
 // Prefill conv over packed prompts (conv + SiLU, no L2, no windows).
-constexpr int kPrefillChunk = 16;   // tokens per wavefront
+#ifndef CV_PREFILL_CHUNK
+#define CV_PREFILL_CHUNK 16
+#endif
+constexpr int kPrefillChunk = CV_PREFILL_CHUNK;   // tokens per wavefront
 struct PrefillArgs {
     const void *x;
     const void *weight;
@@ -87,6 +90,13 @@ struct L2Args {
 // one sequence position, plus 16 bytes so successive rows start on different banks.
 constexpr int tile_pitch(int state_bytes) {
     return kWave * kChannelsPerLane * state_bytes + 16;
+}
+
+// LDS bytes to reserve for a block of `bytes` filled by direct global->LDS loads: each
+// such load instruction writes kWave 16-byte chunks, whole, so the span is rounded up
+// to a multiple of kWave * 16.
+constexpr int lds_dma_span(int bytes) {
+    return (bytes + kWave * 16 - 1) / (kWave * 16) * (kWave * 16);
 }
 
 // Kernel pickers, one per compiled (x bytes, state bytes, variant) object - variant 0

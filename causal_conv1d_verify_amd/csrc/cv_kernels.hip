@@ -104,14 +104,31 @@ __global__ __launch_bounds__(kWave) void cv_verify_kernel(KernelArgs p) {
         }
     }
 
-    uint32_t wr[XW * D];          // weights [CPL][D]
-    uint32_t br[XW];              // bias [CPL]
+    // Weights [nch][D]: the wavefront's block is contiguous, and comes into LDS by
+    // direct global->LDS loads in lane-contiguous 16-byte chunks, just past the state
+    // region.  Per-lane loads of each lane's D taps would touch D/2..D times as many
+    // cache lines per instruction; the weights are read by every row's wavefront, so
+    // those extra line accesses were a measurable share of the launch.  A direct load
+    // fills kWave * 16 bytes of LDS per instruction, so the weights' LDS (and the
+    // packed-row image after it) is reserved in whole multiples of that.
+    const int w_off = CHW * SL * SB;
+    const int img_off = w_off + lds_dma_span(CHW * D * XB);   // LDS offset of the row image
     {
         const rsrc_t w_r = make_rsrc((const char *)p.weight + (int64_t)cb * D * XB,
                                      (uint32_t)(nch * D * XB));
-        const uint32_t lw = on ? (uint32_t)(lane * VB * D) : kOffLane;
+        const int wchunks = nch * D * XB / 16;   // exact: nch * XB is a multiple of 16
+        constexpr int WJ = (CHW * D * XB / 16 + kWave - 1) / kWave;
 #pragma unroll
-        for (int q = 0; q < D; ++q) gload<VB>(w_r, lw + VB * q, 0, wr + XW * q);
+        for (int j = 0; j < WJ; ++j) {
+            const int q = j * kWave + lane;
+            if (j * kWave < wchunks)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    w_r, (lds_void_t *)(lds + w_off + j * kWave * 16), 16,
+                    q < wchunks ? (uint32_t)q * 16u : kOffLane, 0, 0, kNT);
+        }
+    }
+    uint32_t br[XW];              // bias [CPL]
+    {
 #pragma unroll
         for (int w = 0; w < XW; ++w) br[w] = 0u;
         if (p.bias) {
@@ -153,7 +170,6 @@ __global__ __launch_bounds__(kWave) void cv_verify_kernel(KernelArgs p) {
     // below T+W1-1 there and writes the block back whole: the columns past them keep
     // their bits, and every store stays a coalesced 16-byte one.
     const bool row_image = LAYOUT == kRows && p.cu != nullptr && T < p.T;
-    const int img_off = CHW * SL * SB;   // LDS offset of the image, past the state region
     if constexpr (LAYOUT == kRows) {
         if (row_image) {
             const int LS = p.T + W1 - 1;
@@ -194,6 +210,11 @@ __global__ __launch_bounds__(kWave) void cv_verify_kernel(KernelArgs p) {
     }
     __builtin_amdgcn_s_setprio(0);
     lds_barrier();
+
+    uint32_t wr[XW * D];   // the lane's weights [CPL][D] (zeros past d_inner)
+    lds_read_run<VB * D>(lds + w_off + lane * VB * D, wr);
+#pragma unroll
+    for (int w = 0; w < XW * D; ++w) wr[w] = on ? wr[w] : 0u;
 
     uint32_t S[W1][SW];   // initial window columns v[0..W1-1], state-typed bits
     if (contiguous_state) {
