@@ -337,9 +337,11 @@ int conv_verify_restore(const cv_shape_t *s, int32_t layout, void *conv_state,
     const int64_t wg = blocks * (int64_t)s->n_seq;
     if (wg * cvimpl::kWave > (int64_t)UINT32_MAX)
         return fail(CV_ENOTSUP, "grid of %lld workgroups exceeds the launch limit", (long long)wg);
-    // LDS: the channel-major window block (rows layout), then the state region
-    const int64_t lds = (layout == cvimpl::kRows ? (int64_t)kChw * (s->T + s->d_conv - 2) * sb : 0) +
-                        (int64_t)kChw * s->state_len * sb;
+    // LDS: the channel-major window block (rows layout), then the state region; both
+    // are filled by direct global->LDS loads, so their spans are whole load widths
+    const int64_t lds =
+        (layout == cvimpl::kRows ? cvimpl::lds_dma_span(kChw * (s->T + s->d_conv - 2) * sb) : 0) +
+        cvimpl::lds_dma_span(kChw * s->state_len * sb);
     if (lds > cvimpl::kMaxLds)
         return fail(CV_ENOTSUP, "restore needs %lld bytes of LDS (> %d)", (long long)lds, cvimpl::kMaxLds);
     cvimpl::RestoreArgs a;
@@ -384,7 +386,8 @@ int conv_prefill(const cv_shape_t *s, const void *x, const void *weight, const v
         return fail(CV_ENOTSUP, "data pointers must be 16-byte aligned");
     if (!slot_idx && s->n_slots < s->n_seq)
         return fail(CV_EINVAL, "n_slots (%d) < n_seq (%d) with identity slots", s->n_slots, s->n_seq);
-    const int64_t lds = (int64_t)kChw * s->state_len * sb;   // a chunk-0 wavefront's state region
+    // a chunk-0 wavefront's state region, then the weights (direct global->LDS loads)
+    const int64_t lds = (int64_t)kChw * s->state_len * sb + cvimpl::lds_dma_span(kChw * s->d_conv * xb);
     if (lds > cvimpl::kMaxLds)
         return fail(CV_ENOTSUP, "prefill needs %lld bytes of LDS (> %d)", (long long)lds, cvimpl::kMaxLds);
     const int64_t blocks = (C + kChw - 1) / kChw;

@@ -51,6 +51,18 @@ __device__ __forceinline__ void region_load(rsrc_t r, char *dst, int chunks, int
     }
 }
 
+// A contiguous block of `chunks` 16-byte chunks into LDS at dst by direct global->LDS
+// loads: every load is issued before any completes, and no VGPR holds the data.  dst
+// must have lds_dma_span(chunks * 16) bytes.  The caller waits (vmcnt) before reading.
+__device__ __forceinline__ void block_to_lds(rsrc_t r, char *dst, int chunks, int lane) {
+    for (int j = 0; j * kWave < chunks; ++j) {
+        const int q = j * kWave + lane;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t *)(dst + j * kWave * 16), 16,
+                                                 q < chunks ? (uint32_t)q * 16u : kOffLane, 0, 0,
+                                                 kNT);
+    }
+}
+
 // Columns 0..W1-1 of the lane's channels in the LDS copy of the region <- e.
 template <int SB, int W1>
 __device__ __forceinline__ void put_window(char *region, int SL, bool on, int lane,
@@ -99,23 +111,13 @@ __global__ __launch_bounds__(kWave) void cv_restore_kernel(RestoreArgs p) {
     } else if constexpr (LAYOUT == kRows) {
         // columns k..k+W1-1 of each channel's row: every 32-byte sector of the
         // wavefront's row block holds some of them, so the block comes in whole
-        // (coalesced) through LDS and each lane picks its elements out
+        // (coalesced) through LDS, together with the state region below, and each lane
+        // picks its elements out
         const int LS = p.T + W1 - 1;
         const rsrc_t row_r = make_rsrc(
             (const char *)p.win + ((int64_t)slot * p.win_slot + (int64_t)cb * LS) * SB,
             (uint32_t)(nch * LS * SB));
-        const int chunks = nch * LS * SB / 16;
-        for (int q = lane; q < chunks; q += kWave) {
-            uint32_t w4[4];
-            gload<16>(row_r, (uint32_t)q * 16u, 0, w4);
-            *(uint4 *)(lds + q * 16) = make_uint4(w4[0], w4[1], w4[2], w4[3]);
-        }
-        lds_barrier();
-#pragma unroll
-        for (int ch = 0; ch < CPL; ++ch)
-#pragma unroll
-            for (int j = 0; j < W1; ++j)
-                e[ch][j] = on ? lds_get<SB>(lds + ((lane * CPL + ch) * LS + k + j) * SB) : 0u;
+        block_to_lds(row_r, lds, nch * LS * SB / 16, lane);
     } else {
         // time-major rows: column k+j holds the d channels contiguously
         const int LS = p.T + W1 - 1;
@@ -136,12 +138,21 @@ __global__ __launch_bounds__(kWave) void cv_restore_kernel(RestoreArgs p) {
     // columns are then replaced in LDS), and the region leaves whole
     const int SL = p.state_len;
     const int rchunks = nch * SL * SB / 16;
-    char *region = lds + (LAYOUT == kRows ? CHW * (p.T + W1 - 1) * SB : 0);
+    char *region = lds + (LAYOUT == kRows ? lds_dma_span(CHW * (p.T + W1 - 1) * SB) : 0);
     const rsrc_t st_r = make_rsrc(
         (char *)p.state + ((int64_t)slot * p.state_slot + (int64_t)cb * SL) * SB,
         (uint32_t)(nch * SL * SB));
-    if (SL > W1) region_load(st_r, region, rchunks, lane);
+    if (SL > W1) block_to_lds(st_r, region, rchunks, lane);
+    __builtin_amdgcn_s_waitcnt(0);   // every load above has landed (in LDS or VGPRs)
     lds_barrier();
+    if constexpr (LAYOUT == kRows) {
+        const int LS = p.T + W1 - 1;
+#pragma unroll
+        for (int ch = 0; ch < CPL; ++ch)
+#pragma unroll
+            for (int j = 0; j < W1; ++j)
+                e[ch][j] = on ? lds_get<SB>(lds + ((lane * CPL + ch) * LS + k + j) * SB) : 0u;
+    }
     put_window<SB, W1>(region, SL, on, lane, e);
     lds_barrier();
     lds_to_global(region, rchunks, st_r, 0, lane);
@@ -188,19 +199,33 @@ __global__ __launch_bounds__(kWave) void cv_prefill_kernel(PrefillArgs p) {
             for (int w = 0; w < XW; ++w) X[t][w] = 0u;
         }
     }
-    uint32_t wr[XW * D];
-    uint32_t br[XW];
+    // Weights [nch][D] come into LDS past the state region by direct global->LDS
+    // loads in lane-contiguous 16-byte chunks (a fraction of the cache-line accesses
+    // of per-lane tap loads; every chunk's wavefront reads them).
+    extern __shared__ uint4 lds_raw[];
+    char *lds = (char *)lds_raw;
+    const int w_off = CHW * SL * SB;
     {
         const rsrc_t w_r = make_rsrc((const char *)p.weight + (int64_t)cb * D * XB,
                                      (uint32_t)(nch * D * XB));
-        const uint32_t lw = on ? (uint32_t)(lane * VB * D) : kOffLane;
+        const int wchunks = nch * D * XB / 16;   // exact: nch * XB is a multiple of 16
+        constexpr int WJ = (CHW * D * XB / 16 + kWave - 1) / kWave;
 #pragma unroll
-        for (int q = 0; q < D; ++q) gload<VB>(w_r, lw + VB * q, 0, wr + XW * q);
+        for (int j = 0; j < WJ; ++j) {
+            const int q = j * kWave + lane;
+            if (j * kWave < wchunks)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    w_r, (lds_void_t *)(lds + w_off + j * kWave * 16), 16,
+                    q < wchunks ? (uint32_t)q * 16u : kOffLane, 0, 0, kKeep);
+        }
+    }
+    uint32_t br[XW];
+    {
 #pragma unroll
         for (int w = 0; w < XW; ++w) br[w] = 0u;
         if (p.bias) {
             const rsrc_t b_r = make_rsrc((const char *)p.bias + (int64_t)cb * XB, (uint32_t)(nch * XB));
-            gload<VB>(b_r, laneV, 0, br);
+            gload<VB, kKeep>(b_r, laneV, 0, br);
         }
     }
     // The W1 inputs before token t0: x for later chunks; for the first chunk the
@@ -211,8 +236,6 @@ __global__ __launch_bounds__(kWave) void cv_prefill_kernel(PrefillArgs p) {
         (char *)p.state + ((int64_t)slot * p.state_slot + (int64_t)cb * SL) * SB,
         (uint32_t)(nch * SL * SB));
     const int rchunks = nch * SL * SB / 16;
-    extern __shared__ uint4 lds_raw[];
-    char *lds = (char *)lds_raw;
     if (t0 > 0) {
 #pragma unroll
         for (int j = 0; j < W1; ++j) {
@@ -258,6 +281,11 @@ __global__ __launch_bounds__(kWave) void cv_prefill_kernel(PrefillArgs p) {
     }
     __builtin_amdgcn_s_setprio(0);
 
+    lds_barrier();
+    uint32_t wr[XW * D];   // the lane's weights [CPL][D] (zeros past d_inner)
+    lds_read_run<VB * D>(lds + w_off + lane * VB * D, wr);
+#pragma unroll
+    for (int w = 0; w < XW * D; ++w) wr[w] = on ? wr[w] : 0u;
     float wv[CPL][D];
     float bv[CPL];
 #pragma unroll

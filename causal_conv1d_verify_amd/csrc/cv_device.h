@@ -100,9 +100,12 @@ typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) void lds_void_t;
 
 constexpr uint32_t kOffLane = 0x80000000u;
-// Cache policy of every global access: nt (streaming).  Each byte is read or written
-// once per launch, so nothing is worth keeping in L2 or the Infinity Cache.
+// Cache policy of the global accesses: nt (streaming).  Each byte of x, out, conv_state
+// and the windows is read or written once per launch, so none of it is worth keeping
+// in L2 or the Infinity Cache.  The weights (and bias) are the exception: every row's
+// wavefronts read the same block, so their loads use the default policy (kKeep).
 constexpr int kNT = 2;
+constexpr int kKeep = 0;
 
 __device__ __forceinline__ rsrc_t make_rsrc(const void *base, uint32_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
@@ -110,14 +113,14 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void *base, uint32_t bytes) {
 }
 
 // NB-byte (8 or 16) global load / store of words d[0 .. NB/4).
-template <int NB>
+template <int NB, int POL = kNT>
 __device__ __forceinline__ void gload(rsrc_t r, uint32_t voff, uint32_t soff, uint32_t *d) {
     if constexpr (NB == 16) {
-        const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, kNT);
+        const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, POL);
         d[0] = v.x; d[1] = v.y; d[2] = v.z; d[3] = v.w;
     } else {
         static_assert(NB == 8, "8- or 16-byte accesses");
-        const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(r, (int)voff, (int)soff, kNT);
+        const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(r, (int)voff, (int)soff, POL);
         d[0] = v.x; d[1] = v.y;
     }
 }

@@ -9,7 +9,9 @@ namespace cvimpl {
 constexpr int kWave = 64;        // lanes per wavefront on CDNA; one wavefront per workgroup
 constexpr int kChannelsPerLane = 4;   // 256 channels per wavefront
 constexpr int kMaxT = 32;        // largest token bucket compiled
-constexpr int kMaxLds = 65536;   // dynamic LDS a workgroup may request
+// dynamic LDS a workgroup may request: gfx950 has 160 KiB of LDS per compute unit and
+// one workgroup may take all of it
+constexpr int kMaxLds = 163840;
 
 // Rollback-window layouts.
 enum WinLayout { kDense = 0, kRows = 1, kRowsT = 2 };

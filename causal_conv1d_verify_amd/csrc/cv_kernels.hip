@@ -124,7 +124,7 @@ __global__ __launch_bounds__(kWave) void cv_verify_kernel(KernelArgs p) {
             if (j * kWave < wchunks)
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(
                     w_r, (lds_void_t *)(lds + w_off + j * kWave * 16), 16,
-                    q < wchunks ? (uint32_t)q * 16u : kOffLane, 0, 0, kNT);
+                    q < wchunks ? (uint32_t)q * 16u : kOffLane, 0, 0, kKeep);
         }
     }
     uint32_t br[XW];              // bias [CPL]
@@ -134,7 +134,7 @@ __global__ __launch_bounds__(kWave) void cv_verify_kernel(KernelArgs p) {
         if (p.bias) {
             const rsrc_t b_r = make_rsrc((const char *)p.bias + (int64_t)cb * XB,
                                          (uint32_t)(nch * XB));
-            gload<VB>(b_r, laneV, 0, br);
+            gload<VB, kKeep>(b_r, laneV, 0, br);
         }
     }
 

@@ -149,17 +149,20 @@ def test_tree_lds_holds_the_tile_and_the_slabs():
                                              x_seq_stride=T * 1024, out_seq_stride=T * 1024))
         assert rc == 0, detail
         assert info.token_bucket == tb
-        assert info.lds_bytes == max(256 * 3 * 2, (3 + tb) * (256 * 2 + 16) + 2 * 256 * 3 * 2)
+        assert info.lds_bytes == max(256 * 3 * 2 + 2048, (3 + tb) * (256 * 2 + 16) + 2 * 256 * 3 * 2)
 
 
 def test_lds_limit():
-    # a 256-channel wavefront stages its [256, state_len] state rows in LDS: fp32 rows
-    # of 65 columns need 66560 bytes > 64 KiB
-    rc, _, detail = describe(1, shape(state_dtype=lib_mod.CV_F32, state_len=65,
-                                      state_slot_stride=1024 * 65, win_slot_stride=1024 * 10))
+    # a 256-channel wavefront stages its [256, state_len] state rows in LDS and its
+    # weights [256, d_conv] right after them: fp32 rows of 158 columns and bf16 weights
+    # fill the 160 KiB exactly (161792 + 2048 bytes), 159 columns do not fit
+    rc, _, detail = describe(1, shape(state_dtype=lib_mod.CV_F32, state_len=159,
+                                      state_slot_stride=1024 * 159, win_slot_stride=1024 * 10))
     assert rc == ENOTSUP and "LDS" in detail
-    assert describe(1, shape(state_dtype=lib_mod.CV_F32, state_len=64,
-                             state_slot_stride=1024 * 64, win_slot_stride=1024 * 10))[0] == 0
+    rc, info, detail = describe(1, shape(state_dtype=lib_mod.CV_F32, state_len=158,
+                                         state_slot_stride=1024 * 158, win_slot_stride=1024 * 10))
+    assert rc == 0, detail
+    assert info.lds_bytes == 163840
 
 
 @pytest.mark.parametrize("key", [0, 1, 2, 3, 4, "4b", "4s"])
@@ -190,12 +193,13 @@ def test_launch_geometry_of_workloads(key):
     assert (info.channel_blocks - 1) * info.channels_per_wave < wl.d_inner
     assert info.token_bucket >= wl.T and info.token_bucket < 2 * wl.T + 1
     assert info.head_lanes * cpl == wl.head_dim
-    region = 64 * cpl * wl.state_len * sb
+    # while loading: the state region, then the weights in whole 1 KiB load widths
+    first = 64 * cpl * wl.state_len * sb + -(-(64 * cpl * wl.d_conv * xb) // 1024) * 1024
     if wl.layout == "dedup":
         later = wl.row_cols * (64 * cpl * sb + 16)
     else:
         later = 64 * cpl * wl.win_cols * sb * (2 if wl.T > 1 else 1)
-    assert info.lds_bytes == max(region, later) <= 65536
+    assert info.lds_bytes == max(first, later) <= 65536
 
 
 _CHILD = r"""

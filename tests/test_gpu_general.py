@@ -170,6 +170,39 @@ def test_prefill(wl):
     gh.compare_general(p.results(), gh.oracle_general(inp), inp)
 
 
+# LDS past 64 KiB (a gfx950 workgroup may take up to 160 KiB): fp32 state rows of 120
+# columns make a 120 KiB state region, so the weights' direct global->LDS loads, the
+# packed-row image and the restore's state region all land beyond the first 64 KiB.
+BIG_LDS = [c(f"big_lds_{layout}{'_packed' if packed else ''}", n_seq=3, d_inner=520,
+             qk_channels=256, head_dim=64, T=8, layout=layout, state_dtype="f32",
+             state_len=120, accept_offsets=True, permute_slots=True, varlen=packed)
+           for layout in ("dense", "dedup", "dedup_t") for packed in (False, True)]
+
+
+@pytest.mark.parametrize("wl", BIG_LDS, ids=[w.name for w in BIG_LDS])
+def test_big_lds_verify(wl):
+    _verify_case(wl)
+
+
+def test_big_lds_restore_and_prefill():
+    wl = c("big_lds_restore", n_seq=4, d_inner=520, qk_channels=256, head_dim=64, T=8,
+           layout="dedup", state_dtype="f32", state_len=120, accept_offsets=True,
+           permute_slots=True, restore=True)
+    inp = workloads.make_inputs(wl)
+    _say(wl.name, wl)
+    p = gh.GeneralProblem(inp)
+    p.verify()
+    p.restore()
+    gh.compare_general(p.results(), gh.oracle_general(inp, restore=True), inp)
+    wl = c("big_lds_prefill", n_seq=3, d_inner=520, qk_channels=0, T=40, state_dtype="f32",
+           state_len=120, varlen=True, prefill=True, init_frac=0.5)
+    inp = workloads.make_inputs(wl)
+    _say(wl.name, wl)
+    p = gh.GeneralProblem(inp)
+    p.prefill()
+    gh.compare_general(p.results(), gh.oracle_general(inp), inp)
+
+
 @pytest.mark.parametrize("xd", ["bf16", "f32"])
 @pytest.mark.parametrize("hd", [4, 8, 32, 128, 256])
 def test_separate_l2(xd, hd):
