@@ -153,12 +153,12 @@ int plan_verify(int layout, bool tree, bool packed, const cv_shape_t *s, cvimpl:
     int64_t later = 0;
     if (layout == cvimpl::kRows) later = (int64_t)(s->T + s->d_conv - 2) * pitch;
     // While the loads are in flight the weights [channels, d_conv] sit past the state
-    // region, and (packed rows, rows layout) the stored row block past them; both are
-    // filled by direct global->LDS loads, so their spans are whole load-instruction
-    // widths.
+    // region; once they are read, (packed rows, rows layout) the stored row block takes
+    // their place.  Both are filled by direct global->LDS loads, so their spans are
+    // whole load-instruction widths.
     const int64_t first = region + cvimpl::lds_dma_span(kChw * s->d_conv * xb);
     if (layout == cvimpl::kRows && packed) {
-        const int64_t image = first + cvimpl::lds_dma_span(kChw * (s->T + s->d_conv - 2) * sb);
+        const int64_t image = region + cvimpl::lds_dma_span(kChw * (s->T + s->d_conv - 2) * sb);
         if (image > later) later = image;
     }
     if (layout == cvimpl::kDense) later = (tree ? (int64_t)(W1 + tb) * pitch : 0) + slabs;

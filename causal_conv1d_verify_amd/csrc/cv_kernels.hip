@@ -110,9 +110,9 @@ __global__ __launch_bounds__(kWave) void cv_verify_kernel(KernelArgs p) {
     // cache lines per instruction; the weights are read by every row's wavefront, so
     // those extra line accesses were a measurable share of the launch.  A direct load
     // fills kWave * 16 bytes of LDS per instruction, so the weights' LDS (and the
-    // packed-row image after it) is reserved in whole multiples of that.
+    // packed-row image that later takes the same place) is reserved in whole
+    // multiples of that.
     const int w_off = CHW * SL * SB;
-    const int img_off = w_off + lds_dma_span(CHW * D * XB);   // LDS offset of the row image
     {
         const rsrc_t w_r = make_rsrc((const char *)p.weight + (int64_t)cb * D * XB,
                                      (uint32_t)(nch * D * XB));
@@ -151,7 +151,7 @@ __global__ __launch_bounds__(kWave) void cv_verify_kernel(KernelArgs p) {
     // LDS; each lane picks its channels' window out of it, writes its committed window
     // back into it, and the region leaves whole - so every state byte is read once and
     // written once in lane-contiguous 16-byte units, whatever state_len and the offset
-    // are.  (Direct global->LDS loads measured slower here than loads through VGPRs.)
+    // are.  (Direct global->LDS loads measured no faster here than loads through VGPRs.)
     const rsrc_t st_r = make_rsrc((const char *)p.state + ((int64_t)slot * p.state_slot +
                                                            (int64_t)cb * SL) * SB,
                                   (uint32_t)(nch * SL * SB));
@@ -163,27 +163,6 @@ __global__ __launch_bounds__(kWave) void cv_verify_kernel(KernelArgs p) {
     for (int j = 0; j < RJ; ++j) {
         const int q = j * kWave + lane;
         if (j * kWave < rchunks) gload<16>(st_r, q < rchunks ? (uint32_t)q * 16u : kOffLane, 0, sreg[j]);
-    }
-    // Packed rows shorter than the buffer's, rows layout: the slot's row block comes
-    // into LDS as stored (direct global->LDS loads issued with the other loads, so no
-    // wait on them sits behind a store).  The wavefront later overwrites its columns
-    // below T+W1-1 there and writes the block back whole: the columns past them keep
-    // their bits, and every store stays a coalesced 16-byte one.
-    const bool row_image = LAYOUT == kRows && p.cu != nullptr && T < p.T;
-    if constexpr (LAYOUT == kRows) {
-        if (row_image) {
-            const int LS = p.T + W1 - 1;
-            const rsrc_t img_r = make_rsrc(
-                (const char *)p.win + ((int64_t)slot * p.win_slot + (int64_t)cb * LS) * SB,
-                (uint32_t)(nch * LS * SB));
-            const int ichunks = nch * LS * SB / 16;
-            for (int j = 0; j * kWave < ichunks; ++j) {
-                const int q = j * kWave + lane;
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                    img_r, (lds_void_t *)(lds + img_off + j * kWave * 16), 16,
-                    q < ichunks ? (uint32_t)q * 16u : kOffLane, 0, 0, kNT);
-            }
-        }
     }
 #pragma unroll
     for (int j = 0; j < RJ; ++j) {
@@ -215,6 +194,31 @@ __global__ __launch_bounds__(kWave) void cv_verify_kernel(KernelArgs p) {
     lds_read_run<VB * D>(lds + w_off + lane * VB * D, wr);
 #pragma unroll
     for (int w = 0; w < XW * D; ++w) wr[w] = on ? wr[w] : 0u;
+
+    // Packed rows shorter than the buffer's, rows layout: the slot's row block comes
+    // into LDS as stored, where the weights were (direct global->LDS loads, issued
+    // once the weights are in VGPRs and before any store, so no wait on them sits
+    // behind a store).  The wavefront later overwrites its columns below T+W1-1 there
+    // and writes the block back whole: the columns past them keep their bits, and every
+    // store stays a coalesced 16-byte one.
+    const bool row_image = LAYOUT == kRows && p.cu != nullptr && T < p.T;
+    const int img_off = w_off;
+    if constexpr (LAYOUT == kRows) {
+        if (row_image) {
+            __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): the weight reads are done
+            const int LS = p.T + W1 - 1;
+            const rsrc_t img_r = make_rsrc(
+                (const char *)p.win + ((int64_t)slot * p.win_slot + (int64_t)cb * LS) * SB,
+                (uint32_t)(nch * LS * SB));
+            const int ichunks = nch * LS * SB / 16;
+            for (int j = 0; j * kWave < ichunks; ++j) {
+                const int q = j * kWave + lane;
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    img_r, (lds_void_t *)(lds + img_off + j * kWave * 16), 16,
+                    q < ichunks ? (uint32_t)q * 16u : kOffLane, 0, 0, kNT);
+            }
+        }
+    }
 
     uint32_t S[W1][SW];   // initial window columns v[0..W1-1], state-typed bits
     if (contiguous_state) {
@@ -444,6 +448,7 @@ __global__ __launch_bounds__(kWave) void cv_verify_kernel(KernelArgs p) {
             // into it, and the block leaves whole
             constexpr int LC = TB + W1 - 1;   // >= LS
             char *img = lds + img_off;
+            __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): the block has landed
             if (on) {
 #pragma unroll
                 for (int ch = 0; ch < CPL; ++ch)
