@@ -152,11 +152,12 @@ int plan_verify(int layout, bool tree, bool packed, const cv_shape_t *s, cvimpl:
     const int64_t slabs = (int64_t)kChw * W1 * sb * (s->T > 1 ? 2 : 1);
     int64_t later = 0;
     if (layout == cvimpl::kRows) later = (int64_t)(s->T + s->d_conv - 2) * pitch;
-    // While the loads are in flight the weights [channels, d_conv] sit past the state
-    // region; once they are read, (packed rows, rows layout) the stored row block takes
-    // their place.  Both are filled by direct global->LDS loads, so their spans are
-    // whole load-instruction widths.
-    const int64_t first = region + cvimpl::lds_dma_span(kChw * s->d_conv * xb);
+    // While the loads are in flight the weights [channels, d_conv] sit at the start of
+    // LDS; the state region is written over them once they are read, and (packed rows,
+    // rows layout) the stored row block follows the region.  Both are filled by direct
+    // global->LDS loads, so their spans are whole load-instruction widths.
+    const int64_t wspan = cvimpl::lds_dma_span(kChw * s->d_conv * xb);
+    const int64_t first = region > wspan ? region : wspan;
     if (layout == cvimpl::kRows && packed) {
         const int64_t image = region + cvimpl::lds_dma_span(kChw * (s->T + s->d_conv - 2) * sb);
         if (image > later) later = image;

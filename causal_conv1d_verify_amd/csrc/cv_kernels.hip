@@ -105,14 +105,14 @@ __global__ __launch_bounds__(kWave) void cv_verify_kernel(KernelArgs p) {
     }
 
     // Weights [nch][D]: the wavefront's block is contiguous, and comes into LDS by
-    // direct global->LDS loads in lane-contiguous 16-byte chunks, just past the state
-    // region.  Per-lane loads of each lane's D taps would touch D/2..D times as many
-    // cache lines per instruction; the weights are read by every row's wavefront, so
-    // those extra line accesses were a measurable share of the launch.  A direct load
-    // fills kWave * 16 bytes of LDS per instruction, so the weights' LDS (and the
-    // packed-row image that later takes the same place) is reserved in whole
-    // multiples of that.
-    const int w_off = CHW * SL * SB;
+    // direct global->LDS loads in lane-contiguous 16-byte chunks.  Per-lane loads of
+    // each lane's D taps would touch D/2..D times as many cache lines per instruction;
+    // the weights are read by every row's wavefront, so those extra line accesses were
+    // a measurable share of the launch.  They land at the start of LDS and go to VGPRs
+    // once every load has landed, before the state region is written over them: the
+    // two share LDS, which keeps the wavefront's LDS (and so its occupancy) that of the
+    // state region alone.  A direct load fills kWave * 16 bytes of LDS per instruction,
+    // so the weights' LDS is reserved in whole multiples of that.
     {
         const rsrc_t w_r = make_rsrc((const char *)p.weight + (int64_t)cb * D * XB,
                                      (uint32_t)(nch * D * XB));
@@ -123,7 +123,7 @@ __global__ __launch_bounds__(kWave) void cv_verify_kernel(KernelArgs p) {
             const int q = j * kWave + lane;
             if (j * kWave < wchunks)
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                    w_r, (lds_void_t *)(lds + w_off + j * kWave * 16), 16,
+                    w_r, (lds_void_t *)(lds + j * kWave * 16), 16,
                     q < wchunks ? (uint32_t)q * 16u : kOffLane, 0, 0, kKeep);
         }
     }
@@ -164,6 +164,11 @@ __global__ __launch_bounds__(kWave) void cv_verify_kernel(KernelArgs p) {
         const int q = j * kWave + lane;
         if (j * kWave < rchunks) gload<16>(st_r, q < rchunks ? (uint32_t)q * 16u : kOffLane, 0, sreg[j]);
     }
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): every load above has landed
+    uint32_t wr[XW * D];   // the lane's weights [CPL][D] (zeros past d_inner)
+    lds_read_run<VB * D>(lds + lane * VB * D, wr);   // (LDS accesses run in order)
+#pragma unroll
+    for (int w = 0; w < XW * D; ++w) wr[w] = on ? wr[w] : 0u;
 #pragma unroll
     for (int j = 0; j < RJ; ++j) {
         const int q = j * kWave + lane;
@@ -190,19 +195,14 @@ __global__ __launch_bounds__(kWave) void cv_verify_kernel(KernelArgs p) {
     __builtin_amdgcn_s_setprio(0);
     lds_barrier();
 
-    uint32_t wr[XW * D];   // the lane's weights [CPL][D] (zeros past d_inner)
-    lds_read_run<VB * D>(lds + w_off + lane * VB * D, wr);
-#pragma unroll
-    for (int w = 0; w < XW * D; ++w) wr[w] = on ? wr[w] : 0u;
-
     // Packed rows shorter than the buffer's, rows layout: the slot's row block comes
-    // into LDS as stored, where the weights were (direct global->LDS loads, issued
-    // once the weights are in VGPRs and before any store, so no wait on them sits
-    // behind a store).  The wavefront later overwrites its columns below T+W1-1 there
-    // and writes the block back whole: the columns past them keep their bits, and every
-    // store stays a coalesced 16-byte one.
+    // into LDS as stored, past the state region (direct global->LDS loads, issued once
+    // the weights are in VGPRs and before any store, so no wait on them sits behind a
+    // store).  The wavefront later overwrites its columns below T+W1-1 there and writes
+    // the block back whole: the columns past them keep their bits, and every store
+    // stays a coalesced 16-byte one.
     const bool row_image = LAYOUT == kRows && p.cu != nullptr && T < p.T;
-    const int img_off = w_off;
+    const int img_off = CHW * SL * SB;
     if constexpr (LAYOUT == kRows) {
         if (row_image) {
             __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): the weight reads are done

@@ -75,8 +75,8 @@
  *    state_slot_stride and win_slot_stride multiples of 16 bytes; head_dim one of
  *    4, 8, 16, 32, 64, 128, 256 (a head is reduced inside one 256-channel wavefront).
  *  - LDS (else CV_ENOTSUP): a 256-channel wavefront stages its [256, state_len] state
- *    region, its weights and its window tiles in LDS, at most 160 KiB (all of a gfx950
- *    compute unit's): state_len up to 158 fp32 / 316 bf16 columns with bf16 x, d_conv 4.
+ *    region (and its weights, its window tiles) in LDS, at most 160 KiB (all of a gfx950
+ *    compute unit's): state_len up to 160 fp32 / 320 bf16 columns.
  *  - Numerics: the conv accumulates in fp32 as acc = bias (or +0); for w = 0..D-1:
  *    acc = fma(weight[c,w], v[t+w], acc), each step one correctly rounded fused
  *    multiply-add.  SiLU and L2 run in fp32.  Windows and conv_state are moved as bit

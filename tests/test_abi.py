@@ -149,18 +149,18 @@ def test_tree_lds_holds_the_tile_and_the_slabs():
                                              x_seq_stride=T * 1024, out_seq_stride=T * 1024))
         assert rc == 0, detail
         assert info.token_bucket == tb
-        assert info.lds_bytes == max(256 * 3 * 2 + 2048, (3 + tb) * (256 * 2 + 16) + 2 * 256 * 3 * 2)
+        assert info.lds_bytes == max(2048, (3 + tb) * (256 * 2 + 16) + 2 * 256 * 3 * 2)
 
 
 def test_lds_limit():
-    # a 256-channel wavefront stages its [256, state_len] state rows in LDS and its
-    # weights [256, d_conv] right after them: fp32 rows of 158 columns and bf16 weights
-    # fill the 160 KiB exactly (161792 + 2048 bytes), 159 columns do not fit
-    rc, _, detail = describe(1, shape(state_dtype=lib_mod.CV_F32, state_len=159,
-                                      state_slot_stride=1024 * 159, win_slot_stride=1024 * 10))
+    # a 256-channel wavefront stages its [256, state_len] state rows in LDS (the weights
+    # pass through the same bytes first): fp32 rows of 160 columns fill the 160 KiB
+    # exactly, 161 columns do not fit
+    rc, _, detail = describe(1, shape(state_dtype=lib_mod.CV_F32, state_len=161,
+                                      state_slot_stride=1024 * 161, win_slot_stride=1024 * 10))
     assert rc == ENOTSUP and "LDS" in detail
-    rc, info, detail = describe(1, shape(state_dtype=lib_mod.CV_F32, state_len=158,
-                                         state_slot_stride=1024 * 158, win_slot_stride=1024 * 10))
+    rc, info, detail = describe(1, shape(state_dtype=lib_mod.CV_F32, state_len=160,
+                                         state_slot_stride=1024 * 160, win_slot_stride=1024 * 10))
     assert rc == 0, detail
     assert info.lds_bytes == 163840
 
@@ -193,8 +193,9 @@ def test_launch_geometry_of_workloads(key):
     assert (info.channel_blocks - 1) * info.channels_per_wave < wl.d_inner
     assert info.token_bucket >= wl.T and info.token_bucket < 2 * wl.T + 1
     assert info.head_lanes * cpl == wl.head_dim
-    # while loading: the state region, then the weights in whole 1 KiB load widths
-    first = 64 * cpl * wl.state_len * sb + -(-(64 * cpl * wl.d_conv * xb) // 1024) * 1024
+    # while loading: the weights (in whole 1 KiB load widths), then the state region
+    # over the same bytes
+    first = max(64 * cpl * wl.state_len * sb, -(-(64 * cpl * wl.d_conv * xb) // 1024) * 1024)
     if wl.layout == "dedup":
         later = wl.row_cols * (64 * cpl * sb + 16)
     else:
