@@ -54,6 +54,7 @@ class CvLaunchInfo(ctypes.Structure):
         ("channel_blocks", ctypes.c_int32), ("channels_per_wave", ctypes.c_int32),
         ("channels_per_lane", ctypes.c_int32), ("token_bucket", ctypes.c_int32),
         ("lds_bytes", ctypes.c_int32), ("head_lanes", ctypes.c_int32),
+        ("token_chunks", ctypes.c_int32),
     ]
 
 

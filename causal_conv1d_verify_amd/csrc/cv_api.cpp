@@ -175,16 +175,28 @@ int plan_verify(int layout, bool tree, bool packed, const cv_shape_t *s, cvimpl:
         return fail(CV_ENOTSUP, "a row spans more than 2 GiB (x %lld, out %lld, windows %lld bytes)",
                     (long long)x_span, (long long)o_span, (long long)w_span);
 
+    // Token split (dense windows, chain verify): on a grid too small to fill the chip,
+    // each row's tokens are spread over ceil(T / kSplitChunk) wavefronts per channel
+    // block.  Their LDS: chunk 0's state region, the weights, two snapshot slabs.
+    int chunks = 1;
+    int64_t split_lds = 0;
+    if (layout == cvimpl::kDense && !tree && wg < cvimpl::kSplitBelowWaves &&
+        s->T >= 2 * cvimpl::kSplitChunk) {
+        split_lds = region + cvimpl::lds_dma_span(kChw * s->d_conv * xb) + 2 * (int64_t)kChw * W1 * sb;
+        if (split_lds <= kMaxLds) chunks = (s->T + cvimpl::kSplitChunk - 1) / cvimpl::kSplitChunk;
+    }
+
     plan->layout = layout;
     plan->tree = tree ? 1 : 0;
     plan->x_bytes = xb;
     plan->state_bytes = sb;
     plan->d_conv = s->d_conv;
-    plan->token_bucket = tb;
+    plan->token_bucket = chunks > 1 ? cvimpl::kSplitChunk : tb;
+    plan->token_chunks = chunks;
     plan->channels_per_lane = cvimpl::kChannelsPerLane;
     plan->channel_blocks = (int)blocks;
-    plan->workgroups = wg;
-    plan->lds_bytes = (int)lds;
+    plan->workgroups = wg * chunks;
+    plan->lds_bytes = (int)(chunks > 1 ? split_lds : lds);
     plan->head_lanes = head_lanes;
     return CV_OK;
 }
@@ -193,6 +205,7 @@ const void *pick_verify(const cvimpl::Plan &plan) {
     using namespace cvimpl;
     const int d = plan.d_conv, tb = plan.token_bucket;
     const int v = plan.tree ? 3 : plan.layout;
+    if (plan.token_chunks > 1) return pick_split(plan.x_bytes, plan.state_bytes, d);
 #define CV_PICK_FOR(xb, sb)                                  \
     switch (v) {                                             \
         case 0: return pick_kernel_##xb##_##sb##_0(d, tb);   \
@@ -270,6 +283,7 @@ int verify(int layout, bool tree, const cv_shape_t *s, const void *x, const void
     while (plan.head_lanes && (1 << hl_log2) < plan.head_lanes) ++hl_log2;
     a.head_lanes_log2 = hl_log2;
     a.eps = s->l2_eps;
+    a.token_chunks = plan.token_chunks;
     return launch(pick_verify(plan), plan.workgroups, plan.lds_bytes, a, stream);
 }
 
@@ -466,6 +480,7 @@ int conv_verify_describe(int variant, const cv_shape_t *shape, cv_launch_info_t 
     info->token_bucket = plan.token_bucket;
     info->lds_bytes = plan.lds_bytes;
     info->head_lanes = plan.head_lanes;
+    info->token_chunks = plan.token_chunks;
     return CV_OK;
 }
 

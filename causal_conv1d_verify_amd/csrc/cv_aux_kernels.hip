@@ -359,6 +359,256 @@ __global__ __launch_bounds__(kWave) void cv_prefill_kernel(PrefillArgs p) {
     }
 }
 
+// ---- token-split verify (dense windows) --------------------------------------------------
+//
+// The verify of cv_verify_kernel with a row's T tokens spread over ceil(T / TC)
+// wavefronts per 256 channels, for grids too small to fill the chip (a few rows of
+// many draft tokens).  Tokens are independent given their D-1 predecessors, so chunk
+// k computes out and the dense snapshots of tokens [k*TC, k*TC+TC) from x alone,
+// with the D-1 tokens before the chunk as its halo; chunk 0 takes its halo from the
+// state window at column a and is also the wavefront that commits the row's last
+// window, so a slot's state read and write stay in one wavefront and chunks never
+// race.  (Dense snapshots only: a channel-major row is shared by every chunk of a
+// channel.)  Same arithmetic, same order, same rounding as the verify kernel.
+template <int XB, int SB, int D, int TC>
+__global__ __launch_bounds__(kWave) void cv_split_kernel(KernelArgs p) {
+    static_assert(TC >= D - 1, "the halo of a chunk must come from the chunk before");
+    constexpr int W1 = D - 1;
+    constexpr int VB = CPL * XB;
+    constexpr int XW = VB / 4;
+    constexpr int RUNB = CPL * W1 * SB;   // a lane's [CPL][W1] window run
+    constexpr int RUNW = RUNB / 4;
+    extern __shared__ uint4 lds_raw[];
+    char *lds = (char *)lds_raw;
+
+    const int lane = threadIdx.x;
+    const unsigned b = blockIdx.x;
+    const unsigned r2 = b / (unsigned)p.channel_blocks;
+    const int cb = (int)(b - r2 * (unsigned)p.channel_blocks) * CHW;
+    const int row = (int)(r2 / (unsigned)p.token_chunks);
+    const int chunk = (int)(r2 - (unsigned)row * (unsigned)p.token_chunks);
+
+    const int slot = p.slot_idx ? scalar_read(p.slot_idx, row) : row;
+    const int a = p.nat ? scalar_read(p.nat, row) : 0;
+    int T = p.T;
+    int64_t xrow = (int64_t)row * p.x_seq, orow = (int64_t)row * p.out_seq;
+    if (p.cu) {
+        const int c0 = scalar_read(p.cu, row);
+        T = scalar_read(p.cu, row + 1) - c0;
+        xrow = (int64_t)c0 * p.x_tok;
+        orow = (int64_t)c0 * p.out_tok;
+        if (T < 1 || T > p.T) return;
+    }
+    const int t0 = chunk * TC;
+    if (t0 >= T) return;
+    const int nt = min(TC, T - t0);
+    const int SL = p.state_len;
+    const int nch = min(CHW, p.d_inner - cb);
+    const bool on = lane * CPL < nch;
+    const uint32_t laneV = on ? (uint32_t)(lane * VB) : kOffLane;
+
+    // ---- loads: the chunk's x and halo, the weights (LDS), bias, the commit's inputs
+    __builtin_amdgcn_s_setprio(3);
+    const rsrc_t x_r = make_rsrc((const char *)p.x + (xrow + cb) * XB,
+                                 (uint32_t)(((int64_t)(T - 1) * p.x_tok + nch) * XB));
+    uint32_t X[W1 + TC][XW];   // v[t0 + k] for k >= W1 (x_{t0+k-W1}); k < W1: the x halo
+#pragma unroll
+    for (int j = 0; j < TC; ++j) {
+        if (j < nt) {
+            gload<VB>(x_r, laneV, (uint32_t)((t0 + j) * p.x_tok * XB), X[W1 + j]);
+        } else {
+#pragma unroll
+            for (int w = 0; w < XW; ++w) X[W1 + j][w] = 0u;
+        }
+    }
+#pragma unroll
+    for (int h = 0; h < W1; ++h) {
+        if (chunk > 0) {
+            gload<VB>(x_r, laneV, (uint32_t)((t0 - W1 + h) * p.x_tok * XB), X[h]);
+        } else {
+#pragma unroll
+            for (int w = 0; w < XW; ++w) X[h][w] = 0u;
+        }
+    }
+    const int w_off = CHW * SL * SB;   // past chunk 0's state region
+    {
+        const rsrc_t w_r = make_rsrc((const char *)p.weight + (int64_t)cb * D * XB,
+                                     (uint32_t)(nch * D * XB));
+        const int wchunks = nch * D * XB / 16;   // exact: nch * XB is a multiple of 16
+        constexpr int WJ = (CHW * D * XB / 16 + kWave - 1) / kWave;
+#pragma unroll
+        for (int j = 0; j < WJ; ++j) {
+            const int q = j * kWave + lane;
+            if (j * kWave < wchunks)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    w_r, (lds_void_t *)(lds + w_off + j * kWave * 16), 16,
+                    q < wchunks ? (uint32_t)q * 16u : kOffLane, 0, 0, kKeep);
+        }
+    }
+    uint32_t br[XW];
+#pragma unroll
+    for (int w = 0; w < XW; ++w) br[w] = 0u;
+    if (p.bias) {
+        const rsrc_t b_r = make_rsrc((const char *)p.bias + (int64_t)cb * XB, (uint32_t)(nch * XB));
+        gload<VB, kKeep>(b_r, laneV, 0, br);
+    }
+    // chunk 0 commits v[T .. T+W1-1]: x_{T-W1+j}, or start-window column T+j (T < W1)
+    uint32_t cx[W1][XW];
+#pragma unroll
+    for (int j = 0; j < W1; ++j) {
+        if (chunk == 0 && T - W1 + j >= 0) {
+            gload<VB>(x_r, laneV, (uint32_t)((T - W1 + j) * p.x_tok * XB), cx[j]);
+        } else {
+#pragma unroll
+            for (int w = 0; w < XW; ++w) cx[j][w] = 0u;
+        }
+    }
+    // Padded rows (slot -1), and rows whose slot or offset would address outside the
+    // buffers, write nothing; the loads above stay in bounds - wait for them and leave.
+    if (slot < 0 || slot >= p.n_slots || a < 0 || a > SL - W1) {
+        __builtin_amdgcn_s_waitcnt(0);
+        return;
+    }
+    const rsrc_t st_r = make_rsrc((char *)p.state + ((int64_t)slot * p.state_slot + (int64_t)cb * SL) * SB,
+                                  (uint32_t)(nch * SL * SB));
+    const int rchunks = nch * SL * SB / 16;
+    if (chunk == 0) region_load(st_r, lds, rchunks, lane);   // the whole region, through LDS
+    __builtin_amdgcn_s_setprio(0);
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): the weights have landed
+    lds_barrier();
+
+    uint32_t wr[XW * D];   // the lane's weights [CPL][D] (zeros past d_inner)
+    lds_read_run<VB * D>(lds + w_off + lane * VB * D, wr);
+#pragma unroll
+    for (int w = 0; w < XW * D; ++w) wr[w] = on ? wr[w] : 0u;
+    float wv[CPL][D];
+    float bv[CPL];
+#pragma unroll
+    for (int ch = 0; ch < CPL; ++ch) {
+#pragma unroll
+        for (int w = 0; w < D; ++w) wv[ch][w] = elem_val<XB>(wr, ch * D + w);
+        bv[ch] = elem_val<XB>(br, ch);
+    }
+    // the halo v[t0 .. t0+W1-1] as state-typed bits: the start window (chunk 0), else x
+    uint32_t hs[W1][CPL];
+#pragma unroll
+    for (int j = 0; j < W1; ++j)
+#pragma unroll
+        for (int ch = 0; ch < CPL; ++ch)
+            hs[j][ch] = chunk == 0 ? (on ? lds_get<SB>(lds + ((lane * CPL + ch) * SL + a + j) * SB) : 0u)
+                                   : x_to_state_bits<XB, SB>(elem_bits<XB>(X[j], ch));
+    // v[t0 + k], k compile-time: the halo (exact in either type) or x
+    auto val = [&](int k, int ch) -> float {
+        if (k < W1) {
+            const uint32_t bits = hs[k < W1 ? k : 0][ch];
+            return SB == 4 ? __uint_as_float(bits) : __uint_as_float(bits << 16);
+        }
+        return elem_val<XB>(X[k], ch);
+    };
+    auto sbits = [&](int k, int ch) -> uint32_t {
+        return k < W1 ? hs[k < W1 ? k : 0][ch] : x_to_state_bits<XB, SB>(elem_bits<XB>(X[k], ch));
+    };
+
+    // ---- conv + SiLU + per-head L2 -> out (one branch-free chunk)
+    float y[TC][CPL];
+#pragma unroll
+    for (int g = 0; g < TC; ++g)
+#pragma unroll
+        for (int ch = 0; ch < CPL; ++ch) {
+            float acc = bv[ch];
+#pragma unroll
+            for (int w = 0; w < D; ++w) acc = __builtin_fmaf(wv[ch][w], val(g + w, ch), acc);
+            y[g][ch] = silu(acc);
+        }
+    if (cb < p.qk) {   // uniform: this wavefront holds q|k channels
+        const bool lane_l2 = lane * CPL + cb < p.qk;
+        float ss[TC];
+#pragma unroll
+        for (int g = 0; g < TC; ++g) {
+            ss[g] = 0.0f;
+#pragma unroll
+            for (int ch = 0; ch < CPL; ++ch) ss[g] = __builtin_fmaf(y[g][ch], y[g][ch], ss[g]);
+        }
+        group_sums<TC>(ss, p.head_lanes_log2);
+#pragma unroll
+        for (int g = 0; g < TC; ++g) {
+            const float sc = lane_l2 ? __builtin_amdgcn_rsqf(ss[g] + p.eps) : 1.0f;
+#pragma unroll
+            for (int ch = 0; ch < CPL; ++ch) y[g][ch] *= sc;
+        }
+    }
+    const rsrc_t o_r = make_rsrc((char *)p.out + (orow + cb) * XB,
+                                 (uint32_t)(((int64_t)(T - 1) * p.out_tok + nch) * XB));
+#pragma unroll
+    for (int g = 0; g < TC; ++g) {
+        if (g < nt) {
+            uint32_t o[XW];
+            if constexpr (XB == 4) {
+#pragma unroll
+                for (int ch = 0; ch < CPL; ++ch) o[ch] = __float_as_uint(y[g][ch]);
+            } else {
+                typedef float f2 __attribute__((ext_vector_type(2)));
+                typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+#pragma unroll
+                for (int w = 0; w < XW; ++w) {
+                    f2 pr = {y[g][2 * w], y[g][2 * w + 1]};
+                    o[w] = __builtin_bit_cast(uint32_t, __builtin_convertvector(pr, b2));
+                }
+            }
+            gstore<VB>(o_r, laneV, (uint32_t)((t0 + g) * p.out_tok * XB), o);
+        }
+    }
+
+    // ---- chunk 0: the committed window into the staged region, which leaves whole
+    if (chunk == 0) {
+        uint32_t e[CPL][W1];
+#pragma unroll
+        for (int j = 0; j < W1; ++j) {
+            const int m = T + j;   // v index; m < W1: start-window column m
+#pragma unroll
+            for (int ch = 0; ch < CPL; ++ch) {
+                uint32_t v = x_to_state_bits<XB, SB>(elem_bits<XB>(cx[j], ch));
+#pragma unroll
+                for (int q = 0; q < W1; ++q)
+                    if (m == q) v = hs[q][ch];
+                e[ch][j] = v;
+            }
+        }
+        put_window<SB, W1>(lds, SL, on, lane, e);
+        lds_barrier();
+        lds_to_global(lds, rchunks, st_r, 0, lane);
+    }
+
+    // ---- dense snapshots of the chunk's tokens: snapshot t = v[t+1 .. t+W1]; the
+    // wavefront's [nch, W1] slab is contiguous and leaves through one of two
+    // alternating LDS slabs in lane-contiguous 16-byte units
+    constexpr int SLAB = CHW * W1 * SB;
+    char *slabs = lds + w_off + lds_dma_span(CHW * D * XB);
+    const int slab_chunks = nch * W1 * SB / 16;   // exact: nch * SB is a multiple of 16
+    const rsrc_t snap_r = make_rsrc(
+        (char *)p.win + ((int64_t)slot * p.win_slot + (int64_t)cb * W1) * SB,
+        (uint32_t)(((int64_t)(T - 1) * p.d_inner * W1 + (int64_t)nch * W1) * SB));
+#pragma unroll
+    for (int g = 0; g < TC; ++g) {
+        if (g < nt) {
+            uint32_t run[RUNW];   // [CPL][W1], channel-major
+#pragma unroll
+            for (int w = 0; w < RUNW; ++w) {
+                if constexpr (SB == 4) {
+                    run[w] = sbits(g + 1 + w % W1, w / W1);
+                } else {
+                    const int e0 = 2 * w, e1 = 2 * w + 1;
+                    run[w] = sbits(g + 1 + e0 % W1, e0 / W1) | (sbits(g + 1 + e1 % W1, e1 / W1) << 16);
+                }
+            }
+            char *slab = slabs + (g & 1) * SLAB;
+            lds_write_run<RUNB>(slab + lane * RUNB, run);
+            lds_barrier();
+            lds_to_global(slab, slab_chunks, snap_r, (uint32_t)((t0 + g) * p.d_inner * W1 * SB), lane);
+        }
+    }
+}
+
 // ---- separate per-head L2 over q|k -------------------------------------------------------
 
 template <int XB>
@@ -412,6 +662,16 @@ const void *restore_for(int d_conv) {
 }
 
 template <int XB, int SB>
+const void *split_for(int d_conv) {
+    switch (d_conv) {
+        case 2: return (const void *)cv_split_kernel<XB, SB, 2, kSplitChunk>;
+        case 3: return (const void *)cv_split_kernel<XB, SB, 3, kSplitChunk>;
+        case 4: return (const void *)cv_split_kernel<XB, SB, 4, kSplitChunk>;
+        default: return nullptr;
+    }
+}
+
+template <int XB, int SB>
 const void *prefill_for(int d_conv) {
     switch (d_conv) {
         case 2: return (const void *)cv_prefill_kernel<XB, SB, 2, kPrefillChunk>;
@@ -433,6 +693,13 @@ const void *pick_restore(int state_bytes, int d_conv, int layout) {
         if (layout == kRows) return restore_for<2, kRows>(d_conv);
         if (layout == kRowsT) return restore_for<2, kRowsT>(d_conv);
     }
+    return nullptr;
+}
+
+const void *pick_split(int x_bytes, int state_bytes, int d_conv) {
+    if (x_bytes == 4 && state_bytes == 4) return split_for<4, 4>(d_conv);
+    if (x_bytes == 2 && state_bytes == 2) return split_for<2, 2>(d_conv);
+    if (x_bytes == 2 && state_bytes == 4) return split_for<2, 4>(d_conv);
     return nullptr;
 }
 

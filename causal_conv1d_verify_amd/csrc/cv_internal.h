@@ -33,7 +33,13 @@ struct KernelArgs {
     int32_t channel_blocks;    // workgroups per row
     int32_t head_lanes_log2;   // log2(lanes per L2 head); unused when qk == 0
     float eps;
+    int32_t token_chunks;      // token-split verify: workgroups per (row, channel block)
 };
+
+// Token-split verify (dense windows): tokens per wavefront, and the grids it serves -
+// fewer wavefronts than this when each row's tokens stay in one wavefront.
+constexpr int kSplitChunk = 4;
+constexpr int64_t kSplitBelowWaves = 1024;
 
 // What the host decided to launch.
 struct Plan {
@@ -41,7 +47,8 @@ struct Plan {
     int tree;                  // per-token parents (dense windows)
     int x_bytes, state_bytes;  // element sizes: (4,4), (2,2) or (2,4)
     int d_conv;                // 2..4
-    int token_bucket;          // 1,2,4,8,16,24,32 >= T
+    int token_bucket;          // 1,2,4,8,16,24,32 >= T; kSplitChunk when split
+    int token_chunks;          // wavefronts per (row, channel block) along T
     int channels_per_lane;     // kChannelsPerLane
     int channel_blocks;
     int64_t workgroups;
@@ -115,6 +122,7 @@ CV_DECLARE_PICKERS(2, 4)
 #undef CV_DECLARE_PICKERS
 
 const void *pick_restore(int state_bytes, int d_conv, int layout);
+const void *pick_split(int x_bytes, int state_bytes, int d_conv);
 const void *pick_prefill(int x_bytes, int state_bytes, int d_conv);
 const void *pick_l2(int x_bytes);
 

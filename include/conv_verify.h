@@ -92,7 +92,7 @@
 extern "C" {
 #endif
 
-#define CONV_VERIFY_ABI_VERSION 2
+#define CONV_VERIFY_ABI_VERSION 3
 
 /* Only the entry points below are exported from the shared library. */
 #define CV_API __attribute__((visibility("default")))
@@ -255,14 +255,17 @@ CV_API int conv_qk_l2norm(const cv_shape_t *shape, int64_t n_rows, int64_t row_s
  * pointers are not examined).  Lets a caller or a test check, on the host, what the
  * kernel and its grid will assume. */
 typedef struct cv_launch_info {
-    int64_t workgroups;        /* 1-D grid: n_seq * channel_blocks                        */
+    int64_t workgroups;        /* 1-D grid: n_seq * channel_blocks * token_chunks         */
     int32_t threads;           /* per workgroup: one 64-lane wavefront                     */
     int32_t channel_blocks;    /* ceil(d_inner / channels_per_wave)                        */
     int32_t channels_per_wave; /* 64 lanes * channels per lane                             */
     int32_t channels_per_lane; /* 16 bytes of x per lane per token                         */
-    int32_t token_bucket;      /* compile-time token capacity of the chosen kernel (>= T)  */
+    int32_t token_bucket;      /* compile-time tokens per workgroup (>= T unless split)    */
     int32_t lds_bytes;         /* dynamic LDS per workgroup                                */
     int32_t head_lanes;        /* lanes per L2 head (0 when qk_channels == 0)              */
+    int32_t token_chunks;      /* workgroups per (row, channel block) along T: 1, or       */
+                               /* ceil(T / token_bucket) when a small grid of dense-window */
+                               /* chain verify spreads each row's tokens over wavefronts   */
 } cv_launch_info_t;
 
 /* variant: a cv_layout_t, or CV_VARIANT_TREE for conv_verify_update_tree.  Returns

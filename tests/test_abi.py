@@ -187,11 +187,19 @@ def test_launch_geometry_of_workloads(key):
     assert info.channels_per_lane == cpl and info.threads == 64
     assert info.channels_per_wave == 64 * cpl
     assert info.channel_blocks == -(-wl.d_inner // (64 * cpl))
-    # the grid covers every (row, channel block) exactly once
-    assert info.workgroups == wl.n_seq * info.channel_blocks
+    # the grid covers every (row, channel block, token chunk) exactly once
+    assert info.workgroups == wl.n_seq * info.channel_blocks * info.token_chunks
     assert info.channel_blocks * info.channels_per_wave >= wl.d_inner
     assert (info.channel_blocks - 1) * info.channels_per_wave < wl.d_inner
-    assert info.token_bucket >= wl.T and info.token_bucket < 2 * wl.T + 1
+    assert info.token_bucket * info.token_chunks >= wl.T
+    assert info.token_bucket * (info.token_chunks - 1) < wl.T
+    plain = wl.n_seq * info.channel_blocks
+    split = wl.layout == "dense" and plain < 1024 and wl.T >= 8
+    assert (info.token_chunks > 1) == split, (plain, wl.T)
+    if split:
+        assert info.token_bucket == 4
+    else:
+        assert info.token_bucket >= wl.T and info.token_bucket < 2 * wl.T + 1
     assert info.head_lanes * cpl == wl.head_dim
     # while loading: the weights (in whole 1 KiB load widths), then the state region
     # over the same bytes
@@ -200,7 +208,12 @@ def test_launch_geometry_of_workloads(key):
         later = wl.row_cols * (64 * cpl * sb + 16)
     else:
         later = 64 * cpl * wl.win_cols * sb * (2 if wl.T > 1 else 1)
-    assert info.lds_bytes == max(first, later) <= 65536
+    if split:   # chunk 0's state region, the weights, two snapshot slabs
+        first = 64 * cpl * wl.state_len * sb + -(-(64 * cpl * wl.d_conv * xb) // 1024) * 1024
+        later = 2 * 64 * cpl * wl.win_cols * sb
+        assert info.lds_bytes == first + later
+    else:
+        assert info.lds_bytes == max(first, later) <= 65536
 
 
 _CHILD = r"""

@@ -170,6 +170,36 @@ def test_prefill(wl):
     gh.compare_general(p.results(), gh.oracle_general(inp), inp)
 
 
+# Dense-window chain verify on a grid of fewer than 1024 wavefronts (T >= 8) spreads each
+# row's tokens over wavefronts of 4 tokens; one row more and the same shape takes the
+# one-wavefront-per-row kernel.  Both sides of that edge, with offsets and padded rows.
+SPLIT_EDGE = [c(f"split_edge_n{n}_T{T}", n_seq=n, d_inner=1024, qk_channels=512, head_dim=128,
+                T=T, accept_offsets=True, permute_slots=True, pad_frac=0.1, extra_slots=1)
+              for n in (255, 256) for T in (8, 13)]
+
+
+@pytest.mark.parametrize("wl", SPLIT_EDGE, ids=[w.name for w in SPLIT_EDGE])
+def test_split_edge(wl):
+    import causal_conv1d_verify_amd as cv
+    import causal_conv1d_verify_amd._lib as L
+
+    inp = workloads.make_inputs(wl)
+    p = gh.GeneralProblem(inp)
+    d, T = wl.d_inner, wl.T
+    shape = L.CvShape(n_seq=wl.n_seq, T=T, d_inner=d, d_conv=wl.d_conv, qk_channels=wl.qk_channels,
+                      head_dim=wl.head_dim, l2_eps=wl.l2_eps, x_dtype=L.CV_BF16,
+                      state_dtype=L.CV_BF16, n_slots=wl.n_slots, state_len=wl.state_len,
+                      x_seq_stride=p.x.stride(0), x_tok_stride=p.x.stride(1),
+                      out_seq_stride=p.out.stride(0), out_tok_stride=p.out.stride(1),
+                      state_slot_stride=p.conv_state.stride(0),
+                      win_slot_stride=p.windows.stride(0))
+    info = cv.conv_verify_describe("dense", shape)
+    assert (info.token_chunks > 1) == (wl.n_seq * 4 < 1024)
+    _say(wl.name, "token_chunks", info.token_chunks)
+    p.verify()
+    gh.compare_general(p.results(), gh.oracle_general(inp), inp)
+
+
 # LDS past 64 KiB (a gfx950 workgroup may take up to 160 KiB): fp32 state rows of 120
 # columns make a 120 KiB state region, so the weights' direct global->LDS loads, the
 # packed-row image and the restore's state region all land beyond the first 64 KiB.
