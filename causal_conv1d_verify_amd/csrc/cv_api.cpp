@@ -178,6 +178,8 @@ int plan_verify(int layout, bool tree, bool packed, const cv_shape_t *s, cvimpl:
     // Token split (dense windows, chain verify): on a grid too small to fill the chip,
     // each row's tokens are spread over ceil(T / kSplitChunk) wavefronts per channel
     // block.  Their LDS: chunk 0's state region, the weights, two snapshot slabs.
+    // Tree verify splits the same way along its own 4-token chunks (buckets past 8),
+    // each wavefront still building the row's whole v tile.
     int chunks = 1;
     int64_t split_lds = 0;
     if (layout == cvimpl::kDense && !tree && wg < cvimpl::kSplitBelowWaves &&
@@ -185,18 +187,21 @@ int plan_verify(int layout, bool tree, bool packed, const cv_shape_t *s, cvimpl:
         split_lds = region + cvimpl::lds_dma_span(kChw * s->d_conv * xb) + 2 * (int64_t)kChw * W1 * sb;
         if (split_lds <= kMaxLds) chunks = (s->T + cvimpl::kSplitChunk - 1) / cvimpl::kSplitChunk;
     }
+    const bool tree_split = tree && wg < cvimpl::kSplitBelowWaves && tb > 8;
+    if (tree_split) chunks = (s->T + 3) / 4;
 
     plan->layout = layout;
     plan->tree = tree ? 1 : 0;
     plan->x_bytes = xb;
     plan->state_bytes = sb;
     plan->d_conv = s->d_conv;
-    plan->token_bucket = chunks > 1 ? cvimpl::kSplitChunk : tb;
+    const bool dense_split = chunks > 1 && !tree;
+    plan->token_bucket = dense_split ? cvimpl::kSplitChunk : tb;
     plan->token_chunks = chunks;
     plan->channels_per_lane = cvimpl::kChannelsPerLane;
     plan->channel_blocks = (int)blocks;
     plan->workgroups = wg * chunks;
-    plan->lds_bytes = (int)(chunks > 1 ? split_lds : lds);
+    plan->lds_bytes = (int)(dense_split ? split_lds : lds);
     plan->head_lanes = head_lanes;
     return CV_OK;
 }
@@ -205,7 +210,7 @@ const void *pick_verify(const cvimpl::Plan &plan) {
     using namespace cvimpl;
     const int d = plan.d_conv, tb = plan.token_bucket;
     const int v = plan.tree ? 3 : plan.layout;
-    if (plan.token_chunks > 1) return pick_split(plan.x_bytes, plan.state_bytes, d);
+    if (plan.token_chunks > 1 && !plan.tree) return pick_split(plan.x_bytes, plan.state_bytes, d);
 #define CV_PICK_FOR(xb, sb)                                  \
     switch (v) {                                             \
         case 0: return pick_kernel_##xb##_##sb##_0(d, tb);   \

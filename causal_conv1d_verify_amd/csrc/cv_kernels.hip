@@ -56,13 +56,24 @@ __global__ __launch_bounds__(kWave) void cv_verify_kernel(KernelArgs p) {
     constexpr int RUNB = CPL * W1 * SB;       // bytes of a lane's [CPL][W1] window run
     constexpr int RUNW = RUNB / 4;
     constexpr int P = tile_pitch(SB);         // bytes per LDS tile row
+    // Tokens go in chunks with no branch inside a chunk: buckets up to 8 are one chunk;
+    // larger ones use chunks of 4, which bounds the registers and the work past T.
+    constexpr int G = TB <= 8 ? TB : 4;
 
     extern __shared__ uint4 lds_raw[];
     char *lds = (char *)lds_raw;
 
     const int lane = threadIdx.x;
-    const int row = (int)(blockIdx.x / (unsigned)p.channel_blocks);
-    const int cb = (int)(blockIdx.x - (unsigned)row * (unsigned)p.channel_blocks) * CHW;
+    const int r2 = (int)(blockIdx.x / (unsigned)p.channel_blocks);
+    const int cb = (int)(blockIdx.x - (unsigned)r2 * (unsigned)p.channel_blocks) * CHW;
+    // Tree verify on a small grid spreads a row's token chunks over p.token_chunks
+    // wavefronts: each one builds the row's whole v tile (a token's ancestors may be
+    // any earlier token) and computes and writes only its own chunk of tokens.
+    int row = r2, chunk = 0;
+    if constexpr (TREE) {
+        row = r2 / p.token_chunks;
+        chunk = r2 - row * p.token_chunks;
+    }
 
     // The row's slot and offset are read now (scalar loads) and tested once the loads
     // that do not depend on them are on their way.
@@ -79,6 +90,9 @@ __global__ __launch_bounds__(kWave) void cv_verify_kernel(KernelArgs p) {
         xrow = (int64_t)c0 * p.x_tok;
         orow = (int64_t)c0 * p.out_tok;
         if (T < 1 || T > p.T) return;
+    }
+    if constexpr (TREE) {
+        if (chunk * G >= T) return;   // a split row's chunk past its tokens
     }
     const int SL = p.state_len;
     const int nch = min(CHW, p.d_inner - cb);   // channels of this wavefront
@@ -338,15 +352,14 @@ __global__ __launch_bounds__(kWave) void cv_verify_kernel(KernelArgs p) {
     const bool lane_l2 = lane * CPL + cb < p.qk;
     const rsrc_t o_r = make_rsrc((char *)p.out + (orow + cb) * XB,
                                  (uint32_t)(((int64_t)(T - 1) * p.out_tok + nch) * XB));
-    // Tokens go in chunks with no branch inside a chunk: x past T reads as zeros and
-    // those tokens are computed but never stored.  The chunk's exponentials,
-    // reciprocals and cross-lane sums are then independent and overlap.  Buckets up
-    // to 8 are one chunk; larger ones use chunks of 4, which bounds the registers and
-    // the work spent past T.
-    constexpr int G = TB <= 8 ? TB : 4;
+    // Tokens go in chunks of G with no branch inside a chunk: x past T reads as zeros
+    // and those tokens are computed but never stored.  The chunk's exponentials,
+    // reciprocals and cross-lane sums are then independent and overlap.
+    // tree, split: this wavefront's chunk only (the chunks are the G-token chunks)
+    auto mine = [&](int t) { return !TREE || p.token_chunks == 1 || t / G == chunk; };
 #pragma unroll
     for (int t0 = 0; t0 < TB; t0 += G) {
-        if (t0 < T) {   // uniform guard; the loops are fully unrolled
+        if (t0 < T && mine(t0)) {   // uniform guard; the loops are fully unrolled
             float y[G][CPL];
             uint32_t tv[TREE ? G : 1][W1][SW];   // tree: the taps before x_t, from the tile
             if constexpr (TREE) {
@@ -595,7 +608,7 @@ __global__ __launch_bounds__(kWave) void cv_verify_kernel(KernelArgs p) {
             (uint32_t)(((int64_t)(T - 1) * p.d_inner * W1 + (int64_t)nch * W1) * SB));
 #pragma unroll
         for (int t = 0; t < TB; ++t) {
-            if (t < T) {
+            if (t < T && mine(t)) {
                 char *slab = lds + TILE + (t & 1) * SLAB;
                 uint32_t run[RUNW];
                 if constexpr (TREE) {

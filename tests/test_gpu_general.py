@@ -92,6 +92,11 @@ for xd, sd in (("f32", "f32"), ("bf16", "f32")):
                    x_dtype=xd, state_dtype=sd, tree=True, accept_offsets=True))
 TREES.append(c("tree_packed", n_seq=6, d_inner=1032, qk_channels=512, head_dim=128, T=12,
                tree=True, varlen=True, accept_offsets=True, permute_slots=True, pad_frac=0.2))
+# small grids spread a tree row's 4-token chunks over wavefronts; 256 rows x 4 channel
+# blocks is the first grid that keeps one wavefront per row
+for n in (255, 256):
+    TREES.append(c(f"tree_T17_n{n}", n_seq=n, d_inner=1024, qk_channels=512, head_dim=128,
+                   T=17, tree=True, accept_offsets=True, permute_slots=True, pad_frac=0.1))
 
 
 @pytest.mark.parametrize("wl", TREES, ids=[w.name for w in TREES])
