@@ -39,6 +39,8 @@ def _fresh(p, inp):
 CASES = [
     workloads.custom("g_dedup", n_seq=6, d_inner=2048, qk_channels=1024, head_dim=128, T=8,
                      layout="dedup", accept_offsets=True, permute_slots=True, pad_frac=0.2),
+    workloads.custom("g_dense_split", n_seq=6, d_inner=1032, qk_channels=512, head_dim=128,
+                     T=17, layout="dense", accept_offsets=True, permute_slots=True, pad_frac=0.2),
     workloads.custom("g_packed_tree", n_seq=6, d_inner=1032, qk_channels=512, head_dim=128,
                      T=9, tree=True, varlen=True, permute_slots=True),
     workloads.custom("g_restore", n_seq=6, d_inner=1032, qk_channels=512, head_dim=128, T=8,
