@@ -151,7 +151,16 @@ int plan_verify(int layout, bool tree, bool packed, const cv_shape_t *s, cvimpl:
     const int64_t region = (int64_t)kChw * s->state_len * sb;
     const int64_t slabs = (int64_t)kChw * W1 * sb * (s->T > 1 ? 2 : 1);
     int64_t later = 0;
-    if (layout == cvimpl::kRows) later = (int64_t)(s->T + s->d_conv - 2) * pitch;
+    if (layout == cvimpl::kRows) {
+        // T a bucket and fixed rows: the compile-time-length path stages the row block
+        // [channels, T+D-2] lane by lane (in halves past kRowsStageBytes); otherwise the
+        // tile of T+D-2 sequence positions
+        const int64_t block = (int64_t)kChw * (s->T + s->d_conv - 2) * sb;
+        if (!packed && s->T == tb)
+            later = block > cvimpl::kRowsStageBytes ? block / 2 : block;
+        else
+            later = (int64_t)(s->T + s->d_conv - 2) * pitch;
+    }
     // While the loads are in flight the weights [channels, d_conv] sit at the start of
     // LDS; the state region is written over them once they are read, and (packed rows,
     // rows layout) the stored row block follows the region.  Both are filled by direct
@@ -198,6 +207,9 @@ int plan_verify(int layout, bool tree, bool packed, const cv_shape_t *s, cvimpl:
     const bool dense_split = chunks > 1 && !tree;
     plan->token_bucket = dense_split ? cvimpl::kSplitChunk : tb;
     plan->token_chunks = chunks;
+    // The 16-token bucket's lean build (5 wavefronts per SIMD, a few spilled registers)
+    // pays only where LDS lets 5 wavefronts per SIMD be resident.
+    plan->lean = tb == 16 && !dense_split && lds <= cvimpl::kRowsStageBytes;
     plan->channels_per_lane = cvimpl::kChannelsPerLane;
     plan->channel_blocks = (int)blocks;
     plan->workgroups = wg * chunks;
@@ -208,15 +220,15 @@ int plan_verify(int layout, bool tree, bool packed, const cv_shape_t *s, cvimpl:
 
 const void *pick_verify(const cvimpl::Plan &plan) {
     using namespace cvimpl;
-    const int d = plan.d_conv, tb = plan.token_bucket;
+    const int d = plan.d_conv, tb = plan.token_bucket, lean = plan.lean;
     const int v = plan.tree ? 3 : plan.layout;
     if (plan.token_chunks > 1 && !plan.tree) return pick_split(plan.x_bytes, plan.state_bytes, d);
 #define CV_PICK_FOR(xb, sb)                                  \
     switch (v) {                                             \
-        case 0: return pick_kernel_##xb##_##sb##_0(d, tb);   \
-        case 1: return pick_kernel_##xb##_##sb##_1(d, tb);   \
-        case 2: return pick_kernel_##xb##_##sb##_2(d, tb);   \
-        case 3: return pick_kernel_##xb##_##sb##_3(d, tb);   \
+        case 0: return pick_kernel_##xb##_##sb##_0(d, tb, lean); \
+        case 1: return pick_kernel_##xb##_##sb##_1(d, tb, lean); \
+        case 2: return pick_kernel_##xb##_##sb##_2(d, tb, lean); \
+        case 3: return pick_kernel_##xb##_##sb##_3(d, tb, lean); \
         default: return nullptr;                             \
     }
     if (plan.x_bytes == 4 && plan.state_bytes == 4) { CV_PICK_FOR(4, 4) }

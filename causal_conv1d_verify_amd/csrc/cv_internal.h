@@ -36,6 +36,11 @@ struct KernelArgs {
     int32_t token_chunks;      // token-split verify: workgroups per (row, channel block)
 };
 
+// The rows layout's compile-time-length path stages a wavefront's row block in LDS in
+// halves when the block is larger than this: 8 KiB per wavefront leaves LDS for 20
+// resident wavefronts per compute unit (5 per SIMD).
+constexpr int kRowsStageBytes = 8192;
+
 // Token-split verify (dense windows): tokens per wavefront, and the grids it serves -
 // fewer wavefronts than this when each row's tokens stay in one wavefront.
 constexpr int kSplitChunk = 4;
@@ -49,6 +54,7 @@ struct Plan {
     int d_conv;                // 2..4
     int token_bucket;          // 1,2,4,8,16,24,32 >= T; kSplitChunk when split
     int token_chunks;          // wavefronts per (row, channel block) along T
+    int lean;                  // 16-token bucket built for 5 wavefronts per SIMD
     int channels_per_lane;     // kChannelsPerLane
     int channel_blocks;
     int64_t workgroups;
@@ -110,12 +116,12 @@ constexpr int lds_dma_span(int bytes) {
 
 // Kernel pickers, one per compiled (x bytes, state bytes, variant) object - variant 0
 // dense, 1 rows, 2 time-major rows, 3 tree: the kernel for (d_conv, token bucket), or
-// nullptr.
+// nullptr.  lean: the 16-token bucket's build for 5 resident wavefronts per SIMD.
 #define CV_DECLARE_PICKERS(xb, sb)                                   \
-    const void *pick_kernel_##xb##_##sb##_0(int d_conv, int token_bucket); \
-    const void *pick_kernel_##xb##_##sb##_1(int d_conv, int token_bucket); \
-    const void *pick_kernel_##xb##_##sb##_2(int d_conv, int token_bucket); \
-    const void *pick_kernel_##xb##_##sb##_3(int d_conv, int token_bucket);
+    const void *pick_kernel_##xb##_##sb##_0(int d_conv, int token_bucket, int lean); \
+    const void *pick_kernel_##xb##_##sb##_1(int d_conv, int token_bucket, int lean); \
+    const void *pick_kernel_##xb##_##sb##_2(int d_conv, int token_bucket, int lean); \
+    const void *pick_kernel_##xb##_##sb##_3(int d_conv, int token_bucket, int lean);
 CV_DECLARE_PICKERS(4, 4)
 CV_DECLARE_PICKERS(2, 2)
 CV_DECLARE_PICKERS(2, 4)

@@ -43,8 +43,13 @@ namespace {
 
 // LAYOUT: kDense, kRows or kRowsT (rollback windows); TREE: per-token parents (dense
 // windows, nothing committed).  Packed rows (p.cu) are a runtime option of every variant.
-template <int XB, int SB, int D, int TB, int LAYOUT, bool TREE>
-__global__ __launch_bounds__(kWave) void cv_verify_kernel(KernelArgs p) {
+// WPE > 0 asks the register allocator for WPE resident wavefronts per SIMD: the
+// 16-token bucket is built a second time that way (at most 102 VGPRs, a few spilled),
+// for launches whose LDS allows 5 per SIMD, so that a 128-row grid stays resident in
+// one generation.
+template <int XB, int SB, int D, int TB, int LAYOUT, bool TREE, int WPE>
+__global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(WPE > 0 ? WPE : 1)))
+void cv_verify_kernel(KernelArgs p) {
     static_assert(!TREE || LAYOUT == kDense, "tree windows are dense");
     constexpr int CPL = kChannelsPerLane;     // channels per lane
     constexpr int CHW = kWave * CPL;          // channels per wavefront
@@ -475,28 +480,40 @@ __global__ __launch_bounds__(kWave) void cv_verify_kernel(KernelArgs p) {
             // Row length known at compile time: each lane assembles its channels' rows
             // ([CPL][LC], contiguous in the row layout) in registers into LDS at the
             // same offsets, and the wavefront streams the block out lane-contiguously.
+            // A block over kRowsStageBytes goes in two halves of the lanes, so the
+            // wavefront's LDS does not cap the number of resident wavefronts.
             constexpr int LC = TB + W1 - 1;
             constexpr int LANEB = CPL * LC * SB;   // bytes of a lane's rows
             constexpr int CW = LANEB / 4;
             constexpr int PIECE = (LANEB % 16 == 0) ? 16 : 8;
-            char *mine = lds + lane * LANEB;
+            constexpr int HALVES = kWave * LANEB > kRowsStageBytes ? 2 : 1;
+            constexpr int HL = kWave / HALVES;     // lanes per half
 #pragma unroll
-            for (int q = 0; q < CW / (PIECE / 4); ++q) {
-                uint32_t w4[PIECE / 4];
+            for (int h = 0; h < HALVES; ++h) {
+                if (lane / HL == h) {
+                    char *mine = lds + (lane % HL) * LANEB;
 #pragma unroll
-                for (int i = 0; i < PIECE / 4; ++i) {
-                    const int wd = (PIECE / 4) * q + i;
-                    if constexpr (SB == 4) {
-                        w4[i] = sbits(wd % LC + 1, wd / LC);
-                    } else {
-                        const int e0 = 2 * wd, e1 = 2 * wd + 1;
-                        w4[i] = sbits(e0 % LC + 1, e0 / LC) | (sbits(e1 % LC + 1, e1 / LC) << 16);
+                    for (int q = 0; q < CW / (PIECE / 4); ++q) {
+                        uint32_t w4[PIECE / 4];
+#pragma unroll
+                        for (int i = 0; i < PIECE / 4; ++i) {
+                            const int wd = (PIECE / 4) * q + i;
+                            if constexpr (SB == 4) {
+                                w4[i] = sbits(wd % LC + 1, wd / LC);
+                            } else {
+                                const int e0 = 2 * wd, e1 = 2 * wd + 1;
+                                w4[i] = sbits(e0 % LC + 1, e0 / LC) | (sbits(e1 % LC + 1, e1 / LC) << 16);
+                            }
+                        }
+                        lds_write_run<PIECE>(mine + PIECE * q, w4);
                     }
                 }
-                lds_write_run<PIECE>(mine + PIECE * q, w4);
+                lds_barrier();
+                const int c0 = h * HL * CPL;       // the half's first channel
+                const int hch = min(HL * CPL, nch - c0);
+                if (hch > 0) lds_to_global(lds, hch * LC * SB / 16, row_r, (uint32_t)(c0 * LC * SB), lane);
+                if (h + 1 < HALVES) lds_barrier();
             }
-            lds_barrier();
-            lds_to_global(lds, nch * LC * SB / 16, row_r, 0, lane);
         } else {
             // Tile row r holds v[r+1] for the wavefront's channels; rows 0..W1-2 come
             // from the initial window, the rest are x_0..x_{T-1}.
@@ -645,15 +662,17 @@ __global__ __launch_bounds__(kWave) void cv_verify_kernel(KernelArgs p) {
 // so the instantiations build in parallel; each object exports one picker over
 // (d_conv, token bucket).
 template <int XB, int SB, int D, int LAYOUT, bool TREE>
-const void *pick_bucket(int tb) {
+const void *pick_bucket(int tb, bool lean) {
     switch (tb) {
-        case 1: return (const void *)cv_verify_kernel<XB, SB, D, 1, LAYOUT, TREE>;
-        case 2: return (const void *)cv_verify_kernel<XB, SB, D, 2, LAYOUT, TREE>;
-        case 4: return (const void *)cv_verify_kernel<XB, SB, D, 4, LAYOUT, TREE>;
-        case 8: return (const void *)cv_verify_kernel<XB, SB, D, 8, LAYOUT, TREE>;
-        case 16: return (const void *)cv_verify_kernel<XB, SB, D, 16, LAYOUT, TREE>;
-        case 24: return (const void *)cv_verify_kernel<XB, SB, D, 24, LAYOUT, TREE>;
-        case 32: return (const void *)cv_verify_kernel<XB, SB, D, 32, LAYOUT, TREE>;
+        case 1: return (const void *)cv_verify_kernel<XB, SB, D, 1, LAYOUT, TREE, 0>;
+        case 2: return (const void *)cv_verify_kernel<XB, SB, D, 2, LAYOUT, TREE, 0>;
+        case 4: return (const void *)cv_verify_kernel<XB, SB, D, 4, LAYOUT, TREE, 0>;
+        case 8: return (const void *)cv_verify_kernel<XB, SB, D, 8, LAYOUT, TREE, 0>;
+        case 16:
+            return lean ? (const void *)cv_verify_kernel<XB, SB, D, 16, LAYOUT, TREE, 5>
+                        : (const void *)cv_verify_kernel<XB, SB, D, 16, LAYOUT, TREE, 0>;
+        case 24: return (const void *)cv_verify_kernel<XB, SB, D, 24, LAYOUT, TREE, 0>;
+        case 32: return (const void *)cv_verify_kernel<XB, SB, D, 32, LAYOUT, TREE, 0>;
         default: return nullptr;
     }
 }
@@ -667,13 +686,13 @@ const void *pick_bucket(int tb) {
 #define CV_PICK_NAME(xb, sb, v) pick_kernel_##xb##_##sb##_##v
 #define CV_PICK(xb, sb, v) CV_PICK_NAME(xb, sb, v)
 
-const void *CV_PICK(CV_XB, CV_SB, CV_VARIANT)(int d_conv, int token_bucket) {
+const void *CV_PICK(CV_XB, CV_SB, CV_VARIANT)(int d_conv, int token_bucket, int lean) {
     constexpr int layout = CV_VARIANT == 3 ? kDense : CV_VARIANT;
     constexpr bool tree = CV_VARIANT == 3;
     switch (d_conv) {
-        case 2: return pick_bucket<CV_XB, CV_SB, 2, layout, tree>(token_bucket);
-        case 3: return pick_bucket<CV_XB, CV_SB, 3, layout, tree>(token_bucket);
-        case 4: return pick_bucket<CV_XB, CV_SB, 4, layout, tree>(token_bucket);
+        case 2: return pick_bucket<CV_XB, CV_SB, 2, layout, tree>(token_bucket, lean != 0);
+        case 3: return pick_bucket<CV_XB, CV_SB, 3, layout, tree>(token_bucket, lean != 0);
+        case 4: return pick_bucket<CV_XB, CV_SB, 4, layout, tree>(token_bucket, lean != 0);
         default: return nullptr;
     }
 }

@@ -205,7 +205,10 @@ def test_launch_geometry_of_workloads(key):
     # over the same bytes
     first = max(64 * cpl * wl.state_len * sb, -(-(64 * cpl * wl.d_conv * xb) // 1024) * 1024)
     if wl.layout == "dedup":
-        later = wl.row_cols * (64 * cpl * sb + 16)
+        # T is a bucket here: the row block [256, T+D-2] is staged lane by lane, in two
+        # halves when it is over 8 KiB
+        block = 64 * cpl * wl.row_cols * sb
+        later = block // 2 if block > 8192 else block
     else:
         later = 64 * cpl * wl.win_cols * sb * (2 if wl.T > 1 else 1)
     if split:   # chunk 0's state region, the weights, two snapshot slabs
