@@ -44,7 +44,7 @@ def _verify_case(wl, layout=None):
 c = workloads.custom
 LAYOUT_CASES = []
 for layout in ("dense", "dedup", "dedup_t"):
-    for T in (1, 3, 8, 9, 17, 32):
+    for T in (1, 3, 8, 9, 16, 17, 32):
         LAYOUT_CASES.append(c(f"{layout}_T{T}", n_seq=3, d_inner=1032, qk_channels=512,
                               head_dim=128, T=T, layout=layout, accept_offsets=T > 1,
                               permute_slots=True, pad_frac=0.25, extra_slots=2))
@@ -55,6 +55,19 @@ for layout in ("dense", "dedup", "dedup_t"):
     for D in (2, 3):
         LAYOUT_CASES.append(c(f"{layout}_D{D}", n_seq=4, d_inner=520, qk_channels=256,
                               head_dim=64, d_conv=D, T=6, layout=layout, accept_offsets=True))
+
+
+# the rows layout's compile-time-length path: a 16-token block of bf16 rows staged in
+# two halves with the 5-wavefront build (state_len 3), the same with the regular build
+# (state_len 18), and 8 tokens of fp32 rows (a 10 KiB block, in halves)
+LAYOUT_CASES += [
+    c("dedup_T16_lean", n_seq=3, d_inner=1032, qk_channels=512, head_dim=128, T=16,
+      layout="dedup", permute_slots=True, pad_frac=0.25, extra_slots=2),
+    c("dedup_T16_wide_state", n_seq=3, d_inner=1032, qk_channels=512, head_dim=128, T=16,
+      layout="dedup", state_len=18, permute_slots=True),
+    c("dedup_T8_f32_rows", n_seq=3, d_inner=1032, qk_channels=512, head_dim=128, T=8,
+      layout="dedup", state_dtype="f32", accept_offsets=True, permute_slots=True),
+]
 
 
 @pytest.mark.parametrize("wl", LAYOUT_CASES, ids=[w.name for w in LAYOUT_CASES])

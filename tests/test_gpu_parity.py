@@ -29,7 +29,7 @@ def _say(*a):
     print("[case]", *a, flush=True)
 
 
-@pytest.mark.parametrize("key", [0, 1, 2, 3, 4, "4b", "4s"])
+@pytest.mark.parametrize("key", [0, 1, 2, 3, 4, "4b", "4s", "t16"])
 def test_workload_full_size(key):
     wl = workloads.WORKLOADS[key]
     _say(key, wl)
