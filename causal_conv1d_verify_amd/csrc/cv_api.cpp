@@ -191,25 +191,31 @@ int plan_verify(int layout, bool tree, bool packed, const cv_shape_t *s, cvimpl:
     // each wavefront still building the row's whole v tile.
     int chunks = 1;
     int64_t split_lds = 0;
-    if (layout == cvimpl::kDense && !tree && wg < cvimpl::kSplitBelowWaves &&
-        s->T >= 2 * cvimpl::kSplitChunk) {
+    const int64_t dense_chunks = (s->T + cvimpl::kSplitChunk - 1) / cvimpl::kSplitChunk;
+    if (layout == cvimpl::kDense && !tree && s->T >= 2 * cvimpl::kSplitChunk &&
+        wg * dense_chunks <= cvimpl::kSplitMaxWaves) {
         split_lds = region + cvimpl::lds_dma_span(kChw * s->d_conv * xb) + 2 * (int64_t)kChw * W1 * sb;
-        if (split_lds <= kMaxLds) chunks = (s->T + cvimpl::kSplitChunk - 1) / cvimpl::kSplitChunk;
+        if (split_lds <= kMaxLds) chunks = (int)dense_chunks;
     }
-    const bool tree_split = tree && wg < cvimpl::kSplitBelowWaves && tb > 8;
+    const bool tree_split = tree && wg < cvimpl::kTreeSplitBelowWaves && tb > 8;
     if (tree_split) chunks = (s->T + 3) / 4;
+    // Row layouts: chunk 0 of a split row keeps the copies (state commit, row block).
+    const bool rows_split = (layout == cvimpl::kRows || layout == cvimpl::kRowsT) && !tree &&
+                            (tb == 8 || tb == 16) && s->T > 4 &&
+                            wg * ((s->T + 3) / 4) <= cvimpl::kRowsSplitMaxWaves;
+    if (rows_split) chunks = (s->T + 3) / 4;
 
     plan->layout = layout;
     plan->tree = tree ? 1 : 0;
     plan->x_bytes = xb;
     plan->state_bytes = sb;
     plan->d_conv = s->d_conv;
-    const bool dense_split = chunks > 1 && !tree;
+    const bool dense_split = chunks > 1 && layout == cvimpl::kDense && !tree;
     plan->token_bucket = dense_split ? cvimpl::kSplitChunk : tb;
     plan->token_chunks = chunks;
     // The 16-token bucket's lean build (5 wavefronts per SIMD, a few spilled registers)
     // pays only where LDS lets 5 wavefronts per SIMD be resident.
-    plan->lean = tb == 16 && !dense_split && lds <= cvimpl::kRowsStageBytes;
+    plan->lean = tb == 16 && chunks == 1 && lds <= cvimpl::kRowsStageBytes;
     plan->channels_per_lane = cvimpl::kChannelsPerLane;
     plan->channel_blocks = (int)blocks;
     plan->workgroups = wg * chunks;
@@ -221,14 +227,16 @@ int plan_verify(int layout, bool tree, bool packed, const cv_shape_t *s, cvimpl:
 const void *pick_verify(const cvimpl::Plan &plan) {
     using namespace cvimpl;
     const int d = plan.d_conv, tb = plan.token_bucket, lean = plan.lean;
+    const int split = plan.token_chunks > 1 ? 1 : 0;
     const int v = plan.tree ? 3 : plan.layout;
-    if (plan.token_chunks > 1 && !plan.tree) return pick_split(plan.x_bytes, plan.state_bytes, d);
+    if (plan.token_chunks > 1 && !plan.tree && plan.layout == cvimpl::kDense)
+        return pick_split(plan.x_bytes, plan.state_bytes, d);
 #define CV_PICK_FOR(xb, sb)                                  \
     switch (v) {                                             \
-        case 0: return pick_kernel_##xb##_##sb##_0(d, tb, lean); \
-        case 1: return pick_kernel_##xb##_##sb##_1(d, tb, lean); \
-        case 2: return pick_kernel_##xb##_##sb##_2(d, tb, lean); \
-        case 3: return pick_kernel_##xb##_##sb##_3(d, tb, lean); \
+        case 0: return pick_kernel_##xb##_##sb##_0(d, tb, lean, split); \
+        case 1: return pick_kernel_##xb##_##sb##_1(d, tb, lean, split); \
+        case 2: return pick_kernel_##xb##_##sb##_2(d, tb, lean, split); \
+        case 3: return pick_kernel_##xb##_##sb##_3(d, tb, lean, split); \
         default: return nullptr;                             \
     }
     if (plan.x_bytes == 4 && plan.state_bytes == 4) { CV_PICK_FOR(4, 4) }

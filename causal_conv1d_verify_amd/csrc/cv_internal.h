@@ -41,10 +41,18 @@ struct KernelArgs {
 // resident wavefronts per compute unit (5 per SIMD).
 constexpr int kRowsStageBytes = 8192;
 
-// Token-split verify (dense windows): tokens per wavefront, and the grids it serves -
-// fewer wavefronts than this when each row's tokens stay in one wavefront.
+// Token-split verify (dense windows): tokens per wavefront, and the grids it serves:
+// at most kSplitMaxWaves wavefronts once split (measured at d 8192: T 8 gains up to 64
+// rows, T 17 up to 32 rows, e.g. 10.4 -> 5.8 us at 8 rows; larger splits ran slower).
+// Tree verify splits grids of fewer than kTreeSplitBelowWaves one-row wavefronts.
 constexpr int kSplitChunk = 4;
-constexpr int64_t kSplitBelowWaves = 1024;
+constexpr int64_t kSplitMaxWaves = 5120;
+constexpr int64_t kTreeSplitBelowWaves = 1024;
+// Row layouts split a row's 4-token chunks (buckets 8 and 16) when the split grid has at
+// most this many wavefronts (chunk 0 keeps the copies, since a row block is shared by
+// all tokens).  Measured at d 10240: T 8 gains up to 32 rows (5.9 -> 5.1 us at 8 rows),
+// T 16 up to 16 rows (8.2 -> 6.5 us at 8 rows); larger splits ran slower.
+constexpr int64_t kRowsSplitMaxWaves = 2560;
 
 // What the host decided to launch.
 struct Plan {
@@ -116,12 +124,13 @@ constexpr int lds_dma_span(int bytes) {
 
 // Kernel pickers, one per compiled (x bytes, state bytes, variant) object - variant 0
 // dense, 1 rows, 2 time-major rows, 3 tree: the kernel for (d_conv, token bucket), or
-// nullptr.  lean: the 16-token bucket's build for 5 resident wavefronts per SIMD.
+// nullptr.  lean: the 16-token bucket's build for 5 resident wavefronts per SIMD;
+// split: the row layouts' token-split build (buckets 8 and 16).
 #define CV_DECLARE_PICKERS(xb, sb)                                   \
-    const void *pick_kernel_##xb##_##sb##_0(int d_conv, int token_bucket, int lean); \
-    const void *pick_kernel_##xb##_##sb##_1(int d_conv, int token_bucket, int lean); \
-    const void *pick_kernel_##xb##_##sb##_2(int d_conv, int token_bucket, int lean); \
-    const void *pick_kernel_##xb##_##sb##_3(int d_conv, int token_bucket, int lean);
+    const void *pick_kernel_##xb##_##sb##_0(int d_conv, int token_bucket, int lean, int split); \
+    const void *pick_kernel_##xb##_##sb##_1(int d_conv, int token_bucket, int lean, int split); \
+    const void *pick_kernel_##xb##_##sb##_2(int d_conv, int token_bucket, int lean, int split); \
+    const void *pick_kernel_##xb##_##sb##_3(int d_conv, int token_bucket, int lean, int split);
 CV_DECLARE_PICKERS(4, 4)
 CV_DECLARE_PICKERS(2, 2)
 CV_DECLARE_PICKERS(2, 4)

@@ -47,10 +47,15 @@ namespace {
 // 16-token bucket is built a second time that way (at most 102 VGPRs, a few spilled),
 // for launches whose LDS allows 5 per SIMD, so that a 128-row grid stays resident in
 // one generation.
-template <int XB, int SB, int D, int TB, int LAYOUT, bool TREE, int WPE>
+// SPLIT (row layouts, buckets 8 and 16): on a small grid a row's 4-token chunks go to
+// p.token_chunks wavefronts.  Each computes out for its own chunk only; chunk 0 also
+// does every copy (the state commit and the row block, which is shared by all the
+// row's tokens), so the arithmetic on each wavefront's path is a quarter to a half.
+template <int XB, int SB, int D, int TB, int LAYOUT, bool TREE, int WPE, bool SPLIT>
 __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(WPE > 0 ? WPE : 1)))
 void cv_verify_kernel(KernelArgs p) {
     static_assert(!TREE || LAYOUT == kDense, "tree windows are dense");
+    static_assert(!SPLIT || (!TREE && LAYOUT != kDense), "dense chains split in cv_split_kernel");
     constexpr int CPL = kChannelsPerLane;     // channels per lane
     constexpr int CHW = kWave * CPL;          // channels per wavefront
     constexpr int W1 = D - 1;                 // window columns
@@ -63,7 +68,7 @@ void cv_verify_kernel(KernelArgs p) {
     constexpr int P = tile_pitch(SB);         // bytes per LDS tile row
     // Tokens go in chunks with no branch inside a chunk: buckets up to 8 are one chunk;
     // larger ones use chunks of 4, which bounds the registers and the work past T.
-    constexpr int G = TB <= 8 ? TB : 4;
+    constexpr int G = TB <= 8 && !SPLIT ? TB : 4;
 
     extern __shared__ uint4 lds_raw[];
     char *lds = (char *)lds_raw;
@@ -75,10 +80,11 @@ void cv_verify_kernel(KernelArgs p) {
     // wavefronts: each one builds the row's whole v tile (a token's ancestors may be
     // any earlier token) and computes and writes only its own chunk of tokens.
     int row = r2, chunk = 0;
-    if constexpr (TREE) {
+    if constexpr (TREE || SPLIT) {
         row = r2 / p.token_chunks;
         chunk = r2 - row * p.token_chunks;
     }
+    const bool copier = !SPLIT || chunk == 0;   // this wavefront does the copies
 
     // The row's slot and offset are read now (scalar loads) and tested once the loads
     // that do not depend on them are on their way.
@@ -96,7 +102,7 @@ void cv_verify_kernel(KernelArgs p) {
         orow = (int64_t)c0 * p.out_tok;
         if (T < 1 || T > p.T) return;
     }
-    if constexpr (TREE) {
+    if constexpr (TREE || SPLIT) {
         if (chunk * G >= T) return;   // a split row's chunk past its tokens
     }
     const int SL = p.state_len;
@@ -115,7 +121,9 @@ void cv_verify_kernel(KernelArgs p) {
     uint32_t X[TB][XW];   // x_t for the lane's channels
 #pragma unroll
     for (int t = 0; t < TB; ++t) {
-        if (t < T) {
+        // a split row's later chunks need only their tokens and the W1 before them
+        const bool need = copier || (t >= chunk * G - W1 && t < chunk * G + G);
+        if (t < T && need) {
             gload<VB>(x_r, laneV, (uint32_t)(t * p.x_tok * XB), X[t]);
         } else {
 #pragma unroll
@@ -174,7 +182,8 @@ void cv_verify_kernel(KernelArgs p) {
     const rsrc_t st_r = make_rsrc((const char *)p.state + ((int64_t)slot * p.state_slot +
                                                            (int64_t)cb * SL) * SB,
                                   (uint32_t)(nch * SL * SB));
-    const int rchunks = nch * SL * SB / 16;   // exact: nch * SB is a multiple of 16
+    // exact: nch * SB is a multiple of 16; a split row's other chunks take no state
+    const int rchunks = copier ? nch * SL * SB / 16 : 0;
     // chunks per lane, all in flight at once up to RJ; longer regions go in rounds
     constexpr int RJ = (W1 * SB + 3) / 4 > 12 ? (W1 * SB + 3) / 4 : 12;
     uint32_t sreg[RJ][4];
@@ -220,7 +229,7 @@ void cv_verify_kernel(KernelArgs p) {
     // store).  The wavefront later overwrites its columns below T+W1-1 there and writes
     // the block back whole: the columns past them keep their bits, and every store
     // stays a coalesced 16-byte one.
-    const bool row_image = LAYOUT == kRows && p.cu != nullptr && T < p.T;
+    const bool row_image = LAYOUT == kRows && p.cu != nullptr && T < p.T && copier;
     const int img_off = CHW * SL * SB;
     if constexpr (LAYOUT == kRows) {
         if (row_image) {
@@ -361,7 +370,7 @@ void cv_verify_kernel(KernelArgs p) {
     // and those tokens are computed but never stored.  The chunk's exponentials,
     // reciprocals and cross-lane sums are then independent and overlap.
     // tree, split: this wavefront's chunk only (the chunks are the G-token chunks)
-    auto mine = [&](int t) { return !TREE || p.token_chunks == 1 || t / G == chunk; };
+    auto mine = [&](int t) { return (!TREE && !SPLIT) || p.token_chunks == 1 || t / G == chunk; };
 #pragma unroll
     for (int t0 = 0; t0 < TB; t0 += G) {
         if (t0 < T && mine(t0)) {   // uniform guard; the loops are fully unrolled
@@ -427,6 +436,9 @@ void cv_verify_kernel(KernelArgs p) {
                 }
             }
         }
+    }
+    if constexpr (SPLIT) {
+        if (!copier) return;   // its chunk of out is stored; the copies are chunk 0's
     }
     if constexpr (!TREE) {
         // ---- committed window -> conv_state -----------------------------------------------------
@@ -662,17 +674,24 @@ void cv_verify_kernel(KernelArgs p) {
 // so the instantiations build in parallel; each object exports one picker over
 // (d_conv, token bucket).
 template <int XB, int SB, int D, int LAYOUT, bool TREE>
-const void *pick_bucket(int tb, bool lean) {
+const void *pick_bucket(int tb, bool lean, bool split) {
+    if constexpr (!TREE && LAYOUT != kDense) {
+        if (split) {
+            if (tb == 8) return (const void *)cv_verify_kernel<XB, SB, D, 8, LAYOUT, TREE, 0, true>;
+            if (tb == 16) return (const void *)cv_verify_kernel<XB, SB, D, 16, LAYOUT, TREE, 0, true>;
+            return nullptr;
+        }
+    }
     switch (tb) {
-        case 1: return (const void *)cv_verify_kernel<XB, SB, D, 1, LAYOUT, TREE, 0>;
-        case 2: return (const void *)cv_verify_kernel<XB, SB, D, 2, LAYOUT, TREE, 0>;
-        case 4: return (const void *)cv_verify_kernel<XB, SB, D, 4, LAYOUT, TREE, 0>;
-        case 8: return (const void *)cv_verify_kernel<XB, SB, D, 8, LAYOUT, TREE, 0>;
+        case 1: return (const void *)cv_verify_kernel<XB, SB, D, 1, LAYOUT, TREE, 0, false>;
+        case 2: return (const void *)cv_verify_kernel<XB, SB, D, 2, LAYOUT, TREE, 0, false>;
+        case 4: return (const void *)cv_verify_kernel<XB, SB, D, 4, LAYOUT, TREE, 0, false>;
+        case 8: return (const void *)cv_verify_kernel<XB, SB, D, 8, LAYOUT, TREE, 0, false>;
         case 16:
-            return lean ? (const void *)cv_verify_kernel<XB, SB, D, 16, LAYOUT, TREE, 5>
-                        : (const void *)cv_verify_kernel<XB, SB, D, 16, LAYOUT, TREE, 0>;
-        case 24: return (const void *)cv_verify_kernel<XB, SB, D, 24, LAYOUT, TREE, 0>;
-        case 32: return (const void *)cv_verify_kernel<XB, SB, D, 32, LAYOUT, TREE, 0>;
+            return lean ? (const void *)cv_verify_kernel<XB, SB, D, 16, LAYOUT, TREE, 5, false>
+                        : (const void *)cv_verify_kernel<XB, SB, D, 16, LAYOUT, TREE, 0, false>;
+        case 24: return (const void *)cv_verify_kernel<XB, SB, D, 24, LAYOUT, TREE, 0, false>;
+        case 32: return (const void *)cv_verify_kernel<XB, SB, D, 32, LAYOUT, TREE, 0, false>;
         default: return nullptr;
     }
 }
@@ -686,13 +705,13 @@ const void *pick_bucket(int tb, bool lean) {
 #define CV_PICK_NAME(xb, sb, v) pick_kernel_##xb##_##sb##_##v
 #define CV_PICK(xb, sb, v) CV_PICK_NAME(xb, sb, v)
 
-const void *CV_PICK(CV_XB, CV_SB, CV_VARIANT)(int d_conv, int token_bucket, int lean) {
+const void *CV_PICK(CV_XB, CV_SB, CV_VARIANT)(int d_conv, int token_bucket, int lean, int split) {
     constexpr int layout = CV_VARIANT == 3 ? kDense : CV_VARIANT;
     constexpr bool tree = CV_VARIANT == 3;
     switch (d_conv) {
-        case 2: return pick_bucket<CV_XB, CV_SB, 2, layout, tree>(token_bucket, lean != 0);
-        case 3: return pick_bucket<CV_XB, CV_SB, 3, layout, tree>(token_bucket, lean != 0);
-        case 4: return pick_bucket<CV_XB, CV_SB, 4, layout, tree>(token_bucket, lean != 0);
+        case 2: return pick_bucket<CV_XB, CV_SB, 2, layout, tree>(token_bucket, lean != 0, split != 0);
+        case 3: return pick_bucket<CV_XB, CV_SB, 3, layout, tree>(token_bucket, lean != 0, split != 0);
+        case 4: return pick_bucket<CV_XB, CV_SB, 4, layout, tree>(token_bucket, lean != 0, split != 0);
         default: return nullptr;
     }
 }

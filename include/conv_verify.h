@@ -265,8 +265,9 @@ typedef struct cv_launch_info {
     int32_t head_lanes;        /* lanes per L2 head (0 when qk_channels == 0)              */
     int32_t token_chunks;      /* workgroups per (row, channel block) along T: 1, or, on a */
                                /* small grid, ceil(T / 4) - each row's tokens spread over  */
-                               /* wavefronts (dense-window chain verify: token_bucket 4;   */
-                               /* tree verify: each one computes its 4-token chunk)        */
+                               /* wavefronts, each computing its 4-token chunk (dense      */
+                               /* chain verify: token_bucket 4; row layouts: chunk 0 also  */
+                               /* writes the row block and the state)                      */
 } cv_launch_info_t;
 
 /* variant: a cv_layout_t, or CV_VARIANT_TREE for conv_verify_update_tree.  Returns

@@ -194,8 +194,12 @@ def test_launch_geometry_of_workloads(key):
     assert info.token_bucket * info.token_chunks >= wl.T
     assert info.token_bucket * (info.token_chunks - 1) < wl.T
     plain = wl.n_seq * info.channel_blocks
-    split = wl.layout == "dense" and plain < 1024 and wl.T >= 8
-    assert (info.token_chunks > 1) == split, (plain, wl.T)
+    chunks = -(-wl.T // 4)
+    # token split: dense chains when the split grid has at most 5120 wavefronts; row
+    # layouts (buckets 8 and 16) at most 2560
+    split = wl.layout == "dense" and wl.T >= 8 and plain * chunks <= 5120
+    rows_split = wl.layout != "dense" and 4 < wl.T <= 16 and plain * chunks <= 2560
+    assert (info.token_chunks > 1) == (split or rows_split), (plain, wl.T)
     if split:
         assert info.token_bucket == 4
     else:

@@ -188,12 +188,12 @@ def test_prefill(wl):
     gh.compare_general(p.results(), gh.oracle_general(inp), inp)
 
 
-# Dense-window chain verify on a grid of fewer than 1024 wavefronts (T >= 8) spreads each
-# row's tokens over wavefronts of 4 tokens; one row more and the same shape takes the
+# Dense-window chain verify (T >= 8) spreads each row's tokens over wavefronts of 4 tokens
+# when that grid has at most 5120 wavefronts; one row more and the same shape takes the
 # one-wavefront-per-row kernel.  Both sides of that edge, with offsets and padded rows.
 SPLIT_EDGE = [c(f"split_edge_n{n}_T{T}", n_seq=n, d_inner=1024, qk_channels=512, head_dim=128,
                 T=T, accept_offsets=True, permute_slots=True, pad_frac=0.1, extra_slots=1)
-              for n in (255, 256) for T in (8, 13)]
+              for T, edge in ((8, 640), (13, 320)) for n in (edge, edge + 1)]
 
 
 @pytest.mark.parametrize("wl", SPLIT_EDGE, ids=[w.name for w in SPLIT_EDGE])
@@ -212,10 +212,25 @@ def test_split_edge(wl):
                       state_slot_stride=p.conv_state.stride(0),
                       win_slot_stride=p.windows.stride(0))
     info = cv.conv_verify_describe("dense", shape)
-    assert (info.token_chunks > 1) == (wl.n_seq * 4 < 1024)
+    assert (info.token_chunks > 1) == (wl.n_seq * 4 * -(-T // 4) <= 5120)
     _say(wl.name, "token_chunks", info.token_chunks)
     p.verify()
     gh.compare_general(p.results(), gh.oracle_general(inp), inp)
+
+
+# Row layouts split a row's 4-token chunks when the split grid has at most 2560
+# wavefronts (buckets 8 and 16; chunk 0 keeps the state commit and the row block); one
+# row more and the same shape takes the one-wavefront-per-row kernel.
+ROWS_EDGE = [c(f"rows_edge_{layout}_n{n}_T{T}", n_seq=n, d_inner=1024, qk_channels=512,
+               head_dim=128, T=T, layout=layout, accept_offsets=True, permute_slots=True,
+               pad_frac=0.1, extra_slots=1)
+             for layout in ("dedup", "dedup_t") for T, edge in ((8, 320), (13, 160))
+             for n in (edge, edge + 1)]
+
+
+@pytest.mark.parametrize("wl", ROWS_EDGE, ids=[w.name for w in ROWS_EDGE])
+def test_rows_split_edge(wl):
+    _verify_case(wl)
 
 
 # LDS past 64 KiB (a gfx950 workgroup may take up to 160 KiB): fp32 state rows of 120
