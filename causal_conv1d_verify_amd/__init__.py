@@ -17,7 +17,10 @@ Tensors (all on one GPU; bf16 or fp32 as the ABI allows):
                  innermost stride 1, other strides free
     weight       [d_inner, d_conv]       contiguous
     bias         [d_inner] or None
-    conv_state   [n_slots, d_inner, state_len]   contiguous below the slot dimension
+    conv_state   [n_slots, d_inner, state_len], either contiguous below the slot
+                 dimension (channel-major) or the transposed view of a time-major
+                 [n_slots, state_len, >= d_inner] buffer (stride 1 along channels,
+                 state_col_stride = the column stride)
     windows      by layout, contiguous below the slot dimension:
                    "dense"   [n_slots, T, d_inner, d_conv-1]
                    "dedup"   [n_slots, d_inner, T+d_conv-2]   (rows, channel-major)
@@ -118,11 +121,17 @@ def _window_T(layout: str, windows, d_inner: int, d_conv: int) -> int:
     return T
 
 
-def _check_state(conv_state, d_inner):
-    if conv_state.dim() != 3 or conv_state.shape[1] != d_inner or \
-            not _contiguous_below_first(conv_state):
-        raise ValueError("conv_state must be [n_slots, d_inner, state_len], contiguous "
-                         "below the slot dimension")
+def _check_state(conv_state, d_inner) -> int:
+    """Validates conv_state's view; returns the ABI's state_col_stride (0: channel-major)."""
+    if conv_state.dim() == 3 and conv_state.shape[1] == d_inner:
+        if _contiguous_below_first(conv_state):
+            return 0
+        # time-major storage [n_slots, state_len, >= d_inner] seen as [n_slots, d, state_len]
+        if conv_state.stride(1) == 1 and conv_state.stride(2) >= d_inner:
+            return conv_state.stride(2)
+    raise ValueError("conv_state must be [n_slots, d_inner, state_len], contiguous below the "
+                     "slot dimension, or the [n_slots, d_inner, state_len] view of a time-major "
+                     "[n_slots, state_len, >= d_inner] buffer")
 
 
 def _verify_args(layout, tree, x, weight, bias, conv_state, out, windows, qk_channels,
@@ -145,7 +154,7 @@ def _verify_args(layout, tree, x, weight, bias, conv_state, out, windows, qk_cha
     for t in (weight, bias, out):
         if t is not None and t.dtype != x.dtype:
             raise TypeError("x, weight, bias and out must share one dtype")
-    _check_state(conv_state, d_inner)
+    state_col = _check_state(conv_state, d_inner)
     if windows.dtype != conv_state.dtype:
         raise TypeError("conv_state and the window buffer must share one dtype")
     T = _window_T(layout, windows, d_inner, d_conv)
@@ -173,7 +182,8 @@ def _verify_args(layout, tree, x, weight, bias, conv_state, out, windows, qk_cha
         head_dim=head_dim, l2_eps=l2_eps, x_dtype=_dtype_code(x),
         state_dtype=_dtype_code(conv_state), n_slots=n_slots, state_len=state_len,
         x_seq_stride=x_seq, x_tok_stride=x_tok, out_seq_stride=out_seq, out_tok_stride=out_tok,
-        state_slot_stride=conv_state.stride(0), win_slot_stride=windows.stride(0))
+        state_slot_stride=conv_state.stride(0), win_slot_stride=windows.stride(0),
+        state_col_stride=state_col)
     h = ctypes.c_void_p(_stream_handle(stream, dev))
     if tree:
         fn = lib.conv_verify_update_tree
@@ -194,7 +204,7 @@ def _restore_args(conv_state, windows, window_index, layout, d_conv, slot_idx, s
     lib = _lib.load()
     dev = _same_gpu(conv_state, windows, window_index, slot_idx)
     d_inner = conv_state.shape[1] if conv_state.dim() == 3 else -1
-    _check_state(conv_state, d_inner)
+    state_col = _check_state(conv_state, d_inner)
     if windows.dtype != conv_state.dtype:
         raise TypeError("conv_state and the window buffer must share one dtype")
     T = _window_T(layout, windows, d_inner, d_conv)
@@ -207,7 +217,7 @@ def _restore_args(conv_state, windows, window_index, layout, d_conv, slot_idx, s
     shape = _lib.CvShape(n_seq=n_seq, T=T, d_inner=d_inner, d_conv=d_conv, x_dtype=dt,
                          state_dtype=dt, n_slots=n_slots, state_len=state_len,
                          state_slot_stride=conv_state.stride(0),
-                         win_slot_stride=windows.stride(0))
+                         win_slot_stride=windows.stride(0), state_col_stride=state_col)
     args = (ctypes.byref(shape), LAYOUTS[layout], _ptr(conv_state), _ptr(windows),
             _ptr(slot_idx), _ptr(window_index), ctypes.c_void_p(_stream_handle(stream, dev)))
     return lib, dev, lib.conv_verify_restore, args, (shape, conv_state, windows, window_index,
@@ -228,7 +238,7 @@ def _prefill_args(x, weight, bias, conv_state, out, cu_seqlens, max_len, slot_id
     for t in (weight, bias, out):
         if t is not None and t.dtype != x.dtype:
             raise TypeError("x, weight, bias and out must share one dtype")
-    _check_state(conv_state, d_inner)
+    state_col = _check_state(conv_state, d_inner)
     n_seq = cu_seqlens.shape[0] - 1
     _int32_vec("cu_seqlens", cu_seqlens, n_seq + 1)
     _int32_vec("slot_idx", slot_idx, n_seq)
@@ -237,7 +247,8 @@ def _prefill_args(x, weight, bias, conv_state, out, cu_seqlens, max_len, slot_id
     shape = _lib.CvShape(n_seq=n_seq, T=max(1, int(max_len)), d_inner=d_inner, d_conv=d_conv,
                          x_dtype=_dtype_code(x), state_dtype=_dtype_code(conv_state),
                          n_slots=n_slots, state_len=state_len, x_tok_stride=x.stride(0),
-                         out_tok_stride=out.stride(0), state_slot_stride=conv_state.stride(0))
+                         out_tok_stride=out.stride(0), state_slot_stride=conv_state.stride(0),
+                         state_col_stride=state_col)
     args = (ctypes.byref(shape), _ptr(x), _ptr(weight), _ptr(bias), _ptr(conv_state),
             _ptr(slot_idx), _ptr(cu_seqlens), _ptr(has_initial_state), _ptr(out),
             ctypes.c_void_p(_stream_handle(stream, dev)))

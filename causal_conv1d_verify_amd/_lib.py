@@ -45,6 +45,7 @@ class CvShape(ctypes.Structure):
         ("out_seq_stride", ctypes.c_int64), ("out_tok_stride", ctypes.c_int64),
         ("state_slot_stride", ctypes.c_int64),
         ("win_slot_stride", ctypes.c_int64),
+        ("state_col_stride", ctypes.c_int64),
     ]
 
 

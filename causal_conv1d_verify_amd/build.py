@@ -30,13 +30,14 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden", "-Wall", "-Wextra
           f"-I{INCLUDE}", f"-I{CSRC}"]
 
 # The verify kernel source is compiled once per (x bytes, state bytes, variant:
-# 0 dense, 1 rows, 2 time-major rows, 3 tree); those objects, the restore / prefill /
-# L2 kernels and the C ABI build in parallel.
+# 0 dense, 1 rows, 2 time-major rows, 3 tree; conv_state layout: 0 channel-major,
+# 1 time-major); those objects, the restore / prefill / L2 kernels and the C ABI build
+# in parallel.
 SOURCES = [
-    ("cv_kernels.hip", f"cv_kernels_{xb}_{sb}_{v}",
+    ("cv_kernels.hip", f"cv_kernels_{xb}_{sb}_{v}_{tm}",
      [f"--offload-arch={ARCH}", *DEVICE_FLAGS, f"-DCV_XB={xb}", f"-DCV_SB={sb}",
-      f"-DCV_VARIANT={v}"])
-    for xb, sb in ((4, 4), (2, 2), (2, 4)) for v in (0, 1, 2, 3)
+      f"-DCV_VARIANT={v}", f"-DCV_TM={tm}"])
+    for tm in (0, 1) for xb, sb in ((4, 4), (2, 2), (2, 4)) for v in (0, 1, 2, 3)
 ] + [("cv_aux_kernels.hip", "cv_aux_kernels", [f"--offload-arch={ARCH}", *DEVICE_FLAGS]),
      ("cv_api.cpp", "cv_api", [])]
 MAX_JOBS = max(1, min(len(SOURCES), int(os.environ.get("MAX_JOBS", os.cpu_count() or 4))))

@@ -61,12 +61,20 @@ int check_common(const cv_shape_t *s, int *xb_out, int *sb_out) {
     if (s->state_slot_stride < 0 || s->win_slot_stride < 0)
         return fail(CV_EINVAL, "negative slot stride");
     const int64_t C = s->d_inner;
-    if (s->n_slots > 1 && s->state_slot_stride < C * s->state_len)
-        return fail(CV_EINVAL, "state_slot_stride (%lld) < d_inner*state_len",
-                    (long long)s->state_slot_stride);
-    if ((s->state_slot_stride * sb) % 16 || (s->win_slot_stride * sb) % 16)
-        return fail(CV_ENOTSUP, "state/window slot strides must be multiples of 16 bytes");
-    if (C * s->state_len * sb > kSpanLimit)
+    const int64_t col = s->state_col_stride;
+    if (col < 0) return fail(CV_EINVAL, "state_col_stride (%lld) < 0", (long long)col);
+    if (col > 0 && col < C)
+        return fail(CV_EINVAL, "state_col_stride (%lld) < d_inner: state columns overlap",
+                    (long long)col);
+    // elements one slot's state spans, in either layout
+    const int64_t state_span = col > 0 ? (int64_t)(s->state_len - 1) * col + C : C * s->state_len;
+    if (s->n_slots > 1 && s->state_slot_stride < state_span)
+        return fail(CV_EINVAL, "state_slot_stride (%lld) < the %lld elements of a slot's state",
+                    (long long)s->state_slot_stride, (long long)state_span);
+    if ((s->state_slot_stride * sb) % 16 || (s->win_slot_stride * sb) % 16 || (col * sb) % 16)
+        return fail(CV_ENOTSUP, "state/window slot and state column strides must be multiples "
+                                "of 16 bytes");
+    if (state_span * sb > kSpanLimit)
         return fail(CV_ENOTSUP, "a slot's state spans more than 2 GiB");
     *xb_out = xb;
     *sb_out = sb;
@@ -148,7 +156,8 @@ int plan_verify(int layout, bool tree, bool packed, const cv_shape_t *s, cvimpl:
     // wavefront's channels) or one or two dense snapshot slabs [channels, D-1] - after
     // the tree's v tile (D-1+bucket rows) in tree verify.
     const int pitch = cvimpl::tile_pitch(sb);
-    const int64_t region = (int64_t)kChw * s->state_len * sb;
+    // (a time-major conv_state moves by columns through registers, not through LDS)
+    const int64_t region = s->state_col_stride ? 0 : (int64_t)kChw * s->state_len * sb;
     const int64_t slabs = (int64_t)kChw * W1 * sb * (s->T > 1 ? 2 : 1);
     int64_t later = 0;
     if (layout == cvimpl::kRows) {
@@ -216,6 +225,7 @@ int plan_verify(int layout, bool tree, bool packed, const cv_shape_t *s, cvimpl:
     // The 16-token bucket's lean build (5 wavefronts per SIMD, a few spilled registers)
     // pays only where LDS lets 5 wavefronts per SIMD be resident.
     plan->lean = tb == 16 && chunks == 1 && lds <= cvimpl::kRowsStageBytes;
+    plan->state_tm = s->state_col_stride != 0;
     plan->channels_per_lane = cvimpl::kChannelsPerLane;
     plan->channel_blocks = (int)blocks;
     plan->workgroups = wg * chunks;
@@ -230,19 +240,22 @@ const void *pick_verify(const cvimpl::Plan &plan) {
     const int split = plan.token_chunks > 1 ? 1 : 0;
     const int v = plan.tree ? 3 : plan.layout;
     if (plan.token_chunks > 1 && !plan.tree && plan.layout == cvimpl::kDense)
-        return pick_split(plan.x_bytes, plan.state_bytes, d);
-#define CV_PICK_FOR(xb, sb)                                  \
-    switch (v) {                                             \
-        case 0: return pick_kernel_##xb##_##sb##_0(d, tb, lean, split); \
-        case 1: return pick_kernel_##xb##_##sb##_1(d, tb, lean, split); \
-        case 2: return pick_kernel_##xb##_##sb##_2(d, tb, lean, split); \
-        case 3: return pick_kernel_##xb##_##sb##_3(d, tb, lean, split); \
-        default: return nullptr;                             \
+        return pick_split(plan.x_bytes, plan.state_bytes, d, plan.state_tm);
+#define CV_PICK_TM(xb, sb, tm)                                      \
+    switch (v) {                                                    \
+        case 0: return pick_kernel_##xb##_##sb##_0_##tm(d, tb, lean, split); \
+        case 1: return pick_kernel_##xb##_##sb##_1_##tm(d, tb, lean, split); \
+        case 2: return pick_kernel_##xb##_##sb##_2_##tm(d, tb, lean, split); \
+        case 3: return pick_kernel_##xb##_##sb##_3_##tm(d, tb, lean, split); \
+        default: return nullptr;                                    \
     }
+#define CV_PICK_FOR(xb, sb) \
+    if (plan.state_tm) { CV_PICK_TM(xb, sb, 1) } else { CV_PICK_TM(xb, sb, 0) }
     if (plan.x_bytes == 4 && plan.state_bytes == 4) { CV_PICK_FOR(4, 4) }
     if (plan.x_bytes == 2 && plan.state_bytes == 2) { CV_PICK_FOR(2, 2) }
     if (plan.x_bytes == 2 && plan.state_bytes == 4) { CV_PICK_FOR(2, 4) }
 #undef CV_PICK_FOR
+#undef CV_PICK_TM
     return nullptr;
 }
 
@@ -309,6 +322,7 @@ int verify(int layout, bool tree, const cv_shape_t *s, const void *x, const void
     a.head_lanes_log2 = hl_log2;
     a.eps = s->l2_eps;
     a.token_chunks = plan.token_chunks;
+    a.state_col = s->state_col_stride;
     return launch(pick_verify(plan), plan.workgroups, plan.lds_bytes, a, stream);
 }
 
@@ -381,7 +395,7 @@ int conv_verify_restore(const cv_shape_t *s, int32_t layout, void *conv_state,
     // are filled by direct global->LDS loads, so their spans are whole load widths
     const int64_t lds =
         (layout == cvimpl::kRows ? cvimpl::lds_dma_span(kChw * (s->T + s->d_conv - 2) * sb) : 0) +
-        cvimpl::lds_dma_span(kChw * s->state_len * sb);
+        (s->state_col_stride ? 0 : cvimpl::lds_dma_span(kChw * s->state_len * sb));
     if (lds > cvimpl::kMaxLds)
         return fail(CV_ENOTSUP, "restore needs %lld bytes of LDS (> %d)", (long long)lds, cvimpl::kMaxLds);
     cvimpl::RestoreArgs a;
@@ -397,7 +411,8 @@ int conv_verify_restore(const cv_shape_t *s, int32_t layout, void *conv_state,
     a.n_slots = s->n_slots;
     a.state_len = s->state_len;
     a.channel_blocks = (int)blocks;
-    return launch(cvimpl::pick_restore(sb, s->d_conv, layout), wg, (int)lds, a, hip_stream);
+    a.state_col = s->state_col_stride;
+    return launch(cvimpl::pick_restore(sb, s->d_conv, layout, s->state_col_stride != 0), wg, (int)lds, a, hip_stream);
 }
 
 int conv_prefill(const cv_shape_t *s, const void *x, const void *weight, const void *bias,
@@ -427,7 +442,8 @@ int conv_prefill(const cv_shape_t *s, const void *x, const void *weight, const v
     if (!slot_idx && s->n_slots < s->n_seq)
         return fail(CV_EINVAL, "n_slots (%d) < n_seq (%d) with identity slots", s->n_slots, s->n_seq);
     // a chunk-0 wavefront's state region, then the weights (direct global->LDS loads)
-    const int64_t lds = (int64_t)kChw * s->state_len * sb + cvimpl::lds_dma_span(kChw * s->d_conv * xb);
+    const int64_t lds = (s->state_col_stride ? 0 : (int64_t)kChw * s->state_len * sb) +
+                        cvimpl::lds_dma_span(kChw * s->d_conv * xb);
     if (lds > cvimpl::kMaxLds)
         return fail(CV_ENOTSUP, "prefill needs %lld bytes of LDS (> %d)", (long long)lds, cvimpl::kMaxLds);
     const int64_t blocks = (C + kChw - 1) / kChw;
@@ -454,7 +470,8 @@ int conv_prefill(const cv_shape_t *s, const void *x, const void *weight, const v
     a.state_len = s->state_len;
     a.channel_blocks = (int)blocks;
     a.chunks = (int)chunks;
-    return launch(cvimpl::pick_prefill(xb, sb, s->d_conv), wg, (int)lds, a, hip_stream);
+    a.state_col = s->state_col_stride;
+    return launch(cvimpl::pick_prefill(xb, sb, s->d_conv, s->state_col_stride != 0), wg, (int)lds, a, hip_stream);
 }
 
 int conv_qk_l2norm(const cv_shape_t *s, int64_t n_rows, int64_t row_stride, void *x,

@@ -74,9 +74,49 @@ __device__ __forceinline__ void put_window(char *region, int SL, bool on, int la
         for (int j = 0; j < W1; ++j) lds_put<SB>(region + ((lane * CPL + ch) * SL + j) * SB, e[ch][j]);
 }
 
+// Time-major conv_state (column k holds the d channels contiguously): column j of the
+// window e[CPL][W1] as the lane's SCB bytes, stored at column j of the slot.
+template <int SB, int W1>
+__device__ __forceinline__ void store_window_columns(rsrc_t r, uint32_t lane_off, int64_t col_bytes,
+                                                     const uint32_t (&e)[CPL][W1]) {
+    constexpr int SW = CPL * SB / 4;
+#pragma unroll
+    for (int j = 0; j < W1; ++j) {
+        uint32_t c[SW];
+#pragma unroll
+        for (int w = 0; w < SW; ++w)
+            c[w] = SB == 4 ? e[w][j] : (e[2 * w][j] | (e[2 * w + 1][j] << 16));
+        gstore<CPL * SB>(r, lane_off, (uint32_t)(j * col_bytes), c);
+    }
+}
+
+// ... and the other way: columns c0 .. c0+W1-1 into e[CPL][W1] (loads in flight; the
+// compiler waits where e is used).
+template <int SB, int W1>
+__device__ __forceinline__ void load_window_columns(rsrc_t r, uint32_t lane_off, int64_t col_bytes,
+                                                    int c0, uint32_t (&e)[CPL][W1]) {
+    constexpr int SW = CPL * SB / 4;
+#pragma unroll
+    for (int j = 0; j < W1; ++j) {
+        uint32_t c[SW];
+        gload<CPL * SB>(r, lane_off, (uint32_t)((c0 + j) * col_bytes), c);
+#pragma unroll
+        for (int ch = 0; ch < CPL; ++ch) e[ch][j] = elem_bits<SB>(c, ch);
+    }
+}
+
+// A slot's time-major state columns as a buffer resource: state_len columns of
+// `col` elements, the wavefront's nch channels at cb.
+template <int SB>
+__device__ __forceinline__ rsrc_t tm_state_rsrc(void *state, int64_t slot_off, int cb, int SL,
+                                                int64_t col, int nch) {
+    return make_rsrc((char *)state + (slot_off + cb) * SB, (uint32_t)(((int64_t)(SL - 1) * col + nch) * SB));
+}
+
 // ---- accepted-prefix restore ------------------------------------------------------------
 
-template <int SB, int D, int LAYOUT>
+// TM: conv_state time-major (p.state_col is the column stride), built separately.
+template <int SB, int D, int LAYOUT, bool TM>
 __global__ __launch_bounds__(kWave) void cv_restore_kernel(RestoreArgs p) {
     constexpr int W1 = D - 1;
     constexpr int SCB = CPL * SB;
@@ -134,15 +174,17 @@ __global__ __launch_bounds__(kWave) void cv_restore_kernel(RestoreArgs p) {
         }
     }
 
-    // the state region: rows wider than the window come in whole first (the window
-    // columns are then replaced in LDS), and the region leaves whole
+    // the state region (channel-major): rows wider than the window come in whole first
+    // (the window columns are then replaced in LDS), and the region leaves whole.
+    // Time-major: the window's W1 columns are stored straight from registers.
     const int SL = p.state_len;
-    const int rchunks = nch * SL * SB / 16;
+    constexpr bool tm = TM;
+    const int rchunks = tm ? 0 : nch * SL * SB / 16;
     char *region = lds + (LAYOUT == kRows ? lds_dma_span(CHW * (p.T + W1 - 1) * SB) : 0);
     const rsrc_t st_r = make_rsrc(
         (char *)p.state + ((int64_t)slot * p.state_slot + (int64_t)cb * SL) * SB,
         (uint32_t)(nch * SL * SB));
-    if (SL > W1) block_to_lds(st_r, region, rchunks, lane);
+    if (SL > W1 && !tm) block_to_lds(st_r, region, rchunks, lane);
     __builtin_amdgcn_s_waitcnt(0);   // every load above has landed (in LDS or VGPRs)
     lds_barrier();
     if constexpr (LAYOUT == kRows) {
@@ -153,6 +195,13 @@ __global__ __launch_bounds__(kWave) void cv_restore_kernel(RestoreArgs p) {
             for (int j = 0; j < W1; ++j)
                 e[ch][j] = on ? lds_get<SB>(lds + ((lane * CPL + ch) * LS + k + j) * SB) : 0u;
     }
+    if constexpr (tm) {
+        const rsrc_t stm_r = tm_state_rsrc<SB>(p.state, (int64_t)slot * p.state_slot, cb, SL,
+                                               p.state_col, nch);
+        store_window_columns<SB, W1>(stm_r, on ? (uint32_t)(lane * SCB) : kOffLane,
+                                     p.state_col * SB, e);
+        return;
+    }
     put_window<SB, W1>(region, SL, on, lane, e);
     lds_barrier();
     lds_to_global(region, rchunks, st_r, 0, lane);
@@ -160,7 +209,7 @@ __global__ __launch_bounds__(kWave) void cv_restore_kernel(RestoreArgs p) {
 
 // ---- prefill conv -----------------------------------------------------------------------
 
-template <int XB, int SB, int D, int TC>
+template <int XB, int SB, int D, int TC, bool TM>
 __global__ __launch_bounds__(kWave) void cv_prefill_kernel(PrefillArgs p) {
     constexpr int W1 = D - 1;
     constexpr int VB = CPL * XB;
@@ -204,7 +253,8 @@ __global__ __launch_bounds__(kWave) void cv_prefill_kernel(PrefillArgs p) {
     // of per-lane tap loads; every chunk's wavefront reads them).
     extern __shared__ uint4 lds_raw[];
     char *lds = (char *)lds_raw;
-    const int w_off = CHW * SL * SB;
+    constexpr bool tm = TM;   // time-major conv_state: nothing of it in LDS
+    const int w_off = tm ? 0 : CHW * SL * SB;
     {
         const rsrc_t w_r = make_rsrc((const char *)p.weight + (int64_t)cb * D * XB,
                                      (uint32_t)(nch * D * XB));
@@ -247,6 +297,25 @@ __global__ __launch_bounds__(kWave) void cv_prefill_kernel(PrefillArgs p) {
                 hs[j][ch] = 0u;
             }
         }
+    } else if constexpr (tm) {
+        // the first chunk reads the window's W1 columns of the time-major state
+        uint32_t e[CPL][W1];
+        if (init) {
+            load_window_columns<SB, W1>(
+                tm_state_rsrc<SB>(p.state, (int64_t)slot * p.state_slot, cb, SL, p.state_col, nch),
+                on ? (uint32_t)(lane * CPL * SB) : kOffLane, p.state_col * SB, 0, e);
+        }
+#pragma unroll
+        for (int ch = 0; ch < CPL; ++ch)
+#pragma unroll
+            for (int j = 0; j < W1; ++j) hs[j][ch] = init ? e[ch][j] : 0u;
+#pragma unroll
+        for (int ch = 0; ch < CPL; ++ch)
+#pragma unroll
+            for (int j = 0; j < W1; ++j) {
+                const uint32_t bits = hs[j][ch];
+                hv[j][ch] = SB == 4 ? __uint_as_float(bits) : __uint_as_float(bits << 16);
+            }
     } else {
         // the first chunk takes the wavefront's state region through LDS (coalesced):
         // its window is the halo, and the region goes back whole with the commit
@@ -353,6 +422,12 @@ __global__ __launch_bounds__(kWave) void cv_prefill_kernel(PrefillArgs p) {
                 e[ch][j] = v;
             }
         }
+        if constexpr (tm) {
+            store_window_columns<SB, W1>(
+                tm_state_rsrc<SB>(p.state, (int64_t)slot * p.state_slot, cb, SL, p.state_col, nch),
+                on ? (uint32_t)(lane * CPL * SB) : kOffLane, p.state_col * SB, e);
+            return;
+        }
         put_window<SB, W1>(lds, SL, on, lane, e);
         lds_barrier();
         lds_to_global(lds, rchunks, st_r, 0, lane);
@@ -370,7 +445,7 @@ __global__ __launch_bounds__(kWave) void cv_prefill_kernel(PrefillArgs p) {
 // window, so a slot's state read and write stay in one wavefront and chunks never
 // race.  (Dense snapshots only: a channel-major row is shared by every chunk of a
 // channel.)  Same arithmetic, same order, same rounding as the verify kernel.
-template <int XB, int SB, int D, int TC>
+template <int XB, int SB, int D, int TC, bool TM>
 __global__ __launch_bounds__(kWave) void cv_split_kernel(KernelArgs p) {
     static_assert(TC >= D - 1, "the halo of a chunk must come from the chunk before");
     constexpr int W1 = D - 1;
@@ -430,7 +505,8 @@ __global__ __launch_bounds__(kWave) void cv_split_kernel(KernelArgs p) {
             for (int w = 0; w < XW; ++w) X[h][w] = 0u;
         }
     }
-    const int w_off = CHW * SL * SB;   // past chunk 0's state region
+    constexpr bool tm = TM;   // time-major conv_state: nothing of it in LDS
+    const int w_off = tm ? 0 : CHW * SL * SB;   // past chunk 0's state region
     {
         const rsrc_t w_r = make_rsrc((const char *)p.weight + (int64_t)cb * D * XB,
                                      (uint32_t)(nch * D * XB));
@@ -471,8 +547,15 @@ __global__ __launch_bounds__(kWave) void cv_split_kernel(KernelArgs p) {
     }
     const rsrc_t st_r = make_rsrc((char *)p.state + ((int64_t)slot * p.state_slot + (int64_t)cb * SL) * SB,
                                   (uint32_t)(nch * SL * SB));
-    const int rchunks = nch * SL * SB / 16;
-    if (chunk == 0) region_load(st_r, lds, rchunks, lane);   // the whole region, through LDS
+    const int rchunks = tm ? 0 : nch * SL * SB / 16;
+    const rsrc_t stm_r = tm_state_rsrc<SB>(p.state, (int64_t)slot * p.state_slot, cb, SL, p.state_col, nch);
+    const uint32_t laneS = on ? (uint32_t)(lane * CPL * SB) : kOffLane;
+    uint32_t tw[CPL][W1];   // time-major: chunk 0's start window, columns a..a+W1-1
+    if constexpr (tm) {
+        if (chunk == 0) load_window_columns<SB, W1>(stm_r, laneS, p.state_col * SB, a, tw);
+    } else {
+        if (chunk == 0) region_load(st_r, lds, rchunks, lane);   // the whole region, through LDS
+    }
     __builtin_amdgcn_s_setprio(0);
     __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): the weights have landed
     lds_barrier();
@@ -495,7 +578,8 @@ __global__ __launch_bounds__(kWave) void cv_split_kernel(KernelArgs p) {
     for (int j = 0; j < W1; ++j)
 #pragma unroll
         for (int ch = 0; ch < CPL; ++ch)
-            hs[j][ch] = chunk == 0 ? (on ? lds_get<SB>(lds + ((lane * CPL + ch) * SL + a + j) * SB) : 0u)
+            hs[j][ch] = chunk == 0 ? (tm ? tw[ch][j]
+                                         : on ? lds_get<SB>(lds + ((lane * CPL + ch) * SL + a + j) * SB) : 0u)
                                    : x_to_state_bits<XB, SB>(elem_bits<XB>(X[j], ch));
     // v[t0 + k], k compile-time: the halo (exact in either type) or x
     auto val = [&](int k, int ch) -> float {
@@ -574,9 +658,13 @@ __global__ __launch_bounds__(kWave) void cv_split_kernel(KernelArgs p) {
                 e[ch][j] = v;
             }
         }
-        put_window<SB, W1>(lds, SL, on, lane, e);
-        lds_barrier();
-        lds_to_global(lds, rchunks, st_r, 0, lane);
+        if constexpr (tm) {
+            store_window_columns<SB, W1>(stm_r, laneS, p.state_col * SB, e);
+        } else {
+            put_window<SB, W1>(lds, SL, on, lane, e);
+            lds_barrier();
+            lds_to_global(lds, rchunks, st_r, 0, lane);
+        }
     }
 
     // ---- dense snapshots of the chunk's tokens: snapshot t = v[t+1 .. t+W1]; the
@@ -651,62 +739,63 @@ __global__ __launch_bounds__(kWave) void cv_l2_kernel(L2Args p) {
     gstore<VB>(x_r, laneV, 0, o);
 }
 
-template <int SB, int LAYOUT>
+template <int SB, int LAYOUT, bool TM>
 const void *restore_for(int d_conv) {
     switch (d_conv) {
-        case 2: return (const void *)cv_restore_kernel<SB, 2, LAYOUT>;
-        case 3: return (const void *)cv_restore_kernel<SB, 3, LAYOUT>;
-        case 4: return (const void *)cv_restore_kernel<SB, 4, LAYOUT>;
+        case 2: return (const void *)cv_restore_kernel<SB, 2, LAYOUT, TM>;
+        case 3: return (const void *)cv_restore_kernel<SB, 3, LAYOUT, TM>;
+        case 4: return (const void *)cv_restore_kernel<SB, 4, LAYOUT, TM>;
         default: return nullptr;
     }
 }
 
-template <int XB, int SB>
+template <int SB, bool TM>
+const void *restore_layout(int d_conv, int layout) {
+    if (layout == kDense) return restore_for<SB, kDense, TM>(d_conv);
+    if (layout == kRows) return restore_for<SB, kRows, TM>(d_conv);
+    if (layout == kRowsT) return restore_for<SB, kRowsT, TM>(d_conv);
+    return nullptr;
+}
+
+template <int XB, int SB, bool TM>
 const void *split_for(int d_conv) {
     switch (d_conv) {
-        case 2: return (const void *)cv_split_kernel<XB, SB, 2, kSplitChunk>;
-        case 3: return (const void *)cv_split_kernel<XB, SB, 3, kSplitChunk>;
-        case 4: return (const void *)cv_split_kernel<XB, SB, 4, kSplitChunk>;
+        case 2: return (const void *)cv_split_kernel<XB, SB, 2, kSplitChunk, TM>;
+        case 3: return (const void *)cv_split_kernel<XB, SB, 3, kSplitChunk, TM>;
+        case 4: return (const void *)cv_split_kernel<XB, SB, 4, kSplitChunk, TM>;
         default: return nullptr;
     }
 }
 
-template <int XB, int SB>
+template <int XB, int SB, bool TM>
 const void *prefill_for(int d_conv) {
     switch (d_conv) {
-        case 2: return (const void *)cv_prefill_kernel<XB, SB, 2, kPrefillChunk>;
-        case 3: return (const void *)cv_prefill_kernel<XB, SB, 3, kPrefillChunk>;
-        case 4: return (const void *)cv_prefill_kernel<XB, SB, 4, kPrefillChunk>;
+        case 2: return (const void *)cv_prefill_kernel<XB, SB, 2, kPrefillChunk, TM>;
+        case 3: return (const void *)cv_prefill_kernel<XB, SB, 3, kPrefillChunk, TM>;
+        case 4: return (const void *)cv_prefill_kernel<XB, SB, 4, kPrefillChunk, TM>;
         default: return nullptr;
     }
 }
 
 }  // namespace
 
-const void *pick_restore(int state_bytes, int d_conv, int layout) {
-    if (state_bytes == 4) {
-        if (layout == kDense) return restore_for<4, kDense>(d_conv);
-        if (layout == kRows) return restore_for<4, kRows>(d_conv);
-        if (layout == kRowsT) return restore_for<4, kRowsT>(d_conv);
-    } else if (state_bytes == 2) {
-        if (layout == kDense) return restore_for<2, kDense>(d_conv);
-        if (layout == kRows) return restore_for<2, kRows>(d_conv);
-        if (layout == kRowsT) return restore_for<2, kRowsT>(d_conv);
-    }
+const void *pick_restore(int state_bytes, int d_conv, int layout, int tm) {
+    if (state_bytes == 4) return tm ? restore_layout<4, true>(d_conv, layout) : restore_layout<4, false>(d_conv, layout);
+    if (state_bytes == 2) return tm ? restore_layout<2, true>(d_conv, layout) : restore_layout<2, false>(d_conv, layout);
     return nullptr;
 }
 
-const void *pick_split(int x_bytes, int state_bytes, int d_conv) {
-    if (x_bytes == 4 && state_bytes == 4) return split_for<4, 4>(d_conv);
-    if (x_bytes == 2 && state_bytes == 2) return split_for<2, 2>(d_conv);
-    if (x_bytes == 2 && state_bytes == 4) return split_for<2, 4>(d_conv);
+const void *pick_split(int x_bytes, int state_bytes, int d_conv, int tm) {
+    if (x_bytes == 4 && state_bytes == 4) return tm ? split_for<4, 4, true>(d_conv) : split_for<4, 4, false>(d_conv);
+    if (x_bytes == 2 && state_bytes == 2) return tm ? split_for<2, 2, true>(d_conv) : split_for<2, 2, false>(d_conv);
+    if (x_bytes == 2 && state_bytes == 4) return tm ? split_for<2, 4, true>(d_conv) : split_for<2, 4, false>(d_conv);
     return nullptr;
 }
 
-const void *pick_prefill(int x_bytes, int state_bytes, int d_conv) {
-    if (x_bytes == 4 && state_bytes == 4) return prefill_for<4, 4>(d_conv);
-    if (x_bytes == 2 && state_bytes == 2) return prefill_for<2, 2>(d_conv);
-    if (x_bytes == 2 && state_bytes == 4) return prefill_for<2, 4>(d_conv);
+const void *pick_prefill(int x_bytes, int state_bytes, int d_conv, int tm) {
+    if (x_bytes == 4 && state_bytes == 4) return tm ? prefill_for<4, 4, true>(d_conv) : prefill_for<4, 4, false>(d_conv);
+    if (x_bytes == 2 && state_bytes == 2) return tm ? prefill_for<2, 2, true>(d_conv) : prefill_for<2, 2, false>(d_conv);
+    if (x_bytes == 2 && state_bytes == 4) return tm ? prefill_for<2, 4, true>(d_conv) : prefill_for<2, 4, false>(d_conv);
     return nullptr;
 }
 

@@ -34,6 +34,7 @@ struct KernelArgs {
     int32_t head_lanes_log2;   // log2(lanes per L2 head); unused when qk == 0
     float eps;
     int32_t token_chunks;      // token-split verify: workgroups per (row, channel block)
+    int64_t state_col;         // 0: conv_state channel-major; else time-major column stride
 };
 
 // The rows layout's compile-time-length path stages a wavefront's row block in LDS in
@@ -63,6 +64,7 @@ struct Plan {
     int token_bucket;          // 1,2,4,8,16,24,32 >= T; kSplitChunk when split
     int token_chunks;          // wavefronts per (row, channel block) along T
     int lean;                  // 16-token bucket built for 5 wavefronts per SIMD
+    int state_tm;              // conv_state time-major (the kernels' TM build)
     int channels_per_lane;     // kChannelsPerLane
     int channel_blocks;
     int64_t workgroups;
@@ -79,6 +81,7 @@ struct RestoreArgs {
     int64_t state_slot, win_slot;
     int32_t n_seq, T, d_inner, n_slots, state_len;
     int32_t channel_blocks;
+    int64_t state_col;         // 0: conv_state channel-major; else time-major column stride
 };
 
 // Prefill conv over packed prompts (conv + SiLU, no L2, no windows).
@@ -99,6 +102,7 @@ struct PrefillArgs {
     int32_t n_seq, T, d_inner, n_slots, state_len;
     int32_t channel_blocks;
     int32_t chunks;            // token chunks per row: ceil(T / kPrefillChunk)
+    int64_t state_col;         // 0: conv_state channel-major; else time-major column stride
 };
 
 // Separate per-head L2 over the q|k channels of token rows, in place.
@@ -122,23 +126,28 @@ constexpr int lds_dma_span(int bytes) {
     return (bytes + kWave * 16 - 1) / (kWave * 16) * (kWave * 16);
 }
 
-// Kernel pickers, one per compiled (x bytes, state bytes, variant) object - variant 0
-// dense, 1 rows, 2 time-major rows, 3 tree: the kernel for (d_conv, token bucket), or
-// nullptr.  lean: the 16-token bucket's build for 5 resident wavefronts per SIMD;
-// split: the row layouts' token-split build (buckets 8 and 16).
-#define CV_DECLARE_PICKERS(xb, sb)                                   \
-    const void *pick_kernel_##xb##_##sb##_0(int d_conv, int token_bucket, int lean, int split); \
-    const void *pick_kernel_##xb##_##sb##_1(int d_conv, int token_bucket, int lean, int split); \
-    const void *pick_kernel_##xb##_##sb##_2(int d_conv, int token_bucket, int lean, int split); \
-    const void *pick_kernel_##xb##_##sb##_3(int d_conv, int token_bucket, int lean, int split);
+// Kernel pickers, one per compiled (x bytes, state bytes, variant, state layout)
+// object - variant 0 dense, 1 rows, 2 time-major rows, 3 tree; state layout 0
+// channel-major, 1 time-major: the kernel for (d_conv, token bucket), or nullptr.
+// lean: the 16-token bucket's build for 5 resident wavefronts per SIMD; split: the row
+// layouts' token-split build (buckets 8 and 16).
+#define CV_DECLARE_PICKERS_TM(xb, sb, tm)                                   \
+    const void *pick_kernel_##xb##_##sb##_0_##tm(int d_conv, int token_bucket, int lean, int split); \
+    const void *pick_kernel_##xb##_##sb##_1_##tm(int d_conv, int token_bucket, int lean, int split); \
+    const void *pick_kernel_##xb##_##sb##_2_##tm(int d_conv, int token_bucket, int lean, int split); \
+    const void *pick_kernel_##xb##_##sb##_3_##tm(int d_conv, int token_bucket, int lean, int split);
+#define CV_DECLARE_PICKERS(xb, sb) CV_DECLARE_PICKERS_TM(xb, sb, 0) CV_DECLARE_PICKERS_TM(xb, sb, 1)
 CV_DECLARE_PICKERS(4, 4)
 CV_DECLARE_PICKERS(2, 2)
 CV_DECLARE_PICKERS(2, 4)
 #undef CV_DECLARE_PICKERS
+#undef CV_DECLARE_PICKERS_TM
 
-const void *pick_restore(int state_bytes, int d_conv, int layout);
-const void *pick_split(int x_bytes, int state_bytes, int d_conv);
-const void *pick_prefill(int x_bytes, int state_bytes, int d_conv);
+// The kernels below take the state layout at compile time the same way (tm: 1 for a
+// time-major conv_state).
+const void *pick_restore(int state_bytes, int d_conv, int layout, int tm);
+const void *pick_split(int x_bytes, int state_bytes, int d_conv, int tm);
+const void *pick_prefill(int x_bytes, int state_bytes, int d_conv, int tm);
 const void *pick_l2(int x_bytes);
 
 }  // namespace cvimpl

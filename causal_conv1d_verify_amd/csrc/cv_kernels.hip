@@ -51,7 +51,9 @@ namespace {
 // p.token_chunks wavefronts.  Each computes out for its own chunk only; chunk 0 also
 // does every copy (the state commit and the row block, which is shared by all the
 // row's tokens), so the arithmetic on each wavefront's path is a quarter to a half.
-template <int XB, int SB, int D, int TB, int LAYOUT, bool TREE, int WPE, bool SPLIT>
+// TM: conv_state time-major (p.state_col is the column stride), a build of its own so
+// that neither layout's path costs the other registers.
+template <int XB, int SB, int D, int TB, int LAYOUT, bool TREE, int WPE, bool SPLIT, bool TM>
 __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(WPE > 0 ? WPE : 1)))
 void cv_verify_kernel(KernelArgs p) {
     static_assert(!TREE || LAYOUT == kDense, "tree windows are dense");
@@ -173,17 +175,37 @@ void cv_verify_kernel(KernelArgs p) {
         return;
     }
 
-    // conv_state: the wavefront's [nch, state_len] region is contiguous.  It comes in
-    // whole (coalesced 16-byte loads, issued with the other loads) and is staged in
-    // LDS; each lane picks its channels' window out of it, writes its committed window
-    // back into it, and the region leaves whole - so every state byte is read once and
-    // written once in lane-contiguous 16-byte units, whatever state_len and the offset
-    // are.  (Direct global->LDS loads measured no faster here than loads through VGPRs.)
+    // conv_state, channel-major: the wavefront's [nch, state_len] region is contiguous.
+    // It comes in whole (coalesced 16-byte loads, issued with the other loads) and is
+    // staged in LDS; each lane picks its channels' window out of it, writes its
+    // committed window back into it, and the region leaves whole - so every state byte
+    // is read once and written once in lane-contiguous 16-byte units, whatever
+    // state_len and the offset are.  (Direct global->LDS loads measured no faster here
+    // than loads through VGPRs.)
+    // Time-major: column k holds the d channels contiguously, so the window is W1
+    // lane-contiguous column loads at columns a.., like x, and the commit W1 column
+    // stores at columns 0..W1-1; the other columns are never touched.
+    constexpr bool tm = TM;
     const rsrc_t st_r = make_rsrc((const char *)p.state + ((int64_t)slot * p.state_slot +
                                                            (int64_t)cb * SL) * SB,
                                   (uint32_t)(nch * SL * SB));
+    const rsrc_t stm_r = make_rsrc((const char *)p.state + ((int64_t)slot * p.state_slot + cb) * SB,
+                                   (uint32_t)(((int64_t)(SL - 1) * p.state_col + nch) * SB));
+    const uint32_t laneS = on ? (uint32_t)(lane * SCB) : kOffLane;
+    uint32_t S[W1][SW];   // initial window columns v[0..W1-1], state-typed bits
+    if constexpr (tm) {
+#pragma unroll
+        for (int j = 0; j < W1; ++j) {
+            if (copier) {
+                gload<SCB>(stm_r, laneS, (uint32_t)((int64_t)(a + j) * p.state_col * SB), S[j]);
+            } else {
+#pragma unroll
+                for (int w = 0; w < SW; ++w) S[j][w] = 0u;
+            }
+        }
+    }
     // exact: nch * SB is a multiple of 16; a split row's other chunks take no state
-    const int rchunks = copier ? nch * SL * SB / 16 : 0;
+    const int rchunks = copier && !tm ? nch * SL * SB / 16 : 0;
     // chunks per lane, all in flight at once up to RJ; longer regions go in rounds
     constexpr int RJ = (W1 * SB + 3) / 4 > 12 ? (W1 * SB + 3) / 4 : 12;
     uint32_t sreg[RJ][4];
@@ -230,7 +252,7 @@ void cv_verify_kernel(KernelArgs p) {
     // the block back whole: the columns past them keep their bits, and every store
     // stays a coalesced 16-byte one.
     const bool row_image = LAYOUT == kRows && p.cu != nullptr && T < p.T && copier;
-    const int img_off = CHW * SL * SB;
+    const int img_off = tm ? 0 : CHW * SL * SB;
     if constexpr (LAYOUT == kRows) {
         if (row_image) {
             __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): the weight reads are done
@@ -248,8 +270,9 @@ void cv_verify_kernel(KernelArgs p) {
         }
     }
 
-    uint32_t S[W1][SW];   // initial window columns v[0..W1-1], state-typed bits
-    if (contiguous_state) {
+    if (tm) {
+        // the window came in with the loads above
+    } else if (contiguous_state) {
         uint32_t run[RUNW];   // the lane's [CPL][W1] run
         lds_read_run<RUNB>(lds + lane * RUNB, run);
 #pragma unroll
@@ -447,7 +470,14 @@ void cv_verify_kernel(KernelArgs p) {
     #pragma unroll
         for (int t = 0; t < TB; ++t) {
             if (t == T - 1) {
-                if (contiguous_state) {
+                if (tm) {
+    #pragma unroll
+                    for (int j = 0; j < W1; ++j) {
+                        uint32_t col[SW];
+                        column(t + 1 + j, col);
+                        gstore<SCB>(stm_r, laneS, (uint32_t)((int64_t)j * p.state_col * SB), col);
+                    }
+                } else if (contiguous_state) {
                     uint32_t run[RUNW];
                     window_run(t + 1, run);
                     lds_write_run<RUNB>(lds + lane * RUNB, run);
@@ -461,9 +491,11 @@ void cv_verify_kernel(KernelArgs p) {
                 }
             }
         }
-        lds_barrier();
-        lds_to_global(lds, rchunks, st_r, 0, lane);
-        lds_barrier();   // the region's LDS is reused below
+        if (!tm) {
+            lds_barrier();
+            lds_to_global(lds, rchunks, st_r, 0, lane);
+            lds_barrier();   // the region's LDS is reused below
+        }
     }
 
     // ---- rollback windows: pure copies of the inputs ---------------------------------------
@@ -669,49 +701,50 @@ void cv_verify_kernel(KernelArgs p) {
 
 // ---- instantiation ----------------------------------------------------------------------
 //
-// This file is compiled once per (x bytes, state bytes, variant) with CV_XB, CV_SB and
-// CV_VARIANT defined (0 dense, 1 rows, 2 time-major rows, 3 tree with dense windows),
-// so the instantiations build in parallel; each object exports one picker over
-// (d_conv, token bucket).
-template <int XB, int SB, int D, int LAYOUT, bool TREE>
+// This file is compiled once per (x bytes, state bytes, variant, state layout) with
+// CV_XB, CV_SB, CV_VARIANT (0 dense, 1 rows, 2 time-major rows, 3 tree with dense
+// windows) and CV_TM (1: time-major conv_state) defined, so the instantiations build
+// in parallel; each object exports one picker over (d_conv, token bucket).
+template <int XB, int SB, int D, int LAYOUT, bool TREE, bool TM>
 const void *pick_bucket(int tb, bool lean, bool split) {
     if constexpr (!TREE && LAYOUT != kDense) {
         if (split) {
-            if (tb == 8) return (const void *)cv_verify_kernel<XB, SB, D, 8, LAYOUT, TREE, 0, true>;
-            if (tb == 16) return (const void *)cv_verify_kernel<XB, SB, D, 16, LAYOUT, TREE, 0, true>;
+            if (tb == 8) return (const void *)cv_verify_kernel<XB, SB, D, 8, LAYOUT, TREE, 0, true, TM>;
+            if (tb == 16) return (const void *)cv_verify_kernel<XB, SB, D, 16, LAYOUT, TREE, 0, true, TM>;
             return nullptr;
         }
     }
     switch (tb) {
-        case 1: return (const void *)cv_verify_kernel<XB, SB, D, 1, LAYOUT, TREE, 0, false>;
-        case 2: return (const void *)cv_verify_kernel<XB, SB, D, 2, LAYOUT, TREE, 0, false>;
-        case 4: return (const void *)cv_verify_kernel<XB, SB, D, 4, LAYOUT, TREE, 0, false>;
-        case 8: return (const void *)cv_verify_kernel<XB, SB, D, 8, LAYOUT, TREE, 0, false>;
+        case 1: return (const void *)cv_verify_kernel<XB, SB, D, 1, LAYOUT, TREE, 0, false, TM>;
+        case 2: return (const void *)cv_verify_kernel<XB, SB, D, 2, LAYOUT, TREE, 0, false, TM>;
+        case 4: return (const void *)cv_verify_kernel<XB, SB, D, 4, LAYOUT, TREE, 0, false, TM>;
+        case 8: return (const void *)cv_verify_kernel<XB, SB, D, 8, LAYOUT, TREE, 0, false, TM>;
         case 16:
-            return lean ? (const void *)cv_verify_kernel<XB, SB, D, 16, LAYOUT, TREE, 5, false>
-                        : (const void *)cv_verify_kernel<XB, SB, D, 16, LAYOUT, TREE, 0, false>;
-        case 24: return (const void *)cv_verify_kernel<XB, SB, D, 24, LAYOUT, TREE, 0, false>;
-        case 32: return (const void *)cv_verify_kernel<XB, SB, D, 32, LAYOUT, TREE, 0, false>;
+            return lean ? (const void *)cv_verify_kernel<XB, SB, D, 16, LAYOUT, TREE, 5, false, TM>
+                        : (const void *)cv_verify_kernel<XB, SB, D, 16, LAYOUT, TREE, 0, false, TM>;
+        case 24: return (const void *)cv_verify_kernel<XB, SB, D, 24, LAYOUT, TREE, 0, false, TM>;
+        case 32: return (const void *)cv_verify_kernel<XB, SB, D, 32, LAYOUT, TREE, 0, false, TM>;
         default: return nullptr;
     }
 }
 
 }  // namespace
 
-#if !defined(CV_XB) || !defined(CV_SB) || !defined(CV_VARIANT)
-#error "compile with -DCV_XB=<2|4> -DCV_SB=<2|4> -DCV_VARIANT=<0..3>"
+#if !defined(CV_XB) || !defined(CV_SB) || !defined(CV_VARIANT) || !defined(CV_TM)
+#error "compile with -DCV_XB=<2|4> -DCV_SB=<2|4> -DCV_VARIANT=<0..3> -DCV_TM=<0|1>"
 #endif
 
-#define CV_PICK_NAME(xb, sb, v) pick_kernel_##xb##_##sb##_##v
-#define CV_PICK(xb, sb, v) CV_PICK_NAME(xb, sb, v)
+#define CV_PICK_NAME(xb, sb, v, tm) pick_kernel_##xb##_##sb##_##v##_##tm
+#define CV_PICK(xb, sb, v, tm) CV_PICK_NAME(xb, sb, v, tm)
 
-const void *CV_PICK(CV_XB, CV_SB, CV_VARIANT)(int d_conv, int token_bucket, int lean, int split) {
+const void *CV_PICK(CV_XB, CV_SB, CV_VARIANT, CV_TM)(int d_conv, int token_bucket, int lean, int split) {
     constexpr int layout = CV_VARIANT == 3 ? kDense : CV_VARIANT;
     constexpr bool tree = CV_VARIANT == 3;
+    constexpr bool tm = CV_TM != 0;
     switch (d_conv) {
-        case 2: return pick_bucket<CV_XB, CV_SB, 2, layout, tree>(token_bucket, lean != 0, split != 0);
-        case 3: return pick_bucket<CV_XB, CV_SB, 3, layout, tree>(token_bucket, lean != 0, split != 0);
-        case 4: return pick_bucket<CV_XB, CV_SB, 4, layout, tree>(token_bucket, lean != 0, split != 0);
+        case 2: return pick_bucket<CV_XB, CV_SB, 2, layout, tree, tm>(token_bucket, lean != 0, split != 0);
+        case 3: return pick_bucket<CV_XB, CV_SB, 3, layout, tree, tm>(token_bucket, lean != 0, split != 0);
+        case 4: return pick_bucket<CV_XB, CV_SB, 4, layout, tree, tm>(token_bucket, lean != 0, split != 0);
         default: return nullptr;
     }
 }

@@ -58,8 +58,10 @@
  *      out         [n_seq, T, d_inner]     out[i,t,c] = out + i*out_seq_stride + t*out_tok_stride + c
  *      weight      [d_inner, d_conv]       contiguous; weight[c, d_conv-1] multiplies x_t
  *      bias        [d_inner]               contiguous, or NULL (no bias)
- *      conv_state  [n_slots, d_inner, state_len]
+ *      conv_state  [n_slots, d_inner, state_len] (channel-major, state_col_stride == 0):
  *                  state[s,c,k] = conv_state + s*state_slot_stride + c*state_len + k
+ *                  or [n_slots, state_len, d_inner] (time-major, state_col_stride > 0):
+ *                  state[s,c,k] = conv_state + s*state_slot_stride + k*state_col_stride + c
  *      slot_idx    [n_seq] int32 or NULL (row i uses slot i).  -1 marks a padded row.
  *      num_accept_tokens [n_seq] int32 or NULL (all 0): start column a of row i's window.
  *  - A padded row (slot -1) writes nothing at all: not out, not conv_state, not the
@@ -72,11 +74,18 @@
  *  - Buffers must not overlap each other (x and weight/bias may).
  *  - Alignment (else CV_ENOTSUP): every pointer 16-byte aligned; d_inner, the x/out
  *    strides multiples of 16/sizeof(x element) (8 for bf16, 4 for fp32);
- *    state_slot_stride and win_slot_stride multiples of 16 bytes; head_dim one of
+ *    state_slot_stride, state_col_stride and win_slot_stride multiples of 16 bytes;
+ *    head_dim one of
  *    4, 8, 16, 32, 64, 128, 256 (a head is reduced inside one 256-channel wavefront).
- *  - LDS (else CV_ENOTSUP): a 256-channel wavefront stages its [256, state_len] state
- *    region (and its weights, its window tiles) in LDS, at most 160 KiB (all of a gfx950
- *    compute unit's): state_len up to 160 fp32 / 320 bf16 columns.
+ *  - LDS (else CV_ENOTSUP): with a channel-major conv_state, a 256-channel wavefront
+ *    stages its [256, state_len] state region (and its weights, its window tiles) in
+ *    LDS, at most 160 KiB (all of a gfx950 compute unit's): state_len up to 160 fp32 /
+ *    320 bf16 columns.  A time-major conv_state is not staged (no such limit).
+ *  - Which conv_state layout to pick: a channel-major row wider than the window
+ *    (state_len > d_conv-1, as offsets need) puts window bytes in every 32-byte
+ *    sector, so the kernels move such rows whole, read and written back; in the
+ *    time-major layout a window is d_conv-1 contiguous columns of d_inner channels and
+ *    only those move.
  *  - Numerics: the conv accumulates in fp32 as acc = bias (or +0); for w = 0..D-1:
  *    acc = fma(weight[c,w], v[t+w], acc), each step one correctly rounded fused
  *    multiply-add.  SiLU and L2 run in fp32.  Windows and conv_state are moved as bit
@@ -92,7 +101,7 @@
 extern "C" {
 #endif
 
-#define CONV_VERIFY_ABI_VERSION 3
+#define CONV_VERIFY_ABI_VERSION 4
 
 /* Only the entry points below are exported from the shared library. */
 #define CV_API __attribute__((visibility("default")))
@@ -139,6 +148,12 @@ typedef struct cv_shape {
     int64_t state_slot_stride;               /* elements, >= d_inner*state_len if n_slots>1 */
     int64_t win_slot_stride;                 /* elements of the window buffer per slot,
                                                 >= its per-slot size if n_slots > 1         */
+    int64_t state_col_stride;                /* 0: conv_state channel-major (a channel's
+                                                state_len columns contiguous).  > 0:
+                                                time-major, elements between columns,
+                                                >= d_inner; then state_slot_stride >=
+                                                (state_len-1)*state_col_stride + d_inner
+                                                if n_slots > 1                              */
 } cv_shape_t;
 
 /*
@@ -219,7 +234,8 @@ CV_API int conv_verify_update_tree(const cv_shape_t *shape, const void *x, const
  *   `windows` in `layout` (chain verify: k = accepted tokens - 1; tree verify: the
  *   position of the last accepted token).  Columns >= d_conv-1 are not written.
  * Uses shape fields n_seq, T (the window buffer's), d_inner, d_conv, state_dtype,
- * n_slots, state_len, state_slot_stride, win_slot_stride (x fields are ignored).
+ * n_slots, state_len, state_slot_stride, state_col_stride, win_slot_stride (x fields
+ * are ignored).
  * window_index [n_seq] int32 (device).  Rows with k >= T or a slot >= n_slots are
  * skipped.  One launch; returns CV_OK or an error (nothing launched).
  */

@@ -184,7 +184,18 @@ class GeneralProblem:
         self.x = to_torch(inp.x, wl.x_dtype, device)[..., :d]
         self.weight = to_torch(inp.weight, wl.x_dtype, device)
         self.bias = None if inp.bias is None else to_torch(inp.bias, wl.x_dtype, device)
-        self.conv_state = to_torch(inp.conv_state, wl.state_dtype, device)
+        self.state_raw = self.state_raw0 = None
+        if wl.state_tm:
+            # time-major storage [n_slots, state_len, d + pad]; the library gets the
+            # [n_slots, d, state_len] view of it (channel stride 1)
+            n, _, sl = inp.conv_state.shape
+            raw = workloads.poison((n, sl, d + wl.state_col_pad), wl.state_dtype)
+            raw[:, :, :d] = inp.conv_state.transpose(0, 2, 1)
+            self.state_raw0 = raw
+            self.state_raw = to_torch(raw, wl.state_dtype, device)
+            self.conv_state = self.state_raw[:, :, :d].transpose(1, 2)
+        else:
+            self.conv_state = to_torch(inp.conv_state, wl.state_dtype, device)
         i32 = lambda a: None if a is None else to_torch(a, "i32", device)   # noqa: E731
         self.slot_idx, self.nat = i32(inp.slot_idx), i32(inp.num_accept_tokens)
         self.cu, self.parent = i32(inp.cu_seqlens), i32(inp.parent)
@@ -233,6 +244,10 @@ class GeneralProblem:
         wl = self.wl
         res = {"out": to_numpy(self.out_full, wl.x_dtype),
                "conv_state": to_numpy(self.conv_state, wl.state_dtype)}
+        if self.state_raw is not None and wl.state_col_pad:
+            pad = _bits(to_numpy(self.state_raw, wl.state_dtype))[:, :, wl.d_inner:]
+            assert np.array_equal(pad, _bits(self.state_raw0)[:, :, wl.d_inner:]), \
+                "time-major conv_state: padding after a column was written"
         if self.windows is not None:
             res["windows"] = to_numpy(self.windows, wl.state_dtype)
         return res

@@ -65,7 +65,8 @@ def test_abi_version_matches_header():
 def test_shape_struct_layout():
     # offsets of the int64 strides must match the C struct (4-byte fields then 8-aligned)
     assert lib_mod.CvShape.x_seq_stride.offset == 48
-    assert ctypes.sizeof(lib_mod.CvShape) == 96
+    assert ctypes.sizeof(lib_mod.CvShape) == 104
+    assert lib_mod.CvShape.state_col_stride.offset == 96
     assert ctypes.sizeof(lib_mod.CvLaunchInfo) == 40
 
 
@@ -116,6 +117,13 @@ BAD_SHAPES = [
     ("state_slot_overlap", dict(state_slot_stride=1024), EINVAL),
     ("x_stride%8", dict(x_tok_stride=1028, x_seq_stride=8 * 1028), ENOTSUP),
     ("state_slot_unaligned", dict(state_slot_stride=3 * 1024 + 4), ENOTSUP),
+    # time-major conv_state: columns of >= d_inner elements, 16-byte multiples, and a
+    # slot stride covering (state_len-1) columns plus d_inner
+    ("state_col<0", dict(state_col_stride=-1024), EINVAL),
+    ("state_col<d", dict(state_col_stride=1016), EINVAL),
+    ("state_col_unaligned", dict(state_col_stride=1028, state_slot_stride=4096), ENOTSUP),
+    ("state_col_slot_overlap", dict(state_col_stride=1032, state_slot_stride=3 * 1024 + 8),
+     EINVAL),
 ]
 
 
@@ -163,6 +171,26 @@ def test_lds_limit():
                                          state_slot_stride=1024 * 160, win_slot_stride=1024 * 10))
     assert rc == 0, detail
     assert info.lds_bytes == 163840
+
+
+def test_time_major_state_needs_no_lds_region():
+    # a channel-major state row wider than the LDS limit is refused; the same state
+    # stored time-major is not staged, so the LDS is that of the windows alone
+    big = dict(state_dtype=lib_mod.CV_F32, state_len=161, win_slot_stride=1024 * 10)
+    rc, _, detail = describe(1, shape(state_slot_stride=1024 * 161, **big))
+    assert rc == ENOTSUP and "LDS" in detail
+    rc, info, detail = describe(1, shape(state_slot_stride=1024 * 161, state_col_stride=1024, **big))
+    assert rc == 0, detail
+    assert info.lds_bytes == 256 * 10 * 4 // 2   # the fp32 row block [256, 10], in halves
+    # the stress shape: 18 bf16 columns per channel, 16 tokens
+    st = dict(T=16, state_len=18, x_seq_stride=16 * 1024, out_seq_stride=16 * 1024,
+              win_slot_stride=1024 * 18)
+    rc, cm, _ = describe(1, shape(state_slot_stride=1024 * 18, **st))
+    rc2, tm, _ = describe(1, shape(state_slot_stride=1024 * 18, state_col_stride=1024, **st))
+    assert rc == rc2 == 0
+    assert cm.lds_bytes == 256 * 18 * 2 and tm.lds_bytes == 256 * 18 * 2 // 2
+    # a padded column stride, restore and prefill take the same shape
+    assert describe(0, shape(state_col_stride=1032, state_slot_stride=3 * 1032))[0] == 0
 
 
 @pytest.mark.parametrize("key", [0, 1, 2, 3, 4, "4b", "4s"])

@@ -379,3 +379,108 @@ def test_padded_slot_strides(layout):
     pz = gh._bits(workloads.poison((wl.n_slots, pad), wl.state_dtype))
     assert np.array_equal(gh._bits(gh.to_numpy(st_full[:, -pad:].contiguous(), wl.state_dtype)), pz)
     assert np.array_equal(gh._bits(gh.to_numpy(w_full[:, -pad:].contiguous(), wl.state_dtype)), pz)
+
+
+# Time-major conv_state: the pool stored [n_slots, state_len, d (+ pad)], the library
+# handed its [n_slots, d, state_len] view (state_col_stride = the column stride).  Every
+# step kind that reads or writes the state, both sides of the token-split thresholds,
+# the three dtype pairs, D 2..4; padded column strides must keep their poison.
+TM_STATE = []
+for layout in ("dense", "dedup", "dedup_t"):
+    for T, pad in ((1, 0), (3, 16), (8, 0), (16, 8), (17, 0)):
+        TM_STATE.append(c(f"tm_{layout}_T{T}_pad{pad}", n_seq=3, d_inner=1032, qk_channels=512,
+                          head_dim=128, T=T, layout=layout, accept_offsets=T > 1,
+                          permute_slots=True, pad_frac=0.25, extra_slots=2, state_tm=True,
+                          state_col_pad=pad))
+    for xd, sd in (("f32", "f32"), ("bf16", "f32")):
+        TM_STATE.append(c(f"tm_{layout}_{xd}_{sd}", n_seq=3, d_inner=520, qk_channels=256,
+                          head_dim=64, T=9, layout=layout, x_dtype=xd, state_dtype=sd,
+                          accept_offsets=True, permute_slots=True, pad_frac=0.3, state_tm=True,
+                          state_col_pad=4 if sd == "f32" else 8))
+    for D in (2, 3):
+        TM_STATE.append(c(f"tm_{layout}_D{D}", n_seq=4, d_inner=520, qk_channels=256,
+                          head_dim=64, d_conv=D, T=6, layout=layout, accept_offsets=True,
+                          state_tm=True))
+    TM_STATE.append(c(f"tm_packed_{layout}", n_seq=6, d_inner=1032, qk_channels=512,
+                      head_dim=128, T=16, layout=layout, varlen=True, accept_offsets=True,
+                      permute_slots=True, pad_frac=0.2, extra_slots=1, state_tm=True))
+# one-wavefront-per-row grids (past the split thresholds) and the tree
+TM_STATE += [
+    c("tm_dense_nosplit", n_seq=641, d_inner=1024, qk_channels=512, head_dim=128, T=8,
+      accept_offsets=True, permute_slots=True, pad_frac=0.1, state_tm=True),
+    c("tm_dedup_nosplit", n_seq=321, d_inner=1024, qk_channels=512, head_dim=128, T=8,
+      layout="dedup", accept_offsets=True, permute_slots=True, pad_frac=0.1, state_tm=True),
+    c("tm_tree", n_seq=4, d_inner=1032, qk_channels=512, head_dim=128, T=17, tree=True,
+      accept_offsets=True, permute_slots=True, pad_frac=0.25, state_tm=True, state_col_pad=8),
+]
+
+
+@pytest.mark.parametrize("wl", TM_STATE, ids=[w.name for w in TM_STATE])
+def test_time_major_state_verify(wl):
+    _verify_case(wl)
+
+
+TM_RESTORE = [c(f"tm_restore_{layout}", n_seq=6, d_inner=1032, qk_channels=512, head_dim=128,
+                T=8, layout=layout, restore=True, accept_offsets=True, permute_slots=True,
+                pad_frac=0.2, extra_slots=1, state_tm=True, state_col_pad=8)
+              for layout in ("dense", "dedup", "dedup_t")]
+TM_RESTORE.append(c("tm_restore_f32_D3", n_seq=4, d_inner=520, qk_channels=256, head_dim=64,
+                    d_conv=3, T=5, layout="dedup", x_dtype="f32", state_dtype="f32",
+                    restore=True, state_tm=True))
+
+
+@pytest.mark.parametrize("wl", TM_RESTORE, ids=[w.name for w in TM_RESTORE])
+def test_time_major_state_restore(wl):
+    inp = workloads.make_inputs(wl)
+    _say(wl.name, wl)
+    p = gh.GeneralProblem(inp)
+    p.verify()
+    p.restore()
+    gh.compare_general(p.results(), gh.oracle_general(inp, restore=True), inp)
+
+
+TM_PREFILL = [c(f"tm_prefill_D{D}_{xd}_{sd}", n_seq=5, d_inner=520, qk_channels=0, d_conv=D,
+                T=70, x_dtype=xd, state_dtype=sd, varlen=True, prefill=True, init_frac=0.5,
+                permute_slots=True, state_len=D + 3, state_tm=True, state_col_pad=8,
+                seed=workloads.BASE_SEED + 3200 + D)
+              for D in (2, 3, 4) for xd, sd in (("bf16", "bf16"), ("f32", "f32"), ("bf16", "f32"))]
+
+
+@pytest.mark.parametrize("wl", TM_PREFILL, ids=[w.name for w in TM_PREFILL])
+def test_time_major_state_prefill(wl):
+    inp = workloads.make_inputs(wl)
+    _say(wl.name, wl)
+    p = gh.GeneralProblem(inp)
+    p.prefill()
+    gh.compare_general(p.results(), gh.oracle_general(inp), inp)
+
+
+@pytest.mark.parametrize("key", ["4t", "4bt"])
+def test_full_size_time_major_state(key):
+    _verify_case(workloads.WORKLOADS[key])
+
+
+def test_full_size_time_major_state_restore():
+    wl = workloads.WORKLOADS["4rt"]
+    inp = workloads.make_inputs(wl)
+    _say(wl.name)
+    p = gh.GeneralProblem(inp)
+    p.verify()
+    p.restore()
+    gh.compare_general(p.results(), gh.oracle_general(inp, restore=True), inp)
+
+
+def test_time_major_state_equals_channel_major():
+    """The same problem with the state pool in either storage order: identical bits."""
+    wl = c("tm_vs_cm", n_seq=6, d_inner=1032, qk_channels=512, head_dim=128, T=8,
+           layout="dedup", accept_offsets=True, permute_slots=True, pad_frac=0.2)
+    inp = workloads.make_inputs(wl)
+    _say("time-major vs channel-major state")
+    a = gh.GeneralProblem(inp)
+    a.verify()
+    inp_t = dataclasses.replace(inp, wl=dataclasses.replace(wl, state_tm=True, state_col_pad=8))
+    b = gh.GeneralProblem(inp_t)
+    b.verify()
+    ra, rb = a.results(), b.results()
+    for k in ("out", "windows", "conv_state"):
+        assert np.array_equal(gh._bits(ra[k]), gh._bits(rb[k])), k

@@ -76,6 +76,8 @@ class Workload:
     restore: bool = False         # draw accepted-prefix restore indices
     init_frac: float = 1.0        # probability that a row starts from its state
     prefill: bool = False         # conv + SiLU only, no windows; L2 as a separate pass
+    state_tm: bool = False        # conv_state stored time-major [n_slots, state_len, d + pad]
+    state_col_pad: int = 0        # elements after each time-major state column (untouched)
 
     @property
     def win_cols(self) -> int:
@@ -125,6 +127,17 @@ WORKLOADS = {
     "4r": Workload("restore_stress_dedup_t16", 512, 10240, 4096, 128, 4, 16, "bf16", "bf16",
                    "dedup", True, 18, BASE_SEED + 34, accept_offsets=True, pad_frac=0.1,
                    permute_slots=True, restore=True),
+    # the stress problems with conv_state stored time-major ([n_slots, state_len, d]):
+    # the same draws (same seeds), another storage order of the state pool
+    "4t": Workload("stress_dedup_t16_tmstate", 512, 10240, 4096, 128, 4, 16, "bf16", "bf16",
+                   "dedup", True, 18, BASE_SEED + 4, accept_offsets=True, pad_frac=0.1,
+                   permute_slots=True, state_tm=True),
+    "4bt": Workload("stress_dedup_t16_d10200_tmstate", 512, 10200, 4096, 128, 4, 16, "bf16",
+                    "bf16", "dedup", True, 18, BASE_SEED + 104, accept_offsets=True,
+                    pad_frac=0.1, permute_slots=True, state_tm=True),
+    "4rt": Workload("restore_stress_dedup_t16_tmstate", 512, 10240, 4096, 128, 4, 16, "bf16",
+                    "bf16", "dedup", True, 18, BASE_SEED + 34, accept_offsets=True,
+                    pad_frac=0.1, permute_slots=True, restore=True, state_tm=True),
     # tree verify at the K=17 GDN shape (dense windows, nothing committed)
     "1t": Workload("tree_k17_dense", 8, 8192, 4096, 128, 4, 17, "bf16", "bf16", "dense",
                    False, 3, BASE_SEED + 11, tree=True),
