@@ -323,6 +323,7 @@ int verify(int layout, bool tree, const cv_shape_t *s, const void *x, const void
     a.eps = s->l2_eps;
     a.token_chunks = plan.token_chunks;
     a.state_col = s->state_col_stride;
+    a.slot_first = slot_idx != nullptr && plan.workgroups > cvimpl::kResidentWaves;
     return launch(pick_verify(plan), plan.workgroups, plan.lds_bytes, a, stream);
 }
 

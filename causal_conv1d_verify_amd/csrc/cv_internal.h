@@ -35,7 +35,13 @@ struct KernelArgs {
     float eps;
     int32_t token_chunks;      // token-split verify: workgroups per (row, channel block)
     int64_t state_col;         // 0: conv_state channel-major; else time-major column stride
+    int32_t slot_first;        // read the slot before any vector load (padded rows load nothing)
 };
+
+// A launch of more wavefronts than the chip holds at once (256 CUs x 4 SIMDs x 5) runs
+// in generations: there a wavefront waits for its row's slot before loading x, so the
+// x of padded rows is never read; a launch that fits in one generation issues x first.
+constexpr int64_t kResidentWaves = 5120;
 
 // The rows layout's compile-time-length path stages a wavefront's row block in LDS in
 // halves when the block is larger than this: 8 KiB per wavefront leaves LDS for 20

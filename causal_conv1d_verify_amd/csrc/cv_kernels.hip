@@ -107,6 +107,9 @@ void cv_verify_kernel(KernelArgs p) {
     if constexpr (TREE || SPLIT) {
         if (chunk * G >= T) return;   // a split row's chunk past its tokens
     }
+    if (p.slot_first) {
+        if (slot < 0) return;   // a padded row on a multi-generation grid: no load at all
+    }
     const int SL = p.state_len;
     const int nch = min(CHW, p.d_inner - cb);   // channels of this wavefront
     const bool on = lane * CPL < nch;

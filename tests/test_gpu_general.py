@@ -484,3 +484,16 @@ def test_time_major_state_equals_channel_major():
     ra, rb = a.results(), b.results()
     for k in ("out", "windows", "conv_state"):
         assert np.array_equal(gh._bits(ra[k]), gh._bits(rb[k])), k
+
+
+# Grids past one resident generation (5,120 wavefronts) with a slot table read the
+# slot before loading x, so padded rows load nothing; both sides of that edge.
+SLOT_FIRST = [c(f"slot_first_{layout}_n{n}{'_tm' if tm else ''}", n_seq=n, d_inner=1024,
+                qk_channels=512, head_dim=128, T=4, layout=layout, accept_offsets=True,
+                permute_slots=True, pad_frac=0.3, extra_slots=2, state_tm=tm)
+              for layout, tm in (("dedup", False), ("dense", True)) for n in (1280, 1281)]
+
+
+@pytest.mark.parametrize("wl", SLOT_FIRST, ids=[w.name for w in SLOT_FIRST])
+def test_slot_first_edge(wl):
+    _verify_case(wl)
