@@ -324,6 +324,9 @@ int verify(int layout, bool tree, const cv_shape_t *s, const void *x, const void
     a.token_chunks = plan.token_chunks;
     a.state_col = s->state_col_stride;
     a.slot_first = slot_idx != nullptr && plan.workgroups > cvimpl::kResidentWaves;
+    // a partial last channel block leaves the rows' buffers off 128-byte line
+    // boundaries, so neighbouring wavefronts share lines: keep a row's blocks on one XCD
+    a.xcd_remap = s->d_inner % kChw != 0;
     return launch(pick_verify(plan), plan.workgroups, plan.lds_bytes, a, stream);
 }
 

@@ -209,6 +209,17 @@ __device__ __forceinline__ int scalar_read(const int32_t *p, int i) {
     return *((const __attribute__((address_space(4))) int32_t *)p + i);
 }
 
+// Workgroups are handed to MI355X's 8 XCDs round-robin by index, and each XCD has an
+// L2 of its own.  This maps the hardware index b of a grid of G workgroups to a linear
+// work index so that each XCD takes one contiguous range of work indices (XCD x gets
+// the indices b = x, x+8, ...; they map to consecutive work items): neighbouring
+// channel blocks of a row then share one L2, and a cache line that straddles their
+// boundary is fetched, merged and written back once.  A bijection on [0, G).
+__device__ __forceinline__ unsigned xcd_linear(unsigned b, unsigned G) {
+    const unsigned x = b % 8u, k = b / 8u, q = G / 8u, r = G % 8u;
+    return x < r ? x * (q + 1u) + k : r * (q + 1u) + (x - r) * q + k;
+}
+
 // Orders LDS accesses across the workgroup (one wavefront) without waiting for the
 // wavefront's global stores: __syncthreads() is a release fence for all memory, which
 // would make every LDS hand-off wait for the writes issued before it to reach memory.

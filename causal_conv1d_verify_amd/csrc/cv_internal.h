@@ -36,6 +36,7 @@ struct KernelArgs {
     int32_t token_chunks;      // token-split verify: workgroups per (row, channel block)
     int64_t state_col;         // 0: conv_state channel-major; else time-major column stride
     int32_t slot_first;        // read the slot before any vector load (padded rows load nothing)
+    int32_t xcd_remap;         // work index from xcd_linear(blockIdx): a row's blocks on one XCD
 };
 
 // A launch of more wavefronts than the chip holds at once (256 CUs x 4 SIMDs x 5) runs

@@ -76,8 +76,9 @@ void cv_verify_kernel(KernelArgs p) {
     char *lds = (char *)lds_raw;
 
     const int lane = threadIdx.x;
-    const int r2 = (int)(blockIdx.x / (unsigned)p.channel_blocks);
-    const int cb = (int)(blockIdx.x - (unsigned)r2 * (unsigned)p.channel_blocks) * CHW;
+    const unsigned bid = p.xcd_remap ? xcd_linear(blockIdx.x, gridDim.x) : blockIdx.x;
+    const int r2 = (int)(bid / (unsigned)p.channel_blocks);
+    const int cb = (int)(bid - (unsigned)r2 * (unsigned)p.channel_blocks) * CHW;
     // Tree verify on a small grid spreads a row's token chunks over p.token_chunks
     // wavefronts: each one builds the row's whole v tile (a token's ancestors may be
     // any earlier token) and computes and writes only its own chunk of tokens.
