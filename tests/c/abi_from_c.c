@@ -46,6 +46,17 @@ int main(void) {
     bad = s;
     bad.head_dim = 96; bad.qk_channels = 960;
     expect("head_dim 96", conv_verify_describe(CV_WIN_ROWS, &bad, &info), CV_ENOTSUP);
+    /* conv_state stored time-major: columns of >= d_inner elements, no state region in LDS */
+    bad = s;
+    bad.state_col_stride = 10240 - 8;
+    expect("state columns overlap", conv_verify_describe(CV_WIN_ROWS, &bad, &info), CV_EINVAL);
+    cv_launch_info_t cm, tm;
+    bad = s;
+    bad.state_len = 18; bad.state_slot_stride = 10240 * 18;
+    expect("describe rows, 18-column channel-major state", conv_verify_describe(CV_WIN_ROWS, &bad, &cm), CV_OK);
+    bad.state_col_stride = 10240;
+    expect("describe rows, time-major state", conv_verify_describe(CV_WIN_ROWS, &bad, &tm), CV_OK);
+    expect("  time-major state takes less LDS", tm.lds_bytes < cm.lds_bytes, 1);
     /* argument checks run before any HIP call: a NULL x is refused, nothing launched */
     expect("update with NULL x", conv_verify_update(&s, CV_WIN_ROWS, NULL, (void *)0x10000, NULL,
                                                     (void *)0x10000, NULL, NULL, NULL,

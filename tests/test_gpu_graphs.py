@@ -47,6 +47,15 @@ CASES = [
                      layout="dedup_t", restore=True, permute_slots=True),
     workloads.custom("g_prefill", n_seq=4, d_inner=1032, qk_channels=512, head_dim=128, T=40,
                      varlen=True, prefill=True, init_frac=0.5),
+    # the same step kinds with conv_state stored time-major
+    workloads.custom("g_dedup_tmstate", n_seq=6, d_inner=2048, qk_channels=1024, head_dim=128,
+                     T=16, layout="dedup", accept_offsets=True, permute_slots=True, pad_frac=0.2,
+                     state_tm=True),
+    workloads.custom("g_restore_tmstate", n_seq=6, d_inner=1032, qk_channels=512, head_dim=128,
+                     T=8, layout="dense", restore=True, accept_offsets=True, permute_slots=True,
+                     state_tm=True, state_col_pad=8),
+    workloads.custom("g_prefill_tmstate", n_seq=4, d_inner=1032, qk_channels=0, T=40,
+                     varlen=True, prefill=True, init_frac=0.5, state_tm=True),
 ]
 
 
