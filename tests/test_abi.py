@@ -366,3 +366,28 @@ def test_abi_from_plain_c(tmp_path):
     run = subprocess.run([str(exe)], capture_output=True, text=True, env=env, timeout=120)
     assert run.returncode == 0, run.stdout + run.stderr
     assert "MISMATCH" not in run.stdout
+
+
+def test_binding_state_views():
+    """The binding reads the conv_state order from the tensor's view: a contiguous
+    [n_slots, d, state_len] is channel-major (state_col_stride 0); the transposed view
+    of a [n_slots, state_len, >= d] buffer is time-major with its column stride; any
+    other view is refused."""
+    import torch
+
+    import causal_conv1d_verify_amd as cv
+
+    n, d, sl = 3, 1032, 10
+    assert cv._check_state(torch.zeros(n, d, sl), d) == 0
+    tm = torch.zeros(n, sl, d)
+    assert cv._check_state(tm.transpose(1, 2), d) == d
+    padded = torch.zeros(n, sl, d + 8)[:, :, :d]
+    assert cv._check_state(padded.transpose(1, 2), d) == d + 8
+    # a state width of one column is the same memory in both orders
+    assert cv._check_state(torch.zeros(n, 1, d).transpose(1, 2), d) == 0
+    with pytest.raises(ValueError):
+        cv._check_state(torch.zeros(n, sl, d), d)                      # wrong shape
+    with pytest.raises(ValueError):
+        cv._check_state(torch.zeros(n, d, 2 * sl)[:, :, ::2], d)       # strided columns
+    # (a view whose slots overlap each other's columns passes here and is refused by the
+    # library's slot-stride check: test_describe_rejects[state_col_slot_overlap])
