@@ -327,6 +327,7 @@ int verify(int layout, bool tree, const cv_shape_t *s, const void *x, const void
     // a partial last channel block leaves the rows' buffers off 128-byte line
     // boundaries, so neighbouring wavefronts share lines: keep a row's blocks on one XCD
     a.xcd_remap = s->d_inner % kChw != 0;
+    a.out_keep = plan.token_chunks == 1 && plan.workgroups >= cvimpl::kResidentWaves;
     return launch(pick_verify(plan), plan.workgroups, plan.lds_bytes, a, stream);
 }
 

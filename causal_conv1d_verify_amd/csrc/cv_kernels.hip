@@ -459,7 +459,10 @@ void cv_verify_kernel(KernelArgs p) {
                             o[w] = __builtin_bit_cast(uint32_t, __builtin_convertvector(pr, b2));
                         }
                     }
-                    gstore<VB>(o_r, laneV, (uint32_t)(t * p.out_tok * XB), o);
+                    if (p.out_keep)
+                        gstore<VB, kKeep>(o_r, laneV, (uint32_t)(t * p.out_tok * XB), o);
+                    else
+                        gstore<VB>(o_r, laneV, (uint32_t)(t * p.out_tok * XB), o);
                 }
             }
         }
