@@ -328,6 +328,9 @@ int verify(int layout, bool tree, const cv_shape_t *s, const void *x, const void
     // boundaries, so neighbouring wavefronts share lines: keep a row's blocks on one XCD
     a.xcd_remap = s->d_inner % kChw != 0;
     a.out_keep = plan.token_chunks == 1 && plan.workgroups >= cvimpl::kResidentWaves;
+    // dense snapshots gain from it only when a row has one or two of them (256-row T1:
+    // 21.9 -> 21.3 us; T4 and T8 ran 11-13% slower with it)
+    a.snap_keep = a.out_keep && s->T <= 2;
     return launch(pick_verify(plan), plan.workgroups, plan.lds_bytes, a, stream);
 }
 

@@ -106,7 +106,8 @@ constexpr uint32_t kOffLane = 0x80000000u;
 // wavefronts read the same block, so their loads use the default policy (kKeep).  The
 // verify's out stores also take the default policy on launches of a resident generation
 // or more (measured: 14.4 -> 13.8 us on the 128-row T8 shape, 152 -> 132 us on the
-// 512-row T16 one; smaller grids ran 5-15% slower with it, so they keep nt).
+// 512-row T16 one; smaller grids ran 5-15% slower with it, so they keep nt), and so do
+// its dense snapshots when a row has at most two of them.
 constexpr int kNT = 2;
 constexpr int kKeep = 0;
 
@@ -196,12 +197,13 @@ __device__ __forceinline__ void lds_put(char *p, uint32_t v) {
 }
 
 // Streams `chunks` 16-byte chunks from LDS (offset 0) to a buffer, lane-contiguous.
+template <int POL = kNT>
 __device__ __forceinline__ void lds_to_global(const char *lds, int chunks, rsrc_t r, uint32_t soff,
                                               int lane) {
     for (int q = lane; q < chunks; q += kWave) {
         const uint4 v = *(const uint4 *)(lds + q * 16);
         const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
-        gstore<16>(r, (uint32_t)q * 16u, soff, w4);
+        gstore<16, POL>(r, (uint32_t)q * 16u, soff, w4);
     }
 }
 

@@ -38,6 +38,7 @@ struct KernelArgs {
     int32_t slot_first;        // read the slot before any vector load (padded rows load nothing)
     int32_t xcd_remap;         // work index from xcd_linear(blockIdx): a row's blocks on one XCD
     int32_t out_keep;          // out stores with the default cache policy instead of nt
+    int32_t snap_keep;         // dense snapshot stores likewise (launches of out_keep, T <= 2)
 };
 
 // A launch of more wavefronts than the chip holds at once (256 CUs x 4 SIMDs x 5) runs

@@ -699,7 +699,10 @@ void cv_verify_kernel(KernelArgs p) {
                 }
                 lds_write_run<RUNB>(slab + lane * RUNB, run);
                 lds_barrier();
-                lds_to_global(slab, slab_chunks, snap_r, (uint32_t)(t * p.d_inner * W1 * SB), lane);
+                if (p.snap_keep)
+                    lds_to_global<kKeep>(slab, slab_chunks, snap_r, (uint32_t)(t * p.d_inner * W1 * SB), lane);
+                else
+                    lds_to_global(slab, slab_chunks, snap_r, (uint32_t)(t * p.d_inner * W1 * SB), lane);
             }
         }
     }
