@@ -497,16 +497,19 @@ int conv_qk_l2norm(const cv_shape_t *s, int64_t n_rows, int64_t row_stride, void
     if (row_stride % (16 / xb)) return fail(CV_ENOTSUP, "row_stride must be a multiple of %d", 16 / xb);
     if (s->qk_channels % (16 / xb))
         return fail(CV_ENOTSUP, "qk_channels must be a multiple of %d", 16 / xb);
+    if (((int64_t)(cvimpl::kL2Rows - 1) * row_stride + s->qk_channels) * xb > kSpanLimit)
+        return fail(CV_ENOTSUP, "%d rows of x span more than 2 GiB", cvimpl::kL2Rows);
     if (n_rows == 0 || s->qk_channels == 0) return CV_OK;
     if (!x) return fail(CV_EINVAL, "x is NULL");
     if (!aligned16(x)) return fail(CV_ENOTSUP, "x must be 16-byte aligned");
     const int64_t blocks = (s->qk_channels + kChw - 1) / kChw;
-    const int64_t wg = blocks * n_rows;
+    const int64_t wg = blocks * ((n_rows + cvimpl::kL2Rows - 1) / cvimpl::kL2Rows);
     if (wg * cvimpl::kWave > (int64_t)UINT32_MAX)
         return fail(CV_ENOTSUP, "grid of %lld workgroups exceeds the launch limit", (long long)wg);
     cvimpl::L2Args a;
     a.x = x;
     a.row_stride = row_stride;
+    a.n_rows = n_rows;
     a.qk = s->qk_channels;
     a.qk_blocks = (int)blocks;
     a.head_lanes_log2 = hl_log2;

@@ -703,40 +703,61 @@ template <int XB>
 __global__ __launch_bounds__(kWave) void cv_l2_kernel(L2Args p) {
     constexpr int VB = CPL * XB;
     constexpr int XW = VB / 4;
+    constexpr int R = kL2Rows;   // token rows of this wavefront, all loads in flight together
     const int lane = threadIdx.x;
-    const int64_t r = (int64_t)(blockIdx.x / (unsigned)p.qk_blocks);
-    const int cb = (int)(blockIdx.x - (unsigned)r * (unsigned)p.qk_blocks) * CHW;
+    const int64_t rb = (int64_t)(blockIdx.x / (unsigned)p.qk_blocks);
+    const int cb = (int)(blockIdx.x - (unsigned)rb * (unsigned)p.qk_blocks) * CHW;
+    const int64_t r0 = rb * R;
+    const int nr = (int)min((int64_t)R, p.n_rows - r0);   // >= 1: the grid covers the rows once
     const int nch = min(CHW, p.qk - cb);
     const bool on = lane * CPL < nch;
     const uint32_t laneV = on ? (uint32_t)(lane * VB) : kOffLane;
-    const rsrc_t x_r = make_rsrc((char *)p.x + (r * p.row_stride + cb) * XB, (uint32_t)(nch * XB));
-    uint32_t w[XW];
-    gload<VB>(x_r, laneV, 0, w);
-    float y[CPL];
-    float ss[1] = {0.0f};
+    const rsrc_t x_r = make_rsrc((char *)p.x + (r0 * p.row_stride + cb) * XB,
+                                 (uint32_t)(((int64_t)(nr - 1) * p.row_stride + nch) * XB));
+    uint32_t w[R][XW];
 #pragma unroll
-    for (int ch = 0; ch < CPL; ++ch) {
-        y[ch] = elem_val<XB>(w, ch);
-        ss[0] = __builtin_fmaf(y[ch], y[ch], ss[0]);
+    for (int r = 0; r < R; ++r) {
+        if (r < nr) {
+            gload<VB>(x_r, laneV, (uint32_t)(r * p.row_stride * XB), w[r]);
+        } else {
+#pragma unroll
+            for (int q = 0; q < XW; ++q) w[r][q] = 0u;
+        }
+    }
+    float y[R][CPL];
+    float ss[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        ss[r] = 0.0f;
+#pragma unroll
+        for (int ch = 0; ch < CPL; ++ch) {
+            y[r][ch] = elem_val<XB>(w[r], ch);
+            ss[r] = __builtin_fmaf(y[r][ch], y[r][ch], ss[r]);
+        }
     }
     // a head never straddles q|k's end (qk is a multiple of head_dim), so lanes past
     // it form whole groups of their own
-    group_sums<1>(ss, p.head_lanes_log2);
-    const float sc = __builtin_amdgcn_rsqf(ss[0] + p.eps);
-    uint32_t o[XW];
-    if constexpr (XB == 4) {
+    group_sums<R>(ss, p.head_lanes_log2);
 #pragma unroll
-        for (int ch = 0; ch < CPL; ++ch) o[ch] = __float_as_uint(y[ch] * sc);
-    } else {
-        typedef float f2 __attribute__((ext_vector_type(2)));
-        typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+    for (int r = 0; r < R; ++r) {
+        if (r < nr) {
+            const float sc = __builtin_amdgcn_rsqf(ss[r] + p.eps);
+            uint32_t o[XW];
+            if constexpr (XB == 4) {
 #pragma unroll
-        for (int q = 0; q < XW; ++q) {
-            f2 pr = {y[2 * q] * sc, y[2 * q + 1] * sc};
-            o[q] = __builtin_bit_cast(uint32_t, __builtin_convertvector(pr, b2));
+                for (int ch = 0; ch < CPL; ++ch) o[ch] = __float_as_uint(y[r][ch] * sc);
+            } else {
+                typedef float f2 __attribute__((ext_vector_type(2)));
+                typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+#pragma unroll
+                for (int q = 0; q < XW; ++q) {
+                    f2 pr = {y[r][2 * q] * sc, y[r][2 * q + 1] * sc};
+                    o[q] = __builtin_bit_cast(uint32_t, __builtin_convertvector(pr, b2));
+                }
+            }
+            gstore<VB>(x_r, laneV, (uint32_t)(r * p.row_stride * XB), o);
         }
     }
-    gstore<VB>(x_r, laneV, 0, o);
 }
 
 template <int SB, int LAYOUT, bool TM>

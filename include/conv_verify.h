@@ -262,7 +262,8 @@ CV_API int conv_prefill(const cv_shape_t *shape, const void *x, const void *weig
  * (row r at x + r*row_stride, channel stride 1) and each head of head_dim channels in
  * [0, qk_channels): y <- y / sqrt(sum_head y^2 + l2_eps) in fp32, rounded to the x
  * dtype.  Channels >= qk_channels are not touched.  Uses shape fields d_inner,
- * qk_channels, head_dim, l2_eps, x_dtype.
+ * qk_channels, head_dim, l2_eps, x_dtype.  CV_ENOTSUP if 2 consecutive rows span more
+ * than 2 GiB (a wavefront takes 2 rows).
  */
 CV_API int conv_qk_l2norm(const cv_shape_t *shape, int64_t n_rows, int64_t row_stride, void *x,
                    void *hip_stream);
