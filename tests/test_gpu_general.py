@@ -497,3 +497,20 @@ SLOT_FIRST = [c(f"slot_first_{layout}_n{n}{'_tm' if tm else ''}", n_seq=n, d_inn
 @pytest.mark.parametrize("wl", SLOT_FIRST, ids=[w.name for w in SLOT_FIRST])
 def test_slot_first_edge(wl):
     _verify_case(wl)
+
+
+# q|k ending inside a wavefront: lanes of one wavefront split between L2 heads and V
+# channels, for several head sizes, both state orders and layouts.
+QK_EDGE = [c(f"qk{qk}_h{hd}_{layout}{'_tm' if tm else ''}", n_seq=3, d_inner=1032, qk_channels=qk,
+             head_dim=hd, T=T, layout=layout, accept_offsets=True, permute_slots=True,
+             pad_frac=0.25, state_tm=tm)
+           for qk, hd, layout, T, tm in ((384, 128, "dedup", 8, False), (96, 32, "dense", 5, True),
+                                         (776, 8, "dedup_t", 9, False), (1032, 4, "dense", 17, False),
+                                         (640, 64, "dedup", 16, True))]
+QK_EDGE.append(c("one_head_fp32", n_seq=2, d_inner=264, qk_channels=256, head_dim=256, T=3,
+                 x_dtype="f32", state_dtype="f32", accept_offsets=True))
+
+
+@pytest.mark.parametrize("wl", QK_EDGE, ids=[w.name for w in QK_EDGE])
+def test_qk_edges(wl):
+    _verify_case(wl)
