@@ -13,10 +13,13 @@
 //    wavefront; the 1-D grid is n_seq * ceil(d_inner / 256) workgroups.  (256-channel
 //    blocks stream measurably faster on MI355X than 512-channel ones for this traffic
 //    mix: twice the wavefronts keep more requests in flight.)
-//  * Every global access is a lane-contiguous 8- or 16-byte buffer access with the
-//    nt (streaming) policy: x and out per token, and every run of conv_state, the
-//    dense snapshots and the dedup rows, which are staged through LDS so that they
-//    too leave in lane-contiguous units.  Per-token offsets live in SGPRs.
+//  * Every global access is a lane-contiguous 8- or 16-byte buffer access: x and out
+//    per token, the columns of a time-major conv_state and of time-major rows, and
+//    every run of a channel-major conv_state, the dense snapshots and the dedup rows,
+//    which are staged through LDS so that they too leave in lane-contiguous units.
+//    Per-token offsets live in SGPRs.  Loads and stores use the nt (streaming) policy,
+//    except the weights and bias, and out (and short rows' dense snapshots) on
+//    launches of a resident generation or more, which measured faster cached.
 //  * All loads (x for every token, conv_state, weights, bias) are issued before the
 //    first barrier, with raised wave priority; after it the wavefront only stores, so
 //    no wait on a load is ever stuck behind stores (vmcnt counts both).  Later LDS
