@@ -17,6 +17,11 @@ CV_WIN_DENSE = 0
 CV_WIN_ROWS = 1
 CV_WIN_ROWS_T = 2
 CV_VARIANT_TREE = 3
+CV_LAUNCH_STATE_TIME_MAJOR = 1
+CV_LAUNCH_SLOT_FIRST = 2
+CV_LAUNCH_XCD_ORDER = 4
+CV_LAUNCH_OUT_CACHED = 8
+CV_LAUNCH_SNAP_CACHED = 16
 
 EXPORTS = (
     "conv_verify_update_dense",
@@ -55,7 +60,7 @@ class CvLaunchInfo(ctypes.Structure):
         ("channel_blocks", ctypes.c_int32), ("channels_per_wave", ctypes.c_int32),
         ("channels_per_lane", ctypes.c_int32), ("token_bucket", ctypes.c_int32),
         ("lds_bytes", ctypes.c_int32), ("head_lanes", ctypes.c_int32),
-        ("token_chunks", ctypes.c_int32),
+        ("token_chunks", ctypes.c_int32), ("flags", ctypes.c_int32),
     ]
 
 

@@ -231,6 +231,17 @@ int plan_verify(int layout, bool tree, bool packed, const cv_shape_t *s, cvimpl:
     plan->workgroups = wg * chunks;
     plan->lds_bytes = (int)(dense_split ? split_lds : lds);
     plan->head_lanes = head_lanes;
+    // Data-movement choices, each measured on MI355X (none changes a result bit):
+    // a grid of more than one resident generation waits for the slot before loading x
+    // (padded rows then load nothing); a partial last channel block leaves the rows'
+    // buffers off 128-byte line boundaries, so neighbouring wavefronts share lines and a
+    // row's blocks go to one XCD; out (and dense windows of rows of one or two tokens:
+    // 256-row T1 21.9 -> 21.3 us, T4 and T8 ran 11-13% slower) is stored cached on
+    // grids of a resident generation or more with no token split.
+    plan->slot_first = plan->workgroups > cvimpl::kResidentWaves;
+    plan->xcd_remap = s->d_inner % kChw != 0;
+    plan->out_keep = chunks == 1 && plan->workgroups >= cvimpl::kResidentWaves;
+    plan->snap_keep = plan->out_keep && s->T <= 2;
     return CV_OK;
 }
 
@@ -323,14 +334,10 @@ int verify(int layout, bool tree, const cv_shape_t *s, const void *x, const void
     a.eps = s->l2_eps;
     a.token_chunks = plan.token_chunks;
     a.state_col = s->state_col_stride;
-    a.slot_first = slot_idx != nullptr && plan.workgroups > cvimpl::kResidentWaves;
-    // a partial last channel block leaves the rows' buffers off 128-byte line
-    // boundaries, so neighbouring wavefronts share lines: keep a row's blocks on one XCD
-    a.xcd_remap = s->d_inner % kChw != 0;
-    a.out_keep = plan.token_chunks == 1 && plan.workgroups >= cvimpl::kResidentWaves;
-    // dense snapshots gain from it only when a row has one or two of them (256-row T1:
-    // 21.9 -> 21.3 us; T4 and T8 ran 11-13% slower with it)
-    a.snap_keep = a.out_keep && s->T <= 2;
+    a.slot_first = slot_idx != nullptr && plan.slot_first;
+    a.xcd_remap = plan.xcd_remap;
+    a.out_keep = plan.out_keep;
+    a.snap_keep = plan.snap_keep;
     return launch(pick_verify(plan), plan.workgroups, plan.lds_bytes, a, stream);
 }
 
@@ -534,6 +541,11 @@ int conv_verify_describe(int variant, const cv_shape_t *shape, cv_launch_info_t 
     info->lds_bytes = plan.lds_bytes;
     info->head_lanes = plan.head_lanes;
     info->token_chunks = plan.token_chunks;
+    info->flags = (plan.state_tm ? CV_LAUNCH_STATE_TIME_MAJOR : 0) |
+                  (plan.slot_first ? CV_LAUNCH_SLOT_FIRST : 0) |
+                  (plan.xcd_remap ? CV_LAUNCH_XCD_ORDER : 0) |
+                  (plan.out_keep ? CV_LAUNCH_OUT_CACHED : 0) |
+                  (plan.snap_keep ? CV_LAUNCH_SNAP_CACHED : 0);
     return CV_OK;
 }
 

@@ -76,6 +76,10 @@ struct Plan {
     int token_chunks;          // wavefronts per (row, channel block) along T
     int lean;                  // 16-token bucket built for 5 wavefronts per SIMD
     int state_tm;              // conv_state time-major (the kernels' TM build)
+    int slot_first;            // KernelArgs::slot_first when a slot table is passed
+    int xcd_remap;             // KernelArgs::xcd_remap
+    int out_keep;              // KernelArgs::out_keep
+    int snap_keep;             // KernelArgs::snap_keep
     int channels_per_lane;     // kChannelsPerLane
     int channel_blocks;
     int64_t workgroups;

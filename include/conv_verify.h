@@ -285,7 +285,24 @@ typedef struct cv_launch_info {
                                /* wavefronts, each computing its 4-token chunk (dense      */
                                /* chain verify: token_bucket 4; row layouts: chunk 0 also  */
                                /* writes the row block and the state)                      */
+    int32_t flags;             /* CV_LAUNCH_* bits: how the launch moves its data          */
 } cv_launch_info_t;
+
+/* cv_launch_info_t.flags (host-side launch choices; none changes a result bit):
+ *   STATE_TIME_MAJOR  the time-major conv_state build (state_col_stride > 0)
+ *   SLOT_FIRST        with a slot table, a wavefront reads its row's slot before any
+ *                     vector load, so padded rows load nothing (grids of more than
+ *                     5,120 wavefronts: more than one resident generation)
+ *   XCD_ORDER         work items follow MI355X's round-robin XCD dispatch so that a row's
+ *                     channel blocks share one L2 (d_inner not a multiple of 256)
+ *   OUT_CACHED        out is stored with the default cache policy instead of streaming
+ *                     (grids of at least 5,120 wavefronts with no token split)
+ *   SNAP_CACHED       dense windows likewise (OUT_CACHED launches with T <= 2) */
+#define CV_LAUNCH_STATE_TIME_MAJOR 1
+#define CV_LAUNCH_SLOT_FIRST 2
+#define CV_LAUNCH_XCD_ORDER 4
+#define CV_LAUNCH_OUT_CACHED 8
+#define CV_LAUNCH_SNAP_CACHED 16
 
 /* variant: a cv_layout_t, or CV_VARIANT_TREE for conv_verify_update_tree.  Returns
  * CV_OK or an error code. */
