@@ -64,3 +64,33 @@ def test_random_config(wl):
     if wl.restore:
         p.restore()
     gh.compare_general(p.results(), gh.oracle_general(inp, restore=wl.restore), inp)
+
+
+def _draw_large(k: int, rng: np.random.Generator):
+    """A grid of at least one resident generation (>= 5,120 wavefronts), where the launch
+    reads slots first, stores out cached and (partial blocks) follows the XCD order."""
+    d = 8 * int(rng.integers(650, 1281))
+    blocks = -(-d // 256)
+    n = int(rng.integers(-(-5120 // blocks), 700))
+    hd = int(rng.choice((64, 128, 256)))
+    layout = str(rng.choice(["dense", "dedup", "dedup_t"]))
+    tm = bool(rng.random() < 0.5)
+    return workloads.custom(
+        f"rand_large{k}", n_seq=n, d_inner=d, qk_channels=hd * int(rng.integers(0, d // hd + 1)),
+        head_dim=hd, T=int(rng.integers(1, 17)), layout=layout,
+        state_dtype=str(rng.choice(["bf16", "f32"])), bias=bool(rng.random() < 0.5),
+        accept_offsets=True, pad_frac=0.15, permute_slots=True, extra_slots=1, state_tm=tm,
+        state_col_pad=8 if tm else 0, seed=workloads.BASE_SEED + 5500 + k)
+
+
+_rng_large = np.random.default_rng(workloads.BASE_SEED + 5499)
+LARGE = [_draw_large(k, _rng_large) for k in range(6)]
+
+
+@pytest.mark.parametrize("wl", LARGE, ids=[w.name for w in LARGE])
+def test_random_large_grid(wl):
+    print("[case]", wl, flush=True)
+    inp = workloads.make_inputs(wl)
+    p = gh.GeneralProblem(inp)
+    p.verify()
+    gh.compare_general(p.results(), gh.oracle_general(inp), inp)
