@@ -208,7 +208,7 @@ def main(argv=None):
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the verify conv shards by sequence or by "
-              "channel with no exchange, and this build runs on a single MI355X "
+              "channel with no exchange, and the library runs on a single MI355X "
               f"(asked for --gpus {args.gpus}).", file=sys.stderr)
         return 2
 
