@@ -20,8 +20,6 @@ CV_VARIANT_TREE = 3
 CV_LAUNCH_STATE_TIME_MAJOR = 1
 CV_LAUNCH_SLOT_FIRST = 2
 CV_LAUNCH_XCD_ORDER = 4
-CV_LAUNCH_OUT_CACHED = 8
-CV_LAUNCH_SNAP_CACHED = 16
 
 EXPORTS = (
     "conv_verify_update_dense",

@@ -235,13 +235,9 @@ int plan_verify(int layout, bool tree, bool packed, const cv_shape_t *s, cvimpl:
     // a grid of more than one resident generation waits for the slot before loading x
     // (padded rows then load nothing); a partial last channel block leaves the rows'
     // buffers off 128-byte line boundaries, so neighbouring wavefronts share lines and a
-    // row's blocks go to one XCD; out (and dense windows of rows of one or two tokens:
-    // 256-row T1 21.9 -> 21.3 us, T4 and T8 ran 11-13% slower) is stored cached on
-    // grids of a resident generation or more with no token split.
+    // row's blocks go to one XCD.
     plan->slot_first = plan->workgroups > cvimpl::kResidentWaves;
     plan->xcd_remap = s->d_inner % kChw != 0;
-    plan->out_keep = chunks == 1 && plan->workgroups >= cvimpl::kResidentWaves;
-    plan->snap_keep = plan->out_keep && s->T <= 2;
     return CV_OK;
 }
 
@@ -336,8 +332,6 @@ int verify(int layout, bool tree, const cv_shape_t *s, const void *x, const void
     a.state_col = s->state_col_stride;
     a.slot_first = slot_idx != nullptr && plan.slot_first;
     a.xcd_remap = plan.xcd_remap;
-    a.out_keep = plan.out_keep;
-    a.snap_keep = plan.snap_keep;
     return launch(pick_verify(plan), plan.workgroups, plan.lds_bytes, a, stream);
 }
 
@@ -543,9 +537,7 @@ int conv_verify_describe(int variant, const cv_shape_t *shape, cv_launch_info_t 
     info->token_chunks = plan.token_chunks;
     info->flags = (plan.state_tm ? CV_LAUNCH_STATE_TIME_MAJOR : 0) |
                   (plan.slot_first ? CV_LAUNCH_SLOT_FIRST : 0) |
-                  (plan.xcd_remap ? CV_LAUNCH_XCD_ORDER : 0) |
-                  (plan.out_keep ? CV_LAUNCH_OUT_CACHED : 0) |
-                  (plan.snap_keep ? CV_LAUNCH_SNAP_CACHED : 0);
+                  (plan.xcd_remap ? CV_LAUNCH_XCD_ORDER : 0);
     return CV_OK;
 }
 

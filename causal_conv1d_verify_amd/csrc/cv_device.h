@@ -103,11 +103,7 @@ constexpr uint32_t kOffLane = 0x80000000u;
 // Cache policy of the global accesses: nt (streaming).  Each byte of x, out, conv_state
 // and the windows is read or written once per launch, so none of it is worth keeping
 // in L2 or the Infinity Cache.  The weights (and bias) are the exception: every row's
-// wavefronts read the same block, so their loads use the default policy (kKeep).  The
-// verify's out stores also take the default policy on launches of a resident generation
-// or more (measured: 14.4 -> 13.8 us on the 128-row T8 shape, 152 -> 132 us on the
-// 512-row T16 one; smaller grids ran 5-15% slower with it, so they keep nt), and so do
-// its dense snapshots when a row has at most two of them.
+// wavefronts read the same block, so their loads use the default policy (kKeep).
 constexpr int kNT = 2;
 constexpr int kKeep = 0;
 

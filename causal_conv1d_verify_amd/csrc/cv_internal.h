@@ -37,15 +37,11 @@ struct KernelArgs {
     int64_t state_col;         // 0: conv_state channel-major; else time-major column stride
     int32_t slot_first;        // read the slot before any vector load (padded rows load nothing)
     int32_t xcd_remap;         // work index from xcd_linear(blockIdx): a row's blocks on one XCD
-    int32_t out_keep;          // out stores with the default cache policy instead of nt
-    int32_t snap_keep;         // dense snapshot stores likewise (launches of out_keep, T <= 2)
 };
 
 // A launch of more wavefronts than the chip holds at once (256 CUs x 4 SIMDs x 5) runs
 // in generations: there a wavefront waits for its row's slot before loading x, so the
 // x of padded rows is never read; a launch that fits in one generation issues x first.
-// Launches of at least this many wavefronts (and no token split) also store out with the
-// default cache policy rather than nt, which measured faster there and slower below.
 constexpr int64_t kResidentWaves = 5120;
 
 // The rows layout's compile-time-length path stages a wavefront's row block in LDS in
@@ -78,8 +74,6 @@ struct Plan {
     int state_tm;              // conv_state time-major (the kernels' TM build)
     int slot_first;            // KernelArgs::slot_first when a slot table is passed
     int xcd_remap;             // KernelArgs::xcd_remap
-    int out_keep;              // KernelArgs::out_keep
-    int snap_keep;             // KernelArgs::snap_keep
     int channels_per_lane;     // kChannelsPerLane
     int channel_blocks;
     int64_t workgroups;

@@ -18,8 +18,7 @@
 //    every run of a channel-major conv_state, the dense snapshots and the dedup rows,
 //    which are staged through LDS so that they too leave in lane-contiguous units.
 //    Per-token offsets live in SGPRs.  Loads and stores use the nt (streaming) policy,
-//    except the weights and bias, and out (and short rows' dense snapshots) on
-//    launches of a resident generation or more, which measured faster cached.
+//    except the weights and bias, which every row's wavefronts read.
 //  * All loads (x for every token, conv_state, weights, bias) are issued before the
 //    first barrier, with raised wave priority; after it the wavefront only stores, so
 //    no wait on a load is ever stuck behind stores (vmcnt counts both).  Later LDS
@@ -462,10 +461,7 @@ void cv_verify_kernel(KernelArgs p) {
                             o[w] = __builtin_bit_cast(uint32_t, __builtin_convertvector(pr, b2));
                         }
                     }
-                    if (p.out_keep)
-                        gstore<VB, kKeep>(o_r, laneV, (uint32_t)(t * p.out_tok * XB), o);
-                    else
-                        gstore<VB>(o_r, laneV, (uint32_t)(t * p.out_tok * XB), o);
+                    gstore<VB>(o_r, laneV, (uint32_t)(t * p.out_tok * XB), o);
                 }
             }
         }
@@ -702,10 +698,7 @@ void cv_verify_kernel(KernelArgs p) {
                 }
                 lds_write_run<RUNB>(slab + lane * RUNB, run);
                 lds_barrier();
-                if (p.snap_keep)
-                    lds_to_global<kKeep>(slab, slab_chunks, snap_r, (uint32_t)(t * p.d_inner * W1 * SB), lane);
-                else
-                    lds_to_global(slab, slab_chunks, snap_r, (uint32_t)(t * p.d_inner * W1 * SB), lane);
+                lds_to_global(slab, slab_chunks, snap_r, (uint32_t)(t * p.d_inner * W1 * SB), lane);
             }
         }
     }

@@ -294,15 +294,10 @@ typedef struct cv_launch_info {
  *                     vector load, so padded rows load nothing (grids of more than
  *                     5,120 wavefronts: more than one resident generation)
  *   XCD_ORDER         work items follow MI355X's round-robin XCD dispatch so that a row's
- *                     channel blocks share one L2 (d_inner not a multiple of 256)
- *   OUT_CACHED        out is stored with the default cache policy instead of streaming
- *                     (grids of at least 5,120 wavefronts with no token split)
- *   SNAP_CACHED       dense windows likewise (OUT_CACHED launches with T <= 2) */
+ *                     channel blocks share one L2 (d_inner not a multiple of 256) */
 #define CV_LAUNCH_STATE_TIME_MAJOR 1
 #define CV_LAUNCH_SLOT_FIRST 2
 #define CV_LAUNCH_XCD_ORDER 4
-#define CV_LAUNCH_OUT_CACHED 8
-#define CV_LAUNCH_SNAP_CACHED 16
 
 /* variant: a cv_layout_t, or CV_VARIANT_TREE for conv_verify_update_tree.  Returns
  * CV_OK or an error code. */

@@ -37,7 +37,7 @@ int main(void) {
     expect("  token bucket", info.token_bucket, 8);
     expect("  head lanes", info.head_lanes, 32);
     expect("  token chunks", info.token_chunks, 1);
-    expect("  out stored cached (one full generation)", (info.flags & CV_LAUNCH_OUT_CACHED) != 0, 1);
+    expect("  no slot-first wait (one generation)", (info.flags & CV_LAUNCH_SLOT_FIRST) != 0, 0);
     expect("describe time-major rows", conv_verify_describe(CV_WIN_ROWS_T, &s, &info), CV_OK);
     expect("describe dense (rows-sized slots)", conv_verify_describe(CV_WIN_DENSE, &s, &info), CV_EINVAL);
     if (!strlen(conv_verify_last_error())) { puts("missing error detail"); fails = 1; }
