@@ -604,23 +604,8 @@ __global__ __launch_bounds__(kWave) void cv_split_kernel(KernelArgs p) {
             for (int w = 0; w < D; ++w) acc = __builtin_fmaf(wv[ch][w], val(g + w, ch), acc);
             y[g][ch] = silu(acc);
         }
-    if (cb < p.qk) {   // uniform: this wavefront holds q|k channels
-        const bool lane_l2 = lane * CPL + cb < p.qk;
-        float ss[TC];
-#pragma unroll
-        for (int g = 0; g < TC; ++g) {
-            ss[g] = 0.0f;
-#pragma unroll
-            for (int ch = 0; ch < CPL; ++ch) ss[g] = __builtin_fmaf(y[g][ch], y[g][ch], ss[g]);
-        }
-        group_sums<TC>(ss, p.head_lanes_log2);
-#pragma unroll
-        for (int g = 0; g < TC; ++g) {
-            const float sc = lane_l2 ? __builtin_amdgcn_rsqf(ss[g] + p.eps) : 1.0f;
-#pragma unroll
-            for (int ch = 0; ch < CPL; ++ch) y[g][ch] *= sc;
-        }
-    }
+    if (cb < p.qk)   // uniform: this wavefront holds q|k channels
+        head_l2<TC>(y, lane * CPL + cb < p.qk, p.head_lanes_log2, p.eps);
     const rsrc_t o_r = make_rsrc((char *)p.out + (orow + cb) * XB,
                                  (uint32_t)(((int64_t)(T - 1) * p.out_tok + nch) * XB));
 #pragma unroll
@@ -725,33 +710,26 @@ __global__ __launch_bounds__(kWave) void cv_l2_kernel(L2Args p) {
         }
     }
     float y[R][CPL];
-    float ss[R];
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
-        ss[r] = 0.0f;
+    for (int r = 0; r < R; ++r)
 #pragma unroll
-        for (int ch = 0; ch < CPL; ++ch) {
-            y[r][ch] = elem_val<XB>(w[r], ch);
-            ss[r] = __builtin_fmaf(y[r][ch], y[r][ch], ss[r]);
-        }
-    }
+        for (int ch = 0; ch < CPL; ++ch) y[r][ch] = elem_val<XB>(w[r], ch);
     // a head never straddles q|k's end (qk is a multiple of head_dim), so lanes past
-    // it form whole groups of their own
-    group_sums<R>(ss, p.head_lanes_log2);
+    // it form whole groups of their own; they store nothing
+    head_l2<R>(y, on, p.head_lanes_log2, p.eps);
 #pragma unroll
     for (int r = 0; r < R; ++r) {
         if (r < nr) {
-            const float sc = __builtin_amdgcn_rsqf(ss[r] + p.eps);
             uint32_t o[XW];
             if constexpr (XB == 4) {
 #pragma unroll
-                for (int ch = 0; ch < CPL; ++ch) o[ch] = __float_as_uint(y[r][ch] * sc);
+                for (int ch = 0; ch < CPL; ++ch) o[ch] = __float_as_uint(y[r][ch]);
             } else {
                 typedef float f2 __attribute__((ext_vector_type(2)));
                 typedef __bf16 b2 __attribute__((ext_vector_type(2)));
 #pragma unroll
                 for (int q = 0; q < XW; ++q) {
-                    f2 pr = {y[r][2 * q] * sc, y[r][2 * q + 1] * sc};
+                    f2 pr = {y[r][2 * q], y[r][2 * q + 1]};
                     o[q] = __builtin_bit_cast(uint32_t, __builtin_convertvector(pr, b2));
                 }
             }

@@ -45,10 +45,24 @@ __device__ __forceinline__ uint32_t x_to_state_bits(uint32_t xbits) {
     }
 }
 
+// SiLU(p) = p * sigmoid(p) with v_exp_f32 and v_rcp_f32, in a form with no overflow and
+// no intermediate outside fp32's normal range.  With e = 2^q, q = -|p| * log2(e) <= 0:
+// sigmoid(p) = 1 / (1 + e) for p >= 0 and e / (1 + e) for p < 0, so the reciprocal's
+// argument stays in [1, 2].  Neither instruction returns a subnormal, and e leaves the
+// normal range at p ~ -87.3, where SiLU(p) is still a normal fp32 (and bf16) value; so
+// for q < -100 the exponential is taken 64 binades up (normal down to p ~ -131.7) and the
+// product is scaled back by 2^-64 in the last multiply, which rounds into fp32's
+// subnormals like any other multiply (denormals are enabled).  Below p ~ -131.7 the
+// shifted exponential flushes to 0 and the result is -0: the exact value is then under
+// 1e-55, far below half of fp32's smallest subnormal.  q + 64 is exact for q < -100.
+// +-inf give +inf and NaN, and NaN stays NaN, as p / (1 + exp(-p)) does.
 __device__ __forceinline__ float silu(float p) {
-    // p * sigmoid(p) with v_exp_f32 and v_rcp_f32.  For p << 0 the exponential
-    // saturates to +inf and the result is -0.
-    return p * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(p * -1.4426950408889634f));
+    const float q = __builtin_fabsf(p) * -1.4426950408889634f;
+    const bool deep = q < -100.0f;
+    const float e = __builtin_amdgcn_exp2f(deep ? q + 64.0f : q);   // 2^q, or 2^(q + 64)
+    const float scale = deep ? 0x1p-64f : 1.0f;
+    const float r = __builtin_amdgcn_rcpf(__builtin_fmaf(e, scale, 1.0f));   // 1 / (1 + 2^q)
+    return p < 0.0f ? ((p * e) * r) * scale : p * r;
 }
 
 template <int CTRL>
@@ -83,6 +97,89 @@ __device__ __forceinline__ void group_sums(float (&v)[G], int hl_log2) {
 #pragma unroll
         for (int g = 0; g < G; ++g)
             v[g] += __int_as_float(__builtin_amdgcn_ds_bpermute(src, __float_as_int(v[g])));
+    }
+}
+
+// group_sums for one value with every stage selected rather than branched on: the rare
+// path of head_l2 uses it, where branches (and per-stage lane addresses) would hold
+// registers across the whole token loop.
+__device__ __forceinline__ float group_sum_sel(float v, int hl_log2) {
+    float o = dpp<0xB1>(v);
+    v = hl_log2 >= 1 ? v + o : v;
+    o = dpp<0x4E>(v);
+    v = hl_log2 >= 2 ? v + o : v;
+    o = dpp<0x141>(v);
+    v = hl_log2 >= 3 ? v + o : v;
+    o = dpp<0x140>(v);
+    v = hl_log2 >= 4 ? v + o : v;
+    o = __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x401F));
+    v = hl_log2 >= 5 ? v + o : v;
+    o = __int_as_float(__builtin_amdgcn_ds_bpermute((int)((threadIdx.x ^ 32u) << 2), __float_as_int(v)));
+    v = hl_log2 >= 6 ? v + o : v;
+    return v;
+}
+
+// Per-head L2 of G token rows held as y[g][channel], the lane's kChannelsPerLane
+// channels: y <- y / sqrt(S + eps), S = sum_head y^2, on lanes with lane_l2 set (a head
+// is the aligned group of 2^hl_log2 lanes); other lanes keep y.  All lanes active.
+//
+// S runs in fp32 (any reduction order) with v_rsq_f32.  That is accurate while
+// S + eps <= 2^127 (no partial sum overflows) and either S >= 2^-100 (squares below
+// 2^-126 lose bits, but are then at most 2^-42 of S) or eps >= 2^-60 (S is then at most
+// 2^-40 of eps).  When a head of the wavefront is outside that range - |y| from ~1.3e19
+// up, or tiny values with eps < 2^-60 - every head is summed again over y * f for a
+// power of two f that brings its squares into range: 2^-70 after an overflow (|y f| <
+// 2^58, so the sum stays below 2^124 and, as S >= 2^126, above 2^-14), 2^100 for a tiny
+// S (every |y| < 2^-50, so the squares lie in [2^-98, 2^100) unless 0), and 1 for a head
+// that was in range (the same sum, bit for bit).  The scale is then rsq(sum + eps f^2)
+// * f; the multiply by 2^-70 rounds into fp32's subnormals when |y| nears fp32's maximum
+// (still 17 or more significant bits, and |out| <= 1).  Where eps f^2 >= 2^127 the sum is
+// below 2^-27 of it and the scale is rsq(eps).  Left out: eps = 0 with a head whose S is
+// below 2^-256 (every value subnormal), whose scale exceeds fp32's range.  NaN and
+// infinities give what y / sqrt(S + eps) gives.  The stages of the second sum are
+// selected rather than branched on, so the rare path costs the common one no registers.
+template <int G>
+__device__ __forceinline__ void head_l2(float (&y)[G][kChannelsPerLane], bool lane_l2,
+                                        int hl_log2, float eps) {
+    constexpr int CPL = kChannelsPerLane;
+    float ss[G];
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+        ss[g] = 0.0f;
+#pragma unroll
+        for (int ch = 0; ch < CPL; ++ch) ss[g] = __builtin_fmaf(y[g][ch], y[g][ch], ss[g]);
+    }
+    group_sums<G>(ss, hl_log2);
+    bool all_in = true;
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+        all_in = all_in && ss[g] + eps <= 0x1p127f && (ss[g] >= 0x1p-100f || eps >= 0x1p-60f);
+    float sc[G];
+    if (__builtin_amdgcn_ballot_w64(lane_l2 && !all_in) == 0) {
+#pragma unroll
+        for (int g = 0; g < G; ++g) sc[g] = __builtin_amdgcn_rsqf(ss[g] + eps);
+    } else {
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            // f = 1 for a head in range: the same sum again, bit for bit
+            const float f = !(ss[g] + eps <= 0x1p127f) ? 0x1p-70f
+                            : (ss[g] >= 0x1p-100f || eps >= 0x1p-60f) ? 1.0f : 0x1p100f;
+            float s = 0.0f;
+#pragma unroll
+            for (int ch = 0; ch < CPL; ++ch) {
+                const float u = y[g][ch] * f;
+                s = __builtin_fmaf(u, u, s);
+            }
+            s = group_sum_sel(s, hl_log2);
+            const float ep = eps * f * f;
+            sc[g] = ep < 0x1p127f ? __builtin_amdgcn_rsqf(s + ep) * f : __builtin_amdgcn_rsqf(eps);
+        }
+    }
+    if (lane_l2) {
+#pragma unroll
+        for (int g = 0; g < G; ++g)
+#pragma unroll
+            for (int ch = 0; ch < CPL; ++ch) y[g][ch] *= sc[g];
     }
 }
 

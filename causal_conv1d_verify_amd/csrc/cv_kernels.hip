@@ -428,22 +428,7 @@ void cv_verify_kernel(KernelArgs p) {
                     }
                     y[g][ch] = silu(acc);
                 }
-            if (wave_l2) {
-                float ss[G];
-#pragma unroll
-                for (int g = 0; g < G; ++g) {
-                    ss[g] = 0.0f;
-#pragma unroll
-                    for (int ch = 0; ch < CPL; ++ch) ss[g] = __builtin_fmaf(y[g][ch], y[g][ch], ss[g]);
-                }
-                group_sums<G>(ss, p.head_lanes_log2);
-#pragma unroll
-                for (int g = 0; g < G; ++g) {
-                    const float sc = lane_l2 ? __builtin_amdgcn_rsqf(ss[g] + p.eps) : 1.0f;
-#pragma unroll
-                    for (int ch = 0; ch < CPL; ++ch) y[g][ch] *= sc;
-                }
-            }
+            if (wave_l2) head_l2<G>(y, lane_l2, p.head_lanes_log2, p.eps);
 #pragma unroll
             for (int g = 0; g < G; ++g) {
                 const int t = t0 + g;
