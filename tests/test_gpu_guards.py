@@ -93,7 +93,7 @@ CASES += [
       init_frac=0.5, state_len=6),
     c("guard_prefill_tm", n_seq=4, d_inner=1032, qk_channels=0, T=40, varlen=True, prefill=True,
       init_frac=0.5, state_tm=True),
-    # past one resident generation (slot first, cached out), partial blocks (XCD order)
+    # past one resident generation (slot first), partial blocks (XCD order)
     c("guard_large", n_seq=1300, d_inner=1000, qk_channels=512, head_dim=128, T=4,
       layout="dedup", accept_offsets=True, permute_slots=True, pad_frac=0.2, state_tm=True),
     c("guard_large_dense_t1", n_seq=1300, d_inner=1024, qk_channels=512, head_dim=128, T=1,

@@ -68,7 +68,7 @@ def test_random_config(wl):
 
 def _draw_large(k: int, rng: np.random.Generator):
     """A grid of at least one resident generation (>= 5,120 wavefronts), where the launch
-    reads slots first, stores out cached and (partial blocks) follows the XCD order."""
+    reads slots first and (partial blocks) follows the XCD order."""
     d = 8 * int(rng.integers(650, 1281))
     blocks = -(-d // 256)
     n = int(rng.integers(-(-5120 // blocks), 700))
