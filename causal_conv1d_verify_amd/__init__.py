@@ -134,6 +134,17 @@ def _check_state(conv_state, d_inner) -> int:
                      "[n_slots, state_len, >= d_inner] buffer")
 
 
+def _check_window_slots(conv_state, windows) -> int:
+    """The window buffer is indexed by slot like conv_state (the kernels bound a slot by
+    n_slots, then address windows + slot * win_slot_stride), so it must hold at least as
+    many slots as the pool.  Returns n_slots."""
+    n_slots = conv_state.shape[0]
+    if windows.shape[0] < n_slots:
+        raise ValueError(f"the window buffer holds {windows.shape[0]} slots but conv_state has "
+                         f"{n_slots}: windows are indexed by slot, so they need at least as many")
+    return n_slots
+
+
 def _verify_args(layout, tree, x, weight, bias, conv_state, out, windows, qk_channels,
                  head_dim, l2_eps, slot_idx, num_accept_tokens, cu_seqlens, parent, stream):
     import torch
@@ -176,7 +187,8 @@ def _verify_args(layout, tree, x, weight, bias, conv_state, out, windows, qk_cha
         if parent is None or parent.dtype != torch.int32 or tuple(parent.shape) != (n_seq, T) \
                 or not parent.is_contiguous():
             raise ValueError(f"parent must be a contiguous int32 [{n_seq}, {T}] tensor")
-    n_slots, _, state_len = conv_state.shape
+    n_slots = _check_window_slots(conv_state, windows)
+    state_len = conv_state.shape[2]
     shape = _lib.CvShape(
         n_seq=n_seq, T=T, d_inner=d_inner, d_conv=d_conv, qk_channels=qk_channels,
         head_dim=head_dim, l2_eps=l2_eps, x_dtype=_dtype_code(x),
@@ -211,7 +223,8 @@ def _restore_args(conv_state, windows, window_index, layout, d_conv, slot_idx, s
     n_seq = window_index.shape[0]
     _int32_vec("window_index", window_index, n_seq)
     _int32_vec("slot_idx", slot_idx, n_seq)
-    n_slots, _, state_len = conv_state.shape
+    n_slots = _check_window_slots(conv_state, windows)
+    state_len = conv_state.shape[2]
     dt = _dtype_code(conv_state)
     # the restore moves state-typed bits only; x_dtype just has to form a valid pair
     shape = _lib.CvShape(n_seq=n_seq, T=T, d_inner=d_inner, d_conv=d_conv, x_dtype=dt,

@@ -423,3 +423,17 @@ def test_launch_flags_edges():
     # the time-major conv_state build
     f = _flags(1, **dict(rows(128, 8), state_col_stride=10240))[2]
     assert f == L.CV_LAUNCH_STATE_TIME_MAJOR
+
+
+def test_binding_refuses_window_buffers_with_fewer_slots():
+    """Windows are indexed by slot: a buffer with fewer slots than conv_state would let
+    a valid slot address past its end, so the binding refuses it before any launch."""
+    torch = pytest.importorskip("torch")
+    import causal_conv1d_verify_amd as cv
+
+    n, d, sl, T = 6, 256, 3, 4
+    state = torch.zeros(n, d, sl)
+    assert cv._check_window_slots(state, torch.zeros(n, T, d, 3)) == n
+    assert cv._check_window_slots(state, torch.zeros(n + 2, d, T + 2)) == n
+    with pytest.raises(ValueError, match="indexed by slot"):
+        cv._check_window_slots(state, torch.zeros(n - 1, d, T + 2))
