@@ -36,6 +36,22 @@ bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 constexpr int64_t kSpanLimit = ((int64_t)1 << 31) - 16;   // buffer-resource offsets stay below 2^31
 constexpr int kChw = cvimpl::kWave * cvimpl::kChannelsPerLane;
 
+// Size arithmetic on caller-supplied values (all >= 0 where these are used), saturating
+// at INT64_MAX instead of overflowing: the results are only compared against limits,
+// so an absurd size is refused rather than wrapped into an acceptable one.
+int64_t sat_mul(int64_t a, int64_t b) {
+    int64_t r;
+    return __builtin_mul_overflow(a, b, &r) ? INT64_MAX : r;
+}
+int64_t sat_add(int64_t a, int64_t b) {
+    int64_t r;
+    return __builtin_add_overflow(a, b, &r) ? INT64_MAX : r;
+}
+// bytes spanned by `rows` rows `stride` elements apart, the last of `width` elements
+int64_t span_bytes(int64_t rows, int64_t stride, int64_t width, int elem_bytes) {
+    return sat_mul(sat_add(sat_mul(rows - 1, stride), width), elem_bytes);
+}
+
 // Checks shared by every entry point: dtypes, d_conv, channels, state geometry.
 int check_common(const cv_shape_t *s, int *xb_out, int *sb_out) {
     if (!s) return fail(CV_EINVAL, "shape is NULL");
@@ -67,14 +83,15 @@ int check_common(const cv_shape_t *s, int *xb_out, int *sb_out) {
         return fail(CV_EINVAL, "state_col_stride (%lld) < d_inner: state columns overlap",
                     (long long)col);
     // elements one slot's state spans, in either layout
-    const int64_t state_span = col > 0 ? (int64_t)(s->state_len - 1) * col + C : C * s->state_len;
+    const int64_t state_span = col > 0 ? sat_add(sat_mul(s->state_len - 1, col), C)
+                                       : sat_mul(C, s->state_len);
     if (s->n_slots > 1 && s->state_slot_stride < state_span)
         return fail(CV_EINVAL, "state_slot_stride (%lld) < the %lld elements of a slot's state",
                     (long long)s->state_slot_stride, (long long)state_span);
-    if ((s->state_slot_stride * sb) % 16 || (s->win_slot_stride * sb) % 16 || (col * sb) % 16)
+    if (s->state_slot_stride % (16 / sb) || s->win_slot_stride % (16 / sb) || col % (16 / sb))
         return fail(CV_ENOTSUP, "state/window slot and state column strides must be multiples "
                                 "of 16 bytes");
-    if (state_span * sb > kSpanLimit)
+    if (sat_mul(state_span, sb) > kSpanLimit)
         return fail(CV_ENOTSUP, "a slot's state spans more than 2 GiB");
     *xb_out = xb;
     *sb_out = sb;
@@ -133,7 +150,8 @@ int plan_verify(int layout, bool tree, bool packed, const cv_shape_t *s, cvimpl:
     if ((s->T > 1 || packed) && s->out_tok_stride < C)
         return fail(CV_EINVAL, "out_tok_stride (%lld) < d_inner: tokens of out overlap",
                     (long long)s->out_tok_stride);
-    if (!packed && s->n_seq > 1 && s->out_seq_stride < (s->T - 1) * s->out_tok_stride + C)
+    if (!packed && s->n_seq > 1 &&
+        s->out_seq_stride < sat_add(sat_mul(s->T - 1, s->out_tok_stride), C))
         return fail(CV_EINVAL, "out_seq_stride (%lld) too small: rows of out overlap",
                     (long long)s->out_seq_stride);
     const int64_t wps = win_per_slot(layout, s);
@@ -146,7 +164,7 @@ int plan_verify(int layout, bool tree, bool packed, const cv_shape_t *s, cvimpl:
 
     const int64_t blocks = (C + kChw - 1) / kChw;
     const int64_t wg = blocks * (int64_t)s->n_seq;
-    if (wg * kWave > (int64_t)UINT32_MAX)
+    if (sat_mul(wg, kWave) > (int64_t)UINT32_MAX)
         return fail(CV_ENOTSUP, "grid of %lld workgroups exceeds the launch limit", (long long)wg);
     int tb = 1;                                  // token buckets: 1 2 4 8 16 24 32
     while (tb < s->T && tb < 16) tb *= 2;
@@ -186,8 +204,8 @@ int plan_verify(int layout, bool tree, bool packed, const cv_shape_t *s, cvimpl:
         return fail(CV_ENOTSUP, "kernel needs %lld bytes of LDS (> %d)", (long long)lds, kMaxLds);
     // Buffer resources span one row's bytes with a 32-bit size; lanes past d_inner use
     // the offset 2^31, so every span must stay below it.
-    const int64_t x_span = ((int64_t)(s->T - 1) * s->x_tok_stride + C) * xb;
-    const int64_t o_span = ((int64_t)(s->T - 1) * s->out_tok_stride + C) * xb;
+    const int64_t x_span = span_bytes(s->T, s->x_tok_stride, C, xb);
+    const int64_t o_span = span_bytes(s->T, s->out_tok_stride, C, xb);
     const int64_t w_span = wps * sb;
     if (x_span > kSpanLimit || o_span > kSpanLimit || w_span > kSpanLimit)
         return fail(CV_ENOTSUP, "a row spans more than 2 GiB (x %lld, out %lld, windows %lld bytes)",
@@ -398,13 +416,13 @@ int conv_verify_restore(const cv_shape_t *s, int32_t layout, void *conv_state,
         return fail(CV_EINVAL, "n_slots (%d) < n_seq (%d) with identity slots", s->n_slots, s->n_seq);
     const int64_t blocks = (s->d_inner + kChw - 1) / kChw;
     const int64_t wg = blocks * (int64_t)s->n_seq;
-    if (wg * cvimpl::kWave > (int64_t)UINT32_MAX)
+    if (sat_mul(wg, cvimpl::kWave) > (int64_t)UINT32_MAX)
         return fail(CV_ENOTSUP, "grid of %lld workgroups exceeds the launch limit", (long long)wg);
     // LDS: the channel-major window block (rows layout), then the state region; both
     // are filled by direct global->LDS loads, so their spans are whole load widths
     const int64_t lds =
         (layout == cvimpl::kRows ? cvimpl::lds_dma_span(kChw * (s->T + s->d_conv - 2) * sb) : 0) +
-        (s->state_col_stride ? 0 : cvimpl::lds_dma_span(kChw * s->state_len * sb));
+        (s->state_col_stride ? 0 : cvimpl::lds_dma_span((int64_t)kChw * s->state_len * sb));
     if (lds > cvimpl::kMaxLds)
         return fail(CV_ENOTSUP, "restore needs %lld bytes of LDS (> %d)", (long long)lds, cvimpl::kMaxLds);
     cvimpl::RestoreArgs a;
@@ -437,8 +455,8 @@ int conv_prefill(const cv_shape_t *s, const void *x, const void *weight, const v
         return fail(CV_EINVAL, "x/out token strides must be >= d_inner");
     if (s->x_tok_stride % align || s->out_tok_stride % align)
         return fail(CV_ENOTSUP, "x/out token strides must be multiples of %d elements", align);
-    const int64_t x_span = ((int64_t)(s->T - 1) * s->x_tok_stride + C) * xb;
-    const int64_t o_span = ((int64_t)(s->T - 1) * s->out_tok_stride + C) * xb;
+    const int64_t x_span = span_bytes(s->T, s->x_tok_stride, C, xb);
+    const int64_t o_span = span_bytes(s->T, s->out_tok_stride, C, xb);
     if (x_span > kSpanLimit || o_span > kSpanLimit)
         return fail(CV_ENOTSUP, "a prompt spans more than 2 GiB");
     if (s->n_seq == 0 || s->d_inner == 0) return CV_OK;
@@ -457,8 +475,8 @@ int conv_prefill(const cv_shape_t *s, const void *x, const void *weight, const v
         return fail(CV_ENOTSUP, "prefill needs %lld bytes of LDS (> %d)", (long long)lds, cvimpl::kMaxLds);
     const int64_t blocks = (C + kChw - 1) / kChw;
     const int64_t chunks = (s->T + cvimpl::kPrefillChunk - 1) / cvimpl::kPrefillChunk;
-    const int64_t wg = blocks * chunks * (int64_t)s->n_seq;
-    if (wg * cvimpl::kWave > (int64_t)UINT32_MAX)
+    const int64_t wg = sat_mul(sat_mul(blocks, chunks), s->n_seq);
+    if (sat_mul(wg, cvimpl::kWave) > (int64_t)UINT32_MAX)
         return fail(CV_ENOTSUP, "grid of %lld workgroups exceeds the launch limit", (long long)wg);
     cvimpl::PrefillArgs a;
     a.x = x;
@@ -498,14 +516,14 @@ int conv_qk_l2norm(const cv_shape_t *s, int64_t n_rows, int64_t row_stride, void
     if (row_stride % (16 / xb)) return fail(CV_ENOTSUP, "row_stride must be a multiple of %d", 16 / xb);
     if (s->qk_channels % (16 / xb))
         return fail(CV_ENOTSUP, "qk_channels must be a multiple of %d", 16 / xb);
-    if (((int64_t)(cvimpl::kL2Rows - 1) * row_stride + s->qk_channels) * xb > kSpanLimit)
+    if (span_bytes(cvimpl::kL2Rows, row_stride, s->qk_channels, xb) > kSpanLimit)
         return fail(CV_ENOTSUP, "%d rows of x span more than 2 GiB", cvimpl::kL2Rows);
     if (n_rows == 0 || s->qk_channels == 0) return CV_OK;
     if (!x) return fail(CV_EINVAL, "x is NULL");
     if (!aligned16(x)) return fail(CV_ENOTSUP, "x must be 16-byte aligned");
     const int64_t blocks = (s->qk_channels + kChw - 1) / kChw;
-    const int64_t wg = blocks * ((n_rows + cvimpl::kL2Rows - 1) / cvimpl::kL2Rows);
-    if (wg * cvimpl::kWave > (int64_t)UINT32_MAX)
+    const int64_t wg = sat_mul(blocks, n_rows / cvimpl::kL2Rows + (n_rows % cvimpl::kL2Rows != 0));
+    if (sat_mul(wg, cvimpl::kWave) > (int64_t)UINT32_MAX)
         return fail(CV_ENOTSUP, "grid of %lld workgroups exceeds the launch limit", (long long)wg);
     cvimpl::L2Args a;
     a.x = x;

@@ -135,7 +135,7 @@ constexpr int tile_pitch(int state_bytes) {
 // LDS bytes to reserve for a block of `bytes` filled by direct global->LDS loads: each
 // such load instruction writes kWave 16-byte chunks, whole, so the span is rounded up
 // to a multiple of kWave * 16.
-constexpr int lds_dma_span(int bytes) {
+constexpr int64_t lds_dma_span(int64_t bytes) {
     return (bytes + kWave * 16 - 1) / (kWave * 16) * (kWave * 16);
 }
 
