@@ -39,8 +39,8 @@
  *    "Motivation"; Atlas glm5next_kda/mod.rs, decode_k (snapshots a partial accept
  *    rewinds to);
  *  - the prefill conv (conv + SiLU, no L2, no windows) and the separate q|k L2 pass,
- *    Atlas glm5next_kda/mod.rs, module doc and the prefill body ("Prefill conv is
- *    conv + SiLU ONLY - L2 is a separate launch over q|k").
+ *    Atlas glm5next_kda/mod.rs, module doc and the prefill body (the prefill conv
+ *    computes conv and SiLU only; q|k get their L2 in a launch of their own).
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -88,9 +88,15 @@
  *    only those move.
  *  - Numerics: the conv accumulates in fp32 as acc = bias (or +0); for w = 0..D-1:
  *    acc = fma(weight[c,w], v[t+w], acc), each step one correctly rounded fused
- *    multiply-add.  SiLU and L2 run in fp32.  Windows and conv_state are moved as bit
- *    patterns (bf16 -> fp32 widening is exact), so -0.0, subnormals and NaN payloads
- *    survive.
+ *    multiply-add.  SiLU runs in fp32 in a form that neither overflows nor loses
+ *    its subnormal results (p far below zero).  The L2 sums squares in fp32; a head
+ *    whose sum leaves fp32's range (|y| from ~1.3e19, or tiny values with
+ *    l2_eps < 2^-60) is summed again over a power-of-two rescaling of its values.
+ *    One case is outside: l2_eps == 0 with a head whose sum of squares is below
+ *    2^-256 (every value of the head subnormal) gives +-inf or NaN there.  Windows
+ *    and conv_state are moved as bit patterns (bf16 -> fp32 widening is exact), so
+ *    -0.0, subnormals and NaN payloads survive.
+ *  - The window buffer is indexed by slot, like conv_state: it holds n_slots slots.
  */
 #ifndef CONV_VERIFY_H
 #define CONV_VERIFY_H

@@ -12,9 +12,9 @@
  *   position t = 0..T-1, one causal conv1d update of width D over the rolling
  *   window, SiLU, per-head L2 on the q|k channels, then a copy of the new window
  *   into the rollback buffer.  [Atlas docs, fn gdn_verify_fused_conv_kn_batched:
- *   "ALL K draft positions in one launch ... replaces the per-token
- *   conv1d_update_l2norm xK + copy_d2d xK sequence"; the same function's note that
- *   each sequence's window is independent of the others.]
+ *   the fused call covers every draft position in one launch and takes the place
+ *   of K per-token conv-update-with-L2 calls, each followed by a window copy; the
+ *   same function notes that the sequences' windows do not depend on each other.]
  *
  *   - window: D-1 columns of conv_state, read starting at column a =
  *     num_accept_tokens[i] (0 when absent).  [sglang PR 46184, "Modifications"
@@ -22,15 +22,16 @@
  *     (a tile that ignores num_accept_tokens fails the accept-offset cases).]
  *   - conv:   pre = bias[c] + sum_{w<D} W[c,w] * v[t+w], v = [window, x_0 .. x_{T-1}],
  *     W[c,D-1] multiplying the newest input; fp32, one correctly rounded fused
- *     multiply-add per tap in tap order.  [Atlas docs, same function: "Same
- *     numerics as the per-token path (identical accumulation order ...)"; the
- *     fp32 accumulation is the stated precision of the method.]
+ *     multiply-add per tap in tap order.  [Atlas docs, same function: the fused
+ *     kernel keeps the per-token path's numerics and accumulates in the same
+ *     order; the fp32 accumulation is the stated precision of the method.]
  *   - SiLU:   y = pre / (1 + exp(-pre)), in fp64.  [Atlas glm5next_kda/mod.rs, module
- *     doc: "conv1d + SiLU -> L2(q,k only)".]
+ *     doc: the conv is followed by SiLU, then an L2 over q and k alone.]
  *   - L2:     for channels c < qk_channels, head h = c / head_dim:
  *     y <- y / sqrt(sum_{head} y^2 + l2_eps), in fp64.  V channels are untouched.
  *     [Atlas glm5next_kda/mod.rs, Glm5NextKdaConfig::l2_eps: FLA convention
- *     1/sqrt(sum + eps), not max(norm, eps); qk_channels() = 2 * qkv_dim; "V never".]
+ *     1/sqrt(sum + eps), not max(norm, eps); qk_channels() = 2 * qkv_dim; V is never
+ *     normalised.]
  *   - out[i,t,c] = y rounded once to the output dtype (nearest, ties to even).
  *   - the window shifts by one: w <- (w[1..], x_t) in the state dtype.
  *   - the new window is copied into the rollback buffer:
@@ -40,8 +41,8 @@
  *     [sglang PR 46184, "Motivation" (MambaPool's deduplicated [dim, T+K-2] row viewed
  *     as an overlapping [T, dim, K-1] window) and "Scope" (dense windows).]
  *   After the last token conv_state[s, c, 0..D-2] = w, the committed window; columns
- *   >= D-1 are left alone.  [Atlas docs, same function: "conv_state is left holding
- *   the committed (post final-position) window".]
+ *   >= D-1 are left alone.  [Atlas docs, same function: after the call conv_state
+ *   holds the window committed after the last draft position.]
  *
  * Readings where the pages are silent (each is also listed in the design notes):
  * the offset a is the value itself and the committed window goes to columns
@@ -172,9 +173,9 @@ static float state_bits_val(const orc_problem *p, uint32_t bits) {
  *                                                    [T+K-2, dim] per slot
  * ORC_ROWS is MambaPool's deduplicated row; ORC_ROWS_T is its axis-0 layout seen
  * transposed: in both the view's step stride equals its window stride.  [sglang PR
- * 46184, "Modifications" (the step stride == window stride condition, "for any layout
- * with those strides") and its test coverage list ("MambaPool's axis-0 window layout
- * seen transposed").]
+ * 46184, "Modifications": the tile store applies to any layout where the step
+ * stride equals the window stride, and its tests cover the pool's axis-0 window
+ * layout in transposed form.]
  */
 enum { ORC_DENSE = 0, ORC_ROWS = 1, ORC_ROWS_T = 2 };
 
@@ -405,10 +406,9 @@ int orc_restore(const orc_problem *p, int layout, void *conv_state, const void *
 /*
  * Separate per-head L2 over the q|k channels, in place, on rows of x (the prefill
  * conv's output): y <- y / sqrt(sum_head y^2 + eps) in fp64, rounded once to x's
- * dtype.  V channels are untouched.  [Atlas glm5next_kda/mod.rs, module doc: "Decode
- * conv fuses L2; prefill does not and needs a separate l2_norm_bf16 over q|k", and
- * the prefill body: "Prefill conv is conv + SiLU ONLY — L2 is a separate launch
- * over q|k".]
+ * dtype.  V channels are untouched.  [Atlas glm5next_kda/mod.rs, module doc: the
+ * decode conv has the L2 fused in, the prefill conv does not and is followed by its
+ * own L2 launch over q|k; the prefill body computes conv and SiLU only.]
  */
 int orc_l2norm(const orc_problem *p, int64_t n_rows, int64_t row_stride, void *x) {
     if (p->qk_channels < 0 || p->qk_channels > p->d_inner ||
