@@ -51,18 +51,6 @@ __device__ __forceinline__ void region_load(rsrc_t r, char *dst, int chunks, int
     }
 }
 
-// A contiguous block of `chunks` 16-byte chunks into LDS at dst by direct global->LDS
-// loads: every load is issued before any completes, and no VGPR holds the data.  dst
-// must have lds_dma_span(chunks * 16) bytes.  The caller waits (vmcnt) before reading.
-__device__ __forceinline__ void block_to_lds(rsrc_t r, char *dst, int chunks, int lane) {
-    for (int j = 0; j * kWave < chunks; ++j) {
-        const int q = j * kWave + lane;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t *)(dst + j * kWave * 16), 16,
-                                                 q < chunks ? (uint32_t)q * 16u : kOffLane, 0, 0,
-                                                 kNT);
-    }
-}
-
 // Columns 0..W1-1 of the lane's channels in the LDS copy of the region <- e.
 template <int SB, int W1>
 __device__ __forceinline__ void put_window(char *region, int SL, bool on, int lane,
@@ -382,8 +370,9 @@ __global__ __launch_bounds__(kWave) void cv_prefill_kernel(PrefillArgs p) {
 #pragma unroll
                     for (int w = 0; w < D; ++w)
                         acc = __builtin_fmaf(wv[ch][w], val(g0 + g + w, ch), acc);
-                    y[g][ch] = silu(acc);
+                    y[g][ch] = acc;
                 }
+            silu_rows_checked<G>(y);
 #pragma unroll
             for (int g = 0; g < G; ++g) {
                 if (g0 + g < nt) {
@@ -602,8 +591,9 @@ __global__ __launch_bounds__(kWave) void cv_split_kernel(KernelArgs p) {
             float acc = bv[ch];
 #pragma unroll
             for (int w = 0; w < D; ++w) acc = __builtin_fmaf(wv[ch][w], val(g + w, ch), acc);
-            y[g][ch] = silu(acc);
+            y[g][ch] = acc;
         }
+    silu_rows_checked<TC>(y);
     if (cb < p.qk)   // uniform: this wavefront holds q|k channels
         head_l2<TC>(y, lane * CPL + cb < p.qk, p.head_lanes_log2, p.eps);
     const rsrc_t o_r = make_rsrc((char *)p.out + (orow + cb) * XB,

@@ -65,9 +65,55 @@ __device__ __forceinline__ float silu(float p) {
     return p < 0.0f ? ((p * e) * r) * scale : p * r;
 }
 
+// p * rcp(1 + 2^(-p log2 e)): five instructions, exact to the same bar as silu() while
+// p >= kSiluFastMin (then 2^(-p log2 e) <= 2^125.5 and its reciprocal stays normal).
+// Below it the reciprocal would flush to zero and the result become -0.
+constexpr float kSiluFastMin = -87.0f;
+__device__ __forceinline__ float silu_fast(float p) {
+    return p * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(p * -1.4426950408889634f));
+}
+
+// SiLU over G token rows of pre-activations, in place, in the form FULL selects.
+template <bool FULL, int G>
+__device__ __forceinline__ void silu_rows(float (&v)[G][kChannelsPerLane]) {
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+#pragma unroll
+        for (int ch = 0; ch < kChannelsPerLane; ++ch) v[g][ch] = FULL ? silu(v[g][ch]) : silu_fast(v[g][ch]);
+}
+
+// SiLU over G token rows, in place, choosing the form from the values themselves: the
+// five-instruction one unless some value of the wavefront's rows lies below
+// kSiluFastMin (one wavefront-uniform test per call).
+template <int G>
+__device__ __forceinline__ void silu_rows_checked(float (&v)[G][kChannelsPerLane]) {
+    float lo = v[0][0];
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+#pragma unroll
+        for (int ch = 0; ch < kChannelsPerLane; ++ch) lo = __builtin_fminf(lo, v[g][ch]);
+    if (__builtin_amdgcn_ballot_w64(lo < kSiluFastMin) == 0)
+        silu_rows<false, G>(v);
+    else
+        silu_rows<true, G>(v);
+}
+
 template <int CTRL>
 __device__ __forceinline__ float dpp(float v) {
     return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, true));
+}
+
+// v[i] + v[i ^ 16] and v[i] + v[i ^ 32] on every lane i, with gfx950's lane-swap
+// instructions (plain VALU: no LDS round trip, no lane-address register).  With both
+// operands v, the two results of a swap hold the lane pair {v[i], v[i ^ k]}, on both
+// lanes of the pair in the same order, so both lanes get the bit-identical sum.
+__device__ __forceinline__ float xor16_sum(float v) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float xor32_sum(float v) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
 // Sums over the 2^hl_log2 lanes of an aligned lane group (all lanes active), for each
@@ -88,16 +134,12 @@ __device__ __forceinline__ void group_sums(float (&v)[G], int hl_log2) {
     if (hl_log2 >= 4)   // row_mirror: the other half of the 16-lane row
 #pragma unroll
         for (int g = 0; g < G; ++g) v[g] += dpp<0x140>(v[g]);
-    if (hl_log2 >= 5)   // lane ^ 16 inside 32 (ds_swizzle xor mode)
+    if (hl_log2 >= 5)   // lane ^ 16
 #pragma unroll
-        for (int g = 0; g < G; ++g)
-            v[g] += __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v[g]), 0x401F));
-    if (hl_log2 >= 6) {  // lane ^ 32
-        const int src = (int)((threadIdx.x ^ 32u) << 2);
+        for (int g = 0; g < G; ++g) v[g] = xor16_sum(v[g]);
+    if (hl_log2 >= 6)   // lane ^ 32
 #pragma unroll
-        for (int g = 0; g < G; ++g)
-            v[g] += __int_as_float(__builtin_amdgcn_ds_bpermute(src, __float_as_int(v[g])));
-    }
+        for (int g = 0; g < G; ++g) v[g] = xor32_sum(v[g]);
 }
 
 // group_sums for one value with every stage selected rather than branched on: the rare
@@ -112,10 +154,10 @@ __device__ __forceinline__ float group_sum_sel(float v, int hl_log2) {
     v = hl_log2 >= 3 ? v + o : v;
     o = dpp<0x140>(v);
     v = hl_log2 >= 4 ? v + o : v;
-    o = __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x401F));
-    v = hl_log2 >= 5 ? v + o : v;
-    o = __int_as_float(__builtin_amdgcn_ds_bpermute((int)((threadIdx.x ^ 32u) << 2), __float_as_int(v)));
-    v = hl_log2 >= 6 ? v + o : v;
+    o = xor16_sum(v);
+    v = hl_log2 >= 5 ? o : v;
+    o = xor32_sum(v);
+    v = hl_log2 >= 6 ? o : v;
     return v;
 }
 
@@ -150,10 +192,17 @@ __device__ __forceinline__ void head_l2(float (&y)[G][kChannelsPerLane], bool la
         for (int ch = 0; ch < CPL; ++ch) ss[g] = __builtin_fmaf(y[g][ch], y[g][ch], ss[g]);
     }
     group_sums<G>(ss, hl_log2);
-    bool all_in = true;
+    // in range: every S <= 2^126 (then S + eps <= 2^127 for eps <= 2^126; a larger eps
+    // takes the second sum) and, unless eps >= 2^-60, every S >= 2^-100.  A NaN S gives
+    // NaN either way, so the running max / min may drop it.
+    const bool eps_swamps = eps >= 0x1p-60f;
+    float hi = ss[0], lo = ss[0];
 #pragma unroll
-    for (int g = 0; g < G; ++g)
-        all_in = all_in && ss[g] + eps <= 0x1p127f && (ss[g] >= 0x1p-100f || eps >= 0x1p-60f);
+    for (int g = 1; g < G; ++g) {
+        hi = __builtin_fmaxf(hi, ss[g]);
+        lo = __builtin_fminf(lo, ss[g]);
+    }
+    const bool all_in = hi <= 0x1p126f && eps <= 0x1p126f && (eps_swamps || lo >= 0x1p-100f);
     float sc[G];
     if (__builtin_amdgcn_ballot_w64(lane_l2 && !all_in) == 0) {
 #pragma unroll
@@ -163,7 +212,7 @@ __device__ __forceinline__ void head_l2(float (&y)[G][kChannelsPerLane], bool la
         for (int g = 0; g < G; ++g) {
             // f = 1 for a head in range: the same sum again, bit for bit
             const float f = !(ss[g] + eps <= 0x1p127f) ? 0x1p-70f
-                            : (ss[g] >= 0x1p-100f || eps >= 0x1p-60f) ? 1.0f : 0x1p100f;
+                            : (ss[g] >= 0x1p-100f || eps_swamps) ? 1.0f : 0x1p100f;
             float s = 0.0f;
 #pragma unroll
             for (int ch = 0; ch < CPL; ++ch) {
@@ -172,7 +221,11 @@ __device__ __forceinline__ void head_l2(float (&y)[G][kChannelsPerLane], bool la
             }
             s = group_sum_sel(s, hl_log2);
             const float ep = eps * f * f;
-            sc[g] = ep < 0x1p127f ? __builtin_amdgcn_rsqf(s + ep) * f : __builtin_amdgcn_rsqf(eps);
+            // rsq(eps) is uniform: readfirstlane keeps it in a scalar register wherever
+            // the compiler hoists it to
+            const float r_eps = __builtin_bit_cast(
+                float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, __builtin_amdgcn_rsqf(eps))));
+            sc[g] = ep < 0x1p127f ? __builtin_amdgcn_rsqf(s + ep) * f : r_eps;
         }
     }
     if (lane_l2) {
@@ -317,6 +370,24 @@ __device__ __forceinline__ unsigned xcd_linear(unsigned b, unsigned G) {
     const unsigned x = b % 8u, k = b / 8u, q = G / 8u, r = G % 8u;
     return x < r ? x * (q + 1u) + k : r * (q + 1u) + (x - r) * q + k;
 }
+
+// A contiguous block of `chunks` 16-byte chunks into LDS at dst by direct global->LDS
+// loads: every load is issued before any completes, and no VGPR holds the data.  dst
+// must have lds_dma_span(chunks * 16) bytes.  The caller waits (vmcnt) before reading.
+__device__ __forceinline__ void block_to_lds(rsrc_t r, char *dst, int chunks, int lane) {
+    for (int j = 0; j * kWave < chunks; ++j) {
+        const int q = j * kWave + lane;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t *)(dst + j * kWave * 16), 16,
+                                                 q < chunks ? (uint32_t)q * 16u : kOffLane, 0, 0,
+                                                 kNT);
+    }
+}
+
+// The s_waitcnt immediate that waits until at most n (0..63) vector memory operations
+// of the wavefront are outstanding; expcnt and lgkmcnt are left at their maxima (not
+// waited on).  gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8.
+constexpr int vmcnt_imm(int n) { return (n & 0xF) | ((n >> 4) << 14) | 0x0F70; }
+static_assert(vmcnt_imm(0) == 0x0F70 && vmcnt_imm(17) == 0x4F71, "s_waitcnt encoding");
 
 // Orders LDS accesses across the workgroup (one wavefront) without waiting for the
 // wavefront's global stores: __syncthreads() is a release fence for all memory, which

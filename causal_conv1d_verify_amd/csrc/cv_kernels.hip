@@ -19,18 +19,20 @@
 //    which are staged through LDS so that they too leave in lane-contiguous units.
 //    Per-token offsets live in SGPRs.  Loads and stores use the nt (streaming) policy,
 //    except the weights and bias, which every row's wavefronts read.
-//  * All loads (x for every token, conv_state, weights, bias) are issued before the
-//    first barrier, with raised wave priority; after it the wavefront only stores, so
-//    no wait on a load is ever stuck behind stores (vmcnt counts both).  Later LDS
-//    hand-offs use barriers that order LDS only.
-//  * The arithmetic runs as soon as the inputs are in, in branch-free token chunks;
-//    the rollback windows and the committed state (pure copies of the inputs) follow.
+//  * All loads (weights, bias, x for every token, conv_state) are issued up front,
+//    with raised wave priority.  Most builds then wait for all of them once, so that no
+//    wait on a load is ever stuck behind stores (vmcnt counts both in issue order).
+//    The time-major builds of more than one token chunk instead compute each chunk as
+//    its x lands, chunk 0 (the one that takes the conv_state window, whose loads go
+//    out last) at the end.  LDS hand-offs use barriers that order LDS only.
+//  * The arithmetic runs in branch-free token chunks; the rollback windows and the
+//    committed state (pure copies of the inputs) follow.
 //  * The conv is one fused multiply-add per tap in tap order (bias first), the same
 //    order as the per-token path it replaces, so the pre-activation is bit-identical
 //    to a correctly rounded fp32 evaluation of that order.
 //  * L2: a head of H channels spans H/4 lanes; its sum of squares is a butterfly with
-//    DPP inside 16-lane rows (quad_perm, row_half_mirror, row_mirror) and ds_swizzle /
-//    bpermute beyond; every lane of a head ends with the same sum.
+//    DPP inside 16-lane rows (quad_perm, row_half_mirror, row_mirror) and gfx950 lane
+//    swaps (permlane16/32) beyond; every lane of a head ends with the same sum.
 //  * Windows and conv_state move as bit patterns; only the conv reads them as floats.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -73,6 +75,16 @@ void cv_verify_kernel(KernelArgs p) {
     // Tokens go in chunks with no branch inside a chunk: buckets up to 8 are one chunk;
     // larger ones use chunks of 4, which bounds the registers and the work past T.
     constexpr int G = TB <= 8 && !SPLIT ? TB : 4;
+    // A time-major build of more than one token chunk starts computing as its loads
+    // land, rather than after all of them: the compiler's waits before each use count
+    // outstanding loads (and stores) in issue order.  Its loads therefore go out in a
+    // fixed number, whatever T and the bias, so that those counts are exact on every
+    // path: every x token of the bucket (those past T as out-of-range loads, which read
+    // zeros) and the bias (out of range when there is none).  The chunks
+    // that take no state column (tokens W1 and later) go first; the state's W1 column
+    // loads are issued once the first of them has its results, so that they are not
+    // held in registers through it, and land while the other chunks compute.
+    constexpr bool PIPE = TM && !TREE && !SPLIT && G < TB;
 
     extern __shared__ uint4 lds_raw[];
     char *lds = (char *)lds_raw;
@@ -124,20 +136,6 @@ void cv_verify_kernel(KernelArgs p) {
     // wavefronts of a SIMD are ready, the ones still issuing loads go first, so reads
     // enter the memory pipeline ahead of other wavefronts' stores.
     __builtin_amdgcn_s_setprio(3);
-    const rsrc_t x_r = make_rsrc((const char *)p.x + (xrow + cb) * XB,
-                                 (uint32_t)(((int64_t)(T - 1) * p.x_tok + nch) * XB));
-    uint32_t X[TB][XW];   // x_t for the lane's channels
-#pragma unroll
-    for (int t = 0; t < TB; ++t) {
-        // a split row's later chunks need only their tokens and the W1 before them
-        const bool need = copier || (t >= chunk * G - W1 && t < chunk * G + G);
-        if (t < T && need) {
-            gload<VB>(x_r, laneV, (uint32_t)(t * p.x_tok * XB), X[t]);
-        } else {
-#pragma unroll
-            for (int w = 0; w < XW; ++w) X[t][w] = 0u;
-        }
-    }
 
     // Weights [nch][D]: the wavefront's block is contiguous, and comes into LDS by
     // direct global->LDS loads in lane-contiguous 16-byte chunks.  Per-lane loads of
@@ -148,28 +146,59 @@ void cv_verify_kernel(KernelArgs p) {
     // two share LDS, which keeps the wavefront's LDS (and so its occupancy) that of the
     // state region alone.  A direct load fills kWave * 16 bytes of LDS per instruction,
     // so the weights' LDS is reserved in whole multiples of that.
+    // A pipelined build loads each lane's weights straight into VGPRs instead (its
+    // contiguous [CPL][D] run, in 16- or 8-byte loads): the compiler cannot count a
+    // global->LDS load's completion precisely, and would wait for every load before
+    // reading the weights from LDS.
+    uint32_t wr[XW * D];   // the lane's weights [CPL][D] (zeros past d_inner)
     {
         const rsrc_t w_r = make_rsrc((const char *)p.weight + (int64_t)cb * D * XB,
                                      (uint32_t)(nch * D * XB));
-        const int wchunks = nch * D * XB / 16;   // exact: nch * XB is a multiple of 16
-        constexpr int WJ = (CHW * D * XB / 16 + kWave - 1) / kWave;
+        if constexpr (PIPE) {
+            constexpr int WP = VB * D % 16 == 0 ? 16 : 8;   // bytes per load
 #pragma unroll
-        for (int j = 0; j < WJ; ++j) {
-            const int q = j * kWave + lane;
-            if (j * kWave < wchunks)
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                    w_r, (lds_void_t *)(lds + j * kWave * 16), 16,
-                    q < wchunks ? (uint32_t)q * 16u : kOffLane, 0, 0, kKeep);
+            for (int j = 0; j < VB * D / WP; ++j)
+                gload<WP, kKeep>(w_r, on ? (uint32_t)(lane * VB * D + WP * j) : kOffLane, 0,
+                                 wr + WP / 4 * j);
+        } else {
+            const int wchunks = nch * D * XB / 16;   // exact: nch * XB is a multiple of 16
+            constexpr int WJ = (CHW * D * XB / 16 + kWave - 1) / kWave;
+#pragma unroll
+            for (int j = 0; j < WJ; ++j) {
+                const int q = j * kWave + lane;
+                if (j * kWave < wchunks)
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                        w_r, (lds_void_t *)(lds + j * kWave * 16), 16,
+                        q < wchunks ? (uint32_t)q * 16u : kOffLane, 0, 0, kKeep);
+            }
         }
     }
     uint32_t br[XW];              // bias [CPL]
     {
 #pragma unroll
         for (int w = 0; w < XW; ++w) br[w] = 0u;
-        if (p.bias) {
-            const rsrc_t b_r = make_rsrc((const char *)p.bias + (int64_t)cb * XB,
-                                         (uint32_t)(nch * XB));
+        if (PIPE || p.bias) {
+            // without a bias: a resource of no bytes (every lane out of range, zeros)
+            const rsrc_t b_r = make_rsrc(p.bias ? (const char *)p.bias + (int64_t)cb * XB
+                                                : (const char *)p.weight,
+                                         p.bias ? (uint32_t)(nch * XB) : 0u);
             gload<VB, kKeep>(b_r, laneV, 0, br);
+        }
+    }
+    const rsrc_t x_r = make_rsrc((const char *)p.x + (xrow + cb) * XB,
+                                 (uint32_t)(((int64_t)(T - 1) * p.x_tok + nch) * XB));
+    uint32_t X[TB][XW];   // x_t for the lane's channels
+#pragma unroll
+    for (int t = 0; t < TB; ++t) {
+        // a split row's later chunks need only their tokens and the W1 before them
+        const bool need = copier || (t >= chunk * G - W1 && t < chunk * G + G);
+        if constexpr (PIPE) {   // tokens past T: out-of-range loads of zeros
+            gload<VB>(x_r, t < T ? laneV : kOffLane, t < T ? (uint32_t)(t * p.x_tok * XB) : 0u, X[t]);
+        } else if (t < T && need) {
+            gload<VB>(x_r, laneV, (uint32_t)(t * p.x_tok * XB), X[t]);
+        } else {
+#pragma unroll
+            for (int w = 0; w < XW; ++w) X[t][w] = 0u;
         }
     }
 
@@ -199,7 +228,7 @@ void cv_verify_kernel(KernelArgs p) {
                                    (uint32_t)(((int64_t)(SL - 1) * p.state_col + nch) * SB));
     const uint32_t laneS = on ? (uint32_t)(lane * SCB) : kOffLane;
     uint32_t S[W1][SW];   // initial window columns v[0..W1-1], state-typed bits
-    if constexpr (tm) {
+    auto load_state_columns = [&]() __attribute__((always_inline)) {
 #pragma unroll
         for (int j = 0; j < W1; ++j) {
             if (copier) {
@@ -209,7 +238,8 @@ void cv_verify_kernel(KernelArgs p) {
                 for (int w = 0; w < SW; ++w) S[j][w] = 0u;
             }
         }
-    }
+    };
+    if constexpr (tm && !PIPE) load_state_columns();
     // exact: nch * SB is a multiple of 16; a split row's other chunks take no state
     const int rchunks = copier && !tm ? nch * SL * SB / 16 : 0;
     // chunks per lane, all in flight at once up to RJ; longer regions go in rounds
@@ -220,11 +250,12 @@ void cv_verify_kernel(KernelArgs p) {
         const int q = j * kWave + lane;
         if (j * kWave < rchunks) gload<16>(st_r, q < rchunks ? (uint32_t)q * 16u : kOffLane, 0, sreg[j]);
     }
-    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): every load above has landed
-    uint32_t wr[XW * D];   // the lane's weights [CPL][D] (zeros past d_inner)
-    lds_read_run<VB * D>(lds + lane * VB * D, wr);   // (LDS accesses run in order)
+    if constexpr (!PIPE) {
+        __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): every load above has landed
+        lds_read_run<VB * D>(lds + lane * VB * D, wr);   // (LDS accesses run in order)
 #pragma unroll
-    for (int w = 0; w < XW * D; ++w) wr[w] = on ? wr[w] : 0u;
+        for (int w = 0; w < XW * D; ++w) wr[w] = on ? wr[w] : 0u;
+    }
 #pragma unroll
     for (int j = 0; j < RJ; ++j) {
         const int q = j * kWave + lane;
@@ -250,31 +281,6 @@ void cv_verify_kernel(KernelArgs p) {
     }
     __builtin_amdgcn_s_setprio(0);
     lds_barrier();
-
-    // Packed rows shorter than the buffer's, rows layout: the slot's row block comes
-    // into LDS as stored, past the state region (direct global->LDS loads, issued once
-    // the weights are in VGPRs and before any store, so no wait on them sits behind a
-    // store).  The wavefront later overwrites its columns below T+W1-1 there and writes
-    // the block back whole: the columns past them keep their bits, and every store
-    // stays a coalesced 16-byte one.
-    const bool row_image = LAYOUT == kRows && p.cu != nullptr && T < p.T && copier;
-    const int img_off = tm ? 0 : CHW * SL * SB;
-    if constexpr (LAYOUT == kRows) {
-        if (row_image) {
-            __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): the weight reads are done
-            const int LS = p.T + W1 - 1;
-            const rsrc_t img_r = make_rsrc(
-                (const char *)p.win + ((int64_t)slot * p.win_slot + (int64_t)cb * LS) * SB,
-                (uint32_t)(nch * LS * SB));
-            const int ichunks = nch * LS * SB / 16;
-            for (int j = 0; j * kWave < ichunks; ++j) {
-                const int q = j * kWave + lane;
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                    img_r, (lds_void_t *)(lds + img_off + j * kWave * 16), 16,
-                    q < ichunks ? (uint32_t)q * 16u : kOffLane, 0, 0, kNT);
-            }
-        }
-    }
 
     if (tm) {
         // the window came in with the loads above
@@ -400,56 +406,78 @@ void cv_verify_kernel(KernelArgs p) {
     // reciprocals and cross-lane sums are then independent and overlap.
     // tree, split: this wavefront's chunk only (the chunks are the G-token chunks)
     auto mine = [&](int t) { return (!TREE && !SPLIT) || p.token_chunks == 1 || t / G == chunk; };
-#pragma unroll
-    for (int t0 = 0; t0 < TB; t0 += G) {
-        if (t0 < T && mine(t0)) {   // uniform guard; the loops are fully unrolled
-            float y[G][CPL];
-            uint32_t tv[TREE ? G : 1][W1][SW];   // tree: the taps before x_t, from the tile
-            if constexpr (TREE) {
-#pragma unroll
-                for (int g = 0; g < G; ++g)
-#pragma unroll
-                    for (int w = 0; w < W1; ++w)
-                        if (t0 + g < T) tile_col(tree_idx(t0 + g, W1 - w), tv[g][w]);
-            }
+    // after_math runs between a chunk's arithmetic and its stores
+    auto do_chunk = [&](int t0, auto after_math) __attribute__((always_inline)) {
+        float y[G][CPL];
+        uint32_t tv[TREE ? G : 1][W1][SW];   // tree: the taps before x_t, from the tile
+        if constexpr (TREE) {
 #pragma unroll
             for (int g = 0; g < G; ++g)
 #pragma unroll
-                for (int ch = 0; ch < CPL; ++ch) {
-                    float acc = bv[ch];
+                for (int w = 0; w < W1; ++w)
+                    if (t0 + g < T) tile_col(tree_idx(t0 + g, W1 - w), tv[g][w]);
+        }
 #pragma unroll
-                    for (int w = 0; w < D; ++w) {
-                        float v;
-                        if constexpr (TREE)
-                            v = w < W1 ? elem_val<SB>(tv[g][w < W1 ? w : 0], ch) : val(t0 + g + W1, ch);
-                        else
-                            v = val(t0 + g + w, ch);
-                        acc = __builtin_fmaf(wv[ch][w], v, acc);
-                    }
-                    y[g][ch] = silu(acc);
+        for (int g = 0; g < G; ++g)
+#pragma unroll
+            for (int ch = 0; ch < CPL; ++ch) {
+                float acc = bv[ch];
+#pragma unroll
+                for (int w = 0; w < D; ++w) {
+                    float v;
+                    if constexpr (TREE)
+                        v = w < W1 ? elem_val<SB>(tv[g][w < W1 ? w : 0], ch) : val(t0 + g + W1, ch);
+                    else
+                        v = val(t0 + g + w, ch);
+                    acc = __builtin_fmaf(wv[ch][w], v, acc);
                 }
-            if (wave_l2) head_l2<G>(y, lane_l2, p.head_lanes_log2, p.eps);
+                y[g][ch] = acc;
+            }
+        silu_rows_checked<G>(y);
+        if (wave_l2) head_l2<G>(y, lane_l2, p.head_lanes_log2, p.eps);
+        after_math();
 #pragma unroll
-            for (int g = 0; g < G; ++g) {
-                const int t = t0 + g;
-                if (t < T) {
-                    uint32_t o[XW];
-                    if constexpr (XB == 4) {
+        for (int g = 0; g < G; ++g) {
+            const int t = t0 + g;
+            if (t < T) {
+                uint32_t o[XW];
+                if constexpr (XB == 4) {
 #pragma unroll
-                        for (int ch = 0; ch < CPL; ++ch) o[ch] = __float_as_uint(y[g][ch]);
-                    } else {
-                        typedef float f2 __attribute__((ext_vector_type(2)));
-                        typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+                    for (int ch = 0; ch < CPL; ++ch) o[ch] = __float_as_uint(y[g][ch]);
+                } else {
+                    typedef float f2 __attribute__((ext_vector_type(2)));
+                    typedef __bf16 b2 __attribute__((ext_vector_type(2)));
 #pragma unroll
-                        for (int w = 0; w < XW; ++w) {
-                            f2 pr = {y[g][2 * w], y[g][2 * w + 1]};
-                            o[w] = __builtin_bit_cast(uint32_t, __builtin_convertvector(pr, b2));
-                        }
+                    for (int w = 0; w < XW; ++w) {
+                        f2 pr = {y[g][2 * w], y[g][2 * w + 1]};
+                        o[w] = __builtin_bit_cast(uint32_t, __builtin_convertvector(pr, b2));
                     }
-                    gstore<VB>(o_r, laneV, (uint32_t)(t * p.out_tok * XB), o);
                 }
+                gstore<VB>(o_r, laneV, (uint32_t)(t * p.out_tok * XB), o);
             }
         }
+    };
+    auto nothing = []() {};
+    if constexpr (PIPE) {
+        // Chunks 1.. first, chunk 0 last.  The state's loads go out after chunk HC's
+        // arithmetic: chunk 1 where registers allow, the last chunk in the build for 5
+        // wavefronts per SIMD, where holding the state columns any longer would spill
+        // them (and the spill store would wait for every load).  A packed row may have
+        // no token in chunk HC: the loads then go out there all the same.
+        constexpr int NC = TB / G, HC = WPE > 0 ? NC - 1 : 1;
+#pragma unroll
+        for (int c = 1; c < HC; ++c)
+            if (c * G < T) do_chunk(c * G, nothing);
+        if (HC * G < T) do_chunk(HC * G, load_state_columns);
+        else load_state_columns();
+#pragma unroll
+        for (int c = HC + 1; c < NC; ++c)
+            if (c * G < T) do_chunk(c * G, nothing);
+        do_chunk(0, nothing);
+    } else {
+#pragma unroll
+        for (int t0 = 0; t0 < TB; t0 += G)   // uniform guard; the loops are fully unrolled
+            if (t0 < T && mine(t0)) do_chunk(t0, nothing);
     }
     if constexpr (SPLIT) {
         if (!copier) return;   // its chunk of out is stored; the copies are chunk 0's
@@ -496,11 +524,19 @@ void cv_verify_kernel(KernelArgs p) {
         const rsrc_t row_r = make_rsrc(
             (char *)p.win + ((int64_t)slot * p.win_slot + (int64_t)cb * LS) * SB,
             (uint32_t)(nch * LS * SB));
+        // Packed rows shorter than the buffer's: the slot's row block comes into LDS as
+        // stored (direct global->LDS loads, past the state region), each lane writes its
+        // channels' columns below L into it, and the block leaves whole: the columns past
+        // L keep their bits, and every store stays a coalesced 16-byte one.  The block is
+        // loaded here, not with the other loads, so that no other path reaches an LDS
+        // access with a global->LDS load possibly outstanding (the compiler would then
+        // wait there for every earlier store as well).
+        const bool row_image = p.cu != nullptr && T < p.T && copier;
         if (row_image) {
-            // the stored block is in LDS: each lane writes its channels' columns below L
-            // into it, and the block leaves whole
             constexpr int LC = TB + W1 - 1;   // >= LS
-            char *img = lds + img_off;
+            char *img = lds + (tm ? 0 : CHW * SL * SB);
+            __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): earlier LDS accesses are done
+            block_to_lds(row_r, img, nch * LS * SB / 16, lane);
             __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): the block has landed
             if (on) {
 #pragma unroll
@@ -711,8 +747,13 @@ const void *pick_bucket(int tb, bool lean, bool split) {
         case 4: return (const void *)cv_verify_kernel<XB, SB, D, 4, LAYOUT, TREE, 0, false, TM>;
         case 8: return (const void *)cv_verify_kernel<XB, SB, D, 8, LAYOUT, TREE, 0, false, TM>;
         case 16:
-            return lean ? (const void *)cv_verify_kernel<XB, SB, D, 16, LAYOUT, TREE, 5, false, TM>
-                        : (const void *)cv_verify_kernel<XB, SB, D, 16, LAYOUT, TREE, 0, false, TM>;
+            // the 5-wavefront build exists for bf16 x and state with a channel-major
+            // conv_state only: elsewhere it spills heavily, or (time-major) the regular
+            // build's pipelined loads measured faster
+            if constexpr (XB == 2 && SB == 2 && !TM) {
+                if (lean) return (const void *)cv_verify_kernel<XB, SB, D, 16, LAYOUT, TREE, 5, false, TM>;
+            }
+            return (const void *)cv_verify_kernel<XB, SB, D, 16, LAYOUT, TREE, 0, false, TM>;
         case 24: return (const void *)cv_verify_kernel<XB, SB, D, 24, LAYOUT, TREE, 0, false, TM>;
         case 32: return (const void *)cv_verify_kernel<XB, SB, D, 32, LAYOUT, TREE, 0, false, TM>;
         default: return nullptr;

@@ -88,8 +88,8 @@ static void fixed_cases() {
     // the stress problem, conv_state time-major: 512 rows x T 16, 18-column state
     s = shape(512, 16, 10240, 4096, 18, 10240, CV_WIN_ROWS);
     expect("stress tm: rc", conv_verify_update_dedup(&s, A, A, A, A, I, I, A, A, nullptr), CV_OK);
-    expect("stress tm: kernel (lean 16-token build, tm state)", g_stub_launch.code,
-           verify_code(2, 2, 1, 1, 4, 4, 1, 0));
+    expect("stress tm: kernel (regular 16-token build, tm state)", g_stub_launch.code,
+           verify_code(2, 2, 1, 1, 4, 4, 0, 0));
     expect("stress tm: grid", g_stub_launch.grid_x, 512 * 40);
     expect("stress tm: slot-first on (four generations)", kargs().slot_first, 1);
     expect("stress tm: no LDS for the state", g_stub_launch.lds, 256 * 18 * 2 / 2);
