@@ -10,8 +10,9 @@ bias on) - the GB300 workload of sglang PR 46184's benchmark table.
 KEY: 0 1 2 3 4 4b 4s (the chain verify workloads), 4t 4bt (the stress problems with
 conv_state stored time-major), b1 b64 t16 (the pages' table rows:
 bs 1 and 64 at T 8, bs 128 at T 16), 2t (time-major rows), 2v (packed
-rows), 1t (tree verify), 2r / 4r / 4rt (accepted-prefix restore at the headline / stress shape:
-the step is the restore launch after an untimed verify), p (prefill: the step is the prefill conv plus the separate
+rows), 1t (tree verify), 2r / 4r / 4rt / 4rtt (accepted-prefix restore at the headline / stress
+shape, the last two into a time-major state, 4rtt from time-major rows: the step is the restore
+launch after an untimed verify), p (prefill: the step is the prefill conv plus the separate
 q|k L2; the roofline is the prefill conv alone).
 
 Prints ONE JSON line.  `value` is achieved algorithmic HBM bandwidth (GB/s): the

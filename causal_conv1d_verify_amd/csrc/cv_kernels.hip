@@ -250,6 +250,10 @@ void cv_verify_kernel(KernelArgs p) {
         const int q = j * kWave + lane;
         if (j * kWave < rchunks) gload<16>(st_r, q < rchunks ? (uint32_t)q * 16u : kOffLane, 0, sreg[j]);
     }
+    int par = -1;   // tree: lane t < T holds parent[row, t] (loaded with the rest)
+    if constexpr (TREE) {
+        if (lane < T) par = p.parent[(int64_t)row * p.T + lane];
+    }
     if constexpr (!PIPE) {
         __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): every load above has landed
         lds_read_run<VB * D>(lds + lane * VB * D, wr);   // (LDS accesses run in order)
@@ -274,10 +278,6 @@ void cv_verify_kernel(KernelArgs p) {
             if ((j0 + j) * kWave < rchunks && q < rchunks)
                 *(uint4 *)(lds + q * 16) = make_uint4(sreg[j][0], sreg[j][1], sreg[j][2], sreg[j][3]);
         }
-    }
-    int par = -1;   // tree: lane t < T holds parent[row, t]
-    if constexpr (TREE) {
-        if (lane < T) par = p.parent[(int64_t)row * p.T + lane];
     }
     __builtin_amdgcn_s_setprio(0);
     lds_barrier();
@@ -459,21 +459,25 @@ void cv_verify_kernel(KernelArgs p) {
     };
     auto nothing = []() {};
     if constexpr (PIPE) {
-        // Chunks 1.. first, chunk 0 last.  The state's loads go out after chunk HC's
-        // arithmetic: chunk 1 where registers allow, the last chunk in the build for 5
+        // The chunks from C0 on take no window column (their tokens are >= W1): they go
+        // first, the chunks before C0 last.  The state's loads go out after chunk HC's
+        // arithmetic: C0 where registers allow, the last chunk in the build for 5
         // wavefronts per SIMD, where holding the state columns any longer would spill
         // them (and the spill store would wait for every load).  A packed row may have
         // no token in chunk HC: the loads then go out there all the same.
-        constexpr int NC = TB / G, HC = WPE > 0 ? NC - 1 : 1;
+        constexpr int NC = TB / G, C0 = (W1 + G - 1) / G, HC = WPE > 0 ? NC - 1 : C0;
+        static_assert(C0 < NC, "a pipelined build has a chunk that takes no window column");
 #pragma unroll
-        for (int c = 1; c < HC; ++c)
+        for (int c = C0; c < HC; ++c)
             if (c * G < T) do_chunk(c * G, nothing);
         if (HC * G < T) do_chunk(HC * G, load_state_columns);
         else load_state_columns();
 #pragma unroll
         for (int c = HC + 1; c < NC; ++c)
             if (c * G < T) do_chunk(c * G, nothing);
-        do_chunk(0, nothing);
+#pragma unroll
+        for (int c = 0; c < C0; ++c)
+            if (c == 0 || c * G < T) do_chunk(c * G, nothing);
     } else {
 #pragma unroll
         for (int t0 = 0; t0 < TB; t0 += G)   // uniform guard; the loops are fully unrolled

@@ -130,6 +130,10 @@ static void fixed_cases() {
     expect("restore: family", g_stub_launch.code >> 14, 2);
     expect("restore: grid", g_stub_launch.grid_x, 512 * 40);
     expect("restore: LDS = the rows block", g_stub_launch.lds, (256 * 18 * 2 + 1023) / 1024 * 1024);
+    s = shape(512, 16, 10240, 4096, 18, 10240, CV_WIN_ROWS_T);
+    expect("restore from time-major rows: rc", conv_verify_restore(&s, CV_WIN_ROWS_T, A, A, I, I, nullptr), CV_OK);
+    expect("restore from time-major rows: grid", g_stub_launch.grid_x, 512 * 40);
+    expect("restore from time-major rows: no LDS", g_stub_launch.lds, 0);
     s = shape(8, 2048, 10240, 4096, 3, 0, CV_WIN_DENSE);
     expect("prefill: rc", conv_prefill(&s, A, A, nullptr, A, nullptr, I, nullptr, A, nullptr), CV_OK);
     expect("prefill: family", g_stub_launch.code >> 14, 3);

@@ -427,6 +427,13 @@ TM_RESTORE = [c(f"tm_restore_{layout}", n_seq=6, d_inner=1032, qk_channels=512, 
 TM_RESTORE.append(c("tm_restore_f32_D3", n_seq=4, d_inner=520, qk_channels=256, head_dim=64,
                     d_conv=3, T=5, layout="dedup", x_dtype="f32", state_dtype="f32",
                     restore=True, state_tm=True))
+# dense windows and time-major rows into a time-major state at d 2600 (11 channel blocks,
+# the last partial), D 2 and 3, bf16 and fp32 state
+TM_RESTORE += [c(f"tm_restore_{layout}_D{D}_{sd}_d2600", n_seq=5, d_inner=2600, qk_channels=1024,
+                 head_dim=128, d_conv=D, T=6, layout=layout, state_dtype=sd, restore=True,
+                 accept_offsets=True, permute_slots=True, pad_frac=0.2, state_tm=True,
+                 state_col_pad=8)
+               for layout in ("dense", "dedup_t") for D, sd in ((2, "bf16"), (3, "f32"))]
 
 
 @pytest.mark.parametrize("wl", TM_RESTORE, ids=[w.name for w in TM_RESTORE])
@@ -460,8 +467,9 @@ def test_full_size_time_major_state(key):
     _verify_case(workloads.WORKLOADS[key])
 
 
-def test_full_size_time_major_state_restore():
-    wl = workloads.WORKLOADS["4rt"]
+@pytest.mark.parametrize("key", ["4rt", "4rtt"])
+def test_full_size_time_major_state_restore(key):
+    wl = workloads.WORKLOADS[key]
     inp = workloads.make_inputs(wl)
     _say(wl.name)
     p = gh.GeneralProblem(inp)

@@ -138,6 +138,11 @@ WORKLOADS = {
     "4rt": Workload("restore_stress_dedup_t16_tmstate", 512, 10240, 4096, 128, 4, 16, "bf16",
                     "bf16", "dedup", True, 18, BASE_SEED + 34, accept_offsets=True,
                     pad_frac=0.1, permute_slots=True, restore=True, state_tm=True),
+    # ... and from time-major rows, where a window's columns are contiguous: the restore
+    # moves exactly its algorithmic bytes
+    "4rtt": Workload("restore_stress_dedup_t_t16_tmstate", 512, 10240, 4096, 128, 4, 16, "bf16",
+                     "bf16", "dedup_t", True, 18, BASE_SEED + 34, accept_offsets=True,
+                     pad_frac=0.1, permute_slots=True, restore=True, state_tm=True),
     # tree verify at the K=17 GDN shape (dense windows, nothing committed)
     "1t": Workload("tree_k17_dense", 8, 8192, 4096, 128, 4, 17, "bf16", "bf16", "dense",
                    False, 3, BASE_SEED + 11, tree=True),
