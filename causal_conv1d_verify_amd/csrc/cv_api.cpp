@@ -256,7 +256,8 @@ int plan_verify(int layout, bool tree, bool packed, const cv_shape_t *s, cvimpl:
     // a grid of more than one resident generation waits for the slot before loading x
     // (padded rows then load nothing); a partial last channel block leaves the rows'
     // buffers off 128-byte line boundaries, so neighbouring wavefronts share lines and a
-    // row's blocks go to one XCD.
+    // row's blocks go to one XCD (time-major builds there also store with the default
+    // cache policy, so the shared lines merge in L2: a.store_cached).
     plan->slot_first = plan->workgroups > cvimpl::kResidentWaves;
     plan->xcd_remap = s->d_inner % kChw != 0;
     return CV_OK;
@@ -353,6 +354,7 @@ int verify(int layout, bool tree, const cv_shape_t *s, const void *x, const void
     a.state_col = s->state_col_stride;
     a.slot_first = slot_idx != nullptr && plan.slot_first;
     a.xcd_remap = plan.xcd_remap;
+    a.store_cached = plan.xcd_remap && plan.state_tm;
     return launch(pick_verify(plan), plan.workgroups, plan.lds_bytes, a, stream);
 }
 

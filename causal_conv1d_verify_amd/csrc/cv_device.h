@@ -288,12 +288,12 @@ __device__ __forceinline__ void gstore(rsrc_t r, uint32_t voff, uint32_t soff, c
 }
 
 // One EB-byte (2 or 4) element store, for the ends of rows that do not fill a chunk.
-template <int EB>
+template <int EB, int POL = kNT>
 __device__ __forceinline__ void gstore_elem(rsrc_t r, uint32_t voff, uint32_t bits) {
     if constexpr (EB == 4) {
-        __builtin_amdgcn_raw_buffer_store_b32(bits, r, (int)voff, 0, kNT);
+        __builtin_amdgcn_raw_buffer_store_b32(bits, r, (int)voff, 0, POL);
     } else {
-        __builtin_amdgcn_raw_buffer_store_b16((unsigned short)bits, r, (int)voff, 0, kNT);
+        __builtin_amdgcn_raw_buffer_store_b16((unsigned short)bits, r, (int)voff, 0, POL);
     }
 }
 

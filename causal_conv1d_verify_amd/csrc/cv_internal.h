@@ -37,6 +37,7 @@ struct KernelArgs {
     int64_t state_col;         // 0: conv_state channel-major; else time-major column stride
     int32_t slot_first;        // read the slot before any vector load (padded rows load nothing)
     int32_t xcd_remap;         // work index from xcd_linear(blockIdx): a row's blocks on one XCD
+    int32_t store_cached;      // time-major builds: stores with the default cache policy
 };
 
 // A launch of more wavefronts than the chip holds at once (256 CUs x 4 SIMDs x 5) runs

@@ -101,6 +101,14 @@ static void fixed_cases() {
     expect("stress d10200: grid", g_stub_launch.grid_x, 512 * 40);
     expect("stress d10200: XCD order on", kargs().xcd_remap, 1);
     expect("stress d10200: LDS = the state region", g_stub_launch.lds, 256 * 18 * 2);
+    expect("stress d10200: nt stores (channel-major state)", kargs().store_cached, 0);
+    s = shape(512, 16, 10200, 4096, 18, 10240, CV_WIN_ROWS);
+    expect("stress d10200 tm: rc", conv_verify_update_dedup(&s, A, A, A, A, I, I, A, A, nullptr), CV_OK);
+    expect("stress d10200 tm: XCD order on", kargs().xcd_remap, 1);
+    expect("stress d10200 tm: default-policy stores", kargs().store_cached, 1);
+    s = shape(512, 16, 10240, 4096, 18, 10240, CV_WIN_ROWS);
+    expect("stress tm (aligned rows): rc", conv_verify_update_dedup(&s, A, A, A, A, I, I, A, A, nullptr), CV_OK);
+    expect("stress tm (aligned rows): nt stores", kargs().store_cached, 0);
 
     // the K=17 GDN verify: dense windows on a small grid take the token-split kernel
     s = shape(8, 17, 8192, 4096, 3, 0, CV_WIN_DENSE);
