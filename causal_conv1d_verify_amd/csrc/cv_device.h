@@ -92,7 +92,7 @@ __device__ __forceinline__ void silu_rows_checked(float (&v)[G][kChannelsPerLane
     for (int g = 0; g < G; ++g)
 #pragma unroll
         for (int ch = 0; ch < kChannelsPerLane; ++ch) lo = __builtin_fminf(lo, v[g][ch]);
-    if (__builtin_amdgcn_ballot_w64(lo < kSiluFastMin) == 0)
+    if (__builtin_expect(__builtin_amdgcn_ballot_w64(lo < kSiluFastMin) == 0, 1))
         silu_rows<false, G>(v);
     else
         silu_rows<true, G>(v);
@@ -204,7 +204,7 @@ __device__ __forceinline__ void head_l2(float (&y)[G][kChannelsPerLane], bool la
     }
     const bool all_in = hi <= 0x1p126f && eps <= 0x1p126f && (eps_swamps || lo >= 0x1p-100f);
     float sc[G];
-    if (__builtin_amdgcn_ballot_w64(lane_l2 && !all_in) == 0) {
+    if (__builtin_expect(__builtin_amdgcn_ballot_w64(lane_l2 && !all_in) == 0, 1)) {
 #pragma unroll
         for (int g = 0; g < G; ++g) sc[g] = __builtin_amdgcn_rsqf(ss[g] + eps);
     } else {

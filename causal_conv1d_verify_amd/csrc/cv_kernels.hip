@@ -283,36 +283,38 @@ __device__ __forceinline__ void verify_body(const KernelArgs &p) {
     __builtin_amdgcn_s_setprio(0);
     lds_barrier();
 
-    if (tm) {
-        // the window came in with the loads above
-    } else if (contiguous_state) {
-        uint32_t run[RUNW];   // the lane's [CPL][W1] run
-        lds_read_run<RUNB>(lds + lane * RUNB, run);
+    // Channel-major state: each lane picks its window out of the staged region.
+    auto window_from_lds = [&]() __attribute__((always_inline)) {
+        if (contiguous_state) {
+            uint32_t run[RUNW];   // the lane's [CPL][W1] run
+            lds_read_run<RUNB>(lds + lane * RUNB, run);
 #pragma unroll
-        for (int j = 0; j < W1; ++j)
+            for (int j = 0; j < W1; ++j)
 #pragma unroll
-            for (int w = 0; w < SW; ++w) {
-                if constexpr (SB == 4) {
-                    S[j][w] = elem_bits<4>(run, w * W1 + j);
-                } else {
-                    S[j][w] = elem_bits<2>(run, (2 * w) * W1 + j) |
-                              (elem_bits<2>(run, (2 * w + 1) * W1 + j) << 16);
+                for (int w = 0; w < SW; ++w) {
+                    if constexpr (SB == 4) {
+                        S[j][w] = elem_bits<4>(run, w * W1 + j);
+                    } else {
+                        S[j][w] = elem_bits<2>(run, (2 * w) * W1 + j) |
+                                  (elem_bits<2>(run, (2 * w + 1) * W1 + j) << 16);
+                    }
                 }
-            }
-    } else {
-        const char *rec = lds + (lane * CPL * SL + a) * SB;
+        } else {
+            const char *rec = lds + (lane * CPL * SL + a) * SB;
 #pragma unroll
-        for (int j = 0; j < W1; ++j)
+            for (int j = 0; j < W1; ++j)
 #pragma unroll
-            for (int w = 0; w < SW; ++w) {
-                if constexpr (SB == 4) {
-                    S[j][w] = lds_get<4>(rec + (w * SL + j) * 4);
-                } else {
-                    S[j][w] = lds_get<2>(rec + ((2 * w) * SL + j) * 2) |
-                              (lds_get<2>(rec + ((2 * w + 1) * SL + j) * 2) << 16);
+                for (int w = 0; w < SW; ++w) {
+                    if constexpr (SB == 4) {
+                        S[j][w] = lds_get<4>(rec + (w * SL + j) * 4);
+                    } else {
+                        S[j][w] = lds_get<2>(rec + ((2 * w) * SL + j) * 2) |
+                                  (lds_get<2>(rec + ((2 * w + 1) * SL + j) * 2) << 16);
+                    }
                 }
-            }
-    }
+        }
+    };
+    if constexpr (!TM) window_from_lds();   // time-major: the window came in with the loads
 
     float wv[CPL][D];
     float bv[CPL];
@@ -488,6 +490,17 @@ __device__ __forceinline__ void verify_body(const KernelArgs &p) {
         if (!copier) return;   // its chunk of out is stored; the copies are chunk 0's
     }
     if constexpr (!TREE) {
+        // Channel-major state, the 16-token build for 5 wavefronts per SIMD: the window
+        // is read out of LDS again here (the region is untouched until the commit below),
+        // so that it is not held in registers through chunks 1 and later, which take no
+        // window column; the memory clobber keeps the compiler from reusing the first
+        // read.  Holding it there spilled it, and every reload waited for all stores
+        // issued before it (bs128 T16: 28.7 -> 27.1 us).  Builds with registers to spare
+        // keep it (the second read cost the T 8 shapes 2-5%).
+        if constexpr (!TM && WPE > 0) {
+            asm volatile("" ::: "memory");
+            window_from_lds();
+        }
         // ---- committed window -> conv_state -----------------------------------------------------
         // v[T .. T+W1-1] into columns 0..W1-1 of the staged rows (each lane rewrites only
         // its own channels' records, after having read them above), then the region leaves.
