@@ -38,8 +38,8 @@ from . import _lib
 
 __all__ = ["conv_verify_update", "conv_verify_update_dense", "conv_verify_update_dedup",
            "conv_verify_update_tree", "conv_verify_restore", "conv_prefill", "conv_qk_l2norm",
-           "conv_verify_describe", "conv_verify_abi_version", "prepare", "CvError",
-           "library_path", "LAYOUTS"]
+           "conv_verify_describe", "conv_verify_abi_version", "conv_verify_debug_count",
+           "write_count_library", "prepare", "CvError", "library_path", "LAYOUTS"]
 
 library_path = _lib.LIB_PATH
 LAYOUTS = {"dense": _lib.CV_WIN_DENSE, "dedup": _lib.CV_WIN_ROWS, "dedup_t": _lib.CV_WIN_ROWS_T}
@@ -420,3 +420,32 @@ def conv_verify_describe(variant, shape: "_lib.CvShape") -> "_lib.CvLaunchInfo":
 
 def conv_verify_abi_version() -> int:
     return _lib.load().conv_verify_abi_version()
+
+
+# The write-count build of the library, for tests: within `with write_count_library():`
+# every call above goes to libconvverify_wc.so.
+write_count_library = _lib.write_count_library
+
+
+def conv_verify_debug_count(ranges=()):
+    """Write-count build only: count the global stores of later launches into each
+    (buffer, counters) pair of `ranges` (at most 4): counters is an int32 tensor with one
+    element per 2 bytes of buffer, on the same GPU, zeroed by the caller; both must stay
+    alive until the next call (an empty `ranges` clears them)."""
+    lib = _lib.load()
+    if len(ranges) > 4:
+        raise ValueError("at most 4 count ranges")
+    lo = (ctypes.c_void_p * 4)()
+    nbytes = (ctypes.c_uint64 * 4)()
+    cnt = (ctypes.c_void_p * 4)()
+    for k, (buf, counts) in enumerate(ranges):
+        b = buf.numel() * buf.element_size()
+        if not (buf.is_contiguous() and counts.is_contiguous()) or str(counts.dtype) != "torch.int32":
+            raise ValueError("count ranges: contiguous buffers and int32 counters")
+        if counts.numel() * 2 != b:
+            raise ValueError(f"count range {k}: {counts.numel()} counters for {b} bytes")
+        _same_gpu(buf, counts)
+        lo[k], nbytes[k], cnt[k] = buf.data_ptr(), b, counts.data_ptr()
+    rc = lib.conv_verify_debug_count(len(ranges), lo, nbytes, cnt)
+    if rc != _lib.CV_OK:
+        raise CvError(rc, _lib.error_message(lib, rc))

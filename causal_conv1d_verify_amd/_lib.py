@@ -2,10 +2,13 @@
 
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libconvverify.so")
+# The write-count build (tests only; see conv_verify_debug_count in the header).
+LIB_WC_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libconvverify_wc.so")
 
 CV_F32 = 0
 CV_BF16 = 1
@@ -33,6 +36,7 @@ EXPORTS = (
     "conv_verify_strerror",
     "conv_verify_last_error",
     "conv_verify_abi_version",
+    "conv_verify_debug_count",
 )
 
 
@@ -70,11 +74,33 @@ def load() -> ctypes.CDLL:
     global _lib
     if _lib is not None:
         return _lib
-    if not os.path.exists(LIB_PATH):
+    _lib = _open(LIB_PATH)
+    return _lib
+
+
+@contextlib.contextmanager
+def write_count_library():
+    """Within the block, the binding calls the write-count build of the library (tests).
+    The GPU is initialised first: the library's device variables are looked up by symbol,
+    which fails for a code object registered before the HIP runtime found its devices."""
+    import torch
+
+    global _lib
+    torch.cuda.init()
+    prev = _lib
+    _lib = _open(LIB_WC_PATH)
+    try:
+        yield _lib
+    finally:
+        _lib = prev
+
+
+def _open(path: str) -> ctypes.CDLL:
+    if not os.path.exists(path):
         raise ImportError(
-            f"{LIB_PATH} is missing: build it with `python -m causal_conv1d_verify_amd.build` "
+            f"{path} is missing: build it with `python -m causal_conv1d_verify_amd.build` "
             "(or __graft_entry__.build()); the verify conv has no non-HIP implementation")
-    lib = ctypes.CDLL(LIB_PATH)
+    lib = ctypes.CDLL(path)
     upd = [ctypes.POINTER(CvShape)] + [ctypes.c_void_p] * 9
     for name in ("conv_verify_update_dense", "conv_verify_update_dedup"):
         fn = getattr(lib, name)
@@ -100,7 +126,10 @@ def load() -> ctypes.CDLL:
     lib.conv_verify_last_error.argtypes = []
     lib.conv_verify_abi_version.restype = ctypes.c_int
     lib.conv_verify_abi_version.argtypes = []
-    _lib = lib
+    lib.conv_verify_debug_count.restype = ctypes.c_int
+    lib.conv_verify_debug_count.argtypes = [ctypes.c_int32, ctypes.POINTER(ctypes.c_void_p),
+                                            ctypes.POINTER(ctypes.c_uint64),
+                                            ctypes.POINTER(ctypes.c_void_p)]
     return lib
 
 

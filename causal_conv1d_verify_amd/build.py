@@ -16,6 +16,9 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libconvverify.so")
+# The write-count build (tests only): every global store also counts into registered
+# ranges (conv_verify_debug_count).  Its verify objects cover bf16 x and state only.
+LIB_WC = os.path.join(PKG, "libconvverify_wc.so")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
@@ -40,7 +43,14 @@ SOURCES = [
     for tm in (0, 1) for xb, sb in ((4, 4), (2, 2), (2, 4)) for v in (0, 1, 2, 3)
 ] + [("cv_aux_kernels.hip", "cv_aux_kernels", [f"--offload-arch={ARCH}", *DEVICE_FLAGS]),
      ("cv_api.cpp", "cv_api", [])]
-MAX_JOBS = max(1, min(len(SOURCES), int(os.environ.get("MAX_JOBS", os.cpu_count() or 4))))
+SOURCES_WC = [
+    ("cv_kernels.hip", f"wc/cv_kernels_2_2_{v}_{tm}",
+     [f"--offload-arch={ARCH}", *DEVICE_FLAGS, "-DCV_XB=2", "-DCV_SB=2", f"-DCV_VARIANT={v}",
+      f"-DCV_TM={tm}", "-DCV_WRITE_COUNT"])
+    for tm in (0, 1) for v in (0, 1, 2, 3)
+] + [("cv_aux_kernels.hip", "wc/cv_aux_kernels", [f"--offload-arch={ARCH}", *DEVICE_FLAGS, "-DCV_WRITE_COUNT"]),
+     ("cv_api.cpp", "wc/cv_api", ["-DCV_WRITE_COUNT"])]
+MAX_JOBS = max(1, min(len(SOURCES) + len(SOURCES_WC), int(os.environ.get("MAX_JOBS", os.cpu_count() or 4))))
 
 
 def _run(cmd):
@@ -52,14 +62,18 @@ def _run(cmd):
 
 
 def build(verbose: bool = True) -> str:
-    os.makedirs(BUILD, exist_ok=True)
-    objs = []
+    """Builds libconvverify.so and the write-count test library libconvverify_wc.so."""
+    os.makedirs(os.path.join(BUILD, "wc"), exist_ok=True)
     t0 = time.time()
     pending = []
-    for src, stem, extra in SOURCES:
-        obj = os.path.join(BUILD, stem + ".o")
-        pending.append([HIPCC, *COMMON, *extra, "-c", os.path.join(CSRC, src), "-o", obj])
-        objs.append(obj)
+    libs = []
+    for sources, lib in ((SOURCES, LIB), (SOURCES_WC, LIB_WC)):
+        objs = []
+        for src, stem, extra in sources:
+            obj = os.path.join(BUILD, stem + ".o")
+            pending.append([HIPCC, *COMMON, *extra, "-c", os.path.join(CSRC, src), "-o", obj])
+            objs.append(obj)
+        libs.append((lib, objs))
     running = []
 
     def reap(cmd, p):
@@ -80,11 +94,12 @@ def build(verbose: bool = True) -> str:
                                                   stderr=subprocess.PIPE, text=True)))
         cmd, p = running.pop(0)
         reap(cmd, p)
-    tmp = LIB + ".tmp"
-    _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp])
-    os.replace(tmp, LIB)
+    for lib, objs in libs:
+        tmp = lib + ".tmp"
+        _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp])
+        os.replace(tmp, lib)
     if verbose:
-        print(f"built {LIB} in {time.time() - t0:.1f}s", file=sys.stderr)
+        print(f"built {LIB} and {LIB_WC} in {time.time() - t0:.1f}s", file=sys.stderr)
     return LIB
 
 

@@ -7,6 +7,7 @@
 #include <cstdarg>
 #include <cstdint>
 #include <cstdio>
+#include <cstring>
 
 #include "conv_verify.h"
 #include "cv_internal.h"
@@ -576,4 +577,55 @@ const char *conv_verify_last_error(void) { return g_detail; }
 
 int conv_verify_abi_version(void) { return CONV_VERIFY_ABI_VERSION; }
 
+int conv_verify_debug_count(int32_t n, const void *const *lo, const uint64_t *bytes,
+                            void *const *counts) {
+    g_detail[0] = 0;
+#ifdef CV_WRITE_COUNT
+    if (n < 0 || n > 4) return fail(CV_EINVAL, "count ranges: n (%d) outside 0..4", n);
+    if (n > 0 && (!lo || !bytes || !counts)) return fail(CV_EINVAL, "count ranges: NULL array");
+    cvimpl::CountRanges c;
+    std::memset(&c, 0, sizeof c);
+    c.n = n;
+    for (int k = 0; k < n; ++k) {
+        if (!lo[k] || !counts[k] || bytes[k] % 2 != 0)
+            return fail(CV_EINVAL, "count range %d: NULL pointer or odd size", k);
+        c.lo[k] = (const char *)lo[k];
+        c.bytes[k] = bytes[k];
+        c.counts[k] = (uint32_t *)counts[k];
+    }
+    int (*const setters[])(const cvimpl::CountRanges &) = {
+        cvimpl::count_ranges_set_2_2_0_0, cvimpl::count_ranges_set_2_2_1_0,
+        cvimpl::count_ranges_set_2_2_2_0, cvimpl::count_ranges_set_2_2_3_0,
+        cvimpl::count_ranges_set_2_2_0_1, cvimpl::count_ranges_set_2_2_1_1,
+        cvimpl::count_ranges_set_2_2_2_1, cvimpl::count_ranges_set_2_2_3_1,
+        cvimpl::count_ranges_set_aux};
+    for (size_t i = 0; i < sizeof setters / sizeof setters[0]; ++i) {
+        const int e = setters[i](c);
+        if (e != 0)
+            return fail(CV_EHIP_BASE - e, "count ranges: code object %zu: %s (%d)", i,
+                        hipGetErrorName((hipError_t)e), e);
+    }
+    return CV_OK;
+#else
+    (void)n; (void)lo; (void)bytes; (void)counts;
+    return fail(CV_ENOTSUP, "write counting exists only in the write-count build of the library");
+#endif
+}
+
 }  // extern "C"
+
+#ifdef CV_WRITE_COUNT
+// The write-count build compiles the verify objects for bf16 x and state only: the
+// pickers of the other dtype pairs find no kernel (the launch then fails cleanly).
+namespace cvimpl {
+#define CV_NO_PICKER(xb, sb, v, tm) \
+    const void *pick_kernel_##xb##_##sb##_##v##_##tm(int, int, int, int) { return nullptr; }
+#define CV_NO_PICKERS(xb, sb) CV_NO_PICKER(xb, sb, 0, 0) CV_NO_PICKER(xb, sb, 1, 0) \
+    CV_NO_PICKER(xb, sb, 2, 0) CV_NO_PICKER(xb, sb, 3, 0) CV_NO_PICKER(xb, sb, 0, 1) \
+    CV_NO_PICKER(xb, sb, 1, 1) CV_NO_PICKER(xb, sb, 2, 1) CV_NO_PICKER(xb, sb, 3, 1)
+CV_NO_PICKERS(4, 4)
+CV_NO_PICKERS(2, 4)
+#undef CV_NO_PICKERS
+#undef CV_NO_PICKER
+}  // namespace cvimpl
+#endif

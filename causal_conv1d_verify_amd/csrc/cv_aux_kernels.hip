@@ -14,6 +14,7 @@
 //
 // Every global access is a lane-contiguous 8/16-byte buffer access with the streaming
 // policy; conv_state regions always move whole (see region_load).
+#define CV_COUNT_RANGES cv_count_ranges_aux
 #include "cv_device.h"
 #include "cv_internal.h"
 
@@ -253,7 +254,7 @@ __global__ __launch_bounds__(kWave) void cv_prefill_kernel(PrefillArgs p) {
             const int q = j * kWave + lane;
             if (j * kWave < wchunks)
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                    w_r, (lds_void_t *)(lds + w_off + j * kWave * 16), 16,
+                    raw(w_r), (lds_void_t *)(lds + w_off + j * kWave * 16), 16,
                     q < wchunks ? (uint32_t)q * 16u : kOffLane, 0, 0, kKeep);
         }
     }
@@ -506,7 +507,7 @@ __global__ __launch_bounds__(kWave) void cv_split_kernel(KernelArgs p) {
             const int q = j * kWave + lane;
             if (j * kWave < wchunks)
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                    w_r, (lds_void_t *)(lds + w_off + j * kWave * 16), 16,
+                    raw(w_r), (lds_void_t *)(lds + w_off + j * kWave * 16), 16,
                     q < wchunks ? (uint32_t)q * 16u : kOffLane, 0, 0, kKeep);
         }
     }
@@ -767,6 +768,15 @@ const void *prefill_for(int d_conv) {
 }
 
 }  // namespace
+
+#ifdef CV_WRITE_COUNT
+int count_ranges_set_aux(const CountRanges &c) {
+    void *dst = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&dst, HIP_SYMBOL(CV_COUNT_RANGES));
+    if (e != hipSuccess) return (int)e;
+    return (int)hipMemcpy(dst, &c, sizeof c, hipMemcpyHostToDevice);
+}
+#endif
 
 const void *pick_restore(int state_bytes, int d_conv, int layout, int tm) {
     if (state_bytes == 4) return tm ? restore_layout<4, true>(d_conv, layout) : restore_layout<4, false>(d_conv, layout);

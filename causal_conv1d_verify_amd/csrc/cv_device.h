@@ -9,6 +9,15 @@
 
 #include "cv_internal.h"
 
+#ifdef CV_WRITE_COUNT
+// The write-count build's ranges (see count_store below): one variable per code object,
+// named by the including source (CV_COUNT_RANGES) so that no two objects share a symbol.
+#ifndef CV_COUNT_RANGES
+#error "a write-count build names its code object's count ranges (CV_COUNT_RANGES)"
+#endif
+__device__ cvimpl::CountRanges CV_COUNT_RANGES;
+#endif
+
 namespace cvimpl {
 namespace {
 
@@ -244,12 +253,49 @@ __device__ __forceinline__ void head_l2(float (&y)[G][kChannelsPerLane], bool la
 // past the end of d_inner use the lane offset 0x80000000, which the hardware range
 // check turns into a load of zeros / a dropped store.
 
-using rsrc_t = __amdgpu_buffer_rsrc_t;
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) void lds_void_t;
 
 constexpr uint32_t kOffLane = 0x80000000u;
+
+#ifdef CV_WRITE_COUNT
+// The write-count build (a library of its own, for tests): every global store also adds
+// 1, per 2-byte unit it writes, to a counter of the registered range that holds it, so a
+// test can check that each output element is written by exactly one store.  A resource
+// then carries its base and size next to the hardware descriptor; the ranges live in one
+// variable per code object (CV_COUNT_RANGES), set by the host through count_ranges_set_*.
+struct rsrc_t {
+    __amdgpu_buffer_rsrc_t r;
+    const char *base;
+    uint32_t bytes;
+};
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t raw(const rsrc_t &r) { return r.r; }
+__device__ __forceinline__ rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+    return {__builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
+                                              0x00020000),
+            (const char *)base, bytes};
+}
+// The stores the hardware drops (a lane at kOffLane, or past the resource) count nothing.
+__device__ __forceinline__ void count_store(const rsrc_t &r, uint32_t voff, uint32_t soff, int nb) {
+    const CountRanges &cr = ::CV_COUNT_RANGES;
+    const uint64_t off = (uint64_t)voff + soff;
+    if (off + (uint64_t)nb > r.bytes) return;
+    const char *a = r.base + off;
+    for (int k = 0; k < cr.n; ++k) {
+        const char *lo = cr.lo[k];
+        if (a >= lo && a + nb <= lo + cr.bytes[k]) {
+            const uint64_t u = (uint64_t)(a - lo) / 2;
+            for (int i = 0; i < nb / 2; ++i) atomicAdd(cr.counts[k] + u + i, 1u);
+            return;
+        }
+    }
+}
+#else
+using rsrc_t = __amdgpu_buffer_rsrc_t;
+__device__ __forceinline__ rsrc_t raw(rsrc_t r) { return r; }
+__device__ __forceinline__ void count_store(rsrc_t, uint32_t, uint32_t, int) {}
+#endif
 // Cache policy of the global accesses: nt (streaming).  Each byte of x, out, conv_state
 // and the windows is read or written once per launch, so none of it is worth keeping
 // in L2 or the Infinity Cache.  The weights (and bias) are the exception: every row's
@@ -257,20 +303,22 @@ constexpr uint32_t kOffLane = 0x80000000u;
 constexpr int kNT = 2;
 constexpr int kKeep = 0;
 
+#ifndef CV_WRITE_COUNT
 __device__ __forceinline__ rsrc_t make_rsrc(const void *base, uint32_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
                                              0x00020000);
 }
+#endif
 
 // NB-byte (8 or 16) global load / store of words d[0 .. NB/4).
 template <int NB, int POL = kNT>
 __device__ __forceinline__ void gload(rsrc_t r, uint32_t voff, uint32_t soff, uint32_t *d) {
     if constexpr (NB == 16) {
-        const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, POL);
+        const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(raw(r), (int)voff, (int)soff, POL);
         d[0] = v.x; d[1] = v.y; d[2] = v.z; d[3] = v.w;
     } else {
         static_assert(NB == 8, "8- or 16-byte accesses");
-        const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(r, (int)voff, (int)soff, POL);
+        const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(raw(r), (int)voff, (int)soff, POL);
         d[0] = v.x; d[1] = v.y;
     }
 }
@@ -279,22 +327,24 @@ template <int NB, int POL = kNT>
 __device__ __forceinline__ void gstore(rsrc_t r, uint32_t voff, uint32_t soff, const uint32_t *s) {
     if constexpr (NB == 16) {
         const u32x4 v = {s[0], s[1], s[2], s[3]};
-        __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)voff, (int)soff, POL);
+        __builtin_amdgcn_raw_buffer_store_b128(v, raw(r), (int)voff, (int)soff, POL);
     } else {
         static_assert(NB == 8, "8- or 16-byte accesses");
         const u32x2 v = {s[0], s[1]};
-        __builtin_amdgcn_raw_buffer_store_b64(v, r, (int)voff, (int)soff, POL);
+        __builtin_amdgcn_raw_buffer_store_b64(v, raw(r), (int)voff, (int)soff, POL);
     }
+    count_store(r, voff, soff, NB);
 }
 
 // One EB-byte (2 or 4) element store, for the ends of rows that do not fill a chunk.
 template <int EB, int POL = kNT>
 __device__ __forceinline__ void gstore_elem(rsrc_t r, uint32_t voff, uint32_t bits) {
     if constexpr (EB == 4) {
-        __builtin_amdgcn_raw_buffer_store_b32(bits, r, (int)voff, 0, POL);
+        __builtin_amdgcn_raw_buffer_store_b32(bits, raw(r), (int)voff, 0, POL);
     } else {
-        __builtin_amdgcn_raw_buffer_store_b16((unsigned short)bits, r, (int)voff, 0, POL);
+        __builtin_amdgcn_raw_buffer_store_b16((unsigned short)bits, raw(r), (int)voff, 0, POL);
     }
+    count_store(r, voff, 0, EB);
 }
 
 // A run of NB bytes (a multiple of 8) between registers and LDS, in the widest units
@@ -377,7 +427,7 @@ __device__ __forceinline__ unsigned xcd_linear(unsigned b, unsigned G) {
 __device__ __forceinline__ void block_to_lds(rsrc_t r, char *dst, int chunks, int lane) {
     for (int j = 0; j * kWave < chunks; ++j) {
         const int q = j * kWave + lane;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t *)(dst + j * kWave * 16), 16,
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(raw(r), (lds_void_t *)(dst + j * kWave * 16), 16,
                                                  q < chunks ? (uint32_t)q * 16u : kOffLane, 0, 0,
                                                  kNT);
     }

@@ -140,6 +140,22 @@ constexpr int64_t lds_dma_span(int64_t bytes) {
     return (bytes + kWave * 16 - 1) / (kWave * 16) * (kWave * 16);
 }
 
+// The write-count build only (a test library, compiled with CV_WRITE_COUNT): device
+// ranges whose stores are counted, one 32-bit counter per 2 bytes of each range.
+struct CountRanges {
+    int32_t n;                 // ranges in use, 0..4
+    const char *lo[4];
+    uint64_t bytes[4];
+    uint32_t *counts[4];
+};
+// Each code object holds its own copy of the ranges; these set it (write-count build,
+// which compiles the verify objects for bf16 x and state only, and the aux object).
+#define CV_DECLARE_COUNT_SET(v, tm) int count_ranges_set_2_2_##v##_##tm(const CountRanges &c);
+CV_DECLARE_COUNT_SET(0, 0) CV_DECLARE_COUNT_SET(1, 0) CV_DECLARE_COUNT_SET(2, 0) CV_DECLARE_COUNT_SET(3, 0)
+CV_DECLARE_COUNT_SET(0, 1) CV_DECLARE_COUNT_SET(1, 1) CV_DECLARE_COUNT_SET(2, 1) CV_DECLARE_COUNT_SET(3, 1)
+#undef CV_DECLARE_COUNT_SET
+int count_ranges_set_aux(const CountRanges &c);
+
 // Kernel pickers, one per compiled (x bytes, state bytes, variant, state layout)
 // object - variant 0 dense, 1 rows, 2 time-major rows, 3 tree; state layout 0
 // channel-major, 1 time-major: the kernel for (d_conv, token bucket), or nullptr.

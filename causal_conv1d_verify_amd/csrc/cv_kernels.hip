@@ -38,6 +38,9 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#define CV_COUNT_RANGES_NAME(xb, sb, v, tm) cv_count_ranges_##xb##_##sb##_##v##_##tm
+#define CV_COUNT_RANGES_OF(xb, sb, v, tm) CV_COUNT_RANGES_NAME(xb, sb, v, tm)
+#define CV_COUNT_RANGES CV_COUNT_RANGES_OF(CV_XB, CV_SB, CV_VARIANT, CV_TM)
 #include "cv_device.h"
 #include "cv_internal.h"
 
@@ -169,7 +172,7 @@ __device__ __forceinline__ void verify_body(const KernelArgs &p) {
                 const int q = j * kWave + lane;
                 if (j * kWave < wchunks)
                     __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                        w_r, (lds_void_t *)(lds + j * kWave * 16), 16,
+                        raw(w_r), (lds_void_t *)(lds + j * kWave * 16), 16,
                         q < wchunks ? (uint32_t)q * 16u : kOffLane, 0, 0, kKeep);
             }
         }
@@ -805,6 +808,17 @@ const void *pick_bucket(int tb, bool lean, bool split) {
 
 #define CV_PICK_NAME(xb, sb, v, tm) pick_kernel_##xb##_##sb##_##v##_##tm
 #define CV_PICK(xb, sb, v, tm) CV_PICK_NAME(xb, sb, v, tm)
+
+#ifdef CV_WRITE_COUNT
+#define CV_COUNT_SET_NAME(xb, sb, v, tm) count_ranges_set_##xb##_##sb##_##v##_##tm
+#define CV_COUNT_SET(xb, sb, v, tm) CV_COUNT_SET_NAME(xb, sb, v, tm)
+int CV_COUNT_SET(CV_XB, CV_SB, CV_VARIANT, CV_TM)(const CountRanges &c) {
+    void *dst = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&dst, HIP_SYMBOL(CV_COUNT_RANGES));
+    if (e != hipSuccess) return (int)e;
+    return (int)hipMemcpy(dst, &c, sizeof c, hipMemcpyHostToDevice);
+}
+#endif
 
 const void *CV_PICK(CV_XB, CV_SB, CV_VARIANT, CV_TM)(int d_conv, int token_bucket, int lean, int split) {
     constexpr int layout = CV_VARIANT == 3 ? kDense : CV_VARIANT;

@@ -319,6 +319,20 @@ CV_API const char *conv_verify_last_error(void);
 /* CONV_VERIFY_ABI_VERSION of the loaded library. */
 CV_API int conv_verify_abi_version(void);
 
+/* Test instrumentation, for the single-writer check of the outputs (no passage of the
+ * pages defines it; it exists to show that every element is written by one store).
+ * Only libconvverify_wc.so, the write-count build of the library (its verify kernels
+ * for bf16 x and state, and every restore / prefill / L2 kernel), implements it; the
+ * regular library returns CV_ENOTSUP.  Registers n (0..4) device ranges: range k covers
+ * bytes[k] bytes from lo[k] (even), and counts[k] is a device array of bytes[k] / 2
+ * uint32 counters, one per 2 bytes.  Every global store a later launch makes inside a
+ * range adds 1 to the counter of each 2-byte unit it writes; stores outside all ranges
+ * count nothing.  The caller owns every buffer and zeroes the counters; the ranges stay
+ * registered (and must stay allocated) until the next call, n = 0 clears them.  The
+ * counters are added to atomically, so launches of the write-count build run slower. */
+CV_API int conv_verify_debug_count(int32_t n, const void *const *lo, const uint64_t *bytes,
+                                   void *const *counts);
+
 #ifdef __cplusplus
 }
 #endif

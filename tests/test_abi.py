@@ -35,7 +35,7 @@ def _header_functions():
 
 def test_header_and_binding_agree():
     assert _header_functions() == sorted(lib_mod.EXPORTS)
-    assert len(lib_mod.EXPORTS) == 11
+    assert len(lib_mod.EXPORTS) == 12
 
 
 def test_library_exports_nothing_else():
@@ -44,6 +44,24 @@ def test_library_exports_nothing_else():
                          text=True, check=True)
     exported = set(re.findall(r"\bT (\w+)$", res.stdout, re.M))
     assert exported == set(lib_mod.EXPORTS), sorted(exported ^ set(lib_mod.EXPORTS))
+
+
+def test_write_count_library_exports_the_same_symbols():
+    _lib()
+    if not os.path.exists(lib_mod.LIB_WC_PATH):
+        pytest.skip("libconvverify_wc.so not built")
+    res = subprocess.run(["nm", "-D", "--defined-only", lib_mod.LIB_WC_PATH], capture_output=True,
+                         text=True, check=True)
+    exported = set(re.findall(r"\bT (\w+)$", res.stdout, re.M))
+    assert exported == set(lib_mod.EXPORTS), sorted(exported ^ set(lib_mod.EXPORTS))
+
+
+def test_regular_library_does_not_count_writes():
+    """Only the write-count build counts: the regular library refuses, touching no GPU."""
+    lib = _lib()
+    rc = lib.conv_verify_debug_count(0, None, None, None)
+    assert rc == lib_mod.CV_ENOTSUP
+    assert b"write-count build" in lib.conv_verify_last_error()
 
 
 def test_library_exports_every_declared_symbol():
