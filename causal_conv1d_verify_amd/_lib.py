@@ -23,6 +23,7 @@ CV_VARIANT_TREE = 3
 CV_LAUNCH_STATE_TIME_MAJOR = 1
 CV_LAUNCH_SLOT_FIRST = 2
 CV_LAUNCH_XCD_ORDER = 4
+CV_LAUNCH_LINE_ALIGNED = 8
 
 EXPORTS = (
     "conv_verify_update_dense",

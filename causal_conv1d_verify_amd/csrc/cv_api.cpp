@@ -253,30 +253,57 @@ int plan_verify(int layout, bool tree, bool packed, const cv_shape_t *s, cvimpl:
     plan->workgroups = wg * chunks;
     plan->lds_bytes = (int)(dense_split ? split_lds : lds);
     plan->head_lanes = head_lanes;
+    plan->waves_per_group = 1;
+    // The line-aligned build (bf16, time-major conv_state, row layout, full 16-token
+    // rows): when a store range of out, the state columns or the row blocks starts off a
+    // 128-byte line, 4-wavefront workgroups take 1024 channels each and cut their shared
+    // store ranges at the destination's lines (stress shape at d 10200, see the kernel).
+    // Its LDS: two exchange buffers of 4 tokens of out, or the workgroup's row block
+    // after up to 112 bytes of its first line.
+    // (strides are >= 0 here; reduced first, so no product overflows)
+    auto off = [](int64_t stride, int bytes) { return (stride % 128) * bytes % 128 != 0; };
+    const bool off_lines = off(s->out_tok_stride, xb) ||
+                           (s->n_seq > 1 && off(s->out_seq_stride, xb)) ||
+                           off(s->state_col_stride, sb) ||
+                           (s->n_slots > 1 && off(s->state_slot_stride, sb)) ||
+                           (s->n_slots > 1 && off(s->win_slot_stride, sb));
+    if (plan->state_tm && layout == cvimpl::kRows && !tree && !packed && s->T == 16 &&
+        chunks == 1 && xb == 2 && sb == 2 && off_lines) {
+        constexpr int nw = cvimpl::kLineGroupWaves;
+        const int64_t range = (int64_t)kChw * nw;
+        const int64_t out_bufs = 2 * 4 * range * xb;
+        const int64_t block = 128 + range * (s->T + s->d_conv - 2) * sb;
+        plan->waves_per_group = nw;
+        plan->lean = 0;
+        plan->channel_blocks = (int)((C + range - 1) / range);
+        plan->workgroups = (int64_t)plan->channel_blocks * s->n_seq;
+        plan->lds_bytes = (int)(out_bufs > block ? out_bufs : block);
+    }
     // Data-movement choices, each measured on MI355X (none changes a result bit):
     // a grid of more than one resident generation waits for the slot before loading x
     // (padded rows then load nothing); a partial last channel block leaves the rows'
     // buffers off 128-byte line boundaries, so neighbouring wavefronts share lines and a
     // row's blocks go to one XCD (time-major builds there also store with the default
     // cache policy, so the shared lines merge in L2: a.store_cached).
-    plan->slot_first = plan->workgroups > cvimpl::kResidentWaves;
-    plan->xcd_remap = s->d_inner % kChw != 0;
+    plan->slot_first = plan->workgroups * plan->waves_per_group > cvimpl::kResidentWaves;
+    plan->xcd_remap = s->d_inner % kChw != 0 && plan->waves_per_group == 1;
     return CV_OK;
 }
 
 const void *pick_verify(const cvimpl::Plan &plan) {
     using namespace cvimpl;
-    const int d = plan.d_conv, tb = plan.token_bucket, lean = plan.lean;
+    const int d = plan.d_conv, tb = plan.token_bucket;
+    const int build = plan.waves_per_group > 1 ? 2 : plan.lean ? 1 : 0;
     const int split = plan.token_chunks > 1 ? 1 : 0;
     const int v = plan.tree ? 3 : plan.layout;
     if (plan.token_chunks > 1 && !plan.tree && plan.layout == cvimpl::kDense)
         return pick_split(plan.x_bytes, plan.state_bytes, d, plan.state_tm);
 #define CV_PICK_TM(xb, sb, tm)                                      \
     switch (v) {                                                    \
-        case 0: return pick_kernel_##xb##_##sb##_0_##tm(d, tb, lean, split); \
-        case 1: return pick_kernel_##xb##_##sb##_1_##tm(d, tb, lean, split); \
-        case 2: return pick_kernel_##xb##_##sb##_2_##tm(d, tb, lean, split); \
-        case 3: return pick_kernel_##xb##_##sb##_3_##tm(d, tb, lean, split); \
+        case 0: return pick_kernel_##xb##_##sb##_0_##tm(d, tb, build, split); \
+        case 1: return pick_kernel_##xb##_##sb##_1_##tm(d, tb, build, split); \
+        case 2: return pick_kernel_##xb##_##sb##_2_##tm(d, tb, build, split); \
+        case 3: return pick_kernel_##xb##_##sb##_3_##tm(d, tb, build, split); \
         default: return nullptr;                                    \
     }
 #define CV_PICK_FOR(xb, sb) \
@@ -289,15 +316,17 @@ const void *pick_verify(const cvimpl::Plan &plan) {
     return nullptr;
 }
 
-// Enqueues one 1-D launch of 64-lane workgroups; returns CV_OK or the launch error.
+// Enqueues one 1-D launch of workgroups of `waves` 64-lane wavefronts; returns CV_OK or
+// the launch error.
 template <typename Args>
-int launch(const void *fn, int64_t workgroups, int lds_bytes, const Args &args, void *stream) {
+int launch(const void *fn, int64_t workgroups, int lds_bytes, const Args &args, void *stream,
+           int waves = 1) {
     if (!fn)
         return fail(CV_EHIP_BASE - (int)hipErrorInvalidDeviceFunction,
                     "no kernel compiled for this case");
     Args a = args;
     void *kargs[] = {&a};
-    const hipError_t e = hipLaunchKernel(fn, dim3((unsigned)workgroups), dim3(cvimpl::kWave), kargs,
+    const hipError_t e = hipLaunchKernel(fn, dim3((unsigned)workgroups), dim3(cvimpl::kWave * waves), kargs,
                                          (size_t)lds_bytes, (hipStream_t)stream);
     if (e != hipSuccess)
         return fail(CV_EHIP_BASE - (int)e, "kernel launch failed: %s", hipGetErrorString(e));
@@ -356,7 +385,8 @@ int verify(int layout, bool tree, const cv_shape_t *s, const void *x, const void
     a.slot_first = slot_idx != nullptr && plan.slot_first;
     a.xcd_remap = plan.xcd_remap;
     a.store_cached = plan.xcd_remap && plan.state_tm;
-    return launch(pick_verify(plan), plan.workgroups, plan.lds_bytes, a, stream);
+    return launch(pick_verify(plan), plan.workgroups, plan.lds_bytes, a, stream,
+                  plan.waves_per_group);
 }
 
 }  // namespace
@@ -551,7 +581,7 @@ int conv_verify_describe(int variant, const cv_shape_t *shape, cv_launch_info_t 
     int rc = plan_verify(tree ? cvimpl::kDense : variant, tree, false, shape, &plan);
     if (rc) return rc;
     info->workgroups = plan.workgroups;
-    info->threads = cvimpl::kWave;
+    info->threads = cvimpl::kWave * plan.waves_per_group;
     info->channel_blocks = plan.channel_blocks;
     info->channels_per_wave = cvimpl::kWave * plan.channels_per_lane;
     info->channels_per_lane = plan.channels_per_lane;
@@ -561,7 +591,8 @@ int conv_verify_describe(int variant, const cv_shape_t *shape, cv_launch_info_t 
     info->token_chunks = plan.token_chunks;
     info->flags = (plan.state_tm ? CV_LAUNCH_STATE_TIME_MAJOR : 0) |
                   (plan.slot_first ? CV_LAUNCH_SLOT_FIRST : 0) |
-                  (plan.xcd_remap ? CV_LAUNCH_XCD_ORDER : 0);
+                  (plan.xcd_remap ? CV_LAUNCH_XCD_ORDER : 0) |
+                  (plan.waves_per_group > 1 ? CV_LAUNCH_LINE_ALIGNED : 0);
     return CV_OK;
 }
 

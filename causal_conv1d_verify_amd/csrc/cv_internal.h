@@ -50,6 +50,9 @@ constexpr int64_t kResidentWaves = 5120;
 // resident wavefronts per compute unit (5 per SIMD).
 constexpr int kRowsStageBytes = 8192;
 
+// Wavefronts per workgroup of the line-aligned build (1024 consecutive channels).
+constexpr int kLineGroupWaves = 4;
+
 // Token-split verify (dense windows): tokens per wavefront, and the grids it serves:
 // at most kSplitMaxWaves wavefronts once split (measured at d 8192: T 8 gains up to 64
 // rows, T 17 up to 32 rows, e.g. 10.4 -> 5.8 us at 8 rows; larger splits ran slower).
@@ -76,10 +79,11 @@ struct Plan {
     int slot_first;            // KernelArgs::slot_first when a slot table is passed
     int xcd_remap;             // KernelArgs::xcd_remap
     int channels_per_lane;     // kChannelsPerLane
-    int channel_blocks;
+    int channel_blocks;        // workgroups per row (each of waves_per_group wavefronts)
     int64_t workgroups;
     int lds_bytes;
     int head_lanes;
+    int waves_per_group;       // 1, or kLineGroupWaves for the line-aligned build
 };
 
 // Accepted-prefix restore: window widx[i] of row i's slot -> conv_state columns 0..D-2.
@@ -159,12 +163,14 @@ int count_ranges_set_aux(const CountRanges &c);
 // Kernel pickers, one per compiled (x bytes, state bytes, variant, state layout)
 // object - variant 0 dense, 1 rows, 2 time-major rows, 3 tree; state layout 0
 // channel-major, 1 time-major: the kernel for (d_conv, token bucket), or nullptr.
-// lean: the 16-token bucket's build for 5 resident wavefronts per SIMD; split: the row
-// layouts' token-split build (buckets 8 and 16).
+// build: 0 the regular build; 1 the 16-token bucket's build for 5 resident wavefronts per
+// SIMD (lean); 2 the line-aligned build of kLineGroupWaves-wavefront workgroups (bf16,
+// time-major state, row layout, 16 tokens).  split: the row layouts' token-split build
+// (buckets 8 and 16).
 #define CV_DECLARE_PICKERS_TM(xb, sb, tm)                                   \
-    const void *pick_kernel_##xb##_##sb##_0_##tm(int d_conv, int token_bucket, int lean, int split); \
-    const void *pick_kernel_##xb##_##sb##_1_##tm(int d_conv, int token_bucket, int lean, int split); \
-    const void *pick_kernel_##xb##_##sb##_2_##tm(int d_conv, int token_bucket, int lean, int split); \
+    const void *pick_kernel_##xb##_##sb##_0_##tm(int d_conv, int token_bucket, int build, int split); \
+    const void *pick_kernel_##xb##_##sb##_1_##tm(int d_conv, int token_bucket, int build, int split); \
+    const void *pick_kernel_##xb##_##sb##_2_##tm(int d_conv, int token_bucket, int build, int split); \
     const void *pick_kernel_##xb##_##sb##_3_##tm(int d_conv, int token_bucket, int lean, int split);
 #define CV_DECLARE_PICKERS(xb, sb) CV_DECLARE_PICKERS_TM(xb, sb, 0) CV_DECLARE_PICKERS_TM(xb, sb, 1)
 CV_DECLARE_PICKERS(4, 4)

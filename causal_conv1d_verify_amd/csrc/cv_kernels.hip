@@ -38,6 +38,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #define CV_COUNT_RANGES_NAME(xb, sb, v, tm) cv_count_ranges_##xb##_##sb##_##v##_##tm
 #define CV_COUNT_RANGES_OF(xb, sb, v, tm) CV_COUNT_RANGES_NAME(xb, sb, v, tm)
 #define CV_COUNT_RANGES CV_COUNT_RANGES_OF(CV_XB, CV_SB, CV_VARIANT, CV_TM)
@@ -61,8 +63,18 @@ namespace {
 // row's tokens), so the arithmetic on each wavefront's path is a quarter to a half.
 // TM: conv_state time-major (p.state_col is the column stride), a build of its own so
 // that neither layout's path costs the other registers.
+// NW: wavefronts per workgroup.  NW 4 is the line-aligned build (time-major state, row
+// layout, full 16-token rows) for buffers whose rows start off 128-byte lines: the
+// workgroup's 4 wavefronts take 1024 consecutive channels, and every store range they
+// share (a token of out, a column of the state, the row block) goes through LDS and
+// leaves cut at the destination's 128-byte lines, so that only the workgroup's two end
+// lines of each range are written in part.  (With one wavefront per 256 channels, every
+// wavefront boundary splits a line between two wavefronts' stores; a streaming probe of
+// the stress traffic at d 10200 ran 132.6 us that way and 113.2 us line-aligned, against
+// 108.4 us at d 10240.)
 // SPOL: the cache policy of every store (the kernel below picks it).
-template <int XB, int SB, int D, int TB, int LAYOUT, bool TREE, int WPE, bool SPLIT, bool TM, int SPOL>
+template <int XB, int SB, int D, int TB, int LAYOUT, bool TREE, int WPE, bool SPLIT, bool TM, int NW,
+          int SPOL>
 __device__ __forceinline__ void verify_body(const KernelArgs &p) {
     static_assert(!TREE || LAYOUT == kDense, "tree windows are dense");
     static_assert(!SPLIT || (!TREE && LAYOUT != kDense), "dense chains split in cv_split_kernel");
@@ -89,14 +101,21 @@ __device__ __forceinline__ void verify_body(const KernelArgs &p) {
     // loads are issued once the first of them has its results, so that they are not
     // held in registers through it, and land while the other chunks compute.
     constexpr bool PIPE = TM && !TREE && !SPLIT && G < TB;
+    constexpr bool LA = NW > 1;
+    static_assert(!LA || (PIPE && LAYOUT == kRows && TB == 16 && WPE == 0 && XB == SB),
+                  "the line-aligned build: time-major state, row layout, 16-token rows");
+    constexpr int RANGE = NW * CHW;           // channels of a workgroup
 
     extern __shared__ uint4 lds_raw[];
     char *lds = (char *)lds_raw;
 
-    const int lane = threadIdx.x;
-    const unsigned bid = p.xcd_remap ? xcd_linear(blockIdx.x, gridDim.x) : blockIdx.x;
+    const int tid = threadIdx.x;
+    const int lane = LA ? tid % kWave : tid;
+    const int wave = LA ? __builtin_amdgcn_readfirstlane(tid / kWave) : 0;
+    const unsigned bid = !LA && p.xcd_remap ? xcd_linear(blockIdx.x, gridDim.x) : blockIdx.x;
     const int r2 = (int)(bid / (unsigned)p.channel_blocks);
-    const int cb = (int)(bid - (unsigned)r2 * (unsigned)p.channel_blocks) * CHW;
+    const int cbg = (int)(bid - (unsigned)r2 * (unsigned)p.channel_blocks) * RANGE;
+    const int cb = cbg + wave * CHW;            // this wavefront's first channel
     // Tree verify on a small grid spreads a row's token chunks over p.token_chunks
     // wavefronts: each one builds the row's whole v tile (a token's ancestors may be
     // any earlier token) and computes and writes only its own chunk of tokens.
@@ -126,11 +145,17 @@ __device__ __forceinline__ void verify_body(const KernelArgs &p) {
     if constexpr (TREE || SPLIT) {
         if (chunk * G >= T) return;   // a split row's chunk past its tokens
     }
+    if constexpr (LA) {
+        if (p.cu || T != TB) return;   // launched for full unpacked rows only
+    }
     if (p.slot_first) {
         if (slot < 0) return;   // a padded row on a multi-generation grid: no load at all
     }
     const int SL = p.state_len;
-    const int nch = min(CHW, p.d_inner - cb);   // channels of this wavefront
+    // channels of this wavefront (none for the last wavefronts of a line-aligned
+    // workgroup past d_inner: they take part in the workgroup's exchanges only)
+    const int nch = max(0, min(CHW, p.d_inner - cb));
+    const int nchg = min(RANGE, p.d_inner - cbg);   // channels of the workgroup
     const bool on = lane * CPL < nch;
     const uint32_t laneV = on ? (uint32_t)(lane * VB) : kOffLane;
     const bool contiguous_state = SL == W1;
@@ -407,6 +432,41 @@ __device__ __forceinline__ void verify_body(const KernelArgs &p) {
     const bool lane_l2 = lane * CPL + cb < p.qk;
     const rsrc_t o_r = make_rsrc((char *)p.out + (orow + cb) * XB,
                                  (uint32_t)(((int64_t)(T - 1) * p.out_tok + nch) * XB));
+    // Line-aligned build: N contiguous ranges of nb <= NW * kWave * U bytes each, range i
+    // at byte soff0 + i * soff_step of the resource r (whose base address is base), staged
+    // in LDS at src + i * src_step.  The workgroup's threads take consecutive U-byte units
+    // starting at the 128-byte line that holds a range's first byte, so each store
+    // instruction covers whole lines except at the range's two ends; the units of the
+    // range's last, partial line beyond those (at most 120 bytes, so threads of wavefront
+    // 0 only) go in a second store.  Units outside the range are dropped (kOffLane).  All
+    // LDS reads go first, then the stores.
+    constexpr int PASS = NW * kWave;            // threads of the workgroup
+    auto la_store = [&](auto n_ranges, const char *src, int src_step, rsrc_t r, uint64_t base,
+                        uint32_t soff0, uint32_t soff_step, int nb) __attribute__((always_inline)) {
+        constexpr int N = decltype(n_ranges)::value;
+        constexpr int U = VB;
+        uint32_t v[N][U / 4], v2[N][U / 4], off[N], off2[N];
+#pragma unroll
+        for (int i = 0; i < N; ++i) {
+            const uint32_t soff = soff0 + (uint32_t)i * soff_step;
+            const int o = tid * U - (int)((base + soff) & 127u);
+            const int o2 = o + PASS * U;
+            const bool ok = o >= 0 && o < nb, ok2 = o2 < nb;
+            lds_read_run<U>(src + i * src_step + (ok ? o : 0), v[i]);
+            lds_read_run<U>(src + i * src_step + (ok2 ? o2 : 0), v2[i]);
+            off[i] = ok ? (uint32_t)o : kOffLane;
+            off2[i] = ok2 ? (uint32_t)o2 : kOffLane;
+        }
+#pragma unroll
+        for (int i = 0; i < N; ++i) gstore<U, SPOL>(r, off[i], soff0 + (uint32_t)i * soff_step, v[i]);
+        if (wave == 0) {
+#pragma unroll
+            for (int i = 0; i < N; ++i) gstore<U, SPOL>(r, off2[i], soff0 + (uint32_t)i * soff_step, v2[i]);
+        }
+    };
+    constexpr int OUT_ROW = LA ? RANGE * XB : 0;   // LDS bytes of one token of out (workgroup)
+    const rsrc_t og_r = make_rsrc((char *)p.out + (orow + cbg) * XB,
+                                  (uint32_t)(((int64_t)(T - 1) * p.out_tok + nchg) * XB));
     // Tokens go in chunks of G with no branch inside a chunk: x past T reads as zeros
     // and those tokens are computed but never stored.  The chunk's exponentials,
     // reciprocals and cross-lane sums are then independent and overlap.
@@ -442,10 +502,13 @@ __device__ __forceinline__ void verify_body(const KernelArgs &p) {
         silu_rows_checked<G>(y);
         if (wave_l2) head_l2<G>(y, lane_l2, p.head_lanes_log2, p.eps);
         after_math();
+        // line-aligned: the chunk's out goes through one of two LDS buffers (alternate
+        // chunks), so one barrier per chunk orders both the hand-off and the reuse
+        char *ob = lds + ((t0 / G) & 1) * (G * OUT_ROW);
 #pragma unroll
         for (int g = 0; g < G; ++g) {
             const int t = t0 + g;
-            if (t < T) {
+            if (LA || t < T) {
                 uint32_t o[XW];
                 if constexpr (XB == 4) {
 #pragma unroll
@@ -459,8 +522,17 @@ __device__ __forceinline__ void verify_body(const KernelArgs &p) {
                         o[w] = __builtin_bit_cast(uint32_t, __builtin_convertvector(pr, b2));
                     }
                 }
-                gstore<VB, SPOL>(o_r, laneV, (uint32_t)(t * p.out_tok * XB), o);
+                if constexpr (LA)
+                    lds_write_run<VB>(ob + g * OUT_ROW + tid * VB, o);
+                else
+                    gstore<VB, SPOL>(o_r, laneV, (uint32_t)(t * p.out_tok * XB), o);
             }
+        }
+        if constexpr (LA) {   // (full rows: every token of the chunk is below T)
+            lds_barrier();
+            la_store(std::integral_constant<int, G>(), ob, OUT_ROW, og_r,
+                     (uint64_t)(uintptr_t)p.out + (uint64_t)(orow + cbg) * XB,
+                     (uint32_t)(t0 * p.out_tok * XB), (uint32_t)(p.out_tok * XB), nchg * XB);
         }
     };
     auto nothing = []() {};
@@ -510,7 +582,30 @@ __device__ __forceinline__ void verify_body(const KernelArgs &p) {
     #pragma unroll
         for (int t = 0; t < TB; ++t) {
             if (t == T - 1) {
-                if (tm) {
+                if constexpr (LA) {
+                    // through the LDS buffer that the last chunk did not use (the chunk
+                    // before it did, and every wavefront has passed the last chunk's
+                    // barrier since reading it)
+                    constexpr int NC = TB / G, C0 = (W1 + G - 1) / G;
+                    constexpr int LASTC = C0 - 1, PREVC = C0 >= 2 ? C0 - 2 : NC - 1;
+                    static_assert((LASTC & 1) != (PREVC & 1) && W1 * RANGE * SB <= G * OUT_ROW,
+                                  "the commit's LDS buffer");
+                    char *sbuf = lds + ((LASTC & 1) ^ 1) * (G * OUT_ROW);
+    #pragma unroll
+                    for (int j = 0; j < W1; ++j) {
+                        uint32_t col[SW];
+                        column(t + 1 + j, col);
+                        lds_write_run<SCB>(sbuf + j * RANGE * SB + tid * SCB, col);
+                    }
+                    lds_barrier();
+                    const rsrc_t sg_r = make_rsrc(
+                        (char *)p.state + ((int64_t)slot * p.state_slot + cbg) * SB,
+                        (uint32_t)(((int64_t)(SL - 1) * p.state_col + nchg) * SB));
+                    la_store(std::integral_constant<int, W1>(), sbuf, RANGE * SB, sg_r,
+                             (uint64_t)(uintptr_t)p.state +
+                                 (uint64_t)((int64_t)slot * p.state_slot + cbg) * SB,
+                             0u, (uint32_t)(p.state_col * SB), nchg * SB);
+                } else if (tm) {
     #pragma unroll
                     for (int j = 0; j < W1; ++j) {
                         uint32_t col[SW];
@@ -539,7 +634,50 @@ __device__ __forceinline__ void verify_body(const KernelArgs &p) {
     }
 
     // ---- rollback windows: pure copies of the inputs ---------------------------------------
-    if constexpr (LAYOUT == kRows) {
+    if constexpr (LAYOUT == kRows && LA) {
+        // Line-aligned build (full rows: T == p.T == TB).  The workgroup's row block
+        // [nchg][LC] is one contiguous range: each lane's rows [CPL][LC] go into LDS at
+        // their offset in it, after the bytes of the range's first line that precede the
+        // range, and the workgroup stores it in 16-byte units from that line on.
+        constexpr int LC = TB + W1 - 1;
+        constexpr int LANEB = CPL * LC * SB;   // bytes of a lane's rows
+        constexpr int CW = LANEB / 4;
+        constexpr int PIECE = (LANEB % 16 == 0) ? 16 : 8;
+        const int64_t S = ((int64_t)slot * p.win_slot + (int64_t)cbg * LC) * SB;
+        const int delta = (int)(((uint64_t)(uintptr_t)p.win + (uint64_t)S) & 127u);
+        const int nb = nchg * LC * SB;
+        lds_barrier();   // every wavefront has stored the commit out of its LDS buffer
+        if (on) {
+            char *mine = lds + delta + tid * LANEB;
+#pragma unroll
+            for (int q = 0; q < CW / (PIECE / 4); ++q) {
+                uint32_t w4[PIECE / 4];
+#pragma unroll
+                for (int i = 0; i < PIECE / 4; ++i) {
+                    const int wd = (PIECE / 4) * q + i;
+                    if constexpr (SB == 4) {
+                        w4[i] = sbits(wd % LC + 1, wd / LC);
+                    } else {
+                        const int e0 = 2 * wd, e1 = 2 * wd + 1;
+                        w4[i] = sbits(e0 % LC + 1, e0 / LC) | (sbits(e1 % LC + 1, e1 / LC) << 16);
+                    }
+                }
+                lds_write_run<PIECE>(mine + PIECE * q, w4);
+            }
+        }
+        lds_barrier();
+        const rsrc_t rg_r = make_rsrc((char *)p.win + S, (uint32_t)nb);
+        constexpr int NQ = (128 + RANGE * LC * SB + PASS * 16 - 1) / (PASS * 16);
+#pragma unroll
+        for (int q = 0; q < NQ; ++q) {
+            const int k = (q * PASS + tid) * 16;   // offset from the first line
+            const int o = k - delta;
+            const bool ok = o >= 0 && o < nb;
+            uint32_t w[4];
+            lds_read_run<16>(lds + (ok ? k : 0), w);
+            gstore<16, SPOL>(rg_r, ok ? (uint32_t)o : kOffLane, 0, w);
+        }
+    } else if constexpr (LAYOUT == kRows) {
         const int L = T + W1 - 1;             // columns this row writes: v[1 .. T+W1-1]
         const int LS = p.T + W1 - 1;          // columns per channel in the buffer
         const rsrc_t row_r = make_rsrc(
@@ -754,16 +892,17 @@ __device__ __forceinline__ void verify_body(const KernelArgs &p) {
 // 119.2 -> 116.7 us, HBM traffic 1.039 -> 1.027x the algorithmic bytes).  Both bodies sit
 // in one kernel behind a wavefront-uniform branch, so the launch and the register count
 // are those of one body.
-template <int XB, int SB, int D, int TB, int LAYOUT, bool TREE, int WPE, bool SPLIT, bool TM>
-__global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(WPE > 0 ? WPE : 1)))
+// The line-aligned build (NW 4) streams every store: its store ranges leave in whole lines.
+template <int XB, int SB, int D, int TB, int LAYOUT, bool TREE, int WPE, bool SPLIT, bool TM, int NW = 1>
+__global__ __launch_bounds__(kWave * NW) __attribute__((amdgpu_waves_per_eu(WPE > 0 ? WPE : 1)))
 void cv_verify_kernel(KernelArgs p) {
-    if constexpr (TM) {
+    if constexpr (TM && NW == 1) {
         if (p.store_cached) {
-            verify_body<XB, SB, D, TB, LAYOUT, TREE, WPE, SPLIT, TM, 0>(p);
+            verify_body<XB, SB, D, TB, LAYOUT, TREE, WPE, SPLIT, TM, NW, 0>(p);
             return;
         }
     }
-    verify_body<XB, SB, D, TB, LAYOUT, TREE, WPE, SPLIT, TM, kNT>(p);
+    verify_body<XB, SB, D, TB, LAYOUT, TREE, WPE, SPLIT, TM, NW, kNT>(p);
 }
 
 // ---- instantiation ----------------------------------------------------------------------
@@ -772,8 +911,11 @@ void cv_verify_kernel(KernelArgs p) {
 // CV_XB, CV_SB, CV_VARIANT (0 dense, 1 rows, 2 time-major rows, 3 tree with dense
 // windows) and CV_TM (1: time-major conv_state) defined, so the instantiations build
 // in parallel; each object exports one picker over (d_conv, token bucket).
+// build: 0 the regular build, 1 the 16-token build for 5 wavefronts per SIMD (lean),
+// 2 the line-aligned build of 4-wavefront workgroups (16 tokens).
 template <int XB, int SB, int D, int LAYOUT, bool TREE, bool TM>
-const void *pick_bucket(int tb, bool lean, bool split) {
+const void *pick_bucket(int tb, int build, bool split) {
+    const bool lean = build == 1;
     if constexpr (!TREE && LAYOUT != kDense) {
         if (split) {
             if (tb == 8) return (const void *)cv_verify_kernel<XB, SB, D, 8, LAYOUT, TREE, 0, true, TM>;
@@ -787,6 +929,9 @@ const void *pick_bucket(int tb, bool lean, bool split) {
         case 4: return (const void *)cv_verify_kernel<XB, SB, D, 4, LAYOUT, TREE, 0, false, TM>;
         case 8: return (const void *)cv_verify_kernel<XB, SB, D, 8, LAYOUT, TREE, 0, false, TM>;
         case 16:
+            if constexpr (XB == 2 && SB == 2 && TM && LAYOUT == kRows && !TREE) {
+                if (build == 2) return (const void *)cv_verify_kernel<XB, SB, D, 16, LAYOUT, TREE, 0, false, TM, 4>;
+            }
             // the 5-wavefront build exists for bf16 x and state with a channel-major
             // conv_state only: elsewhere it spills heavily, or (time-major) the regular
             // build's pipelined loads measured faster
@@ -820,14 +965,14 @@ int CV_COUNT_SET(CV_XB, CV_SB, CV_VARIANT, CV_TM)(const CountRanges &c) {
 }
 #endif
 
-const void *CV_PICK(CV_XB, CV_SB, CV_VARIANT, CV_TM)(int d_conv, int token_bucket, int lean, int split) {
+const void *CV_PICK(CV_XB, CV_SB, CV_VARIANT, CV_TM)(int d_conv, int token_bucket, int build, int split) {
     constexpr int layout = CV_VARIANT == 3 ? kDense : CV_VARIANT;
     constexpr bool tree = CV_VARIANT == 3;
     constexpr bool tm = CV_TM != 0;
     switch (d_conv) {
-        case 2: return pick_bucket<CV_XB, CV_SB, 2, layout, tree, tm>(token_bucket, lean != 0, split != 0);
-        case 3: return pick_bucket<CV_XB, CV_SB, 3, layout, tree, tm>(token_bucket, lean != 0, split != 0);
-        case 4: return pick_bucket<CV_XB, CV_SB, 4, layout, tree, tm>(token_bucket, lean != 0, split != 0);
+        case 2: return pick_bucket<CV_XB, CV_SB, 2, layout, tree, tm>(token_bucket, build, split != 0);
+        case 3: return pick_bucket<CV_XB, CV_SB, 3, layout, tree, tm>(token_bucket, build, split != 0);
+        case 4: return pick_bucket<CV_XB, CV_SB, 4, layout, tree, tm>(token_bucket, build, split != 0);
         default: return nullptr;
     }
 }

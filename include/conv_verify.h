@@ -279,8 +279,9 @@ CV_API int conv_qk_l2norm(const cv_shape_t *shape, int64_t n_rows, int64_t row_s
  * kernel and its grid will assume. */
 typedef struct cv_launch_info {
     int64_t workgroups;        /* 1-D grid: n_seq * channel_blocks * token_chunks         */
-    int32_t threads;           /* per workgroup: one 64-lane wavefront                     */
-    int32_t channel_blocks;    /* ceil(d_inner / channels_per_wave)                        */
+    int32_t threads;           /* per workgroup: one 64-lane wavefront, or 4 (LINE_ALIGNED) */
+    int32_t channel_blocks;    /* workgroups per row: ceil(d_inner / (channels_per_wave *  */
+                               /* threads / 64))                                           */
     int32_t channels_per_wave; /* 64 lanes * channels per lane                             */
     int32_t channels_per_lane; /* 16 bytes of x per lane per token                         */
     int32_t token_bucket;      /* compile-time tokens per workgroup (>= T unless split)    */
@@ -300,10 +301,14 @@ typedef struct cv_launch_info {
  *                     vector load, so padded rows load nothing (grids of more than
  *                     5,120 wavefronts: more than one resident generation)
  *   XCD_ORDER         work items follow MI355X's round-robin XCD dispatch so that a row's
- *                     channel blocks share one L2 (d_inner not a multiple of 256) */
+ *                     channel blocks share one L2 (d_inner not a multiple of 256)
+ *   LINE_ALIGNED      workgroups of 4 wavefronts over 1024 channels, whose store ranges
+ *                     leave through LDS cut at 128-byte lines (bf16, time-major
+ *                     conv_state, dedup rows, T 16, store rows off 128-byte lines) */
 #define CV_LAUNCH_STATE_TIME_MAJOR 1
 #define CV_LAUNCH_SLOT_FIRST 2
 #define CV_LAUNCH_XCD_ORDER 4
+#define CV_LAUNCH_LINE_ALIGNED 8
 
 /* variant: a cv_layout_t, or CV_VARIANT_TREE for conv_verify_update_tree.  Returns
  * CV_OK or an error code. */

@@ -44,10 +44,12 @@ static void expect(const char *what, long long got, long long want) {
 static void *const A = reinterpret_cast<void *>(0x7f0000100000ull);
 static const int32_t *const I = reinterpret_cast<const int32_t *>(0x7f0000200000ull);
 
-static int verify_code(int xb, int sb, int variant, int tm, int d_conv, int bucket_idx, int lean,
+// build: 0 regular, 1 lean (5 wavefronts per SIMD), 2 line-aligned (4-wavefront workgroups)
+static int verify_code(int xb, int sb, int variant, int tm, int d_conv, int bucket_idx, int build,
                        int split) {
     return ((xb * 2 + sb / 2 - 3) & 7) << 9 | ((variant * 2 + tm) & 7) << 6 | (d_conv & 7) << 3 |
-           (bucket_idx & 7) | (lean ? 1 << 13 : 0) | (split ? 1 << 12 : 0);
+           (bucket_idx & 7) | (build == 1 ? 1 << 13 : 0) | (build == 2 ? 1 << 17 : 0) |
+           (split ? 1 << 12 : 0);
 }
 
 static int64_t wmul(int64_t a, int64_t b);
@@ -102,18 +104,53 @@ static void fixed_cases() {
     expect("stress d10200: XCD order on", kargs().xcd_remap, 1);
     expect("stress d10200: LDS = the state region", g_stub_launch.lds, 256 * 18 * 2);
     expect("stress d10200: nt stores (channel-major state)", kargs().store_cached, 0);
+    // time-major state at d 10200, T 16: the line-aligned build (rows of out and the
+    // row blocks start off 128-byte lines): 4-wavefront workgroups over 1024 channels,
+    // LDS for the workgroup's row block [1024, 18] after up to 112 bytes of its first
+    // line, every store streamed
     s = shape(512, 16, 10200, 4096, 18, 10240, CV_WIN_ROWS);
     expect("stress d10200 tm: rc", conv_verify_update_dedup(&s, A, A, A, A, I, I, A, A, nullptr), CV_OK);
-    expect("stress d10200 tm: XCD order on", kargs().xcd_remap, 1);
-    expect("stress d10200 tm: default-policy stores", kargs().store_cached, 1);
+    expect("stress d10200 tm: kernel (line-aligned build)", g_stub_launch.code,
+           verify_code(2, 2, 1, 1, 4, 4, 2, 0));
+    expect("stress d10200 tm: grid = rows x ceil(d / 1024)", g_stub_launch.grid_x, 512 * 10);
+    expect("stress d10200 tm: block of 4 wavefronts", g_stub_launch.block_x, 256);
+    expect("stress d10200 tm: workgroups per row", kargs().channel_blocks, 10);
+    expect("stress d10200 tm: LDS = 128 + the workgroup's row block", g_stub_launch.lds, 128 + 1024 * 18 * 2);
+    expect("stress d10200 tm: slot-first on (20,480 wavefronts)", kargs().slot_first, 1);
+    expect("stress d10200 tm: no XCD order", kargs().xcd_remap, 0);
+    expect("stress d10200 tm: nt stores", kargs().store_cached, 0);
+    // ... but not with 15 tokens, packed rows, a channel-major state or fp32 x
+    s = shape(512, 15, 10200, 4096, 18, 10240, CV_WIN_ROWS);
+    expect("d10200 tm T15: rc", conv_verify_update_dedup(&s, A, A, A, A, I, I, A, A, nullptr), CV_OK);
+    expect("d10200 tm T15: regular build", g_stub_launch.code, verify_code(2, 2, 1, 1, 4, 4, 0, 0));
+    expect("d10200 tm T15: XCD order on", kargs().xcd_remap, 1);
+    expect("d10200 tm T15: default-policy stores", kargs().store_cached, 1);
+    expect("d10200 tm T15: one wavefront per workgroup", g_stub_launch.block_x, 64);
+    {
+        s = shape(512, 16, 10200, 4096, 18, 10240, CV_WIN_ROWS);
+        expect("d10200 tm packed: rc", conv_verify_update(&s, CV_WIN_ROWS, A, A, A, A, I, I, I, A, A, nullptr), CV_OK);
+        expect("d10200 tm packed: one wavefront per workgroup", g_stub_launch.block_x, 64);
+    }
+    s = shape(512, 16, 10200, 4096, 18, 10240, CV_WIN_ROWS);
+    s.x_dtype = CV_F32; s.state_dtype = CV_F32;
+    s.state_slot_stride = 10240 * 18; s.win_slot_stride = 10200 * 18;
+    expect("d10200 tm f32: rc", conv_verify_update_dedup(&s, A, A, A, A, I, I, A, A, nullptr), CV_OK);
+    expect("d10200 tm f32: one wavefront per workgroup", g_stub_launch.block_x, 64);
     s = shape(512, 16, 10240, 4096, 18, 10240, CV_WIN_ROWS);
     expect("stress tm (aligned rows): rc", conv_verify_update_dedup(&s, A, A, A, A, I, I, A, A, nullptr), CV_OK);
     expect("stress tm (aligned rows): nt stores", kargs().store_cached, 0);
+    expect("stress tm (aligned rows): one wavefront per workgroup", g_stub_launch.block_x, 64);
+    // rows of out off their lines at d 10240 (token stride 10248): line-aligned
+    s = shape(512, 16, 10240, 4096, 18, 10240, CV_WIN_ROWS);
+    s.out_tok_stride = 10248; s.out_seq_stride = wmul(16, 10248);
+    expect("tm, out rows off lines: rc", conv_verify_update_dedup(&s, A, A, A, A, I, I, A, A, nullptr), CV_OK);
+    expect("tm, out rows off lines: line-aligned", g_stub_launch.block_x, 256);
+    expect("tm, out rows off lines: grid", g_stub_launch.grid_x, 512 * 10);
 
     // the K=17 GDN verify: dense windows on a small grid take the token-split kernel
     s = shape(8, 17, 8192, 4096, 3, 0, CV_WIN_DENSE);
     expect("gdn k17: rc", conv_verify_update_dense(&s, A, A, nullptr, A, nullptr, nullptr, A, A, nullptr), CV_OK);
-    expect("gdn k17: split kernel", g_stub_launch.code >> 14, 1);
+    expect("gdn k17: split kernel", (g_stub_launch.code >> 14) & 7, 1);
     expect("gdn k17: grid = rows x blocks x ceil(T/4)", g_stub_launch.grid_x, 8 * 32 * 5);
     expect("gdn k17: token chunks", kargs().token_chunks, 5);
 
@@ -247,7 +284,7 @@ static int64_t pick64(int64_t base) {
 static int64_t wmul(int64_t a, int64_t b) { return (int64_t)((uint64_t)a * (uint64_t)b); }
 
 static void fuzz(int iters) {
-    long long accepted = 0, refused = 0;
+    long long accepted = 0, refused = 0, la = 0;
     for (int it = 0; it < iters; ++it) {
         cv_shape_t s = shape(pick32({1, 7, 64, 128, 512, 4096}), pick32({1, 2, 3, 8, 16, 17, 24, 32}),
                              pick32({8, 256, 1032, 10200, 10240}), 0, 3, 0, CV_WIN_ROWS);
@@ -301,9 +338,30 @@ static void fuzz(int iters) {
                         g_stub_launch.grid_x, g_stub_launch.lds, g_stub_launch.code);
             fails = 1;
         }
+        // the line-aligned build (and only it) takes 4-wavefront workgroups, for bf16 x and
+        // state, a time-major state, dedup rows and 16 tokens; its grid covers each
+        // (row, 1024 channels) once and its LDS holds a row block after one line
+        const bool la_code = launched && g_stub_launch.code >= 0 && (g_stub_launch.code & (1 << 17));
+        if (launched && (g_stub_launch.block_x != 64 && g_stub_launch.block_x != 256)) {
+            std::printf("fuzz %d: block %u  MISMATCH\n", it, g_stub_launch.block_x);
+            fails = 1;
+        }
+        if (launched && la_code != (g_stub_launch.block_x == 256)) {
+            std::printf("fuzz %d: line-aligned kernel with block %u  MISMATCH\n", it, g_stub_launch.block_x);
+            fails = 1;
+        }
+        if (la_code && (s.x_dtype != CV_BF16 || s.state_dtype != CV_BF16 || s.T != 16 ||
+                        s.state_col_stride == 0 || layout != CV_WIN_ROWS || which > 1 ||
+                        g_stub_launch.grid_x != (uint64_t)s.n_seq * ((d + 1023) / 1024) ||
+                        g_stub_launch.lds < (size_t)(128 + 1024 * (s.T + s.d_conv - 2) * 2))) {
+            std::printf("fuzz %d: line-aligned launch of an unexpected shape  MISMATCH\n", it);
+            fails = 1;
+        }
         (rc == CV_OK ? accepted : refused)++;
+        la += la_code;
     }
-    std::printf("fuzz: %d shapes, %lld accepted, %lld refused\n", iters, accepted, refused);
+    std::printf("fuzz: %d shapes, %lld accepted, %lld refused, %lld line-aligned\n", iters, accepted,
+                refused, la);
 }
 
 int main(int argc, char **argv) {

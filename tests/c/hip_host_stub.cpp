@@ -15,7 +15,7 @@
 
 namespace {
 // marker[k] for k = kernel code (see code_of): distinct addresses, never dereferenced
-char g_marker[1 << 17];
+char g_marker[1 << 18];
 }
 
 extern "C" {
@@ -34,15 +34,15 @@ hipError_t g_stub_launch_result = hipSuccess;
 static const void *marker(int code) { return &g_marker[code]; }
 
 // code: family (0 verify, 1 split, 2 restore, 3 prefill, 4 l2) in bits 14..16, the
-// verify pickers' lean and split flags in bits 13 and 12, the picker's other arguments
-// in four 3-bit fields below
+// verify pickers' line-aligned, lean and split flags in bits 17, 13 and 12 (builds 2 and
+// 1), the picker's other arguments in four 3-bit fields below
 static int code_of(int family, int a, int b, int c, int d) {
     return family << 14 | (a & 7) << 9 | (b & 7) << 6 | (c & 7) << 3 | (d & 7);
 }
 
 namespace cvimpl {
 #define CV_STUB_PICK(xb, sb, v, tm)                                                       \
-    const void *pick_kernel_##xb##_##sb##_##v##_##tm(int d_conv, int tb, int lean, int split) { \
+    const void *pick_kernel_##xb##_##sb##_##v##_##tm(int d_conv, int tb, int build, int split) { \
         if (d_conv < 2 || d_conv > 4) return nullptr;                                     \
         int bucket = tb == 1 ? 0 : tb == 2 ? 1 : tb == 4 ? 2 : tb == 8 ? 3 : tb == 16 ? 4  \
                    : tb == 24 ? 5 : tb == 32 ? 6 : -1;                                    \
@@ -52,7 +52,8 @@ namespace cvimpl {
         const bool rows = (v) == 1 || (v) == 2;                                           \
         if (split && rows && tb != 8 && tb != 16) return nullptr;                         \
         return marker(code_of(0, (xb) * 2 + (sb) / 2 - 3, (v) * 2 + (tm), d_conv, bucket) | \
-                      (lean ? 1 << 13 : 0) | (split && rows ? 1 << 12 : 0));              \
+                      (build == 1 ? 1 << 13 : 0) | (build == 2 ? 1 << 17 : 0) |          \
+                      (split && rows ? 1 << 12 : 0));                                     \
     }
 #define CV_STUB_PICKS(xb, sb) \
     CV_STUB_PICK(xb, sb, 0, 0) CV_STUB_PICK(xb, sb, 1, 0) CV_STUB_PICK(xb, sb, 2, 0) CV_STUB_PICK(xb, sb, 3, 0) \
@@ -87,7 +88,7 @@ hipError_t hipLaunchKernel(const void *fn, dim3 grid, dim3 block, void **args, s
     // from the kernel family
     std::memset(g_stub_launch.args, 0, sizeof g_stub_launch.args);
     if (g_stub_launch.code >= 0) {
-        const int family = g_stub_launch.code >> 14;
+        const int family = (g_stub_launch.code >> 14) & 7;
         const size_t n = family <= 1 ? sizeof(cvimpl::KernelArgs)
                        : family == 2 ? sizeof(cvimpl::RestoreArgs)
                        : family == 3 ? sizeof(cvimpl::PrefillArgs) : sizeof(cvimpl::L2Args);

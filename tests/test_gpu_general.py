@@ -494,6 +494,50 @@ def test_time_major_state_equals_channel_major():
         assert np.array_equal(gh._bits(ra[k]), gh._bits(rb[k])), k
 
 
+# The line-aligned build: 4-wavefront workgroups over 1024 channels whose store ranges
+# (tokens of out, state columns, row blocks) leave through LDS cut at 128-byte lines -
+# bf16, time-major state, dedup rows, T 16, some store row off its lines.  Grids past
+# the token-split threshold; last workgroups of 1 to 4 wavefronts with a partial one;
+# D 2..4; padded and permuted slots, accept offsets, padded state columns, x and out
+# with a wider token stride, q|k ending inside a workgroup, rows off lines only through
+# the state's column stride.  Each case checks that the build is the one launched.
+LINE_ALIGNED = [
+    c("la_d1032_D4", n_seq=130, d_inner=1032, qk_channels=512, head_dim=128, T=16,
+      layout="dedup", accept_offsets=True, permute_slots=True, pad_frac=0.2, extra_slots=2,
+      state_tm=True, state_len=18, state_col_pad=8),
+    c("la_d2600_D3", n_seq=60, d_inner=2600, qk_channels=1280, head_dim=64, d_conv=3, T=16,
+      layout="dedup", accept_offsets=True, permute_slots=True, pad_frac=0.1, state_tm=True,
+      state_len=17),
+    c("la_d136_D2", n_seq=650, d_inner=136, qk_channels=128, head_dim=128, d_conv=2, T=16,
+      layout="dedup", accept_offsets=True, permute_slots=True, pad_frac=0.1, state_tm=True,
+      state_len=16),
+    c("la_d3080_qk1152", n_seq=60, d_inner=3080, qk_channels=1152, head_dim=128, T=16,
+      layout="dedup", accept_offsets=True, pad_frac=0.3, state_tm=True, state_len=18,
+      x_tok_stride=3096),
+    c("la_d1024_colpad", n_seq=170, d_inner=1024, qk_channels=512, head_dim=128, T=16,
+      layout="dedup", accept_offsets=True, permute_slots=True, state_tm=True, state_len=18,
+      state_col_pad=8),
+]
+
+
+@pytest.mark.parametrize("wl", LINE_ALIGNED, ids=[w.name for w in LINE_ALIGNED])
+def test_line_aligned_build(wl):
+    import causal_conv1d_verify_amd as cv
+    import causal_conv1d_verify_amd._lib as L
+
+    inp = workloads.make_inputs(wl)
+    p = gh.GeneralProblem(inp)
+    launch = cv.prepare("update", p.x, p.weight, p.bias, p.conv_state, p.out, p.windows,
+                        layout=p.layout, qk_channels=wl.qk_channels, head_dim=wl.head_dim,
+                        l2_eps=wl.l2_eps, slot_idx=p.slot_idx, num_accept_tokens=p.nat)
+    info = cv.conv_verify_describe(p.layout, launch.keepalive[0])
+    assert info.flags & L.CV_LAUNCH_LINE_ALIGNED and info.threads == 256, (info.flags, info.threads)
+    assert info.workgroups == wl.n_seq * -(-wl.d_inner // 1024)
+    _say(wl.name, "workgroups", info.workgroups, "lds", info.lds_bytes)
+    launch()
+    gh.compare_general(p.results(), gh.oracle_general(inp), inp)
+
+
 # Grids past one resident generation (5,120 wavefronts) with a slot table read the
 # slot before loading x, so padded rows load nothing; both sides of that edge.
 SLOT_FIRST = [c(f"slot_first_{layout}_n{n}{'_tm' if tm else ''}", n_seq=n, d_inner=1024,

@@ -14,7 +14,8 @@ conv_state allocation.  For each launch:
 The problems are small versions of the bench shapes, covering every launch kind: chain
 verify in the three window layouts with both conv_state orders (and padded rows, offsets,
 a partial channel block), packed rows, the token splits, the 5-wavefront 16-token build,
-tree verify, the restore from each layout, the prefill and the separate L2.
+the line-aligned build, tree verify, the restore from each layout, the prefill and the
+separate L2.
 """
 
 import numpy as np
@@ -84,6 +85,11 @@ VERIFY += [
       layout="dedup", permute_slots=True),
     c("sw_dense_T16_tm", n_seq=48, d_inner=7168, qk_channels=2048, head_dim=128, T=16,
       layout="dense", state_tm=True, state_len=3),
+    # the line-aligned build (4-wavefront workgroups; sw_dedup_T16_tm takes it too), with
+    # 8-byte row pieces (D 3) and a last workgroup of 3 wavefronts
+    c("sw_line_aligned_D3", n_seq=60, d_inner=2600, qk_channels=1280, head_dim=64, d_conv=3,
+      T=16, layout="dedup", accept_offsets=True, permute_slots=True, pad_frac=0.1,
+      state_tm=True, state_len=17),
     # token splits: the dense chain split kernel (small grid, K 17) and the rows split
     c("sw_dense_K17_split", n_seq=2, d_inner=1024, qk_channels=512, head_dim=128, T=17,
       layout="dense", accept_offsets=True, state_len=20),
