@@ -255,20 +255,14 @@ int plan_verify(int layout, bool tree, bool packed, const cv_shape_t *s, cvimpl:
     plan->head_lanes = head_lanes;
     plan->waves_per_group = 1;
     // The line-aligned build (bf16, time-major conv_state, row layout, full 16-token
-    // rows): when a store range of out, the state columns or the row blocks starts off a
-    // 128-byte line, 4-wavefront workgroups take 1024 channels each and cut their shared
-    // store ranges at the destination's lines (stress shape at d 10200, see the kernel).
-    // Its LDS: two exchange buffers of 4 tokens of out, or the workgroup's row block
-    // after up to 112 bytes of its first line.
-    // (strides are >= 0 here; reduced first, so no product overflows)
-    auto off = [](int64_t stride, int bytes) { return (stride % 128) * bytes % 128 != 0; };
-    const bool off_lines = off(s->out_tok_stride, xb) ||
-                           (s->n_seq > 1 && off(s->out_seq_stride, xb)) ||
-                           off(s->state_col_stride, sb) ||
-                           (s->n_slots > 1 && off(s->state_slot_stride, sb)) ||
-                           (s->n_slots > 1 && off(s->win_slot_stride, sb));
+    // rows): 4-wavefront workgroups take 1024 channels each and cut their shared store
+    // ranges at the destination's 128-byte lines.  Where rows start off those lines, one
+    // wavefront per 256 channels splits a line at every wavefront boundary (stress shape
+    // at d 10200: 116-118 -> 106 us); on aligned rows it measured 1% faster as well
+    // (d 10240: 103.4 -> 102.2 us).  Its LDS: two exchange buffers of 4 tokens of out, or
+    // the workgroup's row block after up to 112 bytes of its first line.
     if (plan->state_tm && layout == cvimpl::kRows && !tree && !packed && s->T == 16 &&
-        chunks == 1 && xb == 2 && sb == 2 && off_lines) {
+        chunks == 1 && xb == 2 && sb == 2) {
         constexpr int nw = cvimpl::kLineGroupWaves;
         const int64_t range = (int64_t)kChw * nw;
         const int64_t out_bufs = 2 * 4 * range * xb;

@@ -64,14 +64,14 @@ namespace {
 // TM: conv_state time-major (p.state_col is the column stride), a build of its own so
 // that neither layout's path costs the other registers.
 // NW: wavefronts per workgroup.  NW 4 is the line-aligned build (time-major state, row
-// layout, full 16-token rows) for buffers whose rows start off 128-byte lines: the
-// workgroup's 4 wavefronts take 1024 consecutive channels, and every store range they
-// share (a token of out, a column of the state, the row block) goes through LDS and
-// leaves cut at the destination's 128-byte lines, so that only the workgroup's two end
-// lines of each range are written in part.  (With one wavefront per 256 channels, every
-// wavefront boundary splits a line between two wavefronts' stores; a streaming probe of
-// the stress traffic at d 10200 ran 132.6 us that way and 113.2 us line-aligned, against
-// 108.4 us at d 10240.)
+// layout, full 16-token rows): the workgroup's 4 wavefronts take 1024 consecutive
+// channels, and every store range they share (a token of out, a column of the state,
+// the row block) goes through LDS and leaves cut at the destination's 128-byte lines, so
+// that only the workgroup's two end lines of each range are written in part.  Where rows
+// start off those lines, one wavefront per 256 channels splits a line between two
+// wavefronts' stores at every wavefront boundary: a streaming probe of the stress
+// traffic at d 10200 ran 132.6 us that way and 113.2 us line-aligned, against 108.4 us
+// at d 10240; the verify itself went from 116-118 to 106 us there.
 // SPOL: the cache policy of every store (the kernel below picks it).
 template <int XB, int SB, int D, int TB, int LAYOUT, bool TREE, int WPE, bool SPLIT, bool TM, int NW,
           int SPOL>

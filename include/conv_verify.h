@@ -304,7 +304,7 @@ typedef struct cv_launch_info {
  *                     channel blocks share one L2 (d_inner not a multiple of 256)
  *   LINE_ALIGNED      workgroups of 4 wavefronts over 1024 channels, whose store ranges
  *                     leave through LDS cut at 128-byte lines (bf16, time-major
- *                     conv_state, dedup rows, T 16, store rows off 128-byte lines) */
+ *                     conv_state, dedup rows, T 16, no token split) */
 #define CV_LAUNCH_STATE_TIME_MAJOR 1
 #define CV_LAUNCH_SLOT_FIRST 2
 #define CV_LAUNCH_XCD_ORDER 4

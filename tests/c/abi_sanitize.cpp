@@ -87,15 +87,24 @@ static void fixed_cases() {
     expect("headline: head lanes log2", kargs().head_lanes_log2, 5);
     expect("headline: channel blocks", kargs().channel_blocks, 40);
 
-    // the stress problem, conv_state time-major: 512 rows x T 16, 18-column state
+    // the stress problem, conv_state time-major: 512 rows x T 16, 18-column state: the
+    // line-aligned build (4-wavefront workgroups over 1024 channels)
     s = shape(512, 16, 10240, 4096, 18, 10240, CV_WIN_ROWS);
     expect("stress tm: rc", conv_verify_update_dedup(&s, A, A, A, A, I, I, A, A, nullptr), CV_OK);
-    expect("stress tm: kernel (regular 16-token build, tm state)", g_stub_launch.code,
-           verify_code(2, 2, 1, 1, 4, 4, 0, 0));
-    expect("stress tm: grid", g_stub_launch.grid_x, 512 * 40);
+    expect("stress tm: kernel (line-aligned 16-token build, tm state)", g_stub_launch.code,
+           verify_code(2, 2, 1, 1, 4, 4, 2, 0));
+    expect("stress tm: grid", g_stub_launch.grid_x, 512 * 10);
+    expect("stress tm: block", g_stub_launch.block_x, 256);
     expect("stress tm: slot-first on (four generations)", kargs().slot_first, 1);
-    expect("stress tm: no LDS for the state", g_stub_launch.lds, 256 * 18 * 2 / 2);
+    expect("stress tm: LDS = 128 + the workgroup's row block", g_stub_launch.lds, 128 + 1024 * 18 * 2);
+    expect("stress tm: nt stores", kargs().store_cached, 0);
     expect("stress tm: identity slots never wait", (conv_verify_update_dedup(&s, A, A, A, A, nullptr, I, A, A, nullptr), kargs().slot_first), 0);
+    // with 8 tokens: the regular build, one wavefront per 256 channels
+    s = shape(512, 8, 10240, 4096, 18, 10240, CV_WIN_ROWS);
+    expect("stress tm T8: rc", conv_verify_update_dedup(&s, A, A, A, A, I, I, A, A, nullptr), CV_OK);
+    expect("stress tm T8: kernel (regular build)", g_stub_launch.code, verify_code(2, 2, 1, 1, 4, 3, 0, 0));
+    expect("stress tm T8: grid", g_stub_launch.grid_x, 512 * 40);
+    expect("stress tm T8: block", g_stub_launch.block_x, 64);
 
     // channel-major 18-column state at d 10200: the state region in LDS, XCD order
     s = shape(512, 16, 10200, 4096, 18, 0, CV_WIN_ROWS);
@@ -119,7 +128,7 @@ static void fixed_cases() {
     expect("stress d10200 tm: slot-first on (20,480 wavefronts)", kargs().slot_first, 1);
     expect("stress d10200 tm: no XCD order", kargs().xcd_remap, 0);
     expect("stress d10200 tm: nt stores", kargs().store_cached, 0);
-    // ... but not with 15 tokens, packed rows, a channel-major state or fp32 x
+    // ... but not with 15 tokens, packed rows or fp32 x
     s = shape(512, 15, 10200, 4096, 18, 10240, CV_WIN_ROWS);
     expect("d10200 tm T15: rc", conv_verify_update_dedup(&s, A, A, A, A, I, I, A, A, nullptr), CV_OK);
     expect("d10200 tm T15: regular build", g_stub_launch.code, verify_code(2, 2, 1, 1, 4, 4, 0, 0));
@@ -136,16 +145,9 @@ static void fixed_cases() {
     s.state_slot_stride = 10240 * 18; s.win_slot_stride = 10200 * 18;
     expect("d10200 tm f32: rc", conv_verify_update_dedup(&s, A, A, A, A, I, I, A, A, nullptr), CV_OK);
     expect("d10200 tm f32: one wavefront per workgroup", g_stub_launch.block_x, 64);
-    s = shape(512, 16, 10240, 4096, 18, 10240, CV_WIN_ROWS);
-    expect("stress tm (aligned rows): rc", conv_verify_update_dedup(&s, A, A, A, A, I, I, A, A, nullptr), CV_OK);
-    expect("stress tm (aligned rows): nt stores", kargs().store_cached, 0);
-    expect("stress tm (aligned rows): one wavefront per workgroup", g_stub_launch.block_x, 64);
-    // rows of out off their lines at d 10240 (token stride 10248): line-aligned
-    s = shape(512, 16, 10240, 4096, 18, 10240, CV_WIN_ROWS);
-    s.out_tok_stride = 10248; s.out_seq_stride = wmul(16, 10248);
-    expect("tm, out rows off lines: rc", conv_verify_update_dedup(&s, A, A, A, A, I, I, A, A, nullptr), CV_OK);
-    expect("tm, out rows off lines: line-aligned", g_stub_launch.block_x, 256);
-    expect("tm, out rows off lines: grid", g_stub_launch.grid_x, 512 * 10);
+    s = shape(512, 8, 10240, 4096, 18, 10240, CV_WIN_ROWS);
+    expect("stress tm T8 (aligned rows): rc", conv_verify_update_dedup(&s, A, A, A, A, I, I, A, A, nullptr), CV_OK);
+    expect("stress tm T8 (aligned rows): nt stores", kargs().store_cached, 0);
 
     // the K=17 GDN verify: dense windows on a small grid take the token-split kernel
     s = shape(8, 17, 8192, 4096, 3, 0, CV_WIN_DENSE);
@@ -339,8 +341,9 @@ static void fuzz(int iters) {
             fails = 1;
         }
         // the line-aligned build (and only it) takes 4-wavefront workgroups, for bf16 x and
-        // state, a time-major state, dedup rows and 16 tokens; its grid covers each
-        // (row, 1024 channels) once and its LDS holds a row block after one line
+        // state, a time-major state, dedup rows and 16 tokens (always, unless split or
+        // packed); its grid covers each (row, 1024 channels) once and its LDS holds a row
+        // block after one line
         const bool la_code = launched && g_stub_launch.code >= 0 && (g_stub_launch.code & (1 << 17));
         if (launched && (g_stub_launch.block_x != 64 && g_stub_launch.block_x != 256)) {
             std::printf("fuzz %d: block %u  MISMATCH\n", it, g_stub_launch.block_x);

@@ -441,8 +441,8 @@ def test_launch_flags_edges():
     # the time-major conv_state build
     f = _flags(1, **dict(rows(128, 8), state_col_stride=10240))[2]
     assert f == L.CV_LAUNCH_STATE_TIME_MAJOR
-    # the line-aligned build: time-major state, dedup rows, T 16, store rows off 128-byte
-    # lines (d 10200: 20,400-byte token rows); 4-wavefront workgroups over 1024 channels
+    # the line-aligned build: bf16, time-major state, dedup rows, T 16; 4-wavefront
+    # workgroups over 1024 channels
     tm16 = lambda n, d, **kw: dict(rows(n, 16, d), state_col_stride=10240,   # noqa: E731
                                    state_slot_stride=10240 * 3, **kw)
     wg, ch, f = _flags(1, **tm16(512, 10200))
@@ -451,13 +451,15 @@ def test_launch_flags_edges():
     # one generation is 5,120 wavefronts = 1,280 such workgroups
     assert _flags(1, **tm16(128, 10200))[2] & L.CV_LAUNCH_SLOT_FIRST == 0
     assert _flags(1, **tm16(129, 10200))[2] & L.CV_LAUNCH_SLOT_FIRST
-    # not for aligned rows, 15 tokens, dense windows, or a channel-major state
-    assert _flags(1, **tm16(512, 10240))[2] & L.CV_LAUNCH_LINE_ALIGNED == 0
+    assert _flags(1, **tm16(512, 10240))[2] & L.CV_LAUNCH_LINE_ALIGNED
+    # not for 15 tokens, dense windows, a channel-major state or fp32
     assert _flags(1, **dict(rows(512, 15, 10200), state_col_stride=10240,
                             state_slot_stride=10240 * 3))[2] & L.CV_LAUNCH_LINE_ALIGNED == 0
     assert _flags(1, **rows(512, 16, 10200))[2] & L.CV_LAUNCH_LINE_ALIGNED == 0
     dense = dict(tm16(512, 10200), win_slot_stride=16 * 10200 * 3)
     assert _flags(0, **dense)[2] & L.CV_LAUNCH_LINE_ALIGNED == 0
+    f32 = dict(tm16(512, 10200), x_dtype=L.CV_F32, state_dtype=L.CV_F32)
+    assert _flags(1, **f32)[2] & L.CV_LAUNCH_LINE_ALIGNED == 0
     # a small grid takes the token split instead
     wg, ch, f = _flags(1, **tm16(8, 10200))
     assert ch == 4 and f & L.CV_LAUNCH_LINE_ALIGNED == 0
@@ -467,7 +469,7 @@ def test_line_aligned_geometry():
     """The line-aligned build's grid covers every (row, 1024-channel range) once, with
     4 wavefronts per workgroup and LDS for the workgroup's row block after up to 112
     bytes of its first line (or two 4-token buffers of out, if larger)."""
-    for d, d_conv in ((10200, 4), (1032, 3), (2600, 2), (136, 4)):
+    for d, d_conv in ((10200, 4), (1032, 3), (2600, 2), (136, 4), (10240, 4)):
         cols = 16 + d_conv - 2
         s = shape(n_seq=700, n_slots=700, T=16, d_inner=d, d_conv=d_conv, qk_channels=0,
                   x_seq_stride=16 * d, x_tok_stride=d, out_seq_stride=16 * d, out_tok_stride=d,

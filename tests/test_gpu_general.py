@@ -496,11 +496,11 @@ def test_time_major_state_equals_channel_major():
 
 # The line-aligned build: 4-wavefront workgroups over 1024 channels whose store ranges
 # (tokens of out, state columns, row blocks) leave through LDS cut at 128-byte lines -
-# bf16, time-major state, dedup rows, T 16, some store row off its lines.  Grids past
-# the token-split threshold; last workgroups of 1 to 4 wavefronts with a partial one;
-# D 2..4; padded and permuted slots, accept offsets, padded state columns, x and out
-# with a wider token stride, q|k ending inside a workgroup, rows off lines only through
-# the state's column stride.  Each case checks that the build is the one launched.
+# bf16, time-major state, dedup rows, T 16.  Grids past the token-split threshold; last
+# workgroups of 1 to 4 wavefronts with a partial one; D 2..4; padded and permuted slots,
+# accept offsets, padded state columns, x and out with a wider token stride, q|k ending
+# inside a workgroup, rows off lines only through the state's column stride, and rows on
+# lines.  Each case checks that the build is the one launched.
 LINE_ALIGNED = [
     c("la_d1032_D4", n_seq=130, d_inner=1032, qk_channels=512, head_dim=128, T=16,
       layout="dedup", accept_offsets=True, permute_slots=True, pad_frac=0.2, extra_slots=2,
@@ -517,6 +517,9 @@ LINE_ALIGNED = [
     c("la_d1024_colpad", n_seq=170, d_inner=1024, qk_channels=512, head_dim=128, T=16,
       layout="dedup", accept_offsets=True, permute_slots=True, state_tm=True, state_len=18,
       state_col_pad=8),
+    c("la_d2048_aligned", n_seq=90, d_inner=2048, qk_channels=1024, head_dim=256, T=16,
+      layout="dedup", accept_offsets=True, permute_slots=True, pad_frac=0.15, extra_slots=1,
+      state_tm=True, state_len=18),
 ]
 
 
