@@ -107,7 +107,9 @@
 extern "C" {
 #endif
 
-#define CONV_VERIFY_ABI_VERSION 4
+/* 5: conv_verify_debug_count; launch info may report 4-wavefront workgroups
+ *    (CV_LAUNCH_LINE_ALIGNED, threads 256). */
+#define CONV_VERIFY_ABI_VERSION 5
 
 /* Only the entry points below are exported from the shared library. */
 #define CV_API __attribute__((visibility("default")))
