@@ -254,24 +254,37 @@ int plan_verify(int layout, bool tree, bool packed, const cv_shape_t *s, cvimpl:
     plan->lds_bytes = (int)(dense_split ? split_lds : lds);
     plan->head_lanes = head_lanes;
     plan->waves_per_group = 1;
-    // The line-aligned build (bf16, time-major conv_state, row layout, full 16-token
-    // rows): 4-wavefront workgroups take 1024 channels each and cut their shared store
-    // ranges at the destination's 128-byte lines.  Where rows start off those lines, one
-    // wavefront per 256 channels splits a line at every wavefront boundary (stress shape
-    // at d 10200: 116-118 -> 106 us); on aligned rows it measured 1% faster as well
-    // (d 10240: 103.4 -> 102.2 us).  Its LDS: two exchange buffers of 4 tokens of out, or
-    // the workgroup's row block after up to 112 bytes of its first line.
-    if (plan->state_tm && layout == cvimpl::kRows && !tree && !packed && s->T == 16 &&
-        chunks == 1 && xb == 2 && sb == 2) {
+    // The line-aligned build (bf16, row layout, full 16-token rows, no token split): 4-wavefront
+    // workgroups take 1024 channels each and cut their shared store ranges at the
+    // destination's 128-byte lines.  Where rows start off those lines, one wavefront per 256
+    // channels splits a line at every wavefront boundary.  With a time-major state it is
+    // taken always: stress shape d 10200 116-118 -> 106 us, and on aligned rows 1% faster
+    // (d 10240: 103.4 -> 102.2 us).  With a channel-major state (whose staged region then
+    // has to leave before the arithmetic, to free the LDS) only where the rows of out start
+    // off lines: d 10200 172.0 -> 164.8 us, but 153.7 -> 162.3 us at d 10240, 160.2 ->
+    // 159.4 us with out on lines and the state off them, and bs128 T16 26.6 -> 32.4 us.
+    // Its LDS: two exchange buffers of 4 tokens of out, the workgroup's row block after up to
+    // 112 bytes of its first line, and a channel-major state's region the same way (built
+    // only where that fits 4 workgroups per compute unit).
+    // (strides are >= 0 here; reduced first, so no product overflows)
+    auto off = [](int64_t stride, int bytes) { return (stride % 128) * bytes % 128 != 0; };
+    const bool out_off_lines = off(s->out_tok_stride, xb) || (s->n_seq > 1 && off(s->out_seq_stride, xb));
+    {
         constexpr int nw = cvimpl::kLineGroupWaves;
         const int64_t range = (int64_t)kChw * nw;
         const int64_t out_bufs = 2 * 4 * range * xb;
         const int64_t block = 128 + range * (s->T + s->d_conv - 2) * sb;
-        plan->waves_per_group = nw;
-        plan->lean = 0;
-        plan->channel_blocks = (int)((C + range - 1) / range);
-        plan->workgroups = (int64_t)plan->channel_blocks * s->n_seq;
-        plan->lds_bytes = (int)(out_bufs > block ? out_bufs : block);
+        const int64_t region = plan->state_tm ? 0 : 128 + range * s->state_len * sb;
+        if (layout == cvimpl::kRows && !tree && !packed && s->T == 16 && chunks == 1 && xb == 2 &&
+            sb == 2 && (plan->state_tm || (out_off_lines && region <= cvimpl::kLineGroupMaxLds))) {
+            int64_t la_lds = out_bufs > block ? out_bufs : block;
+            if (region > la_lds) la_lds = region;
+            plan->waves_per_group = nw;
+            plan->lean = 0;
+            plan->channel_blocks = (int)((C + range - 1) / range);
+            plan->workgroups = (int64_t)plan->channel_blocks * s->n_seq;
+            plan->lds_bytes = (int)la_lds;
+        }
     }
     // Data-movement choices, each measured on MI355X (none changes a result bit):
     // a grid of more than one resident generation waits for the slot before loading x

@@ -50,8 +50,10 @@ constexpr int64_t kResidentWaves = 5120;
 // resident wavefronts per compute unit (5 per SIMD).
 constexpr int kRowsStageBytes = 8192;
 
-// Wavefronts per workgroup of the line-aligned build (1024 consecutive channels).
+// Wavefronts per workgroup of the line-aligned build (1024 consecutive channels), and
+// the most LDS it may take with a channel-major state: 4 workgroups per compute unit.
 constexpr int kLineGroupWaves = 4;
+constexpr int kLineGroupMaxLds = 40960;
 
 // Token-split verify (dense windows): tokens per wavefront, and the grids it serves:
 // at most kSplitMaxWaves wavefronts once split (measured at d 8192: T 8 gains up to 64

@@ -102,8 +102,15 @@ __device__ __forceinline__ void verify_body(const KernelArgs &p) {
     // held in registers through it, and land while the other chunks compute.
     constexpr bool PIPE = TM && !TREE && !SPLIT && G < TB;
     constexpr bool LA = NW > 1;
-    static_assert(!LA || (PIPE && LAYOUT == kRows && TB == 16 && WPE == 0 && XB == SB),
-                  "the line-aligned build: time-major state, row layout, 16-token rows");
+    static_assert(!LA || (!TREE && !SPLIT && G < TB && LAYOUT == kRows && TB == 16 && WPE == 0 &&
+                          XB == SB),
+                  "the line-aligned build: row layout, 16-token rows");
+    // The line-aligned build with a channel-major state: the 4 wavefronts' state regions
+    // lie side by side in LDS as the workgroup's one contiguous region, placed after the
+    // bytes of its first 128-byte line that precede it; the committed window goes in
+    // before the arithmetic (every token's x has landed by then), and the region leaves
+    // cut at lines, so that the LDS is free for the exchange buffers afterwards.
+    constexpr bool LACM = LA && !TM;
     constexpr int RANGE = NW * CHW;           // channels of a workgroup
 
     extern __shared__ uint4 lds_raw[];
@@ -183,7 +190,7 @@ __device__ __forceinline__ void verify_body(const KernelArgs &p) {
     {
         const rsrc_t w_r = make_rsrc((const char *)p.weight + (int64_t)cb * D * XB,
                                      (uint32_t)(nch * D * XB));
-        if constexpr (PIPE) {
+        if constexpr (PIPE || LA) {
             constexpr int WP = VB * D % 16 == 0 ? 16 : 8;   // bytes per load
 #pragma unroll
             for (int j = 0; j < VB * D / WP; ++j)
@@ -271,6 +278,10 @@ __device__ __forceinline__ void verify_body(const KernelArgs &p) {
     if constexpr (tm && !PIPE) load_state_columns();
     // exact: nch * SB is a multiple of 16; a split row's other chunks take no state
     const int rchunks = copier && !tm ? nch * SL * SB / 16 : 0;
+    // line-aligned, channel-major: where this wavefront's region sits in LDS
+    const int64_t sreg_off = ((int64_t)slot * p.state_slot + (int64_t)cbg * SL) * SB;   // bytes
+    const int s_delta = LACM ? (int)(((uint64_t)(uintptr_t)p.state + (uint64_t)sreg_off) & 127u) : 0;
+    char *const rgn = lds + (LACM ? s_delta + wave * CHW * SL * SB : 0);
     // chunks per lane, all in flight at once up to RJ; longer regions go in rounds
     constexpr int RJ = (W1 * SB + 3) / 4 > 12 ? (W1 * SB + 3) / 4 : 12;
     uint32_t sreg[RJ][4];
@@ -285,15 +296,17 @@ __device__ __forceinline__ void verify_body(const KernelArgs &p) {
     }
     if constexpr (!PIPE) {
         __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): every load above has landed
-        lds_read_run<VB * D>(lds + lane * VB * D, wr);   // (LDS accesses run in order)
+        if constexpr (!LA) {
+            lds_read_run<VB * D>(lds + lane * VB * D, wr);   // (LDS accesses run in order)
 #pragma unroll
-        for (int w = 0; w < XW * D; ++w) wr[w] = on ? wr[w] : 0u;
+            for (int w = 0; w < XW * D; ++w) wr[w] = on ? wr[w] : 0u;
+        }
     }
 #pragma unroll
     for (int j = 0; j < RJ; ++j) {
         const int q = j * kWave + lane;
         if (j * kWave < rchunks && q < rchunks)
-            *(uint4 *)(lds + q * 16) = make_uint4(sreg[j][0], sreg[j][1], sreg[j][2], sreg[j][3]);
+            *(uint4 *)(rgn + q * 16) = make_uint4(sreg[j][0], sreg[j][1], sreg[j][2], sreg[j][3]);
     }
     for (int j0 = RJ; j0 * kWave < rchunks; j0 += RJ) {   // state_len beyond the in-flight set
 #pragma unroll
@@ -305,7 +318,7 @@ __device__ __forceinline__ void verify_body(const KernelArgs &p) {
         for (int j = 0; j < RJ; ++j) {
             const int q = (j0 + j) * kWave + lane;
             if ((j0 + j) * kWave < rchunks && q < rchunks)
-                *(uint4 *)(lds + q * 16) = make_uint4(sreg[j][0], sreg[j][1], sreg[j][2], sreg[j][3]);
+                *(uint4 *)(rgn + q * 16) = make_uint4(sreg[j][0], sreg[j][1], sreg[j][2], sreg[j][3]);
         }
     }
     __builtin_amdgcn_s_setprio(0);
@@ -315,7 +328,7 @@ __device__ __forceinline__ void verify_body(const KernelArgs &p) {
     auto window_from_lds = [&]() __attribute__((always_inline)) {
         if (contiguous_state) {
             uint32_t run[RUNW];   // the lane's [CPL][W1] run
-            lds_read_run<RUNB>(lds + lane * RUNB, run);
+            lds_read_run<RUNB>(rgn + lane * RUNB, run);
 #pragma unroll
             for (int j = 0; j < W1; ++j)
 #pragma unroll
@@ -328,7 +341,7 @@ __device__ __forceinline__ void verify_body(const KernelArgs &p) {
                     }
                 }
         } else {
-            const char *rec = lds + (lane * CPL * SL + a) * SB;
+            const char *rec = rgn + (lane * CPL * SL + a) * SB;
 #pragma unroll
             for (int j = 0; j < W1; ++j)
 #pragma unroll
@@ -464,6 +477,16 @@ __device__ __forceinline__ void verify_body(const KernelArgs &p) {
             for (int i = 0; i < N; ++i) gstore<U, SPOL>(r, off2[i], soff0 + (uint32_t)i * soff_step, v2[i]);
         }
     };
+    // A contiguous range of nb bytes staged in LDS at src + delta (delta: the offset of the
+    // range's first byte in its 128-byte line), stored in 16-byte units from that line on.
+    auto la_store_block = [&](const char *src, rsrc_t r, int delta, int nb) __attribute__((always_inline)) {
+        for (int k = tid * 16; k < delta + nb; k += PASS * 16) {
+            const int o = k - delta;
+            uint32_t w[4];
+            lds_read_run<16>(src + (o >= 0 ? k : 0), w);
+            gstore<16, SPOL>(r, o >= 0 ? (uint32_t)o : kOffLane, 0, w);
+        }
+    };
     constexpr int OUT_ROW = LA ? RANGE * XB : 0;   // LDS bytes of one token of out (workgroup)
     const rsrc_t og_r = make_rsrc((char *)p.out + (orow + cbg) * XB,
                                   (uint32_t)(((int64_t)(T - 1) * p.out_tok + nchg) * XB));
@@ -535,6 +558,26 @@ __device__ __forceinline__ void verify_body(const KernelArgs &p) {
                      (uint32_t)(t0 * p.out_tok * XB), (uint32_t)(p.out_tok * XB), nchg * XB);
         }
     };
+    if constexpr (LACM) {
+        // the committed window v[TB .. TB+W1-1] (full rows) into the staged region, then the
+        // workgroup's region leaves whole, before the arithmetic frees the LDS for the
+        // exchange buffers
+        if (contiguous_state) {
+            uint32_t run[RUNW];
+            window_run(TB, run);
+            lds_write_run<RUNB>(rgn + lane * RUNB, run);
+        } else {
+            char *rec = rgn + lane * CPL * SL * SB;
+#pragma unroll
+            for (int ch = 0; ch < CPL; ++ch)
+#pragma unroll
+                for (int j = 0; j < W1; ++j) lds_put<SB>(rec + (ch * SL + j) * SB, sbits(TB + j, ch));
+        }
+        lds_barrier();
+        la_store_block(lds, make_rsrc((char *)p.state + sreg_off, (uint32_t)(nchg * SL * SB)), s_delta,
+                       nchg * SL * SB);
+        lds_barrier();
+    }
     auto nothing = []() {};
     if constexpr (PIPE) {
         // The chunks from C0 on take no window column (their tokens are >= W1): they go
@@ -564,7 +607,7 @@ __device__ __forceinline__ void verify_body(const KernelArgs &p) {
     if constexpr (SPLIT) {
         if (!copier) return;   // its chunk of out is stored; the copies are chunk 0's
     }
-    if constexpr (!TREE) {
+    if constexpr (!TREE && !LACM) {
         // Channel-major state, the 16-token build for 5 wavefronts per SIMD: the window
         // is read out of LDS again here (the region is untouched until the commit below),
         // so that it is not held in registers through chunks 1 and later, which take no
@@ -666,17 +709,7 @@ __device__ __forceinline__ void verify_body(const KernelArgs &p) {
             }
         }
         lds_barrier();
-        const rsrc_t rg_r = make_rsrc((char *)p.win + S, (uint32_t)nb);
-        constexpr int NQ = (128 + RANGE * LC * SB + PASS * 16 - 1) / (PASS * 16);
-#pragma unroll
-        for (int q = 0; q < NQ; ++q) {
-            const int k = (q * PASS + tid) * 16;   // offset from the first line
-            const int o = k - delta;
-            const bool ok = o >= 0 && o < nb;
-            uint32_t w[4];
-            lds_read_run<16>(lds + (ok ? k : 0), w);
-            gstore<16, SPOL>(rg_r, ok ? (uint32_t)o : kOffLane, 0, w);
-        }
+        la_store_block(lds, make_rsrc((char *)p.win + S, (uint32_t)nb), delta, nb);
     } else if constexpr (LAYOUT == kRows) {
         const int L = T + W1 - 1;             // columns this row writes: v[1 .. T+W1-1]
         const int LS = p.T + W1 - 1;          // columns per channel in the buffer
@@ -929,7 +962,7 @@ const void *pick_bucket(int tb, int build, bool split) {
         case 4: return (const void *)cv_verify_kernel<XB, SB, D, 4, LAYOUT, TREE, 0, false, TM>;
         case 8: return (const void *)cv_verify_kernel<XB, SB, D, 8, LAYOUT, TREE, 0, false, TM>;
         case 16:
-            if constexpr (XB == 2 && SB == 2 && TM && LAYOUT == kRows && !TREE) {
+            if constexpr (XB == 2 && SB == 2 && LAYOUT == kRows && !TREE) {
                 if (build == 2) return (const void *)cv_verify_kernel<XB, SB, D, 16, LAYOUT, TREE, 0, false, TM, 4>;
             }
             // the 5-wavefront build exists for bf16 x and state with a channel-major

@@ -106,13 +106,30 @@ static void fixed_cases() {
     expect("stress tm T8: grid", g_stub_launch.grid_x, 512 * 40);
     expect("stress tm T8: block", g_stub_launch.block_x, 64);
 
-    // channel-major 18-column state at d 10200: the state region in LDS, XCD order
+    // channel-major 18-column state at d 10200 (rows of out off 128-byte lines): the
+    // line-aligned build, LDS for the workgroup's state region after one line
     s = shape(512, 16, 10200, 4096, 18, 0, CV_WIN_ROWS);
     expect("stress d10200: rc", conv_verify_update_dedup(&s, A, A, A, A, I, I, A, A, nullptr), CV_OK);
-    expect("stress d10200: grid", g_stub_launch.grid_x, 512 * 40);
-    expect("stress d10200: XCD order on", kargs().xcd_remap, 1);
-    expect("stress d10200: LDS = the state region", g_stub_launch.lds, 256 * 18 * 2);
+    expect("stress d10200: kernel (line-aligned build, channel-major state)", g_stub_launch.code,
+           verify_code(2, 2, 1, 0, 4, 4, 2, 0));
+    expect("stress d10200: grid", g_stub_launch.grid_x, 512 * 10);
+    expect("stress d10200: block", g_stub_launch.block_x, 256);
+    expect("stress d10200: no XCD order", kargs().xcd_remap, 0);
+    expect("stress d10200: LDS = 128 + the workgroup's state region", g_stub_launch.lds, 128 + 1024 * 18 * 2);
     expect("stress d10200: nt stores (channel-major state)", kargs().store_cached, 0);
+    // ... the same with x and out on lines (token stride 10240): one wavefront per 256
+    // channels, the state region in LDS, XCD order
+    s.x_tok_stride = s.out_tok_stride = 10240;
+    s.x_seq_stride = s.out_seq_stride = wmul(16, 10240);
+    expect("stress d10200 strided: rc", conv_verify_update_dedup(&s, A, A, A, A, I, I, A, A, nullptr), CV_OK);
+    expect("stress d10200 strided: grid", g_stub_launch.grid_x, 512 * 40);
+    expect("stress d10200 strided: XCD order on", kargs().xcd_remap, 1);
+    expect("stress d10200 strided: LDS = the state region", g_stub_launch.lds, 256 * 18 * 2);
+    // ... and at d 10240, channel-major: the regular build
+    s = shape(512, 16, 10240, 4096, 18, 0, CV_WIN_ROWS);
+    expect("stress cm: rc", conv_verify_update_dedup(&s, A, A, A, A, I, I, A, A, nullptr), CV_OK);
+    expect("stress cm: regular 16-token build", g_stub_launch.code, verify_code(2, 2, 1, 0, 4, 4, 0, 0));
+    expect("stress cm: block", g_stub_launch.block_x, 64);
     // time-major state at d 10200, T 16: the line-aligned build (rows of out and the
     // row blocks start off 128-byte lines): 4-wavefront workgroups over 1024 channels,
     // LDS for the workgroup's row block [1024, 18] after up to 112 bytes of its first
@@ -341,9 +358,9 @@ static void fuzz(int iters) {
             fails = 1;
         }
         // the line-aligned build (and only it) takes 4-wavefront workgroups, for bf16 x and
-        // state, a time-major state, dedup rows and 16 tokens (always, unless split or
-        // packed); its grid covers each (row, 1024 channels) once and its LDS holds a row
-        // block after one line
+        // state, dedup rows and 16 tokens (not split or packed; a channel-major state only
+        // with rows of out off lines); its grid covers each (row, 1024 channels) once and
+        // its LDS holds a row block (and a channel-major state's region) after one line
         const bool la_code = launched && g_stub_launch.code >= 0 && (g_stub_launch.code & (1 << 17));
         if (launched && (g_stub_launch.block_x != 64 && g_stub_launch.block_x != 256)) {
             std::printf("fuzz %d: block %u  MISMATCH\n", it, g_stub_launch.block_x);
@@ -354,7 +371,11 @@ static void fuzz(int iters) {
             fails = 1;
         }
         if (la_code && (s.x_dtype != CV_BF16 || s.state_dtype != CV_BF16 || s.T != 16 ||
-                        s.state_col_stride == 0 || layout != CV_WIN_ROWS || which > 1 ||
+                        (s.state_col_stride == 0 && s.out_tok_stride % 64 == 0 &&
+                         (s.n_seq == 1 || s.out_seq_stride % 64 == 0)) ||
+                        (s.state_col_stride == 0 &&
+                         g_stub_launch.lds < (size_t)(128 + 1024 * s.state_len * 2)) ||
+                        layout != CV_WIN_ROWS || which > 1 ||
                         g_stub_launch.grid_x != (uint64_t)s.n_seq * ((d + 1023) / 1024) ||
                         g_stub_launch.lds < (size_t)(128 + 1024 * (s.T + s.d_conv - 2) * 2))) {
             std::printf("fuzz %d: line-aligned launch of an unexpected shape  MISMATCH\n", it);

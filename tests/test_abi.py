@@ -231,6 +231,17 @@ def test_launch_geometry_of_workloads(key):
     rc, info, detail = describe(int(wl.layout == "dedup"), s)
     assert rc == 0, detail
     cpl = 4
+    if info.flags & lib_mod.CV_LAUNCH_LINE_ALIGNED:
+        # the line-aligned build (16-token dedup rows whose rows of out start off 128-byte
+        # lines): 4 wavefronts per workgroup over 1024 channels, LDS for the larger of the
+        # exchange buffers, the row block and the state region, each after one line
+        assert wl.T == 16 and wl.layout == "dedup" and (xs * xb) % 128
+        assert info.threads == 256 and info.channels_per_wave == 256
+        assert info.channel_blocks == -(-wl.d_inner // 1024) and info.token_chunks == 1
+        assert info.workgroups == wl.n_seq * info.channel_blocks
+        assert info.lds_bytes == max(2 * 4 * 1024 * xb, 128 + 1024 * wl.row_cols * sb,
+                                     128 + 1024 * wl.state_len * sb)
+        return
     assert info.channels_per_lane == cpl and info.threads == 64
     assert info.channels_per_wave == 64 * cpl
     assert info.channel_blocks == -(-wl.d_inner // (64 * cpl))
@@ -452,10 +463,18 @@ def test_launch_flags_edges():
     assert _flags(1, **tm16(128, 10200))[2] & L.CV_LAUNCH_SLOT_FIRST == 0
     assert _flags(1, **tm16(129, 10200))[2] & L.CV_LAUNCH_SLOT_FIRST
     assert _flags(1, **tm16(512, 10240))[2] & L.CV_LAUNCH_LINE_ALIGNED
-    # not for 15 tokens, dense windows, a channel-major state or fp32
+    # a channel-major state: only where the rows of out start off lines, and its region
+    # (1024 channels x state_len) fits 4 workgroups per compute unit
+    assert _flags(1, **rows(512, 16, 10200))[2] & L.CV_LAUNCH_LINE_ALIGNED
+    assert _flags(1, **rows(512, 16, 10240))[2] & L.CV_LAUNCH_LINE_ALIGNED == 0
+    on_lines = dict(rows(512, 16, 10200), x_tok_stride=10240, out_tok_stride=10240,
+                    x_seq_stride=16 * 10240, out_seq_stride=16 * 10240)
+    assert _flags(1, **on_lines)[2] & L.CV_LAUNCH_LINE_ALIGNED == 0
+    wide = dict(rows(512, 16, 10200), state_len=20, state_slot_stride=10200 * 20)
+    assert _flags(1, **wide)[2] & L.CV_LAUNCH_LINE_ALIGNED == 0
+    # not for 15 tokens, dense windows or fp32
     assert _flags(1, **dict(rows(512, 15, 10200), state_col_stride=10240,
                             state_slot_stride=10240 * 3))[2] & L.CV_LAUNCH_LINE_ALIGNED == 0
-    assert _flags(1, **rows(512, 16, 10200))[2] & L.CV_LAUNCH_LINE_ALIGNED == 0
     dense = dict(tm16(512, 10200), win_slot_stride=16 * 10200 * 3)
     assert _flags(0, **dense)[2] & L.CV_LAUNCH_LINE_ALIGNED == 0
     f32 = dict(tm16(512, 10200), x_dtype=L.CV_F32, state_dtype=L.CV_F32)

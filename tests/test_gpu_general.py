@@ -520,6 +520,20 @@ LINE_ALIGNED = [
     c("la_d2048_aligned", n_seq=90, d_inner=2048, qk_channels=1024, head_dim=256, T=16,
       layout="dedup", accept_offsets=True, permute_slots=True, pad_frac=0.15, extra_slots=1,
       state_tm=True, state_len=18),
+    # channel-major state (taken where the rows of out start off lines): the workgroup's
+    # staged region leaves cut at lines too
+    c("la_cm_d1032_D4", n_seq=130, d_inner=1032, qk_channels=512, head_dim=128, T=16,
+      layout="dedup", accept_offsets=True, permute_slots=True, pad_frac=0.2, extra_slots=2,
+      state_len=18),
+    c("la_cm_d2600_D3", n_seq=60, d_inner=2600, qk_channels=1280, head_dim=64, d_conv=3, T=16,
+      layout="dedup", accept_offsets=True, permute_slots=True, pad_frac=0.1, state_len=17),
+    c("la_cm_d136_D2", n_seq=650, d_inner=136, qk_channels=128, head_dim=128, d_conv=2, T=16,
+      layout="dedup", accept_offsets=True, permute_slots=True, pad_frac=0.1, state_len=16),
+    c("la_cm_d3080_window_state", n_seq=60, d_inner=3080, qk_channels=1152, head_dim=128, T=16,
+      layout="dedup", pad_frac=0.3, permute_slots=True, x_tok_stride=3096),
+    c("la_cm_d2048_sl19", n_seq=90, d_inner=2048, qk_channels=1024, head_dim=256, T=16,
+      layout="dedup", accept_offsets=True, permute_slots=True, pad_frac=0.15, state_len=19,
+      x_tok_stride=2056),
 ]
 
 
