@@ -56,6 +56,13 @@ CASES = [
                      state_tm=True, state_col_pad=8),
     workloads.custom("g_prefill_tmstate", n_seq=4, d_inner=1032, qk_channels=0, T=40,
                      varlen=True, prefill=True, init_frac=0.5, state_tm=True),
+    # the line-aligned build (4-wavefront workgroups, LDS exchanges behind barriers)
+    workloads.custom("g_line_aligned_tm", n_seq=130, d_inner=1032, qk_channels=512,
+                     head_dim=128, T=16, layout="dedup", accept_offsets=True, permute_slots=True,
+                     pad_frac=0.2, state_len=18, state_tm=True),
+    workloads.custom("g_line_aligned_cm", n_seq=130, d_inner=1032, qk_channels=512,
+                     head_dim=128, T=16, layout="dedup", accept_offsets=True, permute_slots=True,
+                     pad_frac=0.2, state_len=18),
 ]
 
 

@@ -98,6 +98,13 @@ CASES += [
       layout="dedup", accept_offsets=True, permute_slots=True, pad_frac=0.2, state_tm=True),
     c("guard_large_dense_t1", n_seq=1300, d_inner=1024, qk_channels=512, head_dim=128, T=1,
       state_dtype="f32"),
+    # the line-aligned build (4-wavefront workgroups; the last one with 3 idle wavefronts),
+    # time-major and channel-major state
+    c("guard_line_aligned_tm", n_seq=130, d_inner=1032, qk_channels=512, head_dim=128, T=16,
+      layout="dedup", accept_offsets=True, permute_slots=True, pad_frac=0.2, state_len=18,
+      state_tm=True, state_col_pad=8),
+    c("guard_line_aligned_cm", n_seq=130, d_inner=1032, qk_channels=512, head_dim=128, T=16,
+      layout="dedup", accept_offsets=True, permute_slots=True, pad_frac=0.2, state_len=18),
 ]
 
 

@@ -90,6 +90,8 @@ VERIFY += [
     c("sw_line_aligned_D3", n_seq=60, d_inner=2600, qk_channels=1280, head_dim=64, d_conv=3,
       T=16, layout="dedup", accept_offsets=True, permute_slots=True, pad_frac=0.1,
       state_tm=True, state_len=17),
+    c("sw_line_aligned_cm", n_seq=130, d_inner=1032, qk_channels=512, head_dim=128, T=16,
+      layout="dedup", accept_offsets=True, permute_slots=True, pad_frac=0.2, state_len=18),
     # token splits: the dense chain split kernel (small grid, K 17) and the rows split
     c("sw_dense_K17_split", n_seq=2, d_inner=1024, qk_channels=512, head_dim=128, T=17,
       layout="dense", accept_offsets=True, state_len=20),
