@@ -259,16 +259,19 @@ int plan_verify(int layout, bool tree, bool packed, const cv_shape_t *s, cvimpl:
     // destination's 128-byte lines.  Where rows start off those lines, one wavefront per 256
     // channels splits a line at every wavefront boundary.  With a time-major state it is
     // taken always: stress shape d 10200 116-118 -> 106 us, and on aligned rows 1% faster
-    // (d 10240: 103.4 -> 102.2 us).  With a channel-major state (whose staged region then
-    // has to leave before the arithmetic, to free the LDS) only where the rows of out start
-    // off lines: d 10200 172.0 -> 164.8 us, but 153.7 -> 162.3 us at d 10240, 160.2 ->
-    // 159.4 us with out on lines and the state off them, and bs128 T16 26.6 -> 32.4 us.
-    // Its LDS: two exchange buffers of 4 tokens of out, the workgroup's row block after up to
-    // 112 bytes of its first line, and a channel-major state's region the same way (built
-    // only where that fits 4 workgroups per compute unit).
+    // (d 10240: 103.4 -> 102.2 us).  With a channel-major state only where a store range (the
+    // rows of out, the slots' state regions or row blocks) starts off lines - d 10200: 172.0
+    // -> 160.3 us; x and out on lines, state and rows off them: 160.4 -> 155.0 us; but all on
+    // lines 153.5 -> 158.7 us and bs128 T16 26.5 -> 30.7 us - and where its LDS allows 3
+    // workgroups per compute unit (state_len <= 18 at bf16).
+    // Its LDS: two exchange buffers of 4 tokens of out (after a channel-major state's staged
+    // region, which holds the workgroup's region after up to 112 bytes of its first line),
+    // or the workgroup's row block placed the same way.
     // (strides are >= 0 here; reduced first, so no product overflows)
     auto off = [](int64_t stride, int bytes) { return (stride % 128) * bytes % 128 != 0; };
-    const bool out_off_lines = off(s->out_tok_stride, xb) || (s->n_seq > 1 && off(s->out_seq_stride, xb));
+    const bool off_lines = off(s->out_tok_stride, xb) ||
+                           (s->n_seq > 1 && off(s->out_seq_stride, xb)) ||
+                           (s->n_slots > 1 && (off(s->state_slot_stride, sb) || off(s->win_slot_stride, sb)));
     {
         constexpr int nw = cvimpl::kLineGroupWaves;
         const int64_t range = (int64_t)kChw * nw;
@@ -276,9 +279,11 @@ int plan_verify(int layout, bool tree, bool packed, const cv_shape_t *s, cvimpl:
         const int64_t block = 128 + range * (s->T + s->d_conv - 2) * sb;
         const int64_t region = plan->state_tm ? 0 : 128 + range * s->state_len * sb;
         if (layout == cvimpl::kRows && !tree && !packed && s->T == 16 && chunks == 1 && xb == 2 &&
-            sb == 2 && (plan->state_tm || (out_off_lines && region <= cvimpl::kLineGroupMaxLds))) {
-            int64_t la_lds = out_bufs > block ? out_bufs : block;
-            if (region > la_lds) la_lds = region;
+            sb == 2 &&
+            (plan->state_tm ||
+             (off_lines && (region + 15) / 16 * 16 + out_bufs <= cvimpl::kLineGroupMaxLds))) {
+            const int64_t staged = (region + 15) / 16 * 16 + out_bufs;
+            const int64_t la_lds = staged > block ? staged : block;
             plan->waves_per_group = nw;
             plan->lean = 0;
             plan->channel_blocks = (int)((C + range - 1) / range);

@@ -51,9 +51,10 @@ constexpr int64_t kResidentWaves = 5120;
 constexpr int kRowsStageBytes = 8192;
 
 // Wavefronts per workgroup of the line-aligned build (1024 consecutive channels), and
-// the most LDS it may take with a channel-major state: 4 workgroups per compute unit.
+// the most LDS it may take with a channel-major state: 3 workgroups per compute unit
+// (LDS is allocated in 512-byte units).
 constexpr int kLineGroupWaves = 4;
-constexpr int kLineGroupMaxLds = 40960;
+constexpr int kLineGroupMaxLds = kMaxLds / 3 / 512 * 512;
 
 // Token-split verify (dense windows): tokens per wavefront, and the grids it serves:
 // at most kSplitMaxWaves wavefronts once split (measured at d 8192: T 8 gains up to 64

@@ -107,9 +107,9 @@ __device__ __forceinline__ void verify_body(const KernelArgs &p) {
                   "the line-aligned build: row layout, 16-token rows");
     // The line-aligned build with a channel-major state: the 4 wavefronts' state regions
     // lie side by side in LDS as the workgroup's one contiguous region, placed after the
-    // bytes of its first 128-byte line that precede it; the committed window goes in
-    // before the arithmetic (every token's x has landed by then), and the region leaves
-    // cut at lines, so that the LDS is free for the exchange buffers afterwards.
+    // bytes of its first 128-byte line that precede it; the exchange buffers of out follow
+    // the region, which stays staged through the arithmetic, takes the committed window
+    // in the copy phase and leaves cut at lines.
     constexpr bool LACM = LA && !TM;
     constexpr int RANGE = NW * CHW;           // channels of a workgroup
 
@@ -488,6 +488,8 @@ __device__ __forceinline__ void verify_body(const KernelArgs &p) {
         }
     };
     constexpr int OUT_ROW = LA ? RANGE * XB : 0;   // LDS bytes of one token of out (workgroup)
+    // where the exchange buffers start: after a channel-major state's staged region
+    const int ob_base = LACM ? (128 + RANGE * SL * SB + 15) / 16 * 16 : 0;
     const rsrc_t og_r = make_rsrc((char *)p.out + (orow + cbg) * XB,
                                   (uint32_t)(((int64_t)(T - 1) * p.out_tok + nchg) * XB));
     // Tokens go in chunks of G with no branch inside a chunk: x past T reads as zeros
@@ -527,7 +529,7 @@ __device__ __forceinline__ void verify_body(const KernelArgs &p) {
         after_math();
         // line-aligned: the chunk's out goes through one of two LDS buffers (alternate
         // chunks), so one barrier per chunk orders both the hand-off and the reuse
-        char *ob = lds + ((t0 / G) & 1) * (G * OUT_ROW);
+        char *ob = lds + ob_base + ((t0 / G) & 1) * (G * OUT_ROW);
 #pragma unroll
         for (int g = 0; g < G; ++g) {
             const int t = t0 + g;
@@ -558,10 +560,9 @@ __device__ __forceinline__ void verify_body(const KernelArgs &p) {
                      (uint32_t)(t0 * p.out_tok * XB), (uint32_t)(p.out_tok * XB), nchg * XB);
         }
     };
-    if constexpr (LACM) {
-        // the committed window v[TB .. TB+W1-1] (full rows) into the staged region, then the
-        // workgroup's region leaves whole, before the arithmetic frees the LDS for the
-        // exchange buffers
+    // Channel-major line-aligned build, copy phase: the committed window v[TB .. TB+W1-1]
+    // (full rows) into the staged region, then the workgroup's region leaves whole.
+    auto lacm_commit = [&]() __attribute__((always_inline)) {
         if (contiguous_state) {
             uint32_t run[RUNW];
             window_run(TB, run);
@@ -576,8 +577,7 @@ __device__ __forceinline__ void verify_body(const KernelArgs &p) {
         lds_barrier();
         la_store_block(lds, make_rsrc((char *)p.state + sreg_off, (uint32_t)(nchg * SL * SB)), s_delta,
                        nchg * SL * SB);
-        lds_barrier();
-    }
+    };
     auto nothing = []() {};
     if constexpr (PIPE) {
         // The chunks from C0 on take no window column (their tokens are >= W1): they go
@@ -607,6 +607,7 @@ __device__ __forceinline__ void verify_body(const KernelArgs &p) {
     if constexpr (SPLIT) {
         if (!copier) return;   // its chunk of out is stored; the copies are chunk 0's
     }
+    if constexpr (LACM) lacm_commit();
     if constexpr (!TREE && !LACM) {
         // Channel-major state, the 16-token build for 5 wavefronts per SIMD: the window
         // is read out of LDS again here (the region is untouched until the commit below),
@@ -689,7 +690,7 @@ __device__ __forceinline__ void verify_body(const KernelArgs &p) {
         const int64_t S = ((int64_t)slot * p.win_slot + (int64_t)cbg * LC) * SB;
         const int delta = (int)(((uint64_t)(uintptr_t)p.win + (uint64_t)S) & 127u);
         const int nb = nchg * LC * SB;
-        lds_barrier();   // every wavefront has stored the commit out of its LDS buffer
+        lds_barrier();   // every wavefront has stored the commit out of LDS
         if (on) {
             char *mine = lds + delta + tid * LANEB;
 #pragma unroll

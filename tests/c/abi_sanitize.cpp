@@ -107,7 +107,8 @@ static void fixed_cases() {
     expect("stress tm T8: block", g_stub_launch.block_x, 64);
 
     // channel-major 18-column state at d 10200 (rows of out off 128-byte lines): the
-    // line-aligned build, LDS for the workgroup's state region after one line
+    // line-aligned build, LDS for the workgroup's state region after one line and the
+    // exchange buffers after it
     s = shape(512, 16, 10200, 4096, 18, 0, CV_WIN_ROWS);
     expect("stress d10200: rc", conv_verify_update_dedup(&s, A, A, A, A, I, I, A, A, nullptr), CV_OK);
     expect("stress d10200: kernel (line-aligned build, channel-major state)", g_stub_launch.code,
@@ -115,16 +116,24 @@ static void fixed_cases() {
     expect("stress d10200: grid", g_stub_launch.grid_x, 512 * 10);
     expect("stress d10200: block", g_stub_launch.block_x, 256);
     expect("stress d10200: no XCD order", kargs().xcd_remap, 0);
-    expect("stress d10200: LDS = 128 + the workgroup's state region", g_stub_launch.lds, 128 + 1024 * 18 * 2);
+    expect("stress d10200: LDS = 128 + the workgroup's state region + 16 KiB", g_stub_launch.lds,
+           128 + 1024 * 18 * 2 + 16384);
     expect("stress d10200: nt stores (channel-major state)", kargs().store_cached, 0);
-    // ... the same with x and out on lines (token stride 10240): one wavefront per 256
-    // channels, the state region in LDS, XCD order
+    // ... the same with x and out on lines (token stride 10240): the state regions and row
+    // blocks are still off them (slot strides of 10200 x 18 elements): line-aligned
     s.x_tok_stride = s.out_tok_stride = 10240;
     s.x_seq_stride = s.out_seq_stride = wmul(16, 10240);
     expect("stress d10200 strided: rc", conv_verify_update_dedup(&s, A, A, A, A, I, I, A, A, nullptr), CV_OK);
-    expect("stress d10200 strided: grid", g_stub_launch.grid_x, 512 * 40);
-    expect("stress d10200 strided: XCD order on", kargs().xcd_remap, 1);
-    expect("stress d10200 strided: LDS = the state region", g_stub_launch.lds, 256 * 18 * 2);
+    expect("stress d10200 strided: block", g_stub_launch.block_x, 256);
+    expect("stress d10200 strided: grid", g_stub_launch.grid_x, 512 * 10);
+    // ... and with every store range on lines: one wavefront per 256 channels, the state
+    // region in LDS, XCD order
+    s.state_slot_stride = wmul(10240, 18);
+    s.win_slot_stride = wmul(10240, 18);
+    expect("stress d10200 all on lines: rc", conv_verify_update_dedup(&s, A, A, A, A, I, I, A, A, nullptr), CV_OK);
+    expect("stress d10200 all on lines: grid", g_stub_launch.grid_x, 512 * 40);
+    expect("stress d10200 all on lines: XCD order on", kargs().xcd_remap, 1);
+    expect("stress d10200 all on lines: LDS = the state region", g_stub_launch.lds, 256 * 18 * 2);
     // ... and at d 10240, channel-major: the regular build
     s = shape(512, 16, 10240, 4096, 18, 0, CV_WIN_ROWS);
     expect("stress cm: rc", conv_verify_update_dedup(&s, A, A, A, A, I, I, A, A, nullptr), CV_OK);
@@ -359,7 +368,7 @@ static void fuzz(int iters) {
         }
         // the line-aligned build (and only it) takes 4-wavefront workgroups, for bf16 x and
         // state, dedup rows and 16 tokens (not split or packed; a channel-major state only
-        // with rows of out off lines); its grid covers each (row, 1024 channels) once and
+        // with a store range off lines); its grid covers each (row, 1024 channels) once and
         // its LDS holds a row block (and a channel-major state's region) after one line
         const bool la_code = launched && g_stub_launch.code >= 0 && (g_stub_launch.code & (1 << 17));
         if (launched && (g_stub_launch.block_x != 64 && g_stub_launch.block_x != 256)) {
@@ -372,9 +381,12 @@ static void fuzz(int iters) {
         }
         if (la_code && (s.x_dtype != CV_BF16 || s.state_dtype != CV_BF16 || s.T != 16 ||
                         (s.state_col_stride == 0 && s.out_tok_stride % 64 == 0 &&
-                         (s.n_seq == 1 || s.out_seq_stride % 64 == 0)) ||
+                         (s.n_seq == 1 || s.out_seq_stride % 64 == 0) &&
+                         (s.n_slots <= 1 ||
+                          (s.state_slot_stride % 64 == 0 && s.win_slot_stride % 64 == 0))) ||
                         (s.state_col_stride == 0 &&
-                         g_stub_launch.lds < (size_t)(128 + 1024 * s.state_len * 2)) ||
+                         (g_stub_launch.lds < (size_t)(128 + 1024 * s.state_len * 2 + 16384) ||
+                          g_stub_launch.lds * 3 > (size_t)cvimpl::kMaxLds)) ||
                         layout != CV_WIN_ROWS || which > 1 ||
                         g_stub_launch.grid_x != (uint64_t)s.n_seq * ((d + 1023) / 1024) ||
                         g_stub_launch.lds < (size_t)(128 + 1024 * (s.T + s.d_conv - 2) * 2))) {

@@ -232,15 +232,19 @@ def test_launch_geometry_of_workloads(key):
     assert rc == 0, detail
     cpl = 4
     if info.flags & lib_mod.CV_LAUNCH_LINE_ALIGNED:
-        # the line-aligned build (16-token dedup rows whose rows of out start off 128-byte
-        # lines): 4 wavefronts per workgroup over 1024 channels, LDS for the larger of the
-        # exchange buffers, the row block and the state region, each after one line
-        assert wl.T == 16 and wl.layout == "dedup" and (xs * xb) % 128
+        # the line-aligned build (16-token dedup rows, some store range off 128-byte
+        # lines): 4 wavefronts per workgroup over 1024 channels; LDS for the larger of the
+        # staged state region (after one line) followed by the exchange buffers, and the
+        # row block (after one line)
+        assert wl.T == 16 and wl.layout == "dedup"
+        assert (xs * xb) % 128 or (wl.d_inner * wl.state_len * sb) % 128 \
+            or (wl.d_inner * wl.row_cols * sb) % 128
         assert info.threads == 256 and info.channels_per_wave == 256
         assert info.channel_blocks == -(-wl.d_inner // 1024) and info.token_chunks == 1
         assert info.workgroups == wl.n_seq * info.channel_blocks
-        assert info.lds_bytes == max(2 * 4 * 1024 * xb, 128 + 1024 * wl.row_cols * sb,
-                                     128 + 1024 * wl.state_len * sb)
+        region = -(-(128 + 1024 * wl.state_len * sb) // 16) * 16
+        assert info.lds_bytes == max(region + 2 * 4 * 1024 * xb, 128 + 1024 * wl.row_cols * sb)
+        assert info.lds_bytes * 3 <= 163840
         return
     assert info.channels_per_lane == cpl and info.threads == 64
     assert info.channels_per_wave == 64 * cpl
@@ -463,14 +467,19 @@ def test_launch_flags_edges():
     assert _flags(1, **tm16(128, 10200))[2] & L.CV_LAUNCH_SLOT_FIRST == 0
     assert _flags(1, **tm16(129, 10200))[2] & L.CV_LAUNCH_SLOT_FIRST
     assert _flags(1, **tm16(512, 10240))[2] & L.CV_LAUNCH_LINE_ALIGNED
-    # a channel-major state: only where the rows of out start off lines, and its region
-    # (1024 channels x state_len) fits 4 workgroups per compute unit
+    # a channel-major state: only where a store range (rows of out, state regions, row
+    # blocks) starts off lines, and its region (1024 channels x state_len) and the exchange
+    # buffers fit 3 workgroups per compute unit
     assert _flags(1, **rows(512, 16, 10200))[2] & L.CV_LAUNCH_LINE_ALIGNED
     assert _flags(1, **rows(512, 16, 10240))[2] & L.CV_LAUNCH_LINE_ALIGNED == 0
-    on_lines = dict(rows(512, 16, 10200), x_tok_stride=10240, out_tok_stride=10240,
-                    x_seq_stride=16 * 10240, out_seq_stride=16 * 10240)
-    assert _flags(1, **on_lines)[2] & L.CV_LAUNCH_LINE_ALIGNED == 0
-    wide = dict(rows(512, 16, 10200), state_len=20, state_slot_stride=10200 * 20)
+    out_on_lines = dict(rows(512, 16, 10200), x_tok_stride=10240, out_tok_stride=10240,
+                        x_seq_stride=16 * 10240, out_seq_stride=16 * 10240)
+    assert _flags(1, **out_on_lines)[2] & L.CV_LAUNCH_LINE_ALIGNED
+    all_on_lines = dict(out_on_lines, state_slot_stride=10240 * 3, win_slot_stride=10240 * 18)
+    assert _flags(1, **all_on_lines)[2] == L.CV_LAUNCH_XCD_ORDER | L.CV_LAUNCH_SLOT_FIRST
+    edge = dict(rows(512, 16, 10200), state_len=18, state_slot_stride=10200 * 18)
+    assert _flags(1, **edge)[2] & L.CV_LAUNCH_LINE_ALIGNED
+    wide = dict(rows(512, 16, 10200), state_len=19, state_slot_stride=10200 * 19)
     assert _flags(1, **wide)[2] & L.CV_LAUNCH_LINE_ALIGNED == 0
     # not for 15 tokens, dense windows or fp32
     assert _flags(1, **dict(rows(512, 15, 10200), state_col_stride=10240,

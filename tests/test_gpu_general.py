@@ -531,8 +531,8 @@ LINE_ALIGNED = [
       layout="dedup", accept_offsets=True, permute_slots=True, pad_frac=0.1, state_len=16),
     c("la_cm_d3080_window_state", n_seq=60, d_inner=3080, qk_channels=1152, head_dim=128, T=16,
       layout="dedup", pad_frac=0.3, permute_slots=True, x_tok_stride=3096),
-    c("la_cm_d2048_sl19", n_seq=90, d_inner=2048, qk_channels=1024, head_dim=256, T=16,
-      layout="dedup", accept_offsets=True, permute_slots=True, pad_frac=0.15, state_len=19,
+    c("la_cm_d2048_sl18", n_seq=90, d_inner=2048, qk_channels=1024, head_dim=256, T=16,
+      layout="dedup", accept_offsets=True, permute_slots=True, pad_frac=0.15, state_len=18,
       x_tok_stride=2056),
 ]
 
