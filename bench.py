@@ -37,6 +37,7 @@ import hashlib
 import json
 import math
 import os
+import re
 import sys
 import time
 
@@ -56,11 +57,20 @@ KERNEL_SRCS = [os.path.join(ROOT, "causal_conv1d_verify_amd", "csrc", f)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
+def _code_of(text: str) -> str:
+    """The source text without its comments and blank lines (string literals in the
+    device sources hold no comment markers), so that a comment edit keeps the hash."""
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    return "\n".join(line.rstrip() for line in text.splitlines() if line.strip())
+
+
 def kernel_hash() -> str:
-    """sha256[:16] over the device sources (every kernel the steps launch)."""
+    """sha256[:16] over the code of the device sources (every kernel the steps launch),
+    comments left out."""
     h = hashlib.sha256()
     for f in KERNEL_SRCS:
-        h.update(open(f, "rb").read())
+        h.update(_code_of(open(f, encoding="utf-8").read()).encode())
     return h.hexdigest()[:16]
 
 

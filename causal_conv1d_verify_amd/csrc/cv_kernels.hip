@@ -12,7 +12,9 @@
 //  * One 64-lane wavefront per workgroup, 4 channels per lane, 256 channels per
 //    wavefront; the 1-D grid is n_seq * ceil(d_inner / 256) workgroups.  (256-channel
 //    blocks stream measurably faster on MI355X than 512-channel ones for this traffic
-//    mix: twice the wavefronts keep more requests in flight.)
+//    mix: twice the wavefronts keep more requests in flight.)  The line-aligned 16-token
+//    build groups 4 such wavefronts over 1024 channels, so that the store ranges they
+//    share leave through LDS cut at 128-byte lines (see verify_body's NW).
 //  * Every global access is a lane-contiguous 8- or 16-byte buffer access: x and out
 //    per token, the columns of a time-major conv_state and of time-major rows, and
 //    every run of a channel-major conv_state, the dense snapshots and the dedup rows,
