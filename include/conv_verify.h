@@ -16,11 +16,12 @@
  * conv_state[s, c, 0 .. D-2] holding the committed window v[T .. T+D-2].
  *
  * Sources (page title, section):
- *  - Atlas docs, fn spark_model::layers::ops::gdn_verify_fused_conv_kn_batched:
- *    all K draft positions in one launch, every per-token rollback snapshot written
- *    inline to a strided intermediates array, conv_state left holding the committed
- *    window (also snapshot K-1), per-token and per-sequence strides, one launch over
- *    n_seq sequences whose windows are independent.
+ *  - Atlas docs, fn spark_model::layers::ops::gdn_verify_fused_conv_kn_batched: one
+ *    launch covers every draft position of every sequence; the same launch writes each
+ *    position's rollback snapshot to a strided buffer; afterwards conv_state holds the
+ *    window committed after the last position (equal to the last snapshot); the
+ *    arguments carry per-token and per-sequence strides; the sequences' windows do not
+ *    interact.
  *  - sglang PR 46184 (dedup conv window tile store), "Motivation" and
  *    "Modifications": the deduplicated per-slot row [dim, T+K-2] viewed as an
  *    overlapping [T, dim, K-1] window with step stride == window stride, written
@@ -32,7 +33,8 @@
  * Beyond that chain verify the library covers, with the same kernels family:
  *  - packed variable-length rows (cu_seqlens), sglang PR 46184, "Related upstream
  *    work" (packed ragged tokens in the verify kernel, so the tile store covers them);
- *  - the time-major row layout (MambaPool's axis-0 window layout seen transposed),
+ *  - the time-major row layout (MambaPool's window layout along axis 0: the
+ *    channel-major rows transposed),
  *    sglang PR 46184, "Modifications" (test coverage);
  *  - tree verify (per-token parents, dense windows), sglang PR 46184, "Scope";
  *  - the accepted-prefix restore (window k -> conv_state), sglang PR 46184,

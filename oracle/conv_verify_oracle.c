@@ -29,9 +29,9 @@
  *     doc: the conv is followed by SiLU, then an L2 over q and k alone.]
  *   - L2:     for channels c < qk_channels, head h = c / head_dim:
  *     y <- y / sqrt(sum_{head} y^2 + l2_eps), in fp64.  V channels are untouched.
- *     [Atlas glm5next_kda/mod.rs, Glm5NextKdaConfig::l2_eps: FLA convention
- *     1/sqrt(sum + eps), not max(norm, eps); qk_channels() = 2 * qkv_dim; V is never
- *     normalised.]
+ *     [Atlas glm5next_kda/mod.rs, Glm5NextKdaConfig::l2_eps: the scale is
+ *     1/sqrt(sum + eps) as in FLA, with no max(norm, eps) clamp; qk_channels() is
+ *     2 * qkv_dim; the V channels are left as they are.]
  *   - out[i,t,c] = y rounded once to the output dtype (nearest, ties to even).
  *   - the window shifts by one: w <- (w[1..], x_t) in the state dtype.
  *   - the new window is copied into the rollback buffer:
@@ -172,10 +172,10 @@ static float state_bits_val(const orc_problem *p, uint32_t bits) {
  *   ORC_ROWS_T win[s, t + j, c]                      the same row stored time-major,
  *                                                    [T+K-2, dim] per slot
  * ORC_ROWS is MambaPool's deduplicated row; ORC_ROWS_T is its axis-0 layout seen
- * transposed: in both the view's step stride equals its window stride.  [sglang PR
- * 46184, "Modifications": the tile store applies to any layout where the step
- * stride equals the window stride, and its tests cover the pool's axis-0 window
- * layout in transposed form.]
+ * transposed: in both, one step along the view moves by the same stride as one
+ * element along a window.  [sglang PR 46184, "Modifications": the tile store serves
+ * every layout with that property, and its tests include the pool's window layout
+ * along axis 0, transposed.]
  */
 enum { ORC_DENSE = 0, ORC_ROWS = 1, ORC_ROWS_T = 2 };
 
