@@ -121,7 +121,7 @@ __device__ __forceinline__ void verify_body(const KernelArgs &p) {
     const int tid = threadIdx.x;
     const int lane = LA ? tid % kWave : tid;
     const int wave = LA ? __builtin_amdgcn_readfirstlane(tid / kWave) : 0;
-    const unsigned bid = !LA && p.xcd_remap ? xcd_linear(blockIdx.x, gridDim.x) : blockIdx.x;
+    const unsigned bid = p.xcd_remap ? xcd_linear(blockIdx.x, gridDim.x) : blockIdx.x;
     const int r2 = (int)(bid / (unsigned)p.channel_blocks);
     const int cbg = (int)(bid - (unsigned)r2 * (unsigned)p.channel_blocks) * RANGE;
     const int cb = cbg + wave * CHW;            // this wavefront's first channel
@@ -455,28 +455,43 @@ __device__ __forceinline__ void verify_body(const KernelArgs &p) {
     // range's last, partial line beyond those (at most 120 bytes, so threads of wavefront
     // 0 only) go in a second store.  Units outside the range are dropped (kOffLane).  All
     // LDS reads go first, then the stores.
+    // With a channel-major state the units of a range's two partial lines are stored with
+    // the default policy (and the workgroups run in XCD order): the neighbouring workgroup,
+    // on the same XCD, writes the rest of such a line, and the two halves merge in L2
+    // instead of reaching HBM as two partial writes (stress d 10200: 159.9 -> 156.7 us).
+    // With a time-major state both measured slower (106.5 -> 108.3 / 110.3 us).
     constexpr int PASS = NW * kWave;            // threads of the workgroup
+    constexpr int PPOL = LACM ? kKeep : SPOL;   // the store policy of partial lines
     auto la_store = [&](auto n_ranges, const char *src, int src_step, rsrc_t r, uint64_t base,
                         uint32_t soff0, uint32_t soff_step, int nb) __attribute__((always_inline)) {
         constexpr int N = decltype(n_ranges)::value;
         constexpr int U = VB;
-        uint32_t v[N][U / 4], v2[N][U / 4], off[N], off2[N];
+        uint32_t v[N][U / 4], v2[N][U / 4], off[N], offp[N], off2[N];
 #pragma unroll
         for (int i = 0; i < N; ++i) {
             const uint32_t soff = soff0 + (uint32_t)i * soff_step;
-            const int o = tid * U - (int)((base + soff) & 127u);
+            const int delta = (int)((base + soff) & 127u);
+            const int o = tid * U - delta;
             const int o2 = o + PASS * U;
             const bool ok = o >= 0 && o < nb, ok2 = o2 < nb;
+            // the unit lies in the range's first or last line, and that line is partial
+            const bool part = (delta != 0 && o < 128 - delta) ||
+                              (((delta + nb) & 127) != 0 && o >= ((delta + nb) & ~127) - delta);
             lds_read_run<U>(src + i * src_step + (ok ? o : 0), v[i]);
             lds_read_run<U>(src + i * src_step + (ok2 ? o2 : 0), v2[i]);
-            off[i] = ok ? (uint32_t)o : kOffLane;
+            off[i] = ok && (PPOL == SPOL || !part) ? (uint32_t)o : kOffLane;
+            offp[i] = ok && part ? (uint32_t)o : kOffLane;
             off2[i] = ok2 ? (uint32_t)o2 : kOffLane;
         }
 #pragma unroll
         for (int i = 0; i < N; ++i) gstore<U, SPOL>(r, off[i], soff0 + (uint32_t)i * soff_step, v[i]);
-        if (wave == 0) {
+        if constexpr (PPOL != SPOL) {
 #pragma unroll
-            for (int i = 0; i < N; ++i) gstore<U, SPOL>(r, off2[i], soff0 + (uint32_t)i * soff_step, v2[i]);
+            for (int i = 0; i < N; ++i) gstore<U, PPOL>(r, offp[i], soff0 + (uint32_t)i * soff_step, v[i]);
+        }
+        if (wave == 0) {   // (the last line: partial)
+#pragma unroll
+            for (int i = 0; i < N; ++i) gstore<U, PPOL>(r, off2[i], soff0 + (uint32_t)i * soff_step, v2[i]);
         }
     };
     // A contiguous range of nb bytes staged in LDS at src + delta (delta: the offset of the
@@ -486,7 +501,9 @@ __device__ __forceinline__ void verify_body(const KernelArgs &p) {
             const int o = k - delta;
             uint32_t w[4];
             lds_read_run<16>(src + (o >= 0 ? k : 0), w);
-            gstore<16, SPOL>(r, o >= 0 ? (uint32_t)o : kOffLane, 0, w);
+            const bool part = k < 128 || k >= ((delta + nb) & ~127);   // first or last line
+            gstore<16, SPOL>(r, o >= 0 && (PPOL == SPOL || !part) ? (uint32_t)o : kOffLane, 0, w);
+            if constexpr (PPOL != SPOL) gstore<16, PPOL>(r, o >= 0 && part ? (uint32_t)o : kOffLane, 0, w);
         }
     };
     constexpr int OUT_ROW = LA ? RANGE * XB : 0;   // LDS bytes of one token of out (workgroup)

@@ -305,7 +305,8 @@ typedef struct cv_launch_info {
  *                     vector load, so padded rows load nothing (grids of more than
  *                     5,120 wavefronts: more than one resident generation)
  *   XCD_ORDER         work items follow MI355X's round-robin XCD dispatch so that a row's
- *                     channel blocks share one L2 (d_inner not a multiple of 256)
+ *                     channel blocks share one L2 (d_inner not a multiple of 256; and the
+ *                     line-aligned build with a channel-major conv_state)
  *   LINE_ALIGNED      workgroups of 4 wavefronts over 1024 channels, whose store ranges
  *                     leave through LDS cut at 128-byte lines (bf16, time-major
  *                     conv_state, dedup rows, T 16, no token split) */

@@ -115,7 +115,7 @@ static void fixed_cases() {
            verify_code(2, 2, 1, 0, 4, 4, 2, 0));
     expect("stress d10200: grid", g_stub_launch.grid_x, 512 * 10);
     expect("stress d10200: block", g_stub_launch.block_x, 256);
-    expect("stress d10200: no XCD order", kargs().xcd_remap, 0);
+    expect("stress d10200: XCD order (neighbouring workgroups share an L2)", kargs().xcd_remap, 1);
     expect("stress d10200: LDS = 128 + the workgroup's state region + 16 KiB", g_stub_launch.lds,
            128 + 1024 * 18 * 2 + 16384);
     expect("stress d10200: nt stores (channel-major state)", kargs().store_cached, 0);

@@ -470,7 +470,8 @@ def test_launch_flags_edges():
     # a channel-major state: only where a store range (rows of out, state regions, row
     # blocks) starts off lines, and its region (1024 channels x state_len) and the exchange
     # buffers fit 3 workgroups per compute unit
-    assert _flags(1, **rows(512, 16, 10200))[2] & L.CV_LAUNCH_LINE_ALIGNED
+    f = _flags(1, **rows(512, 16, 10200))[2]
+    assert f == L.CV_LAUNCH_LINE_ALIGNED | L.CV_LAUNCH_XCD_ORDER | L.CV_LAUNCH_SLOT_FIRST
     assert _flags(1, **rows(512, 16, 10240))[2] & L.CV_LAUNCH_LINE_ALIGNED == 0
     out_on_lines = dict(rows(512, 16, 10200), x_tok_stride=10240, out_tok_stride=10240,
                         x_seq_stride=16 * 10240, out_seq_stride=16 * 10240)
