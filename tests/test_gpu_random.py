@@ -5,6 +5,8 @@ accepts: widths 2-4, 1-32 tokens, the three dtype pairs, the three window layout
 parents, packed rows, accept offsets, padded rows, extra slots, strided x, both
 conv_state orders (time-major with padded columns), q|k of any head count, channel
 counts with partial blocks; about a third are followed by the accepted-prefix restore.
+Six more on grids past one resident generation, and eight on the line-aligned build's
+shapes (16-token bf16 dedup rows past the token-split threshold).
 Each is compared with the oracle's general loop at the
 usual bar (windows and state bit-exact over the whole buffers, out within tolerance,
 poison kept elsewhere).  The draws are fixed, so a failure names a reproducible case.
@@ -94,3 +96,41 @@ def test_random_large_grid(wl):
     p = gh.GeneralProblem(inp)
     p.verify()
     gh.compare_general(p.results(), gh.oracle_general(inp), inp)
+
+
+def _draw_line_aligned(k: int, rng: np.random.Generator):
+    """16-token dedup rows in bf16 on grids past the token-split threshold: the
+    line-aligned build (4-wavefront workgroups), with either conv_state order, random
+    widths, heads, strides and offsets; most draws put some store range off 128-byte
+    lines, where a channel-major state takes the build too."""
+    d = 8 * int(rng.integers(8, 513))
+    blocks = -(-d // 256)
+    n = int(rng.integers(2560 // (4 * blocks) + 1, 2560 // (4 * blocks) + 40))
+    hd = int(rng.choice((32, 64, 128, 256)))
+    D = int(rng.integers(2, 5))
+    offsets = bool(rng.random() < 0.7)
+    tm = bool(rng.random() < 0.5)
+    stride = d + 8 * int(rng.integers(1, 9)) if rng.random() < 0.4 else None
+    return workloads.custom(
+        f"rand_la{k}", n_seq=n, d_inner=d, qk_channels=hd * int(rng.integers(0, d // hd + 1)),
+        head_dim=hd, d_conv=D, T=16, layout="dedup", bias=bool(rng.random() < 0.5),
+        accept_offsets=offsets, state_len=(15 + D - 1) if offsets else int(rng.integers(D - 1, 19)),
+        pad_frac=float(rng.choice([0.0, 0.15, 0.4])), permute_slots=bool(rng.random() < 0.7),
+        extra_slots=int(rng.integers(0, 3)), x_tok_stride=stride, state_tm=tm,
+        state_col_pad=8 * int(rng.integers(0, 3)) if tm else 0,
+        restore=bool(rng.random() < 0.3), seed=workloads.BASE_SEED + 5600 + k)
+
+
+_rng_la = np.random.default_rng(workloads.BASE_SEED + 5599)
+LINE_ALIGNED = [_draw_line_aligned(k, _rng_la) for k in range(8)]
+
+
+@pytest.mark.parametrize("wl", LINE_ALIGNED, ids=[w.name for w in LINE_ALIGNED])
+def test_random_line_aligned(wl):
+    print("[case]", wl, flush=True)
+    inp = workloads.make_inputs(wl)
+    p = gh.GeneralProblem(inp)
+    p.verify()
+    if wl.restore:
+        p.restore()
+    gh.compare_general(p.results(), gh.oracle_general(inp, restore=wl.restore), inp)
