@@ -196,7 +196,10 @@ int plan_verify(int layout, bool tree, bool packed, const cv_shape_t *s, cvimpl:
     const int64_t wspan = cvimpl::lds_dma_span(kChw * s->d_conv * xb);
     const int64_t first = region > wspan ? region : wspan;
     if (layout == cvimpl::kRows && packed) {
-        const int64_t image = region + cvimpl::lds_dma_span(kChw * (s->T + s->d_conv - 2) * sb);
+        // the stored row block of short packed rows, past the state region and the weights
+        // (it is loaded with them)
+        const int64_t image = (region > wspan ? region : wspan) +
+                              cvimpl::lds_dma_span(kChw * (s->T + s->d_conv - 2) * sb);
         if (image > later) later = image;
     }
     if (layout == cvimpl::kDense) later = (tree ? (int64_t)(W1 + tb) * pitch : 0) + slabs;

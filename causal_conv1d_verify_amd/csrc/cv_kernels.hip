@@ -292,6 +292,23 @@ __device__ __forceinline__ void verify_body(const KernelArgs &p) {
         const int q = j * kWave + lane;
         if (j * kWave < rchunks) gload<16>(st_r, q < rchunks ? (uint32_t)q * 16u : kOffLane, 0, sreg[j]);
     }
+    // Packed rows shorter than the buffer's rows (row layout): the slot's stored row block
+    // comes into LDS too (the copy phase rewrites its columns below the row's length and
+    // stores it whole).  Builds that wait for every load at once load it here, with the
+    // others, past both the weights and the state region; pipelined builds, whose waits
+    // count loads in issue order, load it in the copy phase.
+    constexpr bool IMG_EARLY = LAYOUT == kRows && !PIPE && !LA;
+    constexpr int WSPAN = (CHW * D * XB + kWave * 16 - 1) / (kWave * 16) * (kWave * 16);
+    const int img_off = IMG_EARLY ? max(tm ? 0 : CHW * SL * SB, WSPAN) : (tm ? 0 : CHW * SL * SB);
+    const bool row_image = LAYOUT == kRows && p.cu != nullptr && T < p.T && copier;
+    if constexpr (IMG_EARLY) {
+        if (row_image) {
+            const int LS = p.T + W1 - 1;
+            block_to_lds(make_rsrc((char *)p.win + ((int64_t)slot * p.win_slot + (int64_t)cb * LS) * SB,
+                                   (uint32_t)(nch * LS * SB)),
+                         lds + img_off, nch * LS * SB / 16, lane);
+        }
+    }
     int par = -1;   // tree: lane t < T holds parent[row, t] (loaded with the rest)
     if constexpr (TREE) {
         if (lane < T) par = p.parent[(int64_t)row * p.T + lane];
@@ -774,20 +791,20 @@ __device__ __forceinline__ void verify_body(const KernelArgs &p) {
         const rsrc_t row_r = make_rsrc(
             (char *)p.win + ((int64_t)slot * p.win_slot + (int64_t)cb * LS) * SB,
             (uint32_t)(nch * LS * SB));
-        // Packed rows shorter than the buffer's: the slot's row block comes into LDS as
-        // stored (direct global->LDS loads, past the state region), each lane writes its
-        // channels' columns below L into it, and the block leaves whole: the columns past
-        // L keep their bits, and every store stays a coalesced 16-byte one.  The block is
-        // loaded here, not with the other loads, so that no other path reaches an LDS
-        // access with a global->LDS load possibly outstanding (the compiler would then
-        // wait there for every earlier store as well).
-        const bool row_image = p.cu != nullptr && T < p.T && copier;
+        // Packed rows shorter than the buffer's: the slot's row block, as stored, is in LDS
+        // (loaded with the other loads, or here in pipelined builds: there a global->LDS
+        // load still outstanding at a later LDS access would make the compiler wait for
+        // every store issued before it); each lane writes its channels' columns below L
+        // into it, and the block leaves whole: the columns past L keep their bits, and
+        // every store stays a coalesced 16-byte one.
         if (row_image) {
             constexpr int LC = TB + W1 - 1;   // >= LS
-            char *img = lds + (tm ? 0 : CHW * SL * SB);
-            __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): earlier LDS accesses are done
-            block_to_lds(row_r, img, nch * LS * SB / 16, lane);
-            __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): the block has landed
+            char *img = lds + img_off;
+            if constexpr (!IMG_EARLY) {
+                __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): earlier LDS accesses are done
+                block_to_lds(row_r, img, nch * LS * SB / 16, lane);
+                __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): the block has landed
+            }
             if (on) {
 #pragma unroll
                 for (int ch = 0; ch < CPL; ++ch)
