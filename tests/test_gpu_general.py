@@ -583,3 +583,41 @@ QK_EDGE.append(c("one_head_fp32", n_seq=2, d_inner=264, qk_channels=256, head_di
 @pytest.mark.parametrize("wl", QK_EDGE, ids=[w.name for w in QK_EDGE])
 def test_qk_edges(wl):
     _verify_case(wl)
+
+
+@pytest.mark.parametrize("tm", [True, False], ids=["tm", "cm"])
+def test_line_aligned_out_stride_differs_from_x(tm):
+    """The line-aligned build with out in a wider buffer than x (token stride 1048 against
+    x's 1024, so only out's rows start off 128-byte lines): out lands at its own strides,
+    the padding after each of its rows keeps its poison."""
+    import causal_conv1d_verify_amd as cv
+    import causal_conv1d_verify_amd._lib as L
+
+    wl = c(f"la_out_stride_{'tm' if tm else 'cm'}", n_seq=170, d_inner=1024, qk_channels=512,
+           head_dim=128, T=16, layout="dedup", accept_offsets=True, permute_slots=True,
+           pad_frac=0.2, state_len=18, state_tm=tm)
+    inp = workloads.make_inputs(wl)
+    p = gh.GeneralProblem(inp)
+    d, pad = wl.d_inner, 24
+    wide0 = workloads.poison((wl.n_seq, wl.T, d + pad), wl.x_dtype)
+    wide = gh.to_torch(wide0, wl.x_dtype)
+    p.out = wide[..., :d]
+    launch = cv.prepare("update", p.x, p.weight, p.bias, p.conv_state, p.out, p.windows,
+                        layout=p.layout, qk_channels=wl.qk_channels, head_dim=wl.head_dim,
+                        l2_eps=wl.l2_eps, slot_idx=p.slot_idx, num_accept_tokens=p.nat)
+    info = cv.conv_verify_describe(p.layout, launch.keepalive[0])
+    assert info.flags & L.CV_LAUNCH_LINE_ALIGNED and info.threads == 256
+    _say(wl.name, "workgroups", info.workgroups)
+    launch()
+    got = p.results()                      # windows and conv_state (out_full is untouched)
+    ref = gh.oracle_general(inp)
+    for k in ("windows", "conv_state"):
+        assert np.array_equal(gh._bits(got[k]), gh._bits(ref[k])), k
+    out = gh.to_numpy(wide, wl.x_dtype)
+    assert np.array_equal(gh._bits(out[..., d:]), gh._bits(wide0[..., d:])), "padding written"
+    mask = np.zeros(out[..., :d].shape, bool)
+    for idx in gh.computed_tokens(inp):
+        mask[idx + (slice(0, d),)] = True
+    go, ro = out[..., :d], ref["out"][..., :d]
+    assert np.array_equal(gh._bits(go)[~mask], gh._bits(ro)[~mask]), "out written outside the computed tokens"
+    gh.compare_out_elements(go[mask], ro[mask], wl.x_dtype)
