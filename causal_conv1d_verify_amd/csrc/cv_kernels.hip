@@ -515,32 +515,41 @@ __device__ __forceinline__ void verify_body(const KernelArgs &p) {
     // instruction: range 2i+j goes to the threads j * PASS/2 .. (j+1) * PASS/2 - 1, and its
     // last partial line (units past PASS/2) to the first lanes of wavefronts 0 and NW/2.
     // The halves of the workgroup store different ranges, so each lane's offset holds its
-    // range's soff.  Every policy here is SPOL.  (Time-major out: stress d 10200 107.1 ->
-    // 105.5 us; d 10240 unchanged within the spread.)
+    // range's soff; the partial lines take PPOL as above.  (Out, time-major state: stress
+    // d 10200 107.1 -> 105.5 us; channel-major: 154.9 -> 153.8 us; d 10240 unchanged
+    // within the spread.)
     auto la_store16 = [&](auto n_ranges, const char *src, int src_step, rsrc_t r, uint64_t base,
                           uint32_t soff0, uint32_t soff_step, int nb) __attribute__((always_inline)) {
         constexpr int N = decltype(n_ranges)::value;
         constexpr int HP = PASS / 2;               // threads per range
         static_assert(N % 2 == 0 && NW % 2 == 0, "pairs of ranges over two halves");
         const int j = tid / HP, k = tid % HP;
-        uint32_t v[N / 2][4], v2[N / 2][4], off[N / 2], off2[N / 2];
+        uint32_t v[N / 2][4], v2[N / 2][4], off[N / 2], offp[N / 2], off2[N / 2];
 #pragma unroll
         for (int i = 0; i < N / 2; ++i) {
             const int rg = 2 * i + j;
             const uint32_t soff = soff0 + (uint32_t)rg * soff_step;
-            const int o = k * 16 - (int)((base + soff) & 127u);
+            const int delta = (int)((base + soff) & 127u);
+            const int o = k * 16 - delta;
             const int o2 = o + HP * 16;
             const bool ok = o >= 0 && o < nb, ok2 = o2 < nb;
+            const bool part = (delta != 0 && o < 128 - delta) ||
+                              (((delta + nb) & 127) != 0 && o >= ((delta + nb) & ~127) - delta);
             lds_read_run<16>(src + rg * src_step + (ok ? o : 0), v[i]);
             lds_read_run<16>(src + rg * src_step + (ok2 ? o2 : 0), v2[i]);
-            off[i] = ok ? soff + (uint32_t)o : kOffLane;
+            off[i] = ok && (PPOL == SPOL || !part) ? soff + (uint32_t)o : kOffLane;
+            offp[i] = ok && part ? soff + (uint32_t)o : kOffLane;
             off2[i] = ok2 ? soff + (uint32_t)o2 : kOffLane;
         }
 #pragma unroll
         for (int i = 0; i < N / 2; ++i) gstore<16, SPOL>(r, off[i], 0u, v[i]);
+        if constexpr (PPOL != SPOL) {
+#pragma unroll
+            for (int i = 0; i < N / 2; ++i) gstore<16, PPOL>(r, offp[i], 0u, v[i]);
+        }
         if (wave % (NW / 2) == 0) {
 #pragma unroll
-            for (int i = 0; i < N / 2; ++i) gstore<16, SPOL>(r, off2[i], 0u, v2[i]);
+            for (int i = 0; i < N / 2; ++i) gstore<16, PPOL>(r, off2[i], 0u, v2[i]);
         }
     };
     // A contiguous range of nb bytes staged in LDS at src + delta (delta: the offset of the
@@ -624,7 +633,7 @@ __device__ __forceinline__ void verify_body(const KernelArgs &p) {
         if constexpr (LA) {   // (full rows: every token of the chunk is below T)
             lds_barrier();
             // (16-byte units need 16-byte aligned ranges: x, out and their strides are)
-            if constexpr (TM && XB == 2)
+            if constexpr (XB == 2)
                 la_store16(std::integral_constant<int, G>(), ob, OUT_ROW, og_r,
                            (uint64_t)(uintptr_t)p.out + (uint64_t)(orow + cbg) * XB,
                            (uint32_t)(t0 * p.out_tok * XB), (uint32_t)(p.out_tok * XB), nchg * XB);
