@@ -24,6 +24,7 @@ CV_LAUNCH_STATE_TIME_MAJOR = 1
 CV_LAUNCH_SLOT_FIRST = 2
 CV_LAUNCH_XCD_ORDER = 4
 CV_LAUNCH_LINE_ALIGNED = 8
+CV_LAUNCH_HEAD_BLOCKS = 16
 
 EXPORTS = (
     "conv_verify_update_dense",

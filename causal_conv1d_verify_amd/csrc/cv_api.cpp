@@ -99,27 +99,54 @@ int check_common(const cv_shape_t *s, int *xb_out, int *sb_out) {
     return CV_OK;
 }
 
-int head_lanes_of(const cv_shape_t *s, int *head_lanes, int *hl_log2) {
+// L2 head geometry: lanes per head, its log2 (-1 when not a power of two) and the
+// channel blocks of q|k.  align: the channel multiple every block must start and end on
+// (16 bytes of the narrower of the element types that move in 16-byte units).
+int plan_heads(const cv_shape_t *s, int align, int *hl_log2, cvimpl::HeadBlocks *h) {
     using cvimpl::kWave;
     const int cpl = cvimpl::kChannelsPerLane;
-    *head_lanes = 0;
     *hl_log2 = 0;
+    *h = cvimpl::HeadBlocks{0, 0, 0};
     if (s->qk_channels < 0 || s->qk_channels > s->d_inner)
         return fail(CV_EINVAL, "qk_channels (%d) outside 0..d_inner", s->qk_channels);
     if (s->qk_channels == 0) return CV_OK;
     if (s->head_dim <= 0) return fail(CV_EINVAL, "head_dim (%d) <= 0", s->head_dim);
     if (s->qk_channels % s->head_dim)
         return fail(CV_EINVAL, "qk_channels (%d) %% head_dim (%d) != 0", s->qk_channels, s->head_dim);
+    if (!std::isfinite(s->l2_eps) || s->l2_eps < 0.0f)
+        return fail(CV_EINVAL, "l2_eps must be finite and >= 0");
     if (s->head_dim % cpl)
         return fail(CV_ENOTSUP, "head_dim (%d) must be a multiple of %d", s->head_dim, cpl);
     const int hl = s->head_dim / cpl;
-    if (hl > kWave || (hl & (hl - 1)))
-        return fail(CV_ENOTSUP, "head_dim / %d (%d) must be a power of two <= %d", cpl, hl, kWave);
-    *head_lanes = hl;
-    while ((1 << *hl_log2) < hl) ++*hl_log2;
-    if (!std::isfinite(s->l2_eps) || s->l2_eps < 0.0f)
-        return fail(CV_EINVAL, "l2_eps must be finite and >= 0");
+    if (hl > kWave)
+        return fail(CV_ENOTSUP, "head_dim (%d) > %d: a head is reduced inside one wavefront",
+                    s->head_dim, kWave * cpl);
+    h->head_lanes = hl;
+    if ((hl & (hl - 1)) == 0) {   // the head tiles the 256-channel blocks
+        while ((1 << *hl_log2) < hl) ++*hl_log2;
+        return CV_OK;
+    }
+    *hl_log2 = -1;
+    // blocks of k whole heads, each block (and q|k's end, where the 256-channel blocks
+    // begin) on the channel multiple the kernels' 16-byte units need
+    int k = kWave * cpl / s->head_dim;
+    while (k > 0 && (k * s->head_dim) % align) --k;
+    if (k == 0)
+        return fail(CV_ENOTSUP, "head_dim (%d): no block of whole heads of at most %d channels "
+                                "is a multiple of %d", s->head_dim, kWave * cpl, align);
+    if (s->qk_channels % align)
+        return fail(CV_ENOTSUP, "qk_channels (%d) must be a multiple of %d with head_dim %d",
+                    s->qk_channels, align, s->head_dim);
+    h->qk_block_ch = k * s->head_dim;
+    h->qk_blocks = (s->qk_channels + h->qk_block_ch - 1) / h->qk_block_ch;
     return CV_OK;
+}
+
+// Channel blocks per row: uniform 256-channel blocks, or the q|k blocks of whole heads
+// and 256-channel blocks from qk on.
+int64_t row_blocks(const cv_shape_t *s, const cvimpl::HeadBlocks &h) {
+    const int64_t rest = h.qk_blocks ? (int64_t)s->d_inner - s->qk_channels : s->d_inner;
+    return h.qk_blocks + (rest + kChw - 1) / kChw;
 }
 
 int64_t win_per_slot(int layout, const cv_shape_t *s) {
@@ -140,8 +167,9 @@ int plan_verify(int layout, bool tree, bool packed, const cv_shape_t *s, cvimpl:
     if (tree && layout != cvimpl::kDense)
         return fail(CV_EINVAL, "tree verify writes dense windows");
     if (s->T > kMaxT) return fail(CV_ENOTSUP, "T (%d) > %d", s->T, kMaxT);
-    int head_lanes = 0, hl_log2 = 0;
-    rc = head_lanes_of(s, &head_lanes, &hl_log2);
+    int hl_log2 = 0;
+    cvimpl::HeadBlocks heads;
+    rc = plan_heads(s, 16 / (xb < sb ? xb : sb), &hl_log2, &heads);
     if (rc) return rc;
     if (s->x_seq_stride < 0 || s->x_tok_stride < 0 || s->out_seq_stride < 0 || s->out_tok_stride < 0)
         return fail(CV_EINVAL, "negative x/out stride");
@@ -163,7 +191,7 @@ int plan_verify(int layout, bool tree, bool packed, const cv_shape_t *s, cvimpl:
         s->out_tok_stride % align)
         return fail(CV_ENOTSUP, "x/out strides must be multiples of %d elements", align);
 
-    const int64_t blocks = (C + kChw - 1) / kChw;
+    const int64_t blocks = row_blocks(s, heads);
     const int64_t wg = blocks * (int64_t)s->n_seq;
     if (sat_mul(wg, kWave) > (int64_t)UINT32_MAX)
         return fail(CV_ENOTSUP, "grid of %lld workgroups exceeds the launch limit", (long long)wg);
@@ -255,7 +283,9 @@ int plan_verify(int layout, bool tree, bool packed, const cv_shape_t *s, cvimpl:
     plan->channel_blocks = (int)blocks;
     plan->workgroups = wg * chunks;
     plan->lds_bytes = (int)(dense_split ? split_lds : lds);
-    plan->head_lanes = head_lanes;
+    plan->head_lanes = heads.head_lanes;
+    plan->hl_log2 = hl_log2;
+    plan->heads = heads;
     plan->waves_per_group = 1;
     // The line-aligned build (bf16, row layout, full 16-token rows, no token split): 4-wavefront
     // workgroups take 1024 channels each and cut their shared store ranges at the
@@ -282,7 +312,7 @@ int plan_verify(int layout, bool tree, bool packed, const cv_shape_t *s, cvimpl:
         const int64_t block = 128 + range * (s->T + s->d_conv - 2) * sb;
         const int64_t region = plan->state_tm ? 0 : 128 + range * s->state_len * sb;
         if (layout == cvimpl::kRows && !tree && !packed && s->T == 16 && chunks == 1 && xb == 2 &&
-            sb == 2 &&
+            sb == 2 && heads.qk_blocks == 0 &&
             (plan->state_tm ||
              (off_lines && (region + 15) / 16 * 16 + out_bufs <= cvimpl::kLineGroupMaxLds))) {
             const int64_t staged = (region + 15) / 16 * 16 + out_bufs;
@@ -394,9 +424,8 @@ int verify(int layout, bool tree, const cv_shape_t *s, const void *x, const void
     a.n_slots = s->n_slots;
     a.state_len = s->state_len;
     a.channel_blocks = plan.channel_blocks;
-    int hl_log2 = 0;
-    while (plan.head_lanes && (1 << hl_log2) < plan.head_lanes) ++hl_log2;
-    a.head_lanes_log2 = hl_log2;
+    a.head_lanes_log2 = plan.hl_log2;
+    a.heads = plan.heads;
     a.eps = s->l2_eps;
     a.token_chunks = plan.token_chunks;
     a.state_col = s->state_col_stride;
@@ -562,8 +591,9 @@ int conv_qk_l2norm(const cv_shape_t *s, int64_t n_rows, int64_t row_stride, void
     const int xb = dtype_bytes(s->x_dtype);
     if (!xb) return fail(CV_EINVAL, "unknown x dtype %d", s->x_dtype);
     if (s->d_inner < 0) return fail(CV_EINVAL, "d_inner (%d) < 0", s->d_inner);
-    int head_lanes = 0, hl_log2 = 0;
-    int rc = head_lanes_of(s, &head_lanes, &hl_log2);
+    int hl_log2 = 0;
+    cvimpl::HeadBlocks heads;
+    int rc = plan_heads(s, 16 / xb, &hl_log2, &heads);
     if (rc) return rc;
     if (n_rows < 0) return fail(CV_EINVAL, "n_rows (%lld) < 0", (long long)n_rows);
     if (row_stride < s->qk_channels) return fail(CV_EINVAL, "row_stride < qk_channels");
@@ -575,7 +605,7 @@ int conv_qk_l2norm(const cv_shape_t *s, int64_t n_rows, int64_t row_stride, void
     if (n_rows == 0 || s->qk_channels == 0) return CV_OK;
     if (!x) return fail(CV_EINVAL, "x is NULL");
     if (!aligned16(x)) return fail(CV_ENOTSUP, "x must be 16-byte aligned");
-    const int64_t blocks = (s->qk_channels + kChw - 1) / kChw;
+    const int64_t blocks = heads.qk_blocks ? heads.qk_blocks : (s->qk_channels + kChw - 1) / kChw;
     const int64_t wg = sat_mul(blocks, n_rows / cvimpl::kL2Rows + (n_rows % cvimpl::kL2Rows != 0));
     if (sat_mul(wg, cvimpl::kWave) > (int64_t)UINT32_MAX)
         return fail(CV_ENOTSUP, "grid of %lld workgroups exceeds the launch limit", (long long)wg);
@@ -587,6 +617,7 @@ int conv_qk_l2norm(const cv_shape_t *s, int64_t n_rows, int64_t row_stride, void
     a.qk_blocks = (int)blocks;
     a.head_lanes_log2 = hl_log2;
     a.eps = s->l2_eps;
+    a.heads = heads;
     return launch(cvimpl::pick_l2(xb), wg, 0, a, hip_stream);
 }
 
@@ -610,7 +641,8 @@ int conv_verify_describe(int variant, const cv_shape_t *shape, cv_launch_info_t 
     info->flags = (plan.state_tm ? CV_LAUNCH_STATE_TIME_MAJOR : 0) |
                   (plan.slot_first ? CV_LAUNCH_SLOT_FIRST : 0) |
                   (plan.xcd_remap ? CV_LAUNCH_XCD_ORDER : 0) |
-                  (plan.waves_per_group > 1 ? CV_LAUNCH_LINE_ALIGNED : 0);
+                  (plan.waves_per_group > 1 ? CV_LAUNCH_LINE_ALIGNED : 0) |
+                  (plan.heads.qk_blocks ? CV_LAUNCH_HEAD_BLOCKS : 0);
     return CV_OK;
 }
 

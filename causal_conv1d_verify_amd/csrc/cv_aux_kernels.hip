@@ -449,7 +449,8 @@ __global__ __launch_bounds__(kWave) void cv_split_kernel(KernelArgs p) {
     const int lane = threadIdx.x;
     const unsigned b = blockIdx.x;
     const unsigned r2 = b / (unsigned)p.channel_blocks;
-    const int cb = (int)(b - r2 * (unsigned)p.channel_blocks) * CHW;
+    int cend;   // the end of this block's channels
+    const int cb = block_first(p.heads, (int)(b - r2 * (unsigned)p.channel_blocks), p.qk, p.d_inner, cend);
     const int row = (int)(r2 / (unsigned)p.token_chunks);
     const int chunk = (int)(r2 - (unsigned)row * (unsigned)p.token_chunks);
 
@@ -468,7 +469,7 @@ __global__ __launch_bounds__(kWave) void cv_split_kernel(KernelArgs p) {
     if (t0 >= T) return;
     const int nt = min(TC, T - t0);
     const int SL = p.state_len;
-    const int nch = min(CHW, p.d_inner - cb);
+    const int nch = min(CHW, cend - cb);
     const bool on = lane * CPL < nch;
     const uint32_t laneV = on ? (uint32_t)(lane * VB) : kOffLane;
 
@@ -596,7 +597,7 @@ __global__ __launch_bounds__(kWave) void cv_split_kernel(KernelArgs p) {
         }
     silu_rows_checked<TC>(y);
     if (cb < p.qk)   // uniform: this wavefront holds q|k channels
-        head_l2<TC>(y, lane * CPL + cb < p.qk, p.head_lanes_log2, p.eps);
+        head_l2<TC>(y, on && lane * CPL + cb < p.qk, p.head_lanes_log2, p.heads.head_lanes, p.eps);
     const rsrc_t o_r = make_rsrc((char *)p.out + (orow + cb) * XB,
                                  (uint32_t)(((int64_t)(T - 1) * p.out_tok + nch) * XB));
 #pragma unroll
@@ -682,10 +683,12 @@ __global__ __launch_bounds__(kWave) void cv_l2_kernel(L2Args p) {
     constexpr int R = kL2Rows;   // token rows of this wavefront, all loads in flight together
     const int lane = threadIdx.x;
     const int64_t rb = (int64_t)(blockIdx.x / (unsigned)p.qk_blocks);
-    const int cb = (int)(blockIdx.x - (unsigned)rb * (unsigned)p.qk_blocks) * CHW;
+    int cend;   // the end of this block's channels (the q|k blocks end at qk)
+    const int cb = block_first(p.heads, (int)(blockIdx.x - (unsigned)rb * (unsigned)p.qk_blocks), p.qk,
+                               p.qk, cend);
     const int64_t r0 = rb * R;
     const int nr = (int)min((int64_t)R, p.n_rows - r0);   // >= 1: the grid covers the rows once
-    const int nch = min(CHW, p.qk - cb);
+    const int nch = min(CHW, cend - cb);
     const bool on = lane * CPL < nch;
     const uint32_t laneV = on ? (uint32_t)(lane * VB) : kOffLane;
     const rsrc_t x_r = make_rsrc((char *)p.x + (r0 * p.row_stride + cb) * XB,
@@ -705,9 +708,9 @@ __global__ __launch_bounds__(kWave) void cv_l2_kernel(L2Args p) {
     for (int r = 0; r < R; ++r)
 #pragma unroll
         for (int ch = 0; ch < CPL; ++ch) y[r][ch] = elem_val<XB>(w[r], ch);
-    // a head never straddles q|k's end (qk is a multiple of head_dim), so lanes past
-    // it form whole groups of their own; they store nothing
-    head_l2<R>(y, on, p.head_lanes_log2, p.eps);
+    // a head never straddles the block's end (a block holds whole heads), so lanes past
+    // it form groups of their own; they store nothing
+    head_l2<R>(y, on, p.head_lanes_log2, p.heads.head_lanes, p.eps);
 #pragma unroll
     for (int r = 0; r < R; ++r) {
         if (r < nr) {

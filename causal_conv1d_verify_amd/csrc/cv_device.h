@@ -151,6 +151,45 @@ __device__ __forceinline__ void group_sums(float (&v)[G], int hl_log2) {
         for (int g = 0; g < G; ++g) v[g] = xor32_sum(v[g]);
 }
 
+// Sums over groups of hl lanes where hl is not a power of two (3 <= hl <= 63): the groups
+// start at lane 0 and follow one another, and the lanes past the last whole group form a
+// shorter group of their own.  For G values at once, a segmented inclusive scan (step s
+// adds the value s lanes down when that lane is in the same group, so after the steps
+// s = 1, 2, 4, ... < hl a group's last lane holds the group's total, each value added once)
+// is followed by a broadcast of that lane's total to its whole group, so all lanes of a
+// group hold the bit-identical sum.  Lanes move through ds_bpermute (no LDS memory).
+// All lanes active.
+template <int G>
+__device__ __forceinline__ void group_sums_any(float (&v)[G], int hl) {
+    const int lane = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+    const int first = lane - lane % hl;
+    const int last = min(first + hl - 1, kWave - 1);
+    for (int s = 1; s < hl; s *= 2) {   // (uniform)
+        const bool take = lane - s >= first;
+        const int src = (take ? lane - s : lane) * 4;
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            const float t = __int_as_float(__builtin_amdgcn_ds_bpermute(src, __float_as_int(v[g])));
+            v[g] = take ? v[g] + t : v[g];
+        }
+    }
+#pragma unroll
+    for (int g = 0; g < G; ++g) v[g] = __int_as_float(__builtin_amdgcn_ds_bpermute(last * 4, __float_as_int(v[g])));
+}
+
+// The first channel of channel block blk of a row and the end of its channels (before
+// d_inner's end): uniform 256-channel blocks, or the q|k blocks of whole heads followed by
+// 256-channel blocks from qk on (HeadBlocks).
+__device__ __forceinline__ int block_first(const HeadBlocks &h, int blk, int qk, int d_inner, int &cend) {
+    if (blk < h.qk_blocks) {
+        const int c0 = blk * h.qk_block_ch;
+        cend = min(c0 + h.qk_block_ch, qk);
+        return c0;
+    }
+    cend = d_inner;
+    return (h.qk_blocks ? qk : 0) + (blk - h.qk_blocks) * (kWave * kChannelsPerLane);
+}
+
 // group_sums for one value with every stage selected rather than branched on: the rare
 // path of head_l2 uses it, where branches (and per-stage lane addresses) would hold
 // registers across the whole token loop.
@@ -172,7 +211,8 @@ __device__ __forceinline__ float group_sum_sel(float v, int hl_log2) {
 
 // Per-head L2 of G token rows held as y[g][channel], the lane's kChannelsPerLane
 // channels: y <- y / sqrt(S + eps), S = sum_head y^2, on lanes with lane_l2 set (a head
-// is the aligned group of 2^hl_log2 lanes); other lanes keep y.  All lanes active.
+// is the aligned group of 2^hl_log2 lanes, or with hl_log2 < 0 a group of hl lanes as in
+// group_sums_any); other lanes keep y.  All lanes active.
 //
 // S runs in fp32 (any reduction order) with v_rsq_f32.  That is accurate while
 // S + eps <= 2^127 (no partial sum overflows) and either S >= 2^-100 (squares below
@@ -191,7 +231,7 @@ __device__ __forceinline__ float group_sum_sel(float v, int hl_log2) {
 // selected rather than branched on, so the rare path costs the common one no registers.
 template <int G>
 __device__ __forceinline__ void head_l2(float (&y)[G][kChannelsPerLane], bool lane_l2,
-                                        int hl_log2, float eps) {
+                                        int hl_log2, int hl, float eps) {
     constexpr int CPL = kChannelsPerLane;
     float ss[G];
 #pragma unroll
@@ -200,7 +240,10 @@ __device__ __forceinline__ void head_l2(float (&y)[G][kChannelsPerLane], bool la
 #pragma unroll
         for (int ch = 0; ch < CPL; ++ch) ss[g] = __builtin_fmaf(y[g][ch], y[g][ch], ss[g]);
     }
-    group_sums<G>(ss, hl_log2);
+    if (hl_log2 >= 0)
+        group_sums<G>(ss, hl_log2);
+    else
+        group_sums_any<G>(ss, hl);
     // in range: every S <= 2^126 (then S + eps <= 2^127 for eps <= 2^126; a larger eps
     // takes the second sum) and, unless eps >= 2^-60, every S >= 2^-100.  A NaN S gives
     // NaN either way, so the running max / min may drop it.
@@ -228,7 +271,13 @@ __device__ __forceinline__ void head_l2(float (&y)[G][kChannelsPerLane], bool la
                 const float u = y[g][ch] * f;
                 s = __builtin_fmaf(u, u, s);
             }
-            s = group_sum_sel(s, hl_log2);
+            if (hl_log2 >= 0) {
+                s = group_sum_sel(s, hl_log2);
+            } else {
+                float one[1] = {s};
+                group_sums_any<1>(one, hl);
+                s = one[0];
+            }
             const float ep = eps * f * f;
             // rsq(eps) is uniform: readfirstlane keeps it in a scalar register wherever
             // the compiler hoists it to

@@ -16,6 +16,19 @@ constexpr int kMaxLds = 163840;
 // Rollback-window layouts.
 enum WinLayout { kDense = 0, kRows = 1, kRowsT = 2 };
 
+// Per-head L2 geometry shared by the kernels that normalise q|k.  A head of head_lanes
+// lanes (head_dim / kChannelsPerLane) that is a power of two tiles every 256-channel
+// wavefront, and the channel blocks are uniform: block b starts at channel b * 256.  A
+// head of any other size would straddle wavefronts, so there the q|k channels go in
+// qk_blocks blocks of qk_block_ch channels (a whole number of heads, at most 256, the
+// last block possibly shorter), and the channels from qk on in 256-channel blocks after
+// them.  qk_blocks == 0 selects the uniform blocks.
+struct HeadBlocks {
+    int32_t head_lanes;        // lanes per head (head_dim / kChannelsPerLane)
+    int32_t qk_blocks;         // blocks of whole heads; 0: uniform 256-channel blocks
+    int32_t qk_block_ch;       // channels per such block
+};
+
 // Kernel arguments, by value.  Strides are in elements.
 struct KernelArgs {
     const void *x;
@@ -31,13 +44,15 @@ struct KernelArgs {
     int64_t x_seq, x_tok, out_seq, out_tok, state_slot, win_slot;
     int32_t n_seq, T, d_inner, qk, n_slots, state_len;
     int32_t channel_blocks;    // workgroups per row
-    int32_t head_lanes_log2;   // log2(lanes per L2 head); unused when qk == 0
+    int32_t head_lanes_log2;   // log2(lanes per L2 head), -1 when that is not a power of
+                               // two; unused when qk == 0
     float eps;
     int32_t token_chunks;      // token-split verify: workgroups per (row, channel block)
     int64_t state_col;         // 0: conv_state channel-major; else time-major column stride
     int32_t slot_first;        // read the slot before any vector load (padded rows load nothing)
     int32_t xcd_remap;         // work index from xcd_linear(blockIdx): a row's blocks on one XCD
     int32_t store_cached;      // time-major builds: stores with the default cache policy
+    HeadBlocks heads;          // L2 head size and the channel blocks of q|k
 };
 
 // A launch of more wavefronts than the chip holds at once (256 CUs x 4 SIMDs x 5) runs
@@ -86,6 +101,8 @@ struct Plan {
     int64_t workgroups;
     int lds_bytes;
     int head_lanes;
+    int hl_log2;               // log2(head_lanes), -1 when not a power of two
+    HeadBlocks heads;
     int waves_per_group;       // 1, or kLineGroupWaves for the line-aligned build
 };
 
@@ -127,8 +144,9 @@ struct L2Args {
     void *x;
     int64_t row_stride;
     int64_t n_rows;
-    int32_t qk, qk_blocks, head_lanes_log2;
+    int32_t qk, qk_blocks, head_lanes_log2;   // qk_blocks: channel blocks per row
     float eps;
+    HeadBlocks heads;          // as in KernelArgs (uniform: qk_blocks == 0)
 };
 // Token rows per wavefront of the separate L2.  On the prefill batch (12.4k rows of
 // 4096 q|k channels) 1, 2, 4 and 8 rows measured 44.4, 35.6, 38.5 and 41.8 us.

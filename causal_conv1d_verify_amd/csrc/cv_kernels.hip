@@ -10,7 +10,8 @@
 // design of it.  The op moves ~3 bytes per flop, so the design is about HBM:
 //
 //  * One 64-lane wavefront per workgroup, 4 channels per lane, 256 channels per
-//    wavefront; the 1-D grid is n_seq * ceil(d_inner / 256) workgroups.  (256-channel
+//    wavefront; the 1-D grid is n_seq * ceil(d_inner / 256) workgroups (with heads that
+//    do not divide 256 channels, the q|k blocks hold whole heads instead).  (256-channel
 //    blocks stream measurably faster on MI355X than 512-channel ones for this traffic
 //    mix: twice the wavefronts keep more requests in flight.)  The line-aligned 16-token
 //    build groups 4 such wavefronts over 1024 channels, so that the store ranges they
@@ -35,7 +36,10 @@
 //    to a correctly rounded fp32 evaluation of that order.
 //  * L2: a head of H channels spans H/4 lanes; its sum of squares is a butterfly with
 //    DPP inside 16-lane rows (quad_perm, row_half_mirror, row_mirror) and gfx950 lane
-//    swaps (permlane16/32) beyond; every lane of a head ends with the same sum.
+//    swaps (permlane16/32) beyond; every lane of a head ends with the same sum.  A head
+//    whose lane count is not a power of two would straddle wavefronts: there the q|k
+//    channels go in blocks of whole heads (block_first) and each head's sum is a
+//    segmented scan across its lanes (group_sums_any).
 //  * Windows and conv_state move as bit patterns; only the conv reads them as floats.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -123,7 +127,10 @@ __device__ __forceinline__ void verify_body(const KernelArgs &p) {
     const int wave = LA ? __builtin_amdgcn_readfirstlane(tid / kWave) : 0;
     const unsigned bid = p.xcd_remap ? xcd_linear(blockIdx.x, gridDim.x) : blockIdx.x;
     const int r2 = (int)(bid / (unsigned)p.channel_blocks);
-    const int cbg = (int)(bid - (unsigned)r2 * (unsigned)p.channel_blocks) * RANGE;
+    const int blk = (int)(bid - (unsigned)r2 * (unsigned)p.channel_blocks);
+    // (the line-aligned build runs with uniform blocks only)
+    int cend = p.d_inner;                       // the end of this block's channels
+    const int cbg = LA ? blk * RANGE : block_first(p.heads, blk, p.qk, p.d_inner, cend);
     const int cb = cbg + wave * CHW;            // this wavefront's first channel
     // Tree verify on a small grid spreads a row's token chunks over p.token_chunks
     // wavefronts: each one builds the row's whole v tile (a token's ancestors may be
@@ -163,7 +170,7 @@ __device__ __forceinline__ void verify_body(const KernelArgs &p) {
     const int SL = p.state_len;
     // channels of this wavefront (none for the last wavefronts of a line-aligned
     // workgroup past d_inner: they take part in the workgroup's exchanges only)
-    const int nch = max(0, min(CHW, p.d_inner - cb));
+    const int nch = max(0, min(CHW, cend - cb));
     const int nchg = min(RANGE, p.d_inner - cbg);   // channels of the workgroup
     const bool on = lane * CPL < nch;
     const uint32_t laneV = on ? (uint32_t)(lane * VB) : kOffLane;
@@ -461,7 +468,7 @@ __device__ __forceinline__ void verify_body(const KernelArgs &p) {
     // the memory pipeline is still full of other wavefronts' traffic, a wavefront that
     // stores first would stall at its stores with its arithmetic still ahead of it.
     const bool wave_l2 = cb < p.qk;    // uniform: this wavefront holds q|k channels
-    const bool lane_l2 = lane * CPL + cb < p.qk;
+    const bool lane_l2 = on && lane * CPL + cb < p.qk;
     const rsrc_t o_r = make_rsrc((char *)p.out + (orow + cb) * XB,
                                  (uint32_t)(((int64_t)(T - 1) * p.out_tok + nch) * XB));
     // Line-aligned build: N contiguous ranges of nb <= NW * kWave * U bytes each, range i
@@ -602,7 +609,7 @@ __device__ __forceinline__ void verify_body(const KernelArgs &p) {
                 y[g][ch] = acc;
             }
         silu_rows_checked<G>(y);
-        if (wave_l2) head_l2<G>(y, lane_l2, p.head_lanes_log2, p.eps);
+        if (wave_l2) head_l2<G>(y, lane_l2, p.head_lanes_log2, p.heads.head_lanes, p.eps);
         after_math();
         // line-aligned: the chunk's out goes through one of two LDS buffers (alternate
         // chunks), so one barrier per chunk orders both the hand-off and the reuse

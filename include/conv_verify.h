@@ -77,8 +77,12 @@
  *  - Alignment (else CV_ENOTSUP): every pointer 16-byte aligned; d_inner, the x/out
  *    strides multiples of 16/sizeof(x element) (8 for bf16, 4 for fp32);
  *    state_slot_stride, state_col_stride and win_slot_stride multiples of 16 bytes;
- *    head_dim one of
- *    4, 8, 16, 32, 64, 128, 256 (a head is reduced inside one 256-channel wavefront).
+ *    a head is reduced inside one wavefront: head_dim a multiple of 4 up to 256.  A
+ *    head_dim that divides 256 (4, 8, ..., 256) tiles the 256-channel wavefronts; any
+ *    other (12, 96, 192, ...) makes the q|k channels go in blocks of k whole heads, k
+ *    the largest with k * head_dim <= 256 and a multiple of 16/min(sizeof(x element),
+ *    sizeof(state element)), followed by 256-channel blocks from qk_channels on, so
+ *    qk_channels must be such a multiple too (CV_LAUNCH_HEAD_BLOCKS).
  *  - LDS (else CV_ENOTSUP): with a channel-major conv_state, a 256-channel wavefront
  *    stages its [256, state_len] state region (and its weights, its window tiles) in
  *    LDS, at most 160 KiB (all of a gfx950 compute unit's): state_len up to 160 fp32 /
@@ -110,8 +114,10 @@ extern "C" {
 #endif
 
 /* 5: conv_verify_debug_count; launch info may report 4-wavefront workgroups
- *    (CV_LAUNCH_LINE_ALIGNED, threads 256). */
-#define CONV_VERIFY_ABI_VERSION 5
+ *    (CV_LAUNCH_LINE_ALIGNED, threads 256).
+ * 6: heads whose lane count is not a power of two (head_dim 12, 96, 192, ...), with
+ *    CV_LAUNCH_HEAD_BLOCKS. */
+#define CONV_VERIFY_ABI_VERSION 6
 
 /* Only the entry points below are exported from the shared library. */
 #define CV_API __attribute__((visibility("default")))
@@ -144,8 +150,8 @@ typedef struct cv_shape {
     int32_t d_inner;      /* channels, >= 0 (0: nothing to do)                              */
     int32_t d_conv;       /* conv width D, 2..4                                             */
     int32_t qk_channels;  /* leading channels normalised per head, 0..d_inner; 0 = no L2    */
-    int32_t head_dim;     /* channels per L2 head: qk_channels % head_dim == 0 and
-                             head_dim / 4 a power of two <= 64 (4 channels per lane)        */
+    int32_t head_dim;     /* channels per L2 head: qk_channels % head_dim == 0, head_dim a
+                             multiple of 4 (channels per lane) and <= 256; see Alignment   */
     float l2_eps;         /* >= 0 and finite                                                */
     int32_t x_dtype;      /* cv_dtype_t of x, weight, bias and out                          */
     int32_t state_dtype;  /* cv_dtype_t of conv_state and the windows.  Supported pairs
@@ -272,7 +278,8 @@ CV_API int conv_prefill(const cv_shape_t *shape, const void *x, const void *weig
  * (row r at x + r*row_stride, channel stride 1) and each head of head_dim channels in
  * [0, qk_channels): y <- y / sqrt(sum_head y^2 + l2_eps) in fp32, rounded to the x
  * dtype.  Channels >= qk_channels are not touched.  Uses shape fields d_inner,
- * qk_channels, head_dim, l2_eps, x_dtype.  CV_ENOTSUP if 2 consecutive rows span more
+ * qk_channels, head_dim, l2_eps, x_dtype (head_dim as for the verify, its blocks of whole
+ * heads a multiple of 16/sizeof(x element)).  CV_ENOTSUP if 2 consecutive rows span more
  * than 2 GiB (a wavefront takes 2 rows).
  */
 CV_API int conv_qk_l2norm(const cv_shape_t *shape, int64_t n_rows, int64_t row_stride, void *x,
@@ -285,7 +292,8 @@ typedef struct cv_launch_info {
     int64_t workgroups;        /* 1-D grid: n_seq * channel_blocks * token_chunks         */
     int32_t threads;           /* per workgroup: one 64-lane wavefront, or 4 (LINE_ALIGNED) */
     int32_t channel_blocks;    /* workgroups per row: ceil(d_inner / (channels_per_wave *  */
-                               /* threads / 64))                                           */
+                               /* threads / 64)); with HEAD_BLOCKS the q|k blocks of whole */
+                               /* heads, then ceil((d_inner - qk_channels) / 256)          */
     int32_t channels_per_wave; /* 64 lanes * channels per lane                             */
     int32_t channels_per_lane; /* 16 bytes of x per lane per token                         */
     int32_t token_bucket;      /* compile-time tokens per workgroup (>= T unless split)    */
@@ -309,11 +317,15 @@ typedef struct cv_launch_info {
  *                     line-aligned build with a channel-major conv_state)
  *   LINE_ALIGNED      workgroups of 4 wavefronts over 1024 channels, whose store ranges
  *                     leave through LDS cut at 128-byte lines (bf16, time-major
- *                     conv_state, dedup rows, T 16, no token split) */
+ *                     conv_state, dedup rows, T 16, no token split)
+ *   HEAD_BLOCKS       head_dim does not divide 256: the q|k channels go in blocks of
+ *                     whole heads (see Alignment) and each head is summed by a segmented
+ *                     scan across its lanes */
 #define CV_LAUNCH_STATE_TIME_MAJOR 1
 #define CV_LAUNCH_SLOT_FIRST 2
 #define CV_LAUNCH_XCD_ORDER 4
 #define CV_LAUNCH_LINE_ALIGNED 8
+#define CV_LAUNCH_HEAD_BLOCKS 16
 
 /* variant: a cv_layout_t, or CV_VARIANT_TREE for conv_verify_update_tree.  Returns
  * CV_OK or an error code. */

@@ -45,8 +45,13 @@ int main(void) {
     bad.T = 33;
     expect("T = 33", conv_verify_describe(CV_WIN_ROWS, &bad, &info), CV_ENOTSUP);
     bad = s;
-    bad.head_dim = 96; bad.qk_channels = 960;
-    expect("head_dim 96", conv_verify_describe(CV_WIN_ROWS, &bad, &info), CV_ENOTSUP);
+    bad.head_dim = 132; bad.qk_channels = 396;   /* no block of whole heads is 16-byte sized */
+    expect("head_dim 132", conv_verify_describe(CV_WIN_ROWS, &bad, &info), CV_ENOTSUP);
+    bad = s;
+    bad.head_dim = 96; bad.qk_channels = 960;    /* blocks of 2 heads, then 256-channel blocks */
+    expect("head_dim 96", conv_verify_describe(CV_WIN_ROWS, &bad, &info), CV_OK);
+    expect("  q|k in blocks of whole heads", (info.flags & CV_LAUNCH_HEAD_BLOCKS) != 0, 1);
+    expect("  5 + 37 channel blocks", info.channel_blocks, 5 + 37);
     /* conv_state stored time-major: columns of >= d_inner elements, no state region in LDS */
     bad = s;
     bad.state_col_stride = 10240 - 8;

@@ -87,6 +87,27 @@ static void fixed_cases() {
     expect("headline: head lanes log2", kargs().head_lanes_log2, 5);
     expect("headline: channel blocks", kargs().channel_blocks, 40);
 
+    // heads of 96 channels (24 lanes): q|k in blocks of 2 whole heads (192 channels), then
+    // 256-channel blocks from qk on; the segmented head sums (head_lanes_log2 -1)
+    s = shape(128, 8, 10240, 96 * 40, 3, 0, CV_WIN_ROWS);
+    s.head_dim = 96;
+    expect("heads 96: rc", conv_verify_update_dedup(&s, A, A, A, A, I, I, A, A, nullptr), CV_OK);
+    expect("heads 96: grid", g_stub_launch.grid_x, 128 * (20 + 25));
+    expect("heads 96: head lanes log2", kargs().head_lanes_log2, -1);
+    expect("heads 96: head lanes", kargs().heads.head_lanes, 24);
+    expect("heads 96: q|k blocks", kargs().heads.qk_blocks, 20);
+    expect("heads 96: q|k block channels", kargs().heads.qk_block_ch, 192);
+    // the same at T 16 with a time-major state: not the line-aligned build
+    s = shape(512, 16, 10240, 96 * 40, 18, 10240, CV_WIN_ROWS);
+    s.head_dim = 96;
+    expect("heads 96 T16 tm: rc", conv_verify_update_dedup(&s, A, A, A, A, I, I, A, A, nullptr), CV_OK);
+    expect("heads 96 T16 tm: block", g_stub_launch.block_x, 64);
+    expect("heads 96 T16 tm: grid", g_stub_launch.grid_x, 512 * 45);
+    // power-of-two heads keep the uniform blocks
+    s = shape(128, 8, 10240, 4096, 3, 0, CV_WIN_ROWS);
+    expect("heads 128: rc", conv_verify_update_dedup(&s, A, A, A, A, I, I, A, A, nullptr), CV_OK);
+    expect("heads 128: uniform blocks", kargs().heads.qk_blocks, 0);
+
     // the stress problem, conv_state time-major: 512 rows x T 16, 18-column state: the
     // line-aligned build (4-wavefront workgroups over 1024 channels)
     s = shape(512, 16, 10240, 4096, 18, 10240, CV_WIN_ROWS);
@@ -230,7 +251,9 @@ static void refusals() {
         {"n_seq -1", [](cv_shape_t *s) { s->n_seq = -1; }, CV_EINVAL},
         {"d_inner not a multiple of 8", [](cv_shape_t *s) { s->d_inner = 1028; }, CV_ENOTSUP},
         {"qk % head_dim", [](cv_shape_t *s) { s->qk_channels = 1000; }, CV_EINVAL},
-        {"head_dim 96", [](cv_shape_t *s) { s->head_dim = 96; s->qk_channels = 960; }, CV_ENOTSUP},
+        {"head_dim 132", [](cv_shape_t *s) { s->head_dim = 132; s->qk_channels = 396; }, CV_ENOTSUP},
+        {"head_dim 12, qk 36", [](cv_shape_t *s) { s->head_dim = 12; s->qk_channels = 36; }, CV_ENOTSUP},
+        {"head_dim 260", [](cv_shape_t *s) { s->head_dim = 260; s->qk_channels = 520; }, CV_ENOTSUP},
         {"qk > d", [](cv_shape_t *s) { s->qk_channels = s->d_inner + 128; }, CV_EINVAL},
         {"eps NaN", [](cv_shape_t *s) { s->l2_eps = __builtin_nanf(""); }, CV_EINVAL},
         {"eps < 0", [](cv_shape_t *s) { s->l2_eps = -1.0f; }, CV_EINVAL},
@@ -388,6 +411,7 @@ static void fuzz(int iters) {
                          (g_stub_launch.lds < (size_t)(128 + 1024 * s.state_len * 2 + 16384) ||
                           g_stub_launch.lds * 3 > (size_t)cvimpl::kMaxLds)) ||
                         layout != CV_WIN_ROWS || which > 1 ||
+                        (s.qk_channels > 0 && ((s.head_dim / 4) & (s.head_dim / 4 - 1))) ||
                         g_stub_launch.grid_x != (uint64_t)s.n_seq * ((d + 1023) / 1024) ||
                         g_stub_launch.lds < (size_t)(128 + 1024 * (s.T + s.d_conv - 2) * 2))) {
             std::printf("fuzz %d: line-aligned launch of an unexpected shape  MISMATCH\n", it);

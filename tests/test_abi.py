@@ -122,9 +122,13 @@ BAD_SHAPES = [
     ("qk%head", dict(qk_channels=520, head_dim=128), EINVAL),
     ("head<=0", dict(head_dim=0), EINVAL),
     ("head%4", dict(qk_channels=6 * 20, head_dim=6), ENOTSUP),
-    ("head_lanes_3", dict(qk_channels=12 * 20, head_dim=12), ENOTSUP),
-    ("head_lanes_not_pow2", dict(qk_channels=96 * 5, head_dim=96), ENOTSUP),
+    # a head that does not divide 256 channels: blocks of k whole heads, k * head_dim a
+    # multiple of 8 (bf16) and at most 256 - none for 132 channels (33 lanes) - and q|k's
+    # end (where the 256-channel blocks start) a multiple of 8 too
+    ("head_block_none", dict(qk_channels=132 * 3, head_dim=132), ENOTSUP),
+    ("head_blocks_qk%8", dict(qk_channels=12 * 3, head_dim=12), ENOTSUP),
     ("head_lanes>64", dict(qk_channels=1024, head_dim=512), ENOTSUP),
+    ("head_dim>256", dict(qk_channels=520, head_dim=260), ENOTSUP),
     ("eps<0", dict(l2_eps=-1.0), EINVAL),
     ("eps_nan", dict(l2_eps=float("nan")), EINVAL),
     ("eps_inf", dict(l2_eps=float("inf")), EINVAL),
@@ -335,7 +339,7 @@ rc_of("prefill_tok_overlap", lib.conv_prefill(ctypes.byref(shape(T=100, x_tok_st
                                               A, A, None, A, None, A, None, A, None))
 rc_of("prefill_empty_ok", lib.conv_prefill(ctypes.byref(shape(n_seq=0, T=100)), *([None] * 9)))
 rc_of("l2_null_x", lib.conv_qk_l2norm(ctypes.byref(s), 4, 1024, None, None))
-rc_of("l2_bad_head", lib.conv_qk_l2norm(ctypes.byref(shape(head_dim=96, qk_channels=960)), 4, 1024, A, None))
+rc_of("l2_bad_head", lib.conv_qk_l2norm(ctypes.byref(shape(head_dim=132, qk_channels=396)), 4, 1024, A, None))
 rc_of("l2_short_stride", lib.conv_qk_l2norm(ctypes.byref(s), 4, 256, A, None))
 rc_of("l2_no_rows_ok", lib.conv_qk_l2norm(ctypes.byref(s), 0, 1024, None, None))
 print(json.dumps(res))
@@ -492,6 +496,60 @@ def test_launch_flags_edges():
     # a small grid takes the token split instead
     wg, ch, f = _flags(1, **tm16(8, 10200))
     assert ch == 4 and f & L.CV_LAUNCH_LINE_ALIGNED == 0
+
+
+def _head_block(head_dim, align):
+    """Channels per q|k block for a head that does not divide 256: the most whole heads
+    within 256 channels whose channel count is a multiple of align."""
+    k = 256 // head_dim
+    while k and (k * head_dim) % align:
+        k -= 1
+    return k * head_dim
+
+
+@pytest.mark.parametrize("head_dim", [12, 20, 24, 48, 80, 96, 112, 160, 192, 240, 252])
+@pytest.mark.parametrize("dtypes", ["bf16", "f32", "bf16_f32"])
+def test_head_blocks_geometry(head_dim, dtypes):
+    """Heads that do not divide 256 channels: the q|k channels go in blocks of whole heads
+    (then 256-channel blocks from qk on), the grid covers every block once, and no such
+    launch takes the line-aligned build (whose workgroups span 1024 channels)."""
+    L = lib_mod
+    xd, sd = {"bf16": (L.CV_BF16, L.CV_BF16), "f32": (L.CV_F32, L.CV_F32),
+              "bf16_f32": (L.CV_BF16, L.CV_F32)}[dtypes]
+    align = 16 // min(2 if xd == L.CV_BF16 else 4, 2 if sd == L.CV_BF16 else 4)
+    heads = 8 if head_dim % 8 == 0 or align == 4 else 6
+    qk = heads * head_dim
+    d = qk + 1000 + (align - (qk + 1000) % align) % align
+    for layout, T, tm in ((1, 16, 0), (1, 16, d), (0, 8, 0), (2, 3, d), (1, 1, 0)):
+        win = d * (T + 2) if layout else T * d * 3
+        s = shape(n_seq=37, n_slots=37, T=T, d_inner=d, qk_channels=qk, head_dim=head_dim,
+                  x_dtype=xd, state_dtype=sd, x_seq_stride=T * d, x_tok_stride=d,
+                  out_seq_stride=T * d, out_tok_stride=d, state_len=3, state_slot_stride=3 * d,
+                  state_col_stride=tm, win_slot_stride=win)
+        rc, info, detail = describe(layout, s)
+        ch = _head_block(head_dim, align)
+        if ch == 0:
+            assert rc == ENOTSUP, (rc, detail)
+            return
+        assert rc == 0, detail
+        assert info.flags & L.CV_LAUNCH_HEAD_BLOCKS
+        assert info.flags & L.CV_LAUNCH_LINE_ALIGNED == 0 and info.threads == 64
+        assert info.head_lanes * 4 == head_dim
+        assert info.channel_blocks == -(-qk // ch) + -(-(d - qk) // 256)
+        assert info.workgroups == 37 * info.channel_blocks * info.token_chunks
+    # the separate L2 takes the same blocks of whole heads (x's element size only)
+    lib = _lib()
+    rc = lib.conv_qk_l2norm(ctypes.byref(shape(d_inner=d, qk_channels=qk, head_dim=head_dim, x_dtype=xd,
+                                               state_dtype=xd)), 0, d, None, None)
+    assert rc == 0, lib.conv_verify_last_error().decode()
+
+
+def test_power_of_two_heads_keep_uniform_blocks():
+    for hd in (4, 8, 16, 32, 64, 128, 256):
+        rc, info, detail = describe(1, shape(qk_channels=hd * 2, head_dim=hd))
+        assert rc == 0, detail
+        assert info.flags & lib_mod.CV_LAUNCH_HEAD_BLOCKS == 0
+        assert info.channel_blocks == 4 and info.head_lanes * 4 == hd
 
 
 def test_line_aligned_geometry():

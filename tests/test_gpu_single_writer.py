@@ -14,8 +14,8 @@ conv_state allocation.  For each launch:
 The problems are small versions of the bench shapes, covering every launch kind: chain
 verify in the three window layouts with both conv_state orders (and padded rows, offsets,
 a partial channel block), packed rows, the token splits, the 5-wavefront 16-token build,
-the line-aligned build, tree verify, the restore from each layout, the prefill and the
-separate L2.
+the line-aligned build, heads that do not divide 256 channels (blocks of whole heads),
+tree verify, the restore from each layout, the prefill and the separate L2.
 """
 
 import numpy as np
@@ -92,6 +92,11 @@ VERIFY += [
       state_tm=True, state_len=17),
     c("sw_line_aligned_cm", n_seq=130, d_inner=1032, qk_channels=512, head_dim=128, T=16,
       layout="dedup", accept_offsets=True, permute_slots=True, pad_frac=0.2, state_len=18),
+    # heads of 96 channels: q|k in blocks of two whole heads, then 256-channel blocks
+    c("sw_heads96_dedup", n_seq=6, d_inner=1032, qk_channels=480, head_dim=96, T=8,
+      layout="dedup", accept_offsets=True, permute_slots=True, pad_frac=0.2, state_len=12),
+    c("sw_heads192_dense_K17_split", n_seq=2, d_inner=1032, qk_channels=768, head_dim=192, T=17,
+      layout="dense", accept_offsets=True, state_len=20),
     # token splits: the dense chain split kernel (small grid, K 17) and the rows split
     c("sw_dense_K17_split", n_seq=2, d_inner=1024, qk_channels=512, head_dim=128, T=17,
       layout="dense", accept_offsets=True, state_len=20),
