@@ -212,7 +212,8 @@ __device__ __forceinline__ float group_sum_sel(float v, int hl_log2) {
 // Per-head L2 of G token rows held as y[g][channel], the lane's kChannelsPerLane
 // channels: y <- y / sqrt(S + eps), S = sum_head y^2, on lanes with lane_l2 set (a head
 // is the aligned group of 2^hl_log2 lanes, or with hl_log2 < 0 a group of hl lanes as in
-// group_sums_any); other lanes keep y.  All lanes active.
+// group_sums_any); other lanes keep y.  All lanes active.  ANY_HEAD false leaves the second
+// form out of a build that only ever runs with power-of-two heads.
 //
 // S runs in fp32 (any reduction order) with v_rsq_f32.  That is accurate while
 // S + eps <= 2^127 (no partial sum overflows) and either S >= 2^-100 (squares below
@@ -229,7 +230,7 @@ __device__ __forceinline__ float group_sum_sel(float v, int hl_log2) {
 // below 2^-256 (every value subnormal), whose scale exceeds fp32's range.  NaN and
 // infinities give what y / sqrt(S + eps) gives.  The stages of the second sum are
 // selected rather than branched on, so the rare path costs the common one no registers.
-template <int G>
+template <int G, bool ANY_HEAD = true>
 __device__ __forceinline__ void head_l2(float (&y)[G][kChannelsPerLane], bool lane_l2,
                                         int hl_log2, int hl, float eps) {
     constexpr int CPL = kChannelsPerLane;
@@ -240,7 +241,7 @@ __device__ __forceinline__ void head_l2(float (&y)[G][kChannelsPerLane], bool la
 #pragma unroll
         for (int ch = 0; ch < CPL; ++ch) ss[g] = __builtin_fmaf(y[g][ch], y[g][ch], ss[g]);
     }
-    if (hl_log2 >= 0)
+    if (!ANY_HEAD || hl_log2 >= 0)
         group_sums<G>(ss, hl_log2);
     else
         group_sums_any<G>(ss, hl);
@@ -271,7 +272,7 @@ __device__ __forceinline__ void head_l2(float (&y)[G][kChannelsPerLane], bool la
                 const float u = y[g][ch] * f;
                 s = __builtin_fmaf(u, u, s);
             }
-            if (hl_log2 >= 0) {
+            if (!ANY_HEAD || hl_log2 >= 0) {
                 s = group_sum_sel(s, hl_log2);
             } else {
                 float one[1] = {s};
