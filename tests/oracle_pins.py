@@ -106,6 +106,10 @@ def _cases():
     yield c("strided_x", n_seq=3, T=3, d_inner=120, qk_channels=64, head_dim=16,
             x_tok_stride=136, layout="dedup")
     yield c("t17", n_seq=2, T=17, d_inner=64, qk_channels=32, head_dim=16)
+    # heads of 12 and 24 channels (not dividing a power-of-two channel block)
+    yield c("heads12", n_seq=2, T=3, d_inner=72, qk_channels=48, head_dim=12, layout="dedup")
+    yield c("heads24_f32", n_seq=2, T=2, d_inner=80, qk_channels=72, head_dim=24,
+            x_dtype="f32", state_dtype="f32")
 
 
 def pin_brute_dyadic(lib):
@@ -168,19 +172,21 @@ def pin_one_hot_taps(lib):
 
 
 def pin_l2_closed_form(lib):
-    """After L2 each q|k head has sum y^2 = S/(S+eps); V channels keep silu(pre)."""
-    for eps in (1e-6, 0.5, 40.0):
-        wl = workloads.custom("l2", n_seq=2, d_inner=192, qk_channels=128, head_dim=32,
+    """After L2 each q|k head has sum y^2 = S/(S+eps); V channels keep silu(pre).  Heads
+    of 32 channels (4 heads) and of 24 (5 heads)."""
+    for eps, hd, nh in ((1e-6, 32, 4), (0.5, 32, 4), (40.0, 32, 4), (1e-6, 24, 5), (40.0, 24, 5)):
+        qk = hd * nh
+        wl = workloads.custom("l2", n_seq=2, d_inner=192, qk_channels=qk, head_dim=hd,
                               T=3, l2_eps=eps)
         inp = workloads.make_inputs(wl)
         r = _run(inp, lib)
         pre = r["pre"].astype(np.float64)
         s = brute.silu(pre)
         y = r["y"]
-        assert np.allclose(y[:, :, 128:], s[:, :, 128:], rtol=1e-13, atol=1e-300), "V touched"
-        h = s[:, :, :128].reshape(2, 3, 4, 32)
+        assert np.allclose(y[:, :, qk:], s[:, :, qk:], rtol=1e-13, atol=1e-300), "V touched"
+        h = s[:, :, :qk].reshape(2, 3, nh, hd)
         S = (h * h).sum(-1)
-        yh = y[:, :, :128].reshape(2, 3, 4, 32)
+        yh = y[:, :, :qk].reshape(2, 3, nh, hd)
         got = (yh * yh).sum(-1)
         assert np.allclose(got, S / (S + np.float64(np.float32(eps))), rtol=1e-12), "L2 form"
         # direction is unchanged by the normalisation
