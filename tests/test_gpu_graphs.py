@@ -63,6 +63,9 @@ CASES = [
     workloads.custom("g_line_aligned_cm", n_seq=130, d_inner=1032, qk_channels=512,
                      head_dim=128, T=16, layout="dedup", accept_offsets=True, permute_slots=True,
                      pad_frac=0.2, state_len=18),
+    # heads of 96 channels (q|k in blocks of whole heads, segmented head sums)
+    workloads.custom("g_heads96", n_seq=6, d_inner=1032, qk_channels=480, head_dim=96, T=8,
+                     layout="dedup", accept_offsets=True, permute_slots=True, pad_frac=0.2),
 ]
 
 
