@@ -376,8 +376,15 @@ __device__ __forceinline__ void gload(rsrc_t r, uint32_t voff, uint32_t soff, ui
 template <int NB, int POL = kNT>
 __device__ __forceinline__ void gstore(rsrc_t r, uint32_t voff, uint32_t soff, const uint32_t *s) {
     if constexpr (NB == 16) {
+        // The offset goes into the lane offset, the scalar offset stays 0: after a store of
+        // more than 8 bytes whose scalar offset is an SGPR the compiler puts no wait state
+        // before a VALU instruction that overwrites the store's data registers, and on
+        // gfx950 the store then wrote that instruction's result for some lanes (the fourth
+        // dword of lanes 12-15 of each 16-lane row, now and then: the widened fp32
+        // columns of the time-major commit).  With an inline-constant scalar offset the
+        // compiler inserts the wait.  kOffLane + soff stays out of range (soff < 2^31).
         const u32x4 v = {s[0], s[1], s[2], s[3]};
-        __builtin_amdgcn_raw_buffer_store_b128(v, raw(r), (int)voff, (int)soff, POL);
+        __builtin_amdgcn_raw_buffer_store_b128(v, raw(r), (int)(voff + soff), 0, POL);
     } else {
         static_assert(NB == 8, "8- or 16-byte accesses");
         const u32x2 v = {s[0], s[1]};

@@ -568,6 +568,24 @@ def test_slot_first_edge(wl):
     _verify_case(wl)
 
 
+# bf16 x with a time-major fp32 state: the commit widens x into 16-byte fp32 columns and
+# stores them back to back.  A 16-byte store whose scalar offset was an SGPR, followed at
+# once by the widening of the next column into the same registers, wrote that next column
+# into the fourth dword of some lanes now and then (the compiler adds no wait state for that
+# form); every 16-byte store now takes its offset in the lane offset.  Several hundred rows
+# per launch, in each layout, with packed rows and with full ones.
+STORE_WIDE = [c(f"tm_f32_commit_{layout}{'_packed' if packed else ''}", n_seq=300, d_inner=2104,
+                qk_channels=1536, head_dim=256, T=9, state_dtype="f32", layout=layout,
+                accept_offsets=True, varlen=packed, min_len=0, extra_slots=1, state_tm=True,
+                state_len=12, seed=workloads.BASE_SEED + 7700 + 2 * i + packed)
+              for i, layout in enumerate(("dense", "dedup", "dedup_t")) for packed in (False, True)]
+
+
+@pytest.mark.parametrize("wl", STORE_WIDE, ids=[w.name for w in STORE_WIDE])
+def test_time_major_fp32_commit_stores(wl):
+    _verify_case(wl)
+
+
 # q|k ending inside a wavefront: lanes of one wavefront split between L2 heads and V
 # channels, for several head sizes, both state orders and layouts.
 QK_EDGE = [c(f"qk{qk}_h{hd}_{layout}{'_tm' if tm else ''}", n_seq=3, d_inner=1032, qk_channels=qk,
