@@ -584,11 +584,13 @@ def pin_prefill_torch(lib):
 
 def pin_separate_l2(lib):
     """The separate L2 pass: every q|k head ends with sum y^2 = S/(S+eps) (S the head's
-    sum of squares before), V channels keep their bits, for fp32 and bf16 rows and a
-    large eps that makes the eps term visible."""
+    sum of squares before), V channels keep their bits, for fp32 and bf16 rows, a large eps
+    that makes the eps term visible, and heads of 8, 12 and 24 channels."""
     rng = np.random.default_rng(workloads.BASE_SEED + 2600)
-    for xd, eps, tol in (("f32", 1e-6, 1e-6), ("f32", 10.0, 1e-6), ("bf16", 10.0, 2e-2)):
-        C, qk, hd, rows = 48, 32, 8, 5
+    for xd, eps, tol, hd in (("f32", 1e-6, 1e-6, 8), ("f32", 10.0, 1e-6, 8), ("bf16", 10.0, 2e-2, 8),
+                             ("f32", 10.0, 1e-6, 12), ("bf16", 10.0, 2e-2, 24)):
+        C, rows = 56, 5
+        qk = 48 if hd != 8 else 32
         x0 = workloads.to_storage(rng.standard_normal((rows, C + 8)).astype(np.float32), xd)
         x = x0.copy()
         oracle.l2norm(x, d_inner=C, qk_channels=qk, head_dim=hd, l2_eps=eps, x_dtype=xd, lib=lib)
